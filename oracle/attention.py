@@ -1,0 +1,275 @@
+"""Full-score-matrix float64 attention oracle (test infrastructure only).
+
+Definition followed (the forward the attention front end computes; see the
+mslk flash_attn interface.py page, `_flash_attn_fwd` docstring and argument
+checks, and the Blackwell backward page flash_bwd_sm100.py, where the
+probabilities are recomputed as exp2(S*scale*log2e - LSE*log2e), which fixes
+LSE as the natural-log log-sum-exp of the scaled scores):
+
+  for each batch b, query head h, query i:
+    g      = h // (Hq / Hkv)                  consecutive GQA grouping
+    s_ij   = scale * <q[b,i,h,:], k[b,j,g,:]>  for visible keys j
+    LSE_i  = log sum_j exp(s_ij)              natural log
+    O_i    = sum_j exp(s_ij - LSE_i) v[b,j,g,:]
+  a query with no visible key has O = 0 and LSE = -inf (the split-K page's
+  empty-input short-circuit; the sm_120 PR page's all-masked-row guard).
+
+Visible keys (interface page, mask normalization in `_flash_attn_fwd`; the
+backward page's causal/window block bounds, which offset by seqlen_k-seqlen_q):
+  off = Sk - Sq  (bottom-right alignment)
+  j visible iff 0 <= j < Sk
+             and (window_left  is None or j >= i + off - window_left)
+             and (window_right is None or j <= i + off + window_right)
+  causal forces window_right = 0; both window bounds are inclusive.
+
+Inputs are float64 arrays converted exactly from the same bf16 bit patterns the
+GPU reads. All arithmetic is float64.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ---------------------------------------------------------------- masks ----
+
+def normalize_window(causal: bool, window_left: Optional[int], window_right: Optional[int]):
+    """Returns (window_left, window_right) with None meaning unbounded.
+
+    Negative sizes are read as unbounded (the C ABI's encoding of None).
+    Causal forces window_right = 0 (interface page, `_flash_attn_fwd`).
+    """
+    wl = None if (window_left is None or window_left < 0) else int(window_left)
+    wr = None if (window_right is None or window_right < 0) else int(window_right)
+    if causal:
+        wr = 0
+    return wl, wr
+
+
+def visible_mask(seqlen_q: int, seqlen_k: int, causal: bool = False,
+                 window_left: Optional[int] = None,
+                 window_right: Optional[int] = None) -> np.ndarray:
+    """Boolean (Sq, Sk) matrix of visible (query, key) pairs, bottom-right aligned."""
+    wl, wr = normalize_window(causal, window_left, window_right)
+    i = np.arange(seqlen_q, dtype=np.int64)[:, None]
+    j = np.arange(seqlen_k, dtype=np.int64)[None, :]
+    diag = i + (seqlen_k - seqlen_q)
+    vis = np.ones((seqlen_q, seqlen_k), dtype=bool)
+    if wl is not None:
+        vis &= j >= diag - wl
+    if wr is not None:
+        vis &= j <= diag + wr
+    return vis
+
+
+# ------------------------------------------------------------- one head ----
+
+def softmax_lse_rows(s: np.ndarray, vis: np.ndarray):
+    """Row-wise log-sum-exp and probabilities of masked scores.
+
+    s, vis: (n, Sk). Returns (P (n, Sk), LSE (n,)). Empty rows: P = 0, LSE = -inf.
+    """
+    s = np.where(vis, s, NEG_INF)
+    nonempty = vis.any(axis=1)
+    m = np.where(nonempty, s.max(axis=1, initial=NEG_INF), 0.0)
+    e = np.where(vis, np.exp(s - m[:, None]), 0.0)
+    lsum = e.sum(axis=1)
+    lse = np.full(s.shape[0], NEG_INF)
+    lse[nonempty] = m[nonempty] + np.log(lsum[nonempty])
+    p = np.zeros_like(e)
+    p[nonempty] = np.where(vis[nonempty], np.exp(s[nonempty] - lse[nonempty, None]), 0.0)
+    return p, lse
+
+
+def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                   vis: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Single head. q (Sq, D), k (Sk, D), v (Sk, Dv), vis (Sq, Sk) -> O (Sq, Dv), LSE (Sq,)."""
+    s = scale * (q @ k.T)
+    p, lse = softmax_lse_rows(s, vis)
+    return p @ v, lse
+
+
+# ------------------------------------------------------- dense / varlen ----
+
+def attention_dense(q, k, v, scale, causal=False, window_left=None, window_right=None):
+    """q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D) float64 -> O (B, Sq, Hq, Dv), LSE (B, Hq, Sq)."""
+    B, Sq, Hq, _ = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    assert Hq % Hkv == 0
+    r = Hq // Hkv
+    vis = visible_mask(Sq, Sk, causal, window_left, window_right)
+    out = np.zeros((B, Sq, Hq, v.shape[-1]))
+    lse = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // r
+            out[b, :, h], lse[b, h] = attention_head(q[b, :, h], k[b, :, g], v[b, :, g], scale, vis)
+    return out, lse
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
+                     window_left=None, window_right=None):
+    """Packed sequences. q (Tq, Hq, D), k/v (Tk, Hkv, D) -> O (Tq, Hq, Dv), LSE (Hq, Tq).
+
+    The LSE layout (num_heads, total_q) is the interface page's varlen layout.
+    """
+    Hq, Hkv = q.shape[1], k.shape[1]
+    r = Hq // Hkv
+    out = np.zeros((q.shape[0], Hq, v.shape[-1]))
+    lse = np.full((Hq, q.shape[0]), NEG_INF)
+    for b in range(len(cu_seqlens_q) - 1):
+        q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
+        if q1 == q0:
+            continue
+        vis = visible_mask(q1 - q0, k1 - k0, causal, window_left, window_right)
+        for h in range(Hq):
+            g = h // r
+            out[q0:q1, h], lse[h, q0:q1] = attention_head(q[q0:q1, h], k[k0:k1, g],
+                                                          v[k0:k1, g], scale, vis)
+    return out, lse
+
+
+def attention_rows(q_rows: np.ndarray, row_index: np.ndarray, k: np.ndarray, v: np.ndarray,
+                   scale: float, seqlen_q: int, causal=False, window_left=None,
+                   window_right=None):
+    """Selected query rows of one (sequence, head) problem, for sampling huge inputs.
+
+    q_rows (n, D) are the queries at positions row_index (n,) of a length-seqlen_q
+    query sequence; k (Sk, D), v (Sk, Dv) are that head's keys and values.
+    Returns O (n, Dv), LSE (n,), computed from the same definition row by row.
+    """
+    Sk = k.shape[0]
+    full = visible_mask(seqlen_q, Sk, causal, window_left, window_right)
+    vis = full[np.asarray(row_index, dtype=np.int64)]
+    return attention_head(q_rows, k, v, scale, vis)
+
+
+# ------------------------------------------------------------- split-KV ----
+
+def split_bounds(seqlen_k: int, num_splits: int) -> List[Tuple[int, int]]:
+    """Contiguous key ranges [s*c, min(Sk, (s+1)*c)) with c = ceil(Sk / num_splits).
+
+    The split-K page (triton_splitk.py, `FwOp.apply`) sizes splits as
+    ceil(Mk / split_k). Trailing ranges may be empty.
+    """
+    c = -(-seqlen_k // num_splits) if seqlen_k > 0 else 0
+    return [(min(seqlen_k, s * c), min(seqlen_k, (s + 1) * c)) for s in range(num_splits)]
+
+
+def attention_partials(q, k, v, scale, vis, bounds: Sequence[Tuple[int, int]]):
+    """Per-split (O_s, LSE_s) for one head: attention restricted to each key range.
+
+    q (n, D), k/v (Sk, D), vis (n, Sk). Returns O (S, n, Dv), LSE (S, n). An
+    empty range (or one with no visible key for a row) gives O = 0, LSE = -inf.
+    """
+    n = q.shape[0]
+    o_parts = np.zeros((len(bounds), n, v.shape[-1]))
+    lse_parts = np.full((len(bounds), n), NEG_INF)
+    for s, (a, b) in enumerate(bounds):
+        if b <= a:
+            continue
+        o_parts[s], lse_parts[s] = attention_head(q, k[a:b], v[a:b], scale, vis[:, a:b])
+    return o_parts, lse_parts
+
+
+def combine(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """LSE-weighted merge of split partials (interface page, `flash_attn_combine`;
+    split-K page, `merge_attentions`).
+
+    o_parts (S, ..., Dv), lse_parts (S, ...):
+      LSE = max_s LSE_s + log sum_s exp(LSE_s - max_s LSE_s)
+      O   = sum_s exp(LSE_s - LSE) O_s
+    A split with LSE_s = -inf contributes nothing; if all are -inf, O = 0 and
+    LSE = -inf.
+    """
+    m = lse_parts.max(axis=0)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - m_safe), 0.0)
+    total = w.sum(axis=0)
+    lse = np.full(m.shape, NEG_INF)
+    lse[finite] = m_safe[finite] + np.log(total[finite])
+    lse_safe = np.where(finite, lse, 0.0)
+    wn = np.where(np.isfinite(lse_parts), np.exp(lse_parts - lse_safe), 0.0)
+    out = (wn[..., None] * o_parts).sum(axis=0)
+    out[~finite] = 0.0
+    return out, lse
+
+
+# --------------------------------------------------------------- paged -----
+
+def paged_gather(cache: np.ndarray, page_table_row: np.ndarray, seqlen: int) -> np.ndarray:
+    """Contiguous (seqlen, Hkv, D) view of one sequence stored in a paged cache.
+
+    cache (num_pages, page_size, Hkv, D); token t of the sequence lives in page
+    page_table_row[t // page_size], slot t % page_size (interface page, the
+    page_table branch of `_flash_attn_fwd`).
+    """
+    page_size = cache.shape[1]
+    n_pages = -(-seqlen // page_size)
+    pages = [cache[int(page_table_row[p])] for p in range(n_pages)]
+    if not pages:
+        return np.zeros((0,) + cache.shape[2:])
+    return np.concatenate(pages, axis=0)[:seqlen]
+
+
+def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1,
+                 causal=False, window_left=None, window_right=None, heads=None):
+    """One query per sequence over a paged cache.
+
+    q (B, Hq, D) float64. Returns O (B, Hq, Dv), LSE (B, Hq), and the split
+    partials (S, B, Hq, Dv), (S, B, Hq) of the contiguous-range partition used
+    by split_bounds, combined with `combine` to form O and LSE. `heads` limits
+    the work to a subset of query heads (others are left at zero / -inf).
+    """
+    B, Hq, _ = q.shape
+    Hkv = k_cache.shape[2]
+    r = Hq // Hkv
+    heads = range(Hq) if heads is None else heads
+    o_parts = np.zeros((num_splits, B, Hq, v_cache.shape[-1]))
+    lse_parts = np.full((num_splits, B, Hq), NEG_INF)
+    for b in range(B):
+        sk = int(seqused_k[b])
+        kb = paged_gather(k_cache, page_table[b], sk)
+        vb = paged_gather(v_cache, page_table[b], sk)
+        vis = visible_mask(1, sk, causal, window_left, window_right)
+        bounds = split_bounds(sk, num_splits)
+        for h in heads:
+            g = h // r
+            o, l = attention_partials(q[b, h][None, :], kb[:, g], vb[:, g], scale, vis, bounds)
+            o_parts[:, b, h] = o[:, 0]
+            lse_parts[:, b, h] = l[:, 0]
+    out, lse = combine(o_parts, lse_parts)
+    return out, lse, o_parts, lse_parts
+
+
+# ------------------------------------------------------- accounting --------
+
+def visible_pairs(seqlen_q: int, seqlen_k: int, causal=False, window_left=None,
+                  window_right=None) -> int:
+    """Number of visible (query, key) pairs of one head (for FLOP accounting)."""
+    return int(visible_mask(seqlen_q, seqlen_k, causal, window_left, window_right).sum())
+
+
+def bf16_round_nearest_even(x: np.ndarray) -> np.ndarray:
+    """float64 -> nearest bf16 value (ties to even), returned as float64.
+
+    bf16 keeps 8 significant bits: with x = m * 2**e, 0.5 <= |m| < 1, the grid
+    spacing is 2**(e - 8). Scaling by a power of two is exact, so np.round
+    (half to even) on the scaled value rounds exactly. Used by tests to state
+    expected outputs at the output precision.
+    """
+    f = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(f)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
+def flops_causal_adjusted(head_dim: int, num_heads_q: int, pairs_per_head: int) -> float:
+    """4 * D * visible pairs * heads: two matmuls, two flops per multiply-add."""
+    return 4.0 * head_dim * num_heads_q * pairs_per_head
+

@@ -1,0 +1,375 @@
+"""Checks that pin the float64 oracle to facts outside itself.
+
+Each pin returns (ok: bool, detail: str) instead of asserting, so the same
+pins can be run against deliberately broken copies of the oracle (see
+test_oracle_mutants.py) to show that a plausible mistake fails at least one.
+
+What each pin rests on:
+  brute_*        an independent scalar-loop reading of the definition
+  one_key        softmax over one element: O = v0, LSE = s00 exactly
+  equal_keys     two equal scores: O = (v0+v1)/2, LSE = s + ln 2
+  zero_query     Q = 0 makes every visible score 0, so LSE = ln |J(i)| and
+                 O = mean of visible V rows; |J(i)| comes from a closed-form
+                 interval length, not from the oracle's mask
+  prob_sum       sum_j exp(s_ij - LSE_i) = 1
+  const_v        convexity: V rows all equal c => O = c
+  causal_row0    causal, Sq = Sk: query 0 sees key 0 only
+  gqa_as_mha     GQA equals MHA with each KV head repeated Hq/Hkv times
+  split_combine  combining split partials equals the unsplit result,
+                 including empty splits
+  paged          paged gather equals the contiguous layout
+  torch_sdpa     torch's float64 scaled_dot_product_attention on CPU, with
+                 an explicit boolean mask built from the closed-form interval
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle.attention as A
+import oracle.brute as BR
+
+TOL = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, tol=TOL):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.shape != b.shape:
+        return False, f"shape {a.shape} vs {b.shape}"
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    with np.errstate(invalid="ignore"):
+        diff = np.where(both_inf, 0.0, np.abs(a - b))
+    diff = np.where(np.isnan(diff), np.inf, diff)
+    m = float(diff.max(initial=0.0))
+    return m <= tol, f"max diff {m:.3e}"
+
+
+def interval_count(i, sq, sk, causal, wl, wr):
+    """|J(i)| from the closed-form interval [max(0, c - wl), min(sk - 1, c + wr)], c = i + sk - sq."""
+    c = i + sk - sq
+    right = 0 if causal else (None if wr is None or wr < 0 else wr)
+    left = None if wl is None or wl < 0 else wl
+    lo = 0 if left is None else max(0, c - left)
+    hi = sk - 1 if right is None else min(sk - 1, c + right)
+    return max(0, hi - lo + 1), lo, hi
+
+
+MASKS = [
+    dict(causal=False, window_left=None, window_right=None),
+    dict(causal=True, window_left=None, window_right=None),
+    dict(causal=False, window_left=2, window_right=1),
+    dict(causal=True, window_left=3, window_right=None),
+    dict(causal=False, window_left=0, window_right=0),
+    dict(causal=False, window_left=None, window_right=2),
+    dict(causal=False, window_left=1, window_right=None),
+]
+
+SHAPES = [  # (B, Sq, Sk, Hq, Hkv, D)
+    (1, 5, 5, 2, 1, 4),
+    (2, 3, 7, 2, 2, 3),
+    (1, 7, 4, 3, 1, 5),   # Sq > Sk: early causal rows see nothing
+    (1, 1, 6, 4, 2, 8),   # one query (decode-like)
+]
+
+
+def pin_brute_dense():
+    worst = 0.0
+    for si, (B, Sq, Sk, Hq, Hkv, D) in enumerate(SHAPES):
+        rng = _rng(100 + si)
+        q = rng.standard_normal((B, Sq, Hq, D))
+        k = rng.standard_normal((B, Sk, Hkv, D))
+        v = rng.standard_normal((B, Sk, Hkv, D + 1))
+        scale = 0.7
+        for mk in MASKS:
+            o, l = A.attention_dense(q, k, v, scale, **mk)
+            ob, lb = BR.attention_loops(q.tolist(), k.tolist(), v.tolist(), scale, **mk)
+            ok1, d1 = _close(o, np.array(ob))
+            ok2, d2 = _close(l, np.array(lb))
+            if not (ok1 and ok2):
+                return False, f"shape {SHAPES[si]} mask {mk}: O {d1}, LSE {d2}"
+            worst = max(worst, float(np.nanmax(np.abs(o - np.array(ob)))))
+    return True, f"worst {worst:.2e}"
+
+
+def pin_brute_varlen():
+    rng = _rng(7)
+    lq, lk = [3, 0, 5, 2], [4, 2, 5, 6]
+    Hq, Hkv, D = 4, 2, 3
+    cu_q = np.concatenate([[0], np.cumsum(lq)])
+    cu_k = np.concatenate([[0], np.cumsum(lk)])
+    q = rng.standard_normal((cu_q[-1], Hq, D))
+    k = rng.standard_normal((cu_k[-1], Hkv, D))
+    v = rng.standard_normal((cu_k[-1], Hkv, D))
+    for mk in MASKS:
+        o, l = A.attention_varlen(q, k, v, cu_q, cu_k, 0.5, **mk)
+        for b in range(len(lq)):
+            if lq[b] == 0:
+                continue
+            qs = q[cu_q[b]:cu_q[b + 1]][None]
+            ks = k[cu_k[b]:cu_k[b + 1]][None]
+            vs = v[cu_k[b]:cu_k[b + 1]][None]
+            ob, lb = BR.attention_loops(qs.tolist(), ks.tolist(), vs.tolist(), 0.5, **mk)
+            ok1, d1 = _close(o[cu_q[b]:cu_q[b + 1]], np.array(ob)[0])
+            ok2, d2 = _close(l[:, cu_q[b]:cu_q[b + 1]], np.array(lb)[0])
+            if not (ok1 and ok2):
+                return False, f"seq {b} mask {mk}: O {d1}, LSE {d2}"
+    return True, "ok"
+
+
+def pin_one_key():
+    rng = _rng(11)
+    q = rng.standard_normal((1, 1, 1, 6))
+    k = rng.standard_normal((1, 1, 1, 6))
+    v = rng.standard_normal((1, 1, 1, 6))
+    scale = 0.3
+    o, l = A.attention_dense(q, k, v, scale)
+    s00 = scale * float(np.dot(q[0, 0, 0], k[0, 0, 0]))
+    ok1, d1 = _close(o[0, 0, 0], v[0, 0, 0], 0.0)
+    ok2, d2 = _close(l[0, 0, 0], s00, 1e-15)
+    return ok1 and ok2, f"O {d1}, LSE {d2}"
+
+
+def pin_equal_keys():
+    rng = _rng(12)
+    q = rng.standard_normal((1, 1, 1, 5))
+    k1 = rng.standard_normal(5)
+    k = np.stack([k1, k1])[None, :, None, :]
+    v = rng.standard_normal((1, 2, 1, 5))
+    scale = 0.9
+    o, l = A.attention_dense(q, k, v, scale)
+    s = scale * float(np.dot(q[0, 0, 0], k1))
+    ok1, d1 = _close(o[0, 0, 0], (v[0, 0, 0] + v[0, 1, 0]) / 2)
+    ok2, d2 = _close(l[0, 0, 0], s + math.log(2.0))
+    return ok1 and ok2, f"O {d1}, LSE {d2}"
+
+
+def pin_zero_query():
+    for (Sq, Sk) in [(6, 6), (4, 9), (9, 4), (1, 5)]:
+        rng = _rng(Sq * 31 + Sk)
+        q = np.zeros((1, Sq, 2, 3))
+        k = rng.standard_normal((1, Sk, 1, 3))
+        v = rng.standard_normal((1, Sk, 1, 3))
+        for mk in MASKS:
+            o, l = A.attention_dense(q, k, v, 1.0, **mk)
+            for i in range(Sq):
+                n, lo, hi = interval_count(i, Sq, Sk, mk["causal"], mk["window_left"],
+                                           mk["window_right"])
+                exp_lse = math.log(n) if n > 0 else -math.inf
+                exp_o = v[0, lo:hi + 1, 0].mean(axis=0) if n > 0 else np.zeros(3)
+                for h in range(2):
+                    ok1, d1 = _close(l[0, h, i], exp_lse)
+                    ok2, d2 = _close(o[0, i, h], exp_o)
+                    if not (ok1 and ok2):
+                        return False, f"Sq{Sq} Sk{Sk} {mk} row {i}: LSE {d1}, O {d2}"
+    # the varlen sliding-window workload's rule: query i of a length-L sequence
+    # sees min(i + 1, window_left + 1) keys
+    L, wl = 40, 9
+    q = np.zeros((1, L, 1, 2))
+    k = _rng(5).standard_normal((1, L, 1, 2))
+    _, l = A.attention_dense(q, k, k, 1.0, causal=True, window_left=wl, window_right=0)
+    want = np.log(np.minimum(np.arange(L) + 1, wl + 1))
+    ok, d = _close(l[0, 0], want)
+    return ok, f"window count rule {d}"
+
+
+def pin_prob_sum():
+    rng = _rng(13)
+    q = rng.standard_normal((1, 8, 2, 4)) * 3
+    k = rng.standard_normal((1, 8, 2, 4)) * 3
+    for mk in MASKS:
+        vis = A.visible_mask(8, 8, **mk)
+        _, l = A.attention_dense(q, k, k, 0.8, **mk)
+        for h in range(2):
+            s = 0.8 * q[0, :, h] @ k[0, :, h].T
+            for i in range(8):
+                if not vis[i].any():
+                    continue
+                tot = float(np.exp(s[i][vis[i]] - l[0, h, i]).sum())
+                if abs(tot - 1.0) > TOL:
+                    return False, f"{mk} row {i}: sum {tot}"
+    return True, "ok"
+
+
+def pin_const_v():
+    rng = _rng(14)
+    q = rng.standard_normal((2, 5, 4, 3))
+    k = rng.standard_normal((2, 7, 2, 3))
+    c = rng.standard_normal(6)
+    v = np.broadcast_to(c, (2, 7, 2, 6)).copy()
+    for mk in MASKS:
+        o, l = A.attention_dense(q, k, v, 1.1, **mk)
+        for b in range(2):
+            for i in range(5):
+                for h in range(4):
+                    want = c if np.isfinite(l[b, h, i]) else np.zeros(6)
+                    ok, d = _close(o[b, i, h], want)
+                    if not ok:
+                        return False, f"{mk} ({b},{i},{h}) {d}"
+    return True, "ok"
+
+
+def pin_causal_row0():
+    rng = _rng(15)
+    q = rng.standard_normal((1, 6, 2, 4))
+    k = rng.standard_normal((1, 6, 1, 4))
+    v = rng.standard_normal((1, 6, 1, 4))
+    o, l = A.attention_dense(q, k, v, 0.5, causal=True)
+    for h in range(2):
+        ok1, d1 = _close(o[0, 0, h], v[0, 0, 0], 0.0)
+        ok2, d2 = _close(l[0, h, 0], 0.5 * float(np.dot(q[0, 0, h], k[0, 0, 0])), 1e-15)
+        if not (ok1 and ok2):
+            return False, f"head {h}: O {d1} LSE {d2}"
+    return True, "ok"
+
+
+def pin_gqa_as_mha():
+    rng = _rng(16)
+    B, S, Hq, Hkv, D = 2, 6, 6, 2, 4
+    q = rng.standard_normal((B, S, Hq, D))
+    k = rng.standard_normal((B, S, Hkv, D))
+    v = rng.standard_normal((B, S, Hkv, D))
+    r = Hq // Hkv
+    k_rep = np.repeat(k, r, axis=2)  # head h uses KV head h // r
+    v_rep = np.repeat(v, r, axis=2)
+    for mk in MASKS:
+        o1, l1 = A.attention_dense(q, k, v, 0.6, **mk)
+        o2, l2 = A.attention_dense(q, k_rep, v_rep, 0.6, **mk)
+        ok1, d1 = _close(o1, o2, 0.0)
+        ok2, d2 = _close(l1, l2, 0.0)
+        if not (ok1 and ok2):
+            return False, f"{mk}: O {d1} LSE {d2}"
+    return True, "ok"
+
+
+def pin_split_combine():
+    rng = _rng(17)
+    n, Sk, D = 3, 23, 5
+    q = rng.standard_normal((n, D))
+    k = rng.standard_normal((Sk, D))
+    v = rng.standard_normal((Sk, D))
+    for mk in MASKS:
+        vis = A.visible_mask(n, Sk, **mk)
+        o_ref, l_ref = A.attention_head(q, k, v, 0.4, vis)
+        for ns in [1, 2, 5, 23, 40]:  # 40 splits of 23 keys leaves empty splits
+            op, lp = A.attention_partials(q, k, v, 0.4, vis, A.split_bounds(Sk, ns))
+            o, l = A.combine(op, lp)
+            ok1, d1 = _close(o, o_ref)
+            ok2, d2 = _close(l, l_ref)
+            if not (ok1 and ok2):
+                return False, f"{mk} splits {ns}: O {d1} LSE {d2}"
+        # an irregular hand-made partition, including an empty range
+        bounds = [(0, 4), (4, 4), (4, 17), (17, 23)]
+        op, lp = A.attention_partials(q, k, v, 0.4, vis, bounds)
+        o, l = A.combine(op, lp)
+        ok1, d1 = _close(o, o_ref)
+        ok2, d2 = _close(l, l_ref)
+        if not (ok1 and ok2):
+            return False, f"{mk} irregular: O {d1} LSE {d2}"
+    return True, "ok"
+
+
+def pin_paged():
+    rng = _rng(18)
+    B, Hq, Hkv, D, ps, pps = 3, 4, 2, 5, 4, 3
+    num_pages = B * pps + 2
+    q = rng.standard_normal((B, Hq, D))
+    kc = rng.standard_normal((num_pages, ps, Hkv, D))
+    vc = rng.standard_normal((num_pages, ps, Hkv, D))
+    table = rng.permutation(num_pages)[:B * pps].reshape(B, pps)
+    used = np.array([12, 5, 9])
+    o, l, _, _ = A.paged_decode(q, kc, vc, table, used, 0.7, num_splits=3)
+    for b in range(B):
+        # contiguous copy built with explicit per-token indexing
+        kb = np.stack([kc[table[b, t // ps], t % ps] for t in range(used[b])])
+        vb = np.stack([vc[table[b, t // ps], t % ps] for t in range(used[b])])
+        o2, l2 = A.attention_dense(q[b][None, None], kb[None], vb[None], 0.7)
+        ok1, d1 = _close(o[b], o2[0, 0])
+        ok2, d2 = _close(l[b], l2[0, :, 0])
+        if not (ok1 and ok2):
+            return False, f"seq {b}: O {d1} LSE {d2}"
+    return True, "ok"
+
+
+def pin_torch_sdpa():
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(19)
+    for (Sq, Sk) in [(7, 7), (5, 9)]:
+        B, Hq, Hkv, D = 2, 4, 2, 6
+        q = rng.standard_normal((B, Sq, Hq, D))
+        k = rng.standard_normal((B, Sk, Hkv, D))
+        v = rng.standard_normal((B, Sk, Hkv, D))
+        for mk in MASKS:
+            o, l = A.attention_dense(q, k, v, 0.45, **mk)
+            mask = np.zeros((Sq, Sk), dtype=bool)
+            for i in range(Sq):
+                n, lo, hi = interval_count(i, Sq, Sk, mk["causal"], mk["window_left"],
+                                           mk["window_right"])
+                if n > 0:
+                    mask[i, lo:hi + 1] = True
+            rows = mask.any(axis=1)
+            tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+            tk = torch.from_numpy(np.repeat(k, Hq // Hkv, axis=2)).permute(0, 2, 1, 3)
+            tv = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=2)).permute(0, 2, 1, 3)
+            tm = torch.from_numpy(mask)
+            ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=tm, scale=0.45)
+            ref = ref.permute(0, 2, 1, 3).numpy()
+            s = torch.matmul(tq, tk.transpose(-1, -2)) * 0.45
+            s = s.masked_fill(~tm, float("-inf"))
+            lse_ref = torch.logsumexp(s, dim=-1).numpy()
+            ok1, d1 = _close(o[:, rows], ref[:, rows])
+            ok2, d2 = _close(l, lse_ref)
+            if not (ok1 and ok2):
+                return False, f"Sq{Sq} Sk{Sk} {mk}: O {d1} LSE {d2}"
+    return True, "ok"
+
+
+def pin_rows_match_full():
+    rng = _rng(20)
+    Sq, Sk, D = 9, 13, 4
+    q = rng.standard_normal((Sq, D))
+    k = rng.standard_normal((Sk, D))
+    v = rng.standard_normal((Sk, D))
+    for mk in MASKS:
+        o, l = A.attention_head(q, k, v, 0.3, A.visible_mask(Sq, Sk, **mk))
+        idx = np.array([0, 4, 8])
+        o2, l2 = A.attention_rows(q[idx], idx, k, v, 0.3, Sq, **mk)
+        ok1, d1 = _close(o2, o[idx], 0.0)
+        ok2, d2 = _close(l2, l[idx], 0.0)
+        if not (ok1 and ok2):
+            return False, f"{mk}: O {d1} LSE {d2}"
+    return True, "ok"
+
+
+ALL_PINS = {
+    "brute_dense": pin_brute_dense,
+    "brute_varlen": pin_brute_varlen,
+    "one_key": pin_one_key,
+    "equal_keys": pin_equal_keys,
+    "zero_query": pin_zero_query,
+    "prob_sum": pin_prob_sum,
+    "const_v": pin_const_v,
+    "causal_row0": pin_causal_row0,
+    "gqa_as_mha": pin_gqa_as_mha,
+    "split_combine": pin_split_combine,
+    "paged": pin_paged,
+    "torch_sdpa": pin_torch_sdpa,
+    "rows_match_full": pin_rows_match_full,
+}
+
+
+def run_all():
+    """Runs every pin; returns {name: (ok, detail)}. Exceptions count as failures."""
+    res = {}
+    for name, fn in ALL_PINS.items():
+        try:
+            res[name] = fn()
+        except Exception as e:  # a mutant may crash a pin: that is a detection
+            res[name] = (False, f"raised {type(e).__name__}: {e}")
+    return res

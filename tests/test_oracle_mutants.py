@@ -1,0 +1,56 @@
+"""Plants plausible mistakes in the oracle (CPU only) and checks a pin catches each.
+
+Each mutant rewrites one line of one oracle function from its source text,
+installs it in the oracle module for the duration of the test, runs every
+pin, and requires at least one pin to fail.
+"""
+import inspect
+import textwrap
+
+import pytest
+
+import oracle.attention as A
+from tests import oracle_pins as P
+
+MUTANTS = [
+    # (function, original text, mistaken text, what the mistake is)
+    ("visible_mask", "vis &= j >= diag - wl", "vis &= j > diag - wl", "left window off by one"),
+    ("visible_mask", "vis &= j <= diag + wr", "vis &= j < diag + wr", "right window exclusive"),
+    ("visible_mask", "diag = i + (seqlen_k - seqlen_q)", "diag = i", "top-left causal alignment"),
+    ("visible_mask", "diag = i + (seqlen_k - seqlen_q)", "diag = i + (seqlen_q - seqlen_k)",
+     "offset sign flipped"),
+    ("normalize_window", "wr = 0", "wl = 0", "causal sets the wrong side"),
+    ("softmax_lse_rows", "lse[nonempty] = m[nonempty] + np.log(lsum[nonempty])",
+     "lse[nonempty] = np.log(lsum[nonempty])", "LSE drops the max term"),
+    ("softmax_lse_rows", "lse[nonempty] = m[nonempty] + np.log(lsum[nonempty])",
+     "lse[nonempty] = m[nonempty] + np.log2(lsum[nonempty])", "LSE in base 2"),
+    ("attention_head", "s = scale * (q @ k.T)", "s = (q @ k.T)", "scale dropped"),
+    ("attention_head", "return p @ v, lse", "return p @ v[::-1], lse", "values reversed"),
+    ("attention_dense", "g = h // r", "g = h % Hkv", "interleaved GQA grouping"),
+    ("attention_varlen", "g = h // r", "g = h % Hkv", "interleaved GQA grouping (varlen)"),
+    ("attention_varlen", "k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])",
+     "k0, k1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])", "key offsets from query cu"),
+    ("combine", "wn = np.where(np.isfinite(lse_parts), np.exp(lse_parts - lse_safe), 0.0)",
+     "wn = np.where(np.isfinite(lse_parts), np.exp(lse_parts - m_safe), 0.0)",
+     "combine weights not normalised"),
+    ("combine", "lse[finite] = m_safe[finite] + np.log(total[finite])",
+     "lse[finite] = m_safe[finite]", "combined LSE keeps only the max"),
+    ("split_bounds", "return [(min(seqlen_k, s * c), min(seqlen_k, (s + 1) * c)) for s in range(num_splits)]",
+     "return [(min(seqlen_k, s * c), min(seqlen_k, (s + 1) * c - 1)) for s in range(num_splits)]",
+     "split ranges drop their last key"),
+    ("paged_gather", "pages = [cache[int(page_table_row[p])] for p in range(n_pages)]",
+     "pages = [cache[p] for p in range(n_pages)]", "page table ignored"),
+    ("paged_decode", "g = h // r", "g = h % Hkv", "interleaved GQA grouping (paged)"),
+]
+
+
+@pytest.mark.parametrize("fn,orig,bad,what", MUTANTS, ids=[m[3] for m in MUTANTS])
+def test_mutant_is_caught(monkeypatch, fn, orig, bad, what):
+    src = textwrap.dedent(inspect.getsource(getattr(A, fn)))
+    assert orig in src, f"mutation anchor not found in {fn}"
+    ns = dict(vars(A))
+    exec(compile(src.replace(orig, bad), f"<mutant {fn}>", "exec"), ns)
+    monkeypatch.setattr(A, fn, ns[fn])
+    results = P.run_all()
+    failed = [k for k, (ok, _) in results.items() if not ok]
+    assert failed, f"no pin caught mutant '{what}'"
