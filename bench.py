@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one prefill forward on the causal GQA workload (B1, Hq32/Hkv4,
+S4096, D128) plus one paged split-KV decode (B16, Hq32/Hkv4, D128, Sk32768,
+256-token pages in a random page table, 16 splits, then the LSE combine).
+Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout. `value` is the prefill forward's algorithmic
+throughput: 4*D*(visible query-key pairs)*Hq flops per launch (causal pairs
+only) over the launch's duration measured with HIP events on the launch
+stream. The decode half is reported under "decode" as K/V bytes read per
+second (plus Q, O, LSE and page-table bytes). Progress goes to stderr.
+
+Flags: --gpus N (only 1 is supported: the path is single-GPU), --steps K,
+--warmup W, --no-cpu-baseline, --cpu-seconds S (oracle sample budget),
+--all-configs (also time the other benchmark workloads; stderr only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s (causal-adjusted) + decode KV GB/s, % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--all-configs", action="store_true")
+    return ap.parse_args()
+
+
+def prefill_flops(w) -> float:
+    if w.kind == "varlen":
+        pairs = 0
+        for b in range(len(w.cu_seqlens_q) - 1):
+            lq = int(w.cu_seqlens_q[b + 1] - w.cu_seqlens_q[b])
+            lk = int(w.cu_seqlens_k[b + 1] - w.cu_seqlens_k[b])
+            pairs += _pairs(lq, lk, w.causal, w.window_left, w.window_right)
+    else:
+        pairs = w.batch * _pairs(w.seqlen_q, w.seqlen_k, w.causal, w.window_left, w.window_right)
+    return 4.0 * w.head_dim * w.num_heads_q * pairs
+
+
+def _pairs(sq, sk, causal, wl, wr) -> int:
+    """Visible (query, key) pairs of one head, closed form per row."""
+    right = 0 if causal else (None if wr is None or wr < 0 else wr)
+    left = None if wl is None or wl < 0 else wl
+    tot = 0
+    off = sk - sq
+    for i in range(sq):
+        lo = 0 if left is None else max(0, i + off - left)
+        hi = sk - 1 if right is None else min(sk - 1, i + off + right)
+        tot += max(0, hi - lo + 1)
+    return tot
+
+
+def decode_bytes(w) -> int:
+    kv = 2 * int(w.seqused_k.sum()) * w.num_heads_kv * w.head_dim * 2
+    q = w.batch * w.num_heads_q * w.head_dim * 2
+    o = q
+    lse = w.batch * w.num_heads_q * 4
+    table = sum(-(-int(s) // w.page_size) for s in w.seqused_k) * 4
+    return kv + q + o + lse + table
+
+
+class Prefill:
+    def __init__(self, mi, w, torch):
+        from tests.gpu_util import dev_bf16, dev_i32
+        self.mi, self.w = mi, w
+        self.q, self.k, self.v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+        self.kw = dict(softmax_scale=w.softmax_scale, causal=w.causal,
+                       window_left=w.window_left, window_right=w.window_right)
+        if w.kind == "varlen":
+            self.kw.update(cu_seqlens_q=dev_i32(w.cu_seqlens_q), cu_seqlens_k=dev_i32(w.cu_seqlens_k),
+                           max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k)
+        self.out, self.lse = mi.mi_attn_fwd(self.q, self.k, self.v, **self.kw)
+
+    def __call__(self):
+        self.mi.mi_attn_fwd(self.q, self.k, self.v, out=self.out, lse=self.lse, **self.kw)
+
+
+class Decode:
+    def __init__(self, mi, w, torch):
+        from tests.gpu_util import dev_bf16, dev_i32
+        self.mi, self.w = mi, w
+        self.q, self.kc, self.vc = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+        self.pt, self.su = dev_i32(w.page_table), dev_i32(w.seqused_k)
+        nb = mi.mi_attn_decode_workspace_bytes(self.q, self.kc, self.vc, self.pt, w.num_splits)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        self.out, self.lse = mi.mi_attn_decode_splitkv(
+            self.q, self.kc, self.vc, self.pt, seqused_k=self.su, softmax_scale=w.softmax_scale,
+            num_splits=w.num_splits, workspace=self.ws)
+
+    def __call__(self):
+        self.mi.mi_attn_decode_splitkv(self.q, self.kc, self.vc, self.pt, seqused_k=self.su,
+                                       out=self.out, lse=self.lse,
+                                       softmax_scale=self.w.softmax_scale,
+                                       num_splits=self.w.num_splits, workspace=self.ws)
+
+
+def time_launches(torch, fn, n):
+    """Per-launch durations (ms) from HIP events on the launch stream."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(w, budget_s: float):
+    """The float64 oracle (full score matrices) on a bounded sample of the
+    prefill workload: whole query heads, one after another, until the budget
+    is spent. Throughput uses the same causal-adjusted flop count."""
+    import numpy as np
+    import oracle.attention as OA
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    q = W.bf16_bits_to_f64(w.q[0])
+    k = W.bf16_bits_to_f64(w.k[0])
+    v = W.bf16_bits_to_f64(w.v[0])
+    r = w.num_heads_q // w.num_heads_kv
+    vis = OA.visible_mask(w.seqlen_q, w.seqlen_k, w.causal, w.window_left, w.window_right)
+    pairs = int(vis.sum())
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < w.num_heads_q:
+        g = heads // r
+        OA.attention_head(q[:, heads], k[:, g], v[:, g], w.softmax_scale, vis)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.head_dim * pairs * heads
+    del np
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.num_heads_q} query heads of the causal GQA S{w.seqlen_q} "
+                      f"D{w.head_dim} prefill workload, full fp64 score matrices, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention "
+              "path here is single-GPU, see the sharding notes in the design document",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import exact_attention_45_amd as mi
+    import workloads as W
+
+    mi.load()  # raises if the HIP library is missing
+    torch.cuda.init()
+    log("[bench] generating inputs")
+    w2 = W.standard_config(2)
+    w5 = W.standard_config(5)
+    pre = Prefill(mi, w2, torch)
+    dec = Decode(mi, w5, torch)
+    flops = prefill_flops(w2)
+    dbytes = decode_bytes(w5)
+    torch.cuda.synchronize()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        pre()
+        dec()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        pre()
+        e[1].record(stream)
+        e[2].record(stream)
+        dec()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    tflops = flops / (pre_avg * 1e-3) / 1e12
+    gbs = dbytes / (dec_avg * 1e-3) / 1e9
+    log(f"[bench] prefill {pre_avg * 1e3:.1f} us ({tflops:.1f} TFLOP/s), "
+        f"decode {dec_avg * 1e3:.1f} us ({gbs:.0f} GB/s)")
+
+    extra = {}
+    if args.all_configs:
+        for i in (1, 3, 4):
+            wi = W.standard_config(i)
+            p = Prefill(mi, wi, torch)
+            for _ in range(3):
+                p()
+            ms = time_launches(torch, p, max(5, args.steps // 2))
+            ms.sort()
+            med = ms[len(ms) // 2]
+            f = prefill_flops(wi)
+            extra[wi.name] = {"median_us": med * 1e3, "tflops": f / (med * 1e-3) / 1e12,
+                              "frac": f / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+            log(f"[bench] {wi.name}: {med * 1e3:.1f} us, {extra[wi.name]['tflops']:.1f} TFLOP/s")
+            del p
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(w2, args.cpu_seconds)
+        log(f"[bench] oracle {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal GQA prefill B1 Hq32 Hkv4 S4096 D128 (value) + paged split-KV "
+                        "decode B16 Hq32 Hkv4 D128 Sk32768 page256 16 splits (decode)",
+            "prefill_flops_per_launch": flops,
+            "decode_bytes_per_launch": dbytes,
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "kernel": "fwd_kernel<128>", "avg_launch_us": round(pre_avg * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+        "decode": {
+            "value": round(gbs, 1), "unit": "GB/s", "avg_launch_us": round(dec_avg * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "decode_split_kernel<128> + combine_kernel<128>"},
+        },
+    }
+    if extra:
+        rec["other_workloads"] = extra
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,378 @@
+"""Python binding of libmiattn.so: exact attention forward and paged split-KV
+decode for MI355X (gfx950).
+
+This layer only marshals arguments: it reads shapes, strides and data
+pointers from torch tensors, allocates outputs and workspaces with torch when
+the caller passes none, and calls the C ABI declared in include/mi_attn.h on
+torch's current stream. Every step of the computation runs in the library's
+HIP kernels; there is no fallback. If the shared library is missing or fails
+to load, every call raises.
+
+Entry points (same names as the C ABI):
+  mi_attn_fwd(q, k, v, ...)              -> (out, lse)
+  mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, ...) -> (out, lse)
+  mi_attn_combine(o_partial, lse_partial, ...) -> (out, lse)
+  mi_attn_decode_workspace_bytes(...), mi_attn_decode_num_splits(...)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "MiAttnError", "load", "lib_path", "mi_attn_fwd", "mi_attn_decode_splitkv",
+    "mi_attn_combine", "mi_attn_decode_workspace_bytes", "mi_attn_decode_num_splits",
+    "mi_attn_last_error", "mi_attn_version", "FwdParams", "DecodeParams",
+    "MI_ATTN_OK", "MI_ATTN_EINVAL", "MI_ATTN_EUNSUPPORTED", "MI_ATTN_EBOUNDS",
+    "MI_ATTN_EWORKSPACE", "MI_ATTN_EHIP",
+]
+
+MI_ATTN_OK = 0
+MI_ATTN_EINVAL = -1
+MI_ATTN_EUNSUPPORTED = -2
+MI_ATTN_EBOUNDS = -3
+MI_ATTN_EWORKSPACE = -4
+MI_ATTN_EHIP = -5
+_STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EBOUNDS", -4: "EWORKSPACE",
+           -5: "EHIP"}
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG_DIR, "libmiattn.so")
+
+
+class MiAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"mi_attn {_STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_fp = ctypes.c_void_p  # float* passed as raw address
+
+
+class FwdParams(ctypes.Structure):
+    """Mirror of mi_attn_fwd_params (field order and types must match the header)."""
+    _fields_ = [
+        ("q", _vp), ("k", _vp), ("v", _vp), ("out", _vp), ("lse", _fp),
+        ("q_batch_stride", _i64), ("q_row_stride", _i64), ("q_head_stride", _i64),
+        ("k_batch_stride", _i64), ("k_row_stride", _i64), ("k_head_stride", _i64),
+        ("v_batch_stride", _i64), ("v_row_stride", _i64), ("v_head_stride", _i64),
+        ("o_batch_stride", _i64), ("o_row_stride", _i64), ("o_head_stride", _i64),
+        ("batch", _i32), ("seqlen_q", _i32), ("seqlen_k", _i32),
+        ("num_heads_q", _i32), ("num_heads_kv", _i32), ("head_dim", _i32),
+        ("cu_seqlens_q", _vp), ("cu_seqlens_k", _vp),
+        ("total_q", _i32), ("max_seqlen_q", _i32), ("max_seqlen_k", _i32),
+        ("page_table", _vp),
+        ("softmax_scale", ctypes.c_float),
+        ("causal", _i32), ("window_left", _i32), ("window_right", _i32),
+    ]
+
+
+class DecodeParams(ctypes.Structure):
+    """Mirror of mi_attn_decode_params."""
+    _fields_ = [
+        ("q", _vp), ("k_cache", _vp), ("v_cache", _vp), ("page_table", _vp),
+        ("seqused_k", _vp), ("out", _vp), ("lse", _fp),
+        ("q_batch_stride", _i64), ("q_head_stride", _i64),
+        ("o_batch_stride", _i64), ("o_head_stride", _i64),
+        ("batch", _i32), ("num_heads_q", _i32), ("num_heads_kv", _i32), ("head_dim", _i32),
+        ("page_size", _i32), ("num_pages", _i32), ("max_pages_per_seq", _i32),
+        ("softmax_scale", ctypes.c_float),
+        ("causal", _i32), ("window_left", _i32), ("window_right", _i32),
+        ("num_splits", _i32),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_LIB = None
+
+
+def load(path: Optional[str] = None):
+    """Loads the shared library (once). Raises if it is missing or incomplete."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    p = path or lib_path()
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} not found: build it with `python -m exact_attention_45_amd.build` "
+            "(the library has no CPU fallback)")
+    lib = ctypes.CDLL(p)
+    lib.mi_attn_fwd.argtypes = [ctypes.POINTER(FwdParams), _vp]
+    lib.mi_attn_fwd.restype = ctypes.c_int
+    lib.mi_attn_decode_splitkv.argtypes = [ctypes.POINTER(DecodeParams), _vp]
+    lib.mi_attn_decode_splitkv.restype = ctypes.c_int
+    lib.mi_attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeParams)]
+    lib.mi_attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.mi_attn_decode_num_splits.argtypes = [ctypes.POINTER(DecodeParams)]
+    lib.mi_attn_decode_num_splits.restype = ctypes.c_int
+    lib.mi_attn_combine.argtypes = [_vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _vp]
+    lib.mi_attn_combine.restype = ctypes.c_int
+    lib.mi_attn_last_error.argtypes = []
+    lib.mi_attn_last_error.restype = ctypes.c_char_p
+    lib.mi_attn_version.argtypes = []
+    lib.mi_attn_version.restype = ctypes.c_char_p
+    if path is None:
+        _LIB = lib
+    return lib
+
+
+def mi_attn_last_error() -> str:
+    return load().mi_attn_last_error().decode()
+
+
+def mi_attn_version() -> str:
+    return load().mi_attn_version().decode()
+
+
+def _check(rc: int):
+    if rc != MI_ATTN_OK:
+        raise MiAttnError(rc, mi_attn_last_error())
+
+
+def _stream_ptr(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _req_bf16(name, t, device=None):
+    import torch
+    if t.dtype != torch.bfloat16:
+        raise MiAttnError(MI_ATTN_EINVAL, f"{name} must be bfloat16 (got {t.dtype})")
+    if not t.is_cuda:
+        raise MiAttnError(MI_ATTN_EINVAL, f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise MiAttnError(MI_ATTN_EINVAL, f"{name} is on {t.device}, expected {device}")
+    if t.stride(-1) != 1:
+        raise MiAttnError(MI_ATTN_EINVAL, f"{name} must be contiguous in its last dimension")
+
+
+def _req_i32(name, t, shape, device):
+    import torch
+    if t.dtype != torch.int32 or not t.is_cuda or t.device != device:
+        raise MiAttnError(MI_ATTN_EINVAL, f"{name} must be an int32 tensor on {device}")
+    if not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise MiAttnError(MI_ATTN_EINVAL, f"{name} must be contiguous with shape {tuple(shape)}")
+
+
+def _win(x: Optional[int]) -> int:
+    return -1 if x is None else int(x)
+
+
+def mi_attn_fwd(q, k, v, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=None,
+                max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                softmax_scale: Optional[float] = None, causal: bool = False,
+                window_left: Optional[int] = None, window_right: Optional[int] = None,
+                return_lse: bool = True) -> Tuple:
+    """Exact attention forward (interface page, `_flash_attn_fwd` contract).
+
+    Dense: q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D); lse (B, Hq, Sq).
+    Varlen: q (Tq, Hq, D), k/v (Tk, Hkv, D), cu_seqlens_q/k int32 (B+1,);
+    lse (Hq, Tq). max_seqlen_q/k default to the token totals (no device sync).
+    """
+    import torch
+    lib = load()
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _req_bf16(n, t, dev)
+    varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
+    if varlen and (cu_seqlens_q is None or cu_seqlens_k is None):
+        raise MiAttnError(MI_ATTN_EINVAL, "cu_seqlens_q and cu_seqlens_k go together")
+    hq, d = q.shape[-2], q.shape[-1]
+    hkv = k.shape[-2]
+    if v.shape[-1] != d or k.shape[-1] != d:
+        raise MiAttnError(MI_ATTN_EUNSUPPORTED, "head_dim of q, k and v must match")
+    if varlen:
+        if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape:
+            raise MiAttnError(MI_ATTN_EINVAL, "varlen q/k/v must be (tokens, heads, head_dim)")
+        batch = cu_seqlens_q.shape[0] - 1
+        _req_i32("cu_seqlens_q", cu_seqlens_q, (batch + 1,), dev)
+        _req_i32("cu_seqlens_k", cu_seqlens_k, (batch + 1,), dev)
+        total_q = q.shape[0]
+        max_q = total_q if max_seqlen_q is None else int(max_seqlen_q)
+        max_k = k.shape[0] if max_seqlen_k is None else int(max_seqlen_k)
+        seq_shape = (total_q,)
+        lse_shape = (hq, total_q)
+    else:
+        if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+            raise MiAttnError(MI_ATTN_EINVAL, "dense q/k/v must be (batch, seqlen, heads, head_dim)")
+        batch, sq = q.shape[0], q.shape[1]
+        if k.shape[0] != batch:
+            raise MiAttnError(MI_ATTN_EINVAL, "q and k batch sizes differ")
+        total_q, max_q, max_k = batch * sq, sq, k.shape[1]
+        seq_shape = (batch, sq)
+        lse_shape = (batch, hq, sq)
+    if out is None:
+        out = torch.empty(*seq_shape, hq, d, dtype=torch.bfloat16, device=dev)
+    else:
+        _req_bf16("out", out, dev)
+        if tuple(out.shape) != (*seq_shape, hq, d):
+            raise MiAttnError(MI_ATTN_EINVAL, f"out must have shape {(*seq_shape, hq, d)}")
+    if lse is None and return_lse:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
+    elif lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != lse_shape \
+                or lse.device != dev:
+            raise MiAttnError(MI_ATTN_EINVAL, f"lse must be contiguous float32 {lse_shape}")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+
+    p = FwdParams()
+    p.q, p.k, p.v, p.out, p.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse)
+    if varlen:
+        p.q_row_stride, p.q_head_stride = q.stride(0), q.stride(1)
+        p.k_row_stride, p.k_head_stride = k.stride(0), k.stride(1)
+        p.v_row_stride, p.v_head_stride = v.stride(0), v.stride(1)
+        p.o_row_stride, p.o_head_stride = out.stride(0), out.stride(1)
+        p.cu_seqlens_q, p.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
+    else:
+        p.q_batch_stride, p.q_row_stride, p.q_head_stride = q.stride(0), q.stride(1), q.stride(2)
+        p.k_batch_stride, p.k_row_stride, p.k_head_stride = k.stride(0), k.stride(1), k.stride(2)
+        p.v_batch_stride, p.v_row_stride, p.v_head_stride = v.stride(0), v.stride(1), v.stride(2)
+        p.o_batch_stride, p.o_row_stride, p.o_head_stride = (out.stride(0), out.stride(1),
+                                                             out.stride(2))
+        p.seqlen_q, p.seqlen_k = max_q, max_k
+    p.batch, p.num_heads_q, p.num_heads_kv, p.head_dim = batch, hq, hkv, d
+    p.total_q, p.max_seqlen_q, p.max_seqlen_k = total_q, max_q, max_k
+    p.softmax_scale = scale
+    p.causal, p.window_left, p.window_right = int(bool(causal)), _win(window_left), _win(window_right)
+    _check(lib.mi_attn_fwd(ctypes.byref(p), _stream_ptr(dev)))
+    return out, lse
+
+
+def _decode_params(q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
+                   num_splits, window_left, workspace) -> DecodeParams:
+    p = DecodeParams()
+    p.q, p.k_cache, p.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
+    p.page_table, p.seqused_k, p.out, p.lse = _ptr(page_table), _ptr(seqused_k), _ptr(out), _ptr(lse)
+    p.q_batch_stride, p.q_head_stride = q.stride(0), q.stride(1)
+    if out is not None:
+        p.o_batch_stride, p.o_head_stride = out.stride(0), out.stride(1)
+    p.batch, p.num_heads_q, p.head_dim = q.shape[0], q.shape[1], q.shape[2]
+    p.num_pages, p.page_size, p.num_heads_kv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    p.max_pages_per_seq = page_table.shape[1]
+    p.softmax_scale = (1.0 / math.sqrt(q.shape[2]) if softmax_scale is None
+                       else float(softmax_scale))
+    p.causal, p.window_left, p.window_right = 0, _win(window_left), -1
+    p.num_splits = int(num_splits)
+    if workspace is not None:
+        p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return p
+
+
+def mi_attn_decode_workspace_bytes(q, k_cache, v_cache, page_table, num_splits: int = 0) -> int:
+    lib = load()
+    p = _decode_params(q, k_cache, v_cache, page_table, None, None, None, None, num_splits, None,
+                       None)
+    n = lib.mi_attn_decode_workspace_bytes(ctypes.byref(p))
+    if n == 0:
+        raise MiAttnError(MI_ATTN_EINVAL, mi_attn_last_error())
+    return n
+
+
+def mi_attn_decode_num_splits(q, k_cache, v_cache, page_table, num_splits: int = 0) -> int:
+    lib = load()
+    p = _decode_params(q, k_cache, v_cache, page_table, None, None, None, None, num_splits, None,
+                       None)
+    n = lib.mi_attn_decode_num_splits(ctypes.byref(p))
+    _check(min(n, 0))
+    return n
+
+
+def check_paged_bounds(page_table, seqused_k, num_pages: int, page_size: int):
+    """Host-side check of page-table contents (one device-to-host copy).
+
+    Mirrors the block-table bounds check on the sm_120 PR page: every page a
+    sequence uses must be in [0, num_pages), and seqused_k must fit the table.
+    """
+    pt = page_table.cpu()
+    cap = pt.shape[1] * page_size
+    used = seqused_k.cpu() if seqused_k is not None else None
+    for b in range(pt.shape[0]):
+        n = cap if used is None else int(used[b])
+        if n < 0 or n > cap:
+            raise MiAttnError(MI_ATTN_EBOUNDS, f"seqused_k[{b}] = {n} outside [0, {cap}]")
+        npg = -(-n // page_size)
+        if npg:
+            row = pt[b, :npg]
+            if int(row.min()) < 0 or int(row.max()) >= num_pages:
+                raise MiAttnError(MI_ATTN_EBOUNDS, f"page_table row {b} references a page "
+                                                   f"outside [0, {num_pages})")
+
+
+def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=None, lse=None,
+                           softmax_scale: Optional[float] = None, num_splits: int = 0,
+                           window_left: Optional[int] = None, workspace=None,
+                           return_lse: bool = True, check_bounds: bool = False):
+    """One query token per sequence against a paged cache, split along keys.
+
+    q (B, Hq, D); k/v cache (num_pages, page_size, Hkv, D) contiguous;
+    page_table int32 (B, max_pages); seqused_k int32 (B,) or None.
+    Returns out (B, Hq, D) bf16 and lse (B, Hq) float32.
+    """
+    import torch
+    lib = load()
+    dev = q.device
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _req_bf16(n, t, dev)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise MiAttnError(MI_ATTN_EINVAL, "q must be (B, Hq, D) and caches (pages, page_size, Hkv, D)")
+    if not k_cache.is_contiguous() or not v_cache.is_contiguous():
+        raise MiAttnError(MI_ATTN_EINVAL, "k_cache and v_cache must be contiguous")
+    B, hq, d = q.shape
+    _req_i32("page_table", page_table, (B, page_table.shape[1]), dev)
+    if seqused_k is not None:
+        _req_i32("seqused_k", seqused_k, (B,), dev)
+    if check_bounds:
+        check_paged_bounds(page_table, seqused_k, k_cache.shape[0], k_cache.shape[1])
+    if out is None:
+        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=dev)
+    else:
+        _req_bf16("out", out, dev)
+    if lse is None and return_lse:
+        lse = torch.empty(B, hq, dtype=torch.float32, device=dev)
+    if workspace is None:
+        nbytes = mi_attn_decode_workspace_bytes(q, k_cache, v_cache, page_table, num_splits)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    p = _decode_params(q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
+                       num_splits, window_left, workspace)
+    _check(lib.mi_attn_decode_splitkv(ctypes.byref(p), _stream_ptr(dev)))
+    return out, lse
+
+
+def mi_attn_combine(o_partial, lse_partial, out=None, lse=None, return_lse: bool = True):
+    """LSE-weighted merge (interface page, `flash_attn_combine`).
+
+    o_partial float32 (rows, splits, D) contiguous, lse_partial float32
+    (rows, splits) contiguous. Returns out (rows, D) bf16 and lse (rows,).
+    """
+    import torch
+    lib = load()
+    dev = o_partial.device
+    if o_partial.dtype != torch.float32 or lse_partial.dtype != torch.float32:
+        raise MiAttnError(MI_ATTN_EINVAL, "partials must be float32")
+    if not (o_partial.is_contiguous() and lse_partial.is_contiguous()) or o_partial.dim() != 3 \
+            or tuple(lse_partial.shape) != tuple(o_partial.shape[:2]):
+        raise MiAttnError(MI_ATTN_EINVAL, "o_partial (rows, splits, D) and lse_partial "
+                                          "(rows, splits) must be contiguous")
+    rows, splits, d = o_partial.shape
+    if out is None:
+        out = torch.empty(rows, d, dtype=torch.bfloat16, device=dev)
+    else:
+        _req_bf16("out", out, dev)
+    if lse is None and return_lse:
+        lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    rc = lib.mi_attn_combine(o_partial.data_ptr(), lse_partial.data_ptr(), out.data_ptr(),
+                             out.stride(0), _ptr(lse), rows, splits, d, _stream_ptr(dev))
+    _check(rc)
+    return out, lse

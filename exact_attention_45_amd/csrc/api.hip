@@ -1,0 +1,331 @@
+// C ABI entry points: argument validation, mask normalisation, launch
+// configuration. Every check here runs before any HIP call, so invalid
+// requests return an error without touching the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kernels.hpp"
+#include "mi_attn.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MI_ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool stride_ok(int64_t s) { return s >= 0 && (s % 8) == 0; }
+bool dim_supported(int d) { return d == 64 || d == 128 || d == 256; }
+
+// Mask normalisation (interface page, `_flash_attn_fwd`): causal forces a
+// right window of 0; negative sizes are unbounded.
+void normalise_window(int causal, int wl_in, int wr_in, int* wl, int* wr) {
+  *wl = wl_in < 0 ? -1 : wl_in;
+  *wr = wr_in < 0 ? -1 : wr_in;
+  if (causal) *wr = 0;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Split count when the caller passes 0. Same shape as the interface page's
+// `num_splits_heuristic` (no split for <= 4 key blocks; otherwise enough
+// splits to give every compute unit work, capped at 128 and at the number
+// of key blocks), counting one workgroup per (sequence, KV head, row block).
+int split_heuristic(const mi_attn_decode_params* p) {
+  const int cap = p->max_pages_per_seq * p->page_size;
+  const int n_blocks = (cap + mi_attn::kDecBlockN - 1) / mi_attn::kDecBlockN;
+  if (n_blocks <= 4) return 1;
+  int cus = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        v > 0)
+      cus = v;
+  }
+  const int group = p->num_heads_q / p->num_heads_kv;
+  const long work = (long)p->batch * p->num_heads_kv * ((group + 31) / 32);
+  // two resident workgroups per compute unit keep enough loads in flight
+  const long want = std::max(1L, (2L * cus) / std::max(1L, work));
+  return (int)std::max(1L, std::min<long>({want, 128L, (long)n_blocks}));
+}
+
+// Shape and scalar checks (enough to size the workspace).
+int check_decode(const mi_attn_decode_params* p) {
+  if (p == nullptr) return fail(MI_ATTN_EINVAL, "params is NULL");
+  if (p->batch < 0 || p->num_heads_q <= 0 || p->num_heads_kv <= 0)
+    return fail(MI_ATTN_EINVAL, "batch must be >= 0 and head counts > 0");
+  if (p->num_heads_q % p->num_heads_kv != 0)
+    return fail(MI_ATTN_EINVAL, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
+                p->num_heads_q, p->num_heads_kv);
+  if (!dim_supported(p->head_dim))
+    return fail(MI_ATTN_EUNSUPPORTED, "head_dim %d not supported (64, 128, 256)", p->head_dim);
+  if (p->page_size <= 0 || p->num_pages <= 0 || p->max_pages_per_seq <= 0)
+    return fail(MI_ATTN_EINVAL, "page_size, num_pages and max_pages_per_seq must be > 0");
+  if ((int64_t)p->max_pages_per_seq * p->page_size > INT32_MAX)
+    return fail(MI_ATTN_EBOUNDS, "max_pages_per_seq * page_size overflows int32");
+  if ((int64_t)p->num_pages * p->page_size * p->num_heads_kv * p->head_dim > INT64_MAX / 4)
+    return fail(MI_ATTN_EINVAL, "cache too large");
+  if (p->num_splits < 0 || p->num_splits > 256)
+    return fail(MI_ATTN_EINVAL, "num_splits must be in 0..256 (got %d)", p->num_splits);
+  if (!isfinite(p->softmax_scale) || p->softmax_scale < 0.0f)
+    return fail(MI_ATTN_EUNSUPPORTED, "softmax_scale must be finite and >= 0");
+  return MI_ATTN_OK;
+}
+
+// Pointer, alignment and stride checks, needed only to launch.
+int check_decode_pointers(const mi_attn_decode_params* p) {
+  if (p->batch == 0) return MI_ATTN_OK;
+  if (!p->q || !p->k_cache || !p->v_cache || !p->page_table || !p->out)
+    return fail(MI_ATTN_EINVAL, "q, k_cache, v_cache, page_table and out must be non-NULL");
+  if (!aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->v_cache) || !aligned16(p->out))
+    return fail(MI_ATTN_EINVAL, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (!stride_ok(p->q_batch_stride) || !stride_ok(p->q_head_stride) ||
+      !stride_ok(p->o_batch_stride) || !stride_ok(p->o_head_stride))
+    return fail(MI_ATTN_EINVAL, "q/out strides must be non-negative multiples of 8 elements");
+  return MI_ATTN_OK;
+}
+
+int resolved_splits(const mi_attn_decode_params* p) {
+  return p->num_splits > 0 ? p->num_splits : split_heuristic(p);
+}
+
+size_t workspace_for(const mi_attn_decode_params* p, int splits) {
+  const size_t rows = (size_t)p->batch * p->num_heads_q;
+  return round_up(rows * splits * p->head_dim * sizeof(float)) +
+         round_up(rows * splits * sizeof(float));
+}
+
+template <class F>
+hipError_t by_dim(int d, F&& f) {
+  switch (d) {
+    case 64: return f(std::integral_constant<int, 64>{});
+    case 128: return f(std::integral_constant<int, 128>{});
+    default: return f(std::integral_constant<int, 256>{});
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mi_attn_last_error(void) { return g_err; }
+
+const char* mi_attn_version(void) { return "mi_attn 0.1.0 gfx950"; }
+
+int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
+  if (p == nullptr) return fail(MI_ATTN_EINVAL, "params is NULL");
+  if (p->page_table != nullptr)
+    return fail(MI_ATTN_EUNSUPPORTED, "paged K/V in the prefill forward is not supported; "
+                                      "use mi_attn_decode_splitkv");
+  const bool varlen = p->cu_seqlens_q != nullptr || p->cu_seqlens_k != nullptr;
+  if (varlen && (p->cu_seqlens_q == nullptr || p->cu_seqlens_k == nullptr))
+    return fail(MI_ATTN_EINVAL, "cu_seqlens_q and cu_seqlens_k must both be given");
+  if (p->batch < 0 || p->num_heads_q <= 0 || p->num_heads_kv <= 0)
+    return fail(MI_ATTN_EINVAL, "batch must be >= 0 and head counts > 0");
+  if (p->num_heads_q % p->num_heads_kv != 0)
+    return fail(MI_ATTN_EINVAL, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
+                p->num_heads_q, p->num_heads_kv);
+  if (!dim_supported(p->head_dim))
+    return fail(MI_ATTN_EUNSUPPORTED, "head_dim %d not supported (64, 128, 256)", p->head_dim);
+  if (!isfinite(p->softmax_scale) || p->softmax_scale < 0.0f)
+    return fail(MI_ATTN_EUNSUPPORTED, "softmax_scale must be finite and >= 0");
+  int max_q, max_k;
+  if (varlen) {
+    if (p->max_seqlen_q < 0 || p->max_seqlen_k < 0 || p->total_q < 0)
+      return fail(MI_ATTN_EINVAL, "max_seqlen_q/k and total_q must be >= 0 for varlen");
+    max_q = p->max_seqlen_q;
+    max_k = p->max_seqlen_k;
+  } else {
+    if (p->seqlen_q < 0 || p->seqlen_k < 0)
+      return fail(MI_ATTN_EINVAL, "seqlen_q and seqlen_k must be >= 0");
+    max_q = p->seqlen_q;
+    max_k = p->seqlen_k;
+  }
+  const int group = p->num_heads_q / p->num_heads_kv;
+  if ((int64_t)max_q * group > INT32_MAX - mi_attn::kFwdBlockM)
+    return fail(MI_ATTN_EINVAL, "seqlen_q * (num_heads_q / num_heads_kv) overflows int32");
+  if (p->batch == 0 || max_q == 0) return ok();
+  if (!p->q || !p->k || !p->v || !p->out)
+    return fail(MI_ATTN_EINVAL, "q, k, v and out must be non-NULL");
+  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->out))
+    return fail(MI_ATTN_EINVAL, "q, k, v and out must be 16-byte aligned");
+  const int64_t strides[] = {p->q_row_stride, p->q_head_stride, p->k_row_stride, p->k_head_stride,
+                             p->v_row_stride, p->v_head_stride, p->o_row_stride, p->o_head_stride};
+  for (int64_t s : strides)
+    if (!stride_ok(s))
+      return fail(MI_ATTN_EINVAL, "row/head strides must be non-negative multiples of 8");
+  if (!varlen) {
+    const int64_t bstr[] = {p->q_batch_stride, p->k_batch_stride, p->v_batch_stride,
+                            p->o_batch_stride};
+    for (int64_t s : bstr)
+      if (!stride_ok(s))
+        return fail(MI_ATTN_EINVAL, "batch strides must be non-negative multiples of 8");
+  }
+  (void)max_k;
+
+  mi_attn::FwdArgs a{};
+  a.q = p->q;
+  a.k = p->k;
+  a.v = p->v;
+  a.out = p->out;
+  a.lse = p->lse;
+  a.q_bs = p->q_batch_stride;
+  a.q_rs = p->q_row_stride;
+  a.q_hs = p->q_head_stride;
+  a.k_bs = p->k_batch_stride;
+  a.k_rs = p->k_row_stride;
+  a.k_hs = p->k_head_stride;
+  a.v_bs = p->v_batch_stride;
+  a.v_rs = p->v_row_stride;
+  a.v_hs = p->v_head_stride;
+  a.o_bs = p->o_batch_stride;
+  a.o_rs = p->o_row_stride;
+  a.o_hs = p->o_head_stride;
+  a.cu_q = p->cu_seqlens_q;
+  a.cu_k = p->cu_seqlens_k;
+  a.batch = p->batch;
+  a.seqlen_q = varlen ? 0 : p->seqlen_q;
+  a.seqlen_k = varlen ? 0 : p->seqlen_k;
+  a.hq = p->num_heads_q;
+  a.hkv = p->num_heads_kv;
+  a.group = group;
+  a.total_q = p->total_q;
+  a.num_m_blocks = (int)(((int64_t)max_q * group + mi_attn::kFwdBlockM - 1) / mi_attn::kFwdBlockM);
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  normalise_window(p->causal, p->window_left, p->window_right, &a.wl, &a.wr);
+  if ((int64_t)a.num_m_blocks * a.hkv * a.batch > INT32_MAX)
+    return fail(MI_ATTN_EINVAL, "launch grid too large");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = by_dim(p->head_dim, [&](auto dc) {
+    return mi_attn::launch_fwd<decltype(dc)::value>(a, s);
+  });
+  if (e != hipSuccess) return fail(MI_ATTN_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int mi_attn_decode_num_splits(const mi_attn_decode_params* p) {
+  int rc = check_decode(p);
+  if (rc != MI_ATTN_OK) return rc;
+  return resolved_splits(p);
+}
+
+size_t mi_attn_decode_workspace_bytes(const mi_attn_decode_params* p) {
+  if (check_decode(p) != MI_ATTN_OK) return 0;
+  return workspace_for(p, resolved_splits(p));
+}
+
+int mi_attn_decode_splitkv(const mi_attn_decode_params* p, void* stream) {
+  int rc = check_decode(p);
+  if (rc == MI_ATTN_OK) rc = check_decode_pointers(p);
+  if (rc != MI_ATTN_OK) return rc;
+  if (p->batch == 0) return ok();
+  const int splits = resolved_splits(p);
+  const size_t need = workspace_for(p, splits);
+  if (p->workspace == nullptr || p->workspace_bytes < need)
+    return fail(MI_ATTN_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                p->workspace == nullptr ? (size_t)0 : p->workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(p->workspace) & (kAlign - 1)) != 0)
+    return fail(MI_ATTN_EWORKSPACE, "workspace must be 256-byte aligned");
+
+  const int group = p->num_heads_q / p->num_heads_kv;
+  const size_t rows = (size_t)p->batch * p->num_heads_q;
+  mi_attn::DecodeArgs a{};
+  a.q = p->q;
+  a.k_cache = p->k_cache;
+  a.v_cache = p->v_cache;
+  a.page_table = p->page_table;
+  a.seqused_k = p->seqused_k;
+  a.o_part = static_cast<float*>(p->workspace);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(p->workspace) +
+                                        round_up(rows * splits * p->head_dim * sizeof(float)));
+  a.q_bs = p->q_batch_stride;
+  a.q_hs = p->q_head_stride;
+  a.batch = p->batch;
+  a.hq = p->num_heads_q;
+  a.hkv = p->num_heads_kv;
+  a.group = group;
+  a.page_size = p->page_size;
+  a.num_pages = p->num_pages;
+  a.max_pages = p->max_pages_per_seq;
+  a.num_splits = splits;
+  a.row_blocks = (group + 31) / 32;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  int wl, wr;
+  normalise_window(p->causal, p->window_left, p->window_right, &wl, &wr);
+  a.wl = wl;
+  if ((int64_t)a.batch * a.hkv * a.row_blocks * splits > INT32_MAX)
+    return fail(MI_ATTN_EINVAL, "launch grid too large");
+
+  mi_attn::CombineArgs cb{};
+  cb.o_part = a.o_part;
+  cb.lse_part = a.lse_part;
+  cb.out = p->out;
+  cb.lse = p->lse;
+  cb.rows = (int)rows;
+  cb.num_splits = splits;
+  // out rows are (batch, head): require the (b, h) -> row map to be affine
+  if (p->o_batch_stride != (int64_t)p->num_heads_q * p->o_head_stride)
+    return fail(MI_ATTN_EINVAL, "out must have o_batch_stride == num_heads_q * o_head_stride");
+  cb.out_row_stride = p->o_head_stride;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = by_dim(p->head_dim, [&](auto dc) {
+    hipError_t r = mi_attn::launch_decode<decltype(dc)::value>(a, s);
+    if (r != hipSuccess) return r;
+    return mi_attn::launch_combine<decltype(dc)::value>(cb, s);
+  });
+  if (e != hipSuccess) return fail(MI_ATTN_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int mi_attn_combine(const float* o_partial, const float* lse_partial, void* out,
+                    int64_t out_row_stride, float* lse, int32_t rows, int32_t num_splits,
+                    int32_t head_dim, void* stream) {
+  if (rows < 0) return fail(MI_ATTN_EINVAL, "rows must be >= 0");
+  if (num_splits < 1 || num_splits > 256)
+    return fail(MI_ATTN_EINVAL, "num_splits must be in 1..256 (got %d)", num_splits);
+  if (!dim_supported(head_dim))
+    return fail(MI_ATTN_EUNSUPPORTED, "head_dim %d not supported (64, 128, 256)", head_dim);
+  if (rows == 0) return ok();
+  if (!o_partial || !lse_partial || !out)
+    return fail(MI_ATTN_EINVAL, "o_partial, lse_partial and out must be non-NULL");
+  if (out_row_stride < head_dim || (out_row_stride % 8) != 0 || !aligned16(out))
+    return fail(MI_ATTN_EINVAL, "out must be 16-byte aligned with a row stride >= head_dim, "
+                                "multiple of 8");
+  mi_attn::CombineArgs cb{};
+  cb.o_part = o_partial;
+  cb.lse_part = lse_partial;
+  cb.out = out;
+  cb.out_row_stride = out_row_stride;
+  cb.lse = lse;
+  cb.rows = rows;
+  cb.num_splits = num_splits;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = by_dim(head_dim, [&](auto dc) {
+    return mi_attn::launch_combine<decltype(dc)::value>(cb, s);
+  });
+  if (e != hipSuccess) return fail(MI_ATTN_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

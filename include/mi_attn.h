@@ -1,0 +1,213 @@
+/*
+ * mi_attn.h - C ABI of the MI355X (gfx950) exact-attention library.
+ *
+ * Two operations, both exact scaled-dot-product attention with a natural-log
+ * log-sum-exp (LSE) output:
+ *
+ *   mi_attn_fwd             prefill / training-style forward over dense or
+ *                           packed variable-length (cu_seqlens) batches.
+ *   mi_attn_decode_splitkv  one query token per sequence against a paged K/V
+ *                           cache, split along the key axis into partials
+ *                           that an LSE-weighted combine then merges.
+ *
+ * What is computed (the forward of the mslk flash_attn interface.py page,
+ * `_flash_attn_fwd` / `flash_attn_varlen_func`; LSE is the natural-log
+ * log-sum-exp that the flash_bwd_sm100.py page's probability recompute
+ * P = exp2(S * scale * log2e - LSE * log2e) assumes):
+ *
+ *   for batch b, query head h, query row i:
+ *     g     = h / (Hq / Hkv)                      (consecutive GQA groups)
+ *     s_ij  = softmax_scale * dot(q[b,i,h,:], k[b,j,g,:])   for visible j
+ *     LSE_i = log(sum_j exp(s_ij))
+ *     O_i   = sum_j exp(s_ij - LSE_i) * v[b,j,g,:]        (rounded to bf16)
+ *   A row with no visible key gets O = 0 and LSE = -inf.
+ *
+ * Visible keys (interface page, mask normalisation; bottom-right alignment
+ * as in the backward page's causal/window block bounds): with
+ * off = seqlen_k - seqlen_q of that sequence, key j is visible to row i iff
+ *   j < seqlen_k,
+ *   window_left  < 0  or  j >= i + off - window_left,
+ *   window_right < 0  or  j <= i + off + window_right,
+ * and causal != 0 forces window_right = 0. A negative window size means
+ * "unbounded" (the interface page's None).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The
+ *     library never allocates, frees or synchronises; work is enqueued on
+ *     `stream` (a hipStream_t; NULL means the null stream) and runs
+ *     asynchronously.
+ *   - Element types: q, k, v, out are bfloat16 (passed as void*); lse and the
+ *     split partials are float32; index arrays are int32.
+ *   - Strides are in elements. The last (head_dim) dimension must be
+ *     contiguous; base pointers and strides must keep 16-byte alignment of
+ *     each row (head_dim % 8 == 0, strides % 8 == 0, pointers 16-byte
+ *     aligned).
+ *   - Supported head_dim: 64, 128, 256 (the interface page allows <= 256 in
+ *     multiples of 8; other sizes return MI_ATTN_EUNSUPPORTED).
+ *   - Return value: MI_ATTN_OK, or a negative mi_attn_status; on error
+ *     nothing is enqueued and mi_attn_last_error() describes the problem.
+ *   - The contents of device index arrays (cu_seqlens, seqused_k,
+ *     page_table) are trusted: the host cannot read them without a
+ *     synchronisation. Callers that cannot guarantee them should check on
+ *     the host first (the Python binding does, on request). The decode
+ *     kernel still refuses to dereference a page id outside [0, num_pages):
+ *     the affected split is written as NaN instead of faulting.
+ */
+#ifndef MI_ATTN_H
+#define MI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MI_ATTN_OK = 0,
+  MI_ATTN_EINVAL = -1,        /* bad pointer, shape, stride or alignment      */
+  MI_ATTN_EUNSUPPORTED = -2,  /* valid request this build does not implement  */
+  MI_ATTN_EBOUNDS = -3,       /* host-visible lengths exceed a table capacity */
+  MI_ATTN_EWORKSPACE = -4,    /* workspace missing or too small               */
+  MI_ATTN_EHIP = -5           /* the HIP runtime reported an error at launch  */
+} mi_attn_status;
+
+/* ------------------------------------------------------------------------
+ * Prefill forward.
+ *
+ * Dense batch (cu_seqlens_q == cu_seqlens_k == NULL):
+ *   q   [batch, seqlen_q, num_heads_q,  head_dim]  strides q_batch_stride,
+ *                                                   q_row_stride, q_head_stride
+ *   k,v [batch, seqlen_k, num_heads_kv, head_dim]  (k_*, v_* strides)
+ *   out [batch, seqlen_q, num_heads_q,  head_dim]  (o_* strides)
+ *   lse [batch, num_heads_q, seqlen_q] float32, contiguous, or NULL.
+ *
+ * Packed variable-length batch (both cu_seqlens non-NULL; interface page,
+ * `flash_attn_varlen_func`): sequence b owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]); batch strides are ignored.
+ *   q   [total_q, num_heads_q, head_dim]
+ *   k,v [total_k, num_heads_kv, head_dim]
+ *   lse [num_heads_q, total_q] float32, contiguous, or NULL.
+ *   max_seqlen_q / max_seqlen_k must bound every sequence's length (they
+ *   size the launch grid); seqlen_q / seqlen_k are ignored.
+ *
+ * num_heads_q must be a multiple of num_heads_kv. Query heads sharing a KV
+ * head are processed together (GQA packing), so one K/V tile load serves all
+ * of them. softmax_scale must be finite; the Python binding passes
+ * 1/sqrt(head_dim) when the caller gives none (interface page default).
+ * page_table must be NULL: paged K/V is served by mi_attn_decode_splitkv.
+ * --------------------------------------------------------------------- */
+typedef struct {
+  const void *q, *k, *v;
+  void *out;
+  float *lse;
+  int64_t q_batch_stride, q_row_stride, q_head_stride;
+  int64_t k_batch_stride, k_row_stride, k_head_stride;
+  int64_t v_batch_stride, v_row_stride, v_head_stride;
+  int64_t o_batch_stride, o_row_stride, o_head_stride;
+  int32_t batch, seqlen_q, seqlen_k;
+  int32_t num_heads_q, num_heads_kv, head_dim;
+  const int32_t *cu_seqlens_q, *cu_seqlens_k; /* device, [batch+1], or NULL  */
+  int32_t total_q;                            /* varlen: rows of q and lse   */
+  int32_t max_seqlen_q, max_seqlen_k;         /* varlen: host upper bounds   */
+  const int32_t *page_table;                  /* must be NULL                */
+  float softmax_scale;
+  int32_t causal, window_left, window_right;
+} mi_attn_fwd_params;
+
+int mi_attn_fwd(const mi_attn_fwd_params *p, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Split-KV decode over a paged cache (split-K decoding page,
+ * triton_splitk.py `FwOp.apply`; interface page, the page_table and
+ * num_splits paths of `_flash_attn_fwd` and `flash_attn_combine`).
+ *
+ *   q        [batch, num_heads_q, head_dim] bf16, strides q_batch_stride,
+ *            q_head_stride (one query token per sequence)
+ *   k_cache,
+ *   v_cache  [num_pages, page_size, num_heads_kv, head_dim] bf16, contiguous
+ *   page_table [batch, max_pages_per_seq] int32, row-contiguous: token t of
+ *            sequence b lives in page page_table[b][t / page_size], slot
+ *            t % page_size
+ *   seqused_k [batch] int32 keys per sequence, or NULL for
+ *            max_pages_per_seq * page_size; each must be in
+ *            [0, max_pages_per_seq * page_size]
+ *   out      [batch, num_heads_q, head_dim] bf16, strides o_batch_stride,
+ *            o_head_stride
+ *   lse      [batch, num_heads_q] float32 contiguous, or NULL
+ *
+ * The query sits at position seqused_k[b] - 1 (bottom-right alignment), so
+ * causal and window_right change nothing; window_left >= 0 restricts keys to
+ * the last window_left + 1.
+ *
+ * Keys are split into num_splits contiguous ranges (num_splits == 0 picks a
+ * count from the occupancy heuristic; 1..256 are taken as given). Each split
+ * writes float32 partials (O_s, LSE_s) into the workspace; the combine step
+ * (the same kernel as mi_attn_combine) then forms
+ *   LSE = log(sum_s exp(LSE_s)),  O = sum_s exp(LSE_s - LSE) * O_s,
+ * where an empty split has LSE_s = -inf and contributes nothing.
+ *
+ * workspace: caller-allocated device memory of at least
+ * mi_attn_decode_workspace_bytes(p) bytes, 256-byte aligned. Two launches
+ * on `stream`; concurrent calls must use distinct workspaces.
+ * --------------------------------------------------------------------- */
+typedef struct {
+  const void *q;
+  const void *k_cache, *v_cache;
+  const int32_t *page_table;
+  const int32_t *seqused_k;
+  void *out;
+  float *lse;
+  int64_t q_batch_stride, q_head_stride;
+  int64_t o_batch_stride, o_head_stride;
+  int32_t batch, num_heads_q, num_heads_kv, head_dim;
+  int32_t page_size, num_pages, max_pages_per_seq;
+  float softmax_scale;
+  int32_t causal, window_left, window_right;
+  int32_t num_splits;
+  void *workspace;
+  size_t workspace_bytes;
+} mi_attn_decode_params;
+
+/* The split count mi_attn_decode_splitkv will use for *p (resolves
+ * num_splits == 0), or a negative mi_attn_status if *p is invalid. */
+int mi_attn_decode_num_splits(const mi_attn_decode_params *p);
+
+/* Workspace bytes mi_attn_decode_splitkv needs for *p; 0 if *p is invalid
+ * (mi_attn_last_error() then says why). Layout: float32 O partials
+ * [batch * num_heads_q][splits][head_dim], then float32 LSE partials
+ * [batch * num_heads_q][splits], each 256-byte aligned. */
+size_t mi_attn_decode_workspace_bytes(const mi_attn_decode_params *p);
+
+int mi_attn_decode_splitkv(const mi_attn_decode_params *p, void *stream);
+
+/* ------------------------------------------------------------------------
+ * LSE-weighted combine of split partials (interface page,
+ * `flash_attn_combine` / `_flash_attn_fwd_combine`; split-K page,
+ * `merge_attentions`).
+ *
+ *   o_partial   [rows, num_splits, head_dim] float32, contiguous
+ *   lse_partial [rows, num_splits] float32, contiguous
+ *   out         bf16, row r at out + r * out_row_stride (head_dim contiguous)
+ *   lse         [rows] float32, or NULL
+ * num_splits in 1..256, head_dim in {64, 128, 256}. A row whose partial LSEs
+ * are all -inf gets O = 0 and LSE = -inf. This is the merge the decode path
+ * runs; exported so a caller holding partials from elsewhere (for example
+ * key shards on other devices) can merge them.
+ * --------------------------------------------------------------------- */
+int mi_attn_combine(const float *o_partial, const float *lse_partial, void *out,
+                    int64_t out_row_stride, float *lse, int32_t rows, int32_t num_splits,
+                    int32_t head_dim, void *stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char *mi_attn_last_error(void);
+
+/* Library version string. */
+const char *mi_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_ATTN_H */

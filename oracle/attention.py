@@ -52,13 +52,17 @@ def normalize_window(causal: bool, window_left: Optional[int], window_right: Opt
 
 def visible_mask(seqlen_q: int, seqlen_k: int, causal: bool = False,
                  window_left: Optional[int] = None,
-                 window_right: Optional[int] = None) -> np.ndarray:
-    """Boolean (Sq, Sk) matrix of visible (query, key) pairs, bottom-right aligned."""
+                 window_right: Optional[int] = None, rows=None) -> np.ndarray:
+    """Boolean (Sq, Sk) matrix of visible (query, key) pairs, bottom-right aligned.
+
+    `rows` restricts the result to the given query positions (n, Sk).
+    """
     wl, wr = normalize_window(causal, window_left, window_right)
-    i = np.arange(seqlen_q, dtype=np.int64)[:, None]
+    i = np.arange(seqlen_q, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    i = i[:, None]
     j = np.arange(seqlen_k, dtype=np.int64)[None, :]
     diag = i + (seqlen_k - seqlen_q)
-    vis = np.ones((seqlen_q, seqlen_k), dtype=bool)
+    vis = np.ones((i.shape[0], seqlen_k), dtype=bool)
     if wl is not None:
         vis &= j >= diag - wl
     if wr is not None:
@@ -143,9 +147,7 @@ def attention_rows(q_rows: np.ndarray, row_index: np.ndarray, k: np.ndarray, v: 
     query sequence; k (Sk, D), v (Sk, Dv) are that head's keys and values.
     Returns O (n, Dv), LSE (n,), computed from the same definition row by row.
     """
-    Sk = k.shape[0]
-    full = visible_mask(seqlen_q, Sk, causal, window_left, window_right)
-    vis = full[np.asarray(row_index, dtype=np.int64)]
+    vis = visible_mask(seqlen_q, k.shape[0], causal, window_left, window_right, rows=row_index)
     return attention_head(q_rows, k, v, scale, vis)
 
 
