@@ -44,7 +44,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the "
+                         "reference kernel for scaling HBM byte counters), then exit")
     return ap.parse_args()
+
+
+def copy_calibration(torch):
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 5 copies of {n} bytes")
 
 
 def prefill_flops(w) -> float:
@@ -177,6 +192,10 @@ def main():
     import exact_attention_45_amd as mi
     import workloads as W
 
+    if args.copy_calibration:
+        torch.cuda.init()
+        copy_calibration(torch)
+        return
     mi.load()  # raises if the HIP library is missing
     torch.cuda.init()
     log("[bench] generating inputs")
