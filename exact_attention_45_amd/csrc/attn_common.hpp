@@ -71,6 +71,29 @@ __device__ __forceinline__ f32x16 zero_f32x16() {
   return r;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lanes 4e..4e+3 each point at four consecutive 16-bit elements of "row" e
+// (e = 0..3); lane i of the group receives element i of rows 0..3. With V
+// row-major (key, dim) in LDS and lane j pointing at key j/4, dims 4*(j%4),
+// lane i gets dim i of four consecutive keys: an MFMA operand fragment whose
+// contraction index is the key. (Semantics measured on gfx950.)
+__device__ __forceinline__ bf16x4 ds_read_tr16(const __bf16* p) {
+  typedef __attribute__((ext_vector_type(4))) short s16x4;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<__bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations
+// (lgkmcnt = 0), not for outstanding global loads: register prefetches for
+// later tiles stay in flight across it. (__syncthreads also waits vmcnt = 0.)
+// s_waitcnt encoding (gfx9): vmcnt[3:0]|expcnt[6:4]|lgkmcnt[11:8]|vmcnt_hi[15:14];
+// 0xC07F = vmcnt 63, expcnt 7, lgkmcnt 0.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+}
+
 // 16-byte global load / store of raw bits.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 

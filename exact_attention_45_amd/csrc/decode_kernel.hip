@@ -22,6 +22,7 @@
 //   * Page ids are looked up per key row; an id outside [0, num_pages) is
 //     never dereferenced and turns the split's partial into NaN.
 #include <climits>
+#include <type_traits>
 
 #include "attn_common.hpp"
 #include "kernels.hpp"
@@ -29,25 +30,31 @@
 namespace mi_attn {
 
 template <int D>
-struct DecTile {
-  static constexpr int BN = kDecBlockN;   // 128 keys per tile
-  static constexpr int KS = D + 8;
-  static constexpr int VS = BN + 4;
-  static constexpr int CPR = D / 8;
-  static constexpr int NCH = BN * CPR / 256;
-  static constexpr int LDS_TILE = BN * KS + D * VS;      // elements (bf16)
-  static constexpr int LDS_MERGE = 4 * D * 32 + 4 * 64;  // floats: O^T per wave + m, l
-  static constexpr int LDS_BYTES =
-      (LDS_TILE * 2 > LDS_MERGE * 4) ? LDS_TILE * 2 : LDS_MERGE * 4;
+struct DecCfg {
+  static constexpr int BN = kDecBlockN;              // 128 keys per tile, 32 per wave
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per key row
+  static constexpr int ROWS_PER_LD = 64 / CPR;       // rows one wave instruction covers
+  static constexpr int NCH = BN * CPR / 256;         // chunks per thread per tensor
+  static constexpr int TILE = BN * D;                // elements per K (or V) tile
+  static constexpr int NBUF = D <= 128 ? 2 : 1;      // LDS tile buffers
+  static constexpr int NSET = D <= 128 ? 2 : 1;      // register prefetch sets
+  static constexpr int LDS_TILES = NBUF * 2 * TILE * 2;          // bytes
+  static constexpr int LDS_MERGE = (4 * D * 32 + 4 * 64) * 4;    // bytes
+  static constexpr int LDS_BYTES = LDS_TILES > LDS_MERGE ? LDS_TILES : LDS_MERGE;
 };
 
 template <int D>
+__device__ __forceinline__ int dswz(int key, int c) {
+  return D >= 128 ? (c ^ ((key & 7) << 1)) : (c ^ ((key & 3) << 1));
+}
+
+template <int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
-  using T = DecTile<D>;
-  constexpr int BN = T::BN, KS = T::KS, VS = T::VS, NCH = T::NCH;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS_BYTES];
-  __bf16* sK = reinterpret_cast<__bf16*>(smem);
-  __bf16* sV = sK + BN * KS;
+  using C = DecCfg<D>;
+  constexpr int BN = C::BN, CPR = C::CPR, NCH = C::NCH, TILE = C::TILE;
+  constexpr int NBUF = C::NBUF, NSET = C::NSET;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
+  __bf16* tiles = reinterpret_cast<__bf16*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,16 +83,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   chunk = (chunk + BN - 1) / BN * BN;
   const int k_begin = min(sk, kv_lo + split * chunk);
   const int k_end = min(sk, k_begin + chunk);
+  const int n_tiles = (k_end - k_begin + BN - 1) / BN;
 
   // ---- this lane's query head
   const int col = rb * 32 + c32;
   const bool valid = col < a.group;
   const int hq = hk * a.group + (valid ? col : 0);
   const __bf16* qp = static_cast<const __bf16*>(a.q) + (int64_t)b * a.q_bs + (int64_t)hq * a.q_hs;
+  // branch-free: invalid lanes read head 0's row and zero it afterwards (a
+  // load under a divergent branch makes every later wait drain all loads)
   bf16x8 qf[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c)
-    qf[c] = valid ? as_bf16x8(ld16(qp + 16 * c + 8 * half)) : zero_bf16x8();
+  for (int c = 0; c < D / 16; ++c) {
+    const bf16x8 x = as_bf16x8(ld16(qp + 16 * c + 8 * half));
+    qf[c] = valid ? x : zero_bf16x8();
+  }
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -93,63 +105,118 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   float m_run = kNegInf;
   float l_run = 0.0f;
 
-  const __bf16* kc = static_cast<const __bf16*>(a.k_cache);
-  const __bf16* vc = static_cast<const __bf16*>(a.v_cache);
+  const __bf16* kc = static_cast<const __bf16*>(a.k_cache) + (int64_t)hk * D;
+  const __bf16* vc = static_cast<const __bf16*>(a.v_cache) + (int64_t)hk * D;
   const int64_t tok_stride = (int64_t)a.hkv * D;
   const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
-  uint4 kreg[NCH], vreg[NCH];
+  const int ld_c = lane % CPR;
+  const int ld_r = lane / CPR;
 
-  // each wave instruction moves 32 key rows x 2 chunks; 4 row groups of 32
-  auto chunk_row = [&](int u) { return ((u * 4 + wave) & 3) * 32 + c32; };
-  auto chunk_col = [&](int u) { return (((u * 4 + wave) >> 2) * 2 + half) * 8; };
+  // Register prefetch sets. Page ids of tile t+1 are requested before the
+  // K/V loads of tile t: load counters retire in issue order, so a page id
+  // requested after a tile's loads could not be used until that tile landed.
+  uint4 kreg[NSET][NCH], vreg[NSET][NCH];
+  int pid[2][NCH];  // by tile parity
 
-  auto load_tile = [&](int n0) {
+  auto tile_row = [&](int u) { return (u * 4 + wave) * C::ROWS_PER_LD + ld_r; };
+  // Loads are branch-free per lane (divergent branches around loads make the
+  // compiler drain every outstanding load): a key past the split end is
+  // clamped to the last key (its scores are masked), and a page id outside
+  // the cache is replaced by page 0 and flags the split as NaN. Only the
+  // wave-uniform `t < n_tiles` test skips work.
+  // slot = t & 1 (compile-time at every call site). Requests for tiles past
+  // the split's end are still issued, so every wait count in the loop is
+  // static; their keys clamp to the split's last key (a cached row whose
+  // page id its own tile already checks), and their scores are masked.
+  auto fetch_pages = [&](int t, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int key = n0 + chunk_row(u);
-      const int cc = chunk_col(u);
-      kreg[u] = make_uint4(0, 0, 0, 0);
-      vreg[u] = make_uint4(0, 0, 0, 0);
-      if (key < k_end) {
-        const int page = ptab[key / a.page_size];
-        if (page >= 0 && page < a.num_pages) {
-          const int64_t off =
-              ((int64_t)page * a.page_size + key % a.page_size) * tok_stride + (int64_t)hk * D + cc;
-          kreg[u] = ld16(kc + off);
-          vreg[u] = ld16(vc + off);
-        } else {
-          bad_page = true;
-        }
-      }
+      const int key = min(k_begin + t * BN + tile_row(u), k_end - 1);
+      pid[slot][u] = ptab[key / a.page_size];
     }
   };
-  auto store_tile = [&]() {
+  auto load_tile = [&](int t, auto set_c, auto slot_c) {
+    constexpr int set = decltype(set_c)::value;
+    constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int row = chunk_row(u);
-      const int cc = chunk_col(u);
-      *reinterpret_cast<uint4*>(&sK[row * KS + cc]) = kreg[u];
-      const bf16x8 vv = as_bf16x8(vreg[u]);
+      const int key = min(k_begin + t * BN + tile_row(u), k_end - 1);
+      const bool ok = pid[slot][u] >= 0 && pid[slot][u] < a.num_pages;
+      bad_page |= !ok;
+      const int page = ok ? pid[slot][u] : 0;
+      const int64_t off =
+          ((int64_t)page * a.page_size + key % a.page_size) * tok_stride + ld_c * 8;
+      kreg[set][u] = ld16(kc + off);
+      vreg[set][u] = ld16(vc + off);
+    }
+  };
+  auto store_tile = [&](auto set_c, int buf) {
+    constexpr int set = decltype(set_c)::value;
+    __bf16* sK = tiles + buf * 2 * TILE;
+    __bf16* sV = sK + TILE;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sV[(cc + e) * VS + row] = vv[e];
+    for (int u = 0; u < NCH; ++u) {
+      const int row = tile_row(u);
+      const int p = row * D + dswz<D>(row, ld_c) * 8;
+      *reinterpret_cast<uint4*>(&sK[p]) = kreg[set][u];
+      *reinterpret_cast<uint4*>(&sV[p]) = vreg[set][u];
     }
   };
 
+  // transposing V fragment reads: lane j of 16-lane group g points at key j/4
+  const int tr_g = lane >> 4;
+  const int tr_j = lane & 15;
+  const int tr_key = tr_j >> 2;
+  const int tr_c = (tr_g & 1) * 2 + ((tr_j & 3) >> 1);
+  const int tr_e = (tr_j & 1) * 4;
   const float c = a.scale_log2;
-  if (k_begin < k_end) load_tile(k_begin);
-  for (int n0 = k_begin; n0 < k_end; n0 += BN) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (n0 + BN < k_end) load_tile(n0 + BN);
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, NSET == 2 ? 1 : 0>;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using PN = std::integral_constant<int, NSET & 1>;         // slot of tile NSET
+  using PN1 = std::integral_constant<int, (NSET + 1) & 1>;  // slot of tile NSET+1
+
+  // Issue order: pages(t+1) before loads(t); loads(t) before store(t).
+  // Prologue: tile 0 in LDS, tiles 1..NSET in flight.
+  if (n_tiles > 0) {
+    fetch_pages(0, P0{});
+    fetch_pages(1, P1{});
+    load_tile(0, S0{}, P0{});
+    if (NSET == 2) {
+      fetch_pages(2, P0{});
+      load_tile(1, S1{}, P1{});
+    }
+    fetch_pages(NSET + 1, PN1{});
+    store_tile(S0{}, 0);
+    load_tile(NSET, S0{}, PN{});
+    lds_barrier();
+  }
+
+  // one tile; `par` = t & 1 as a compile-time constant (register set and
+  // LDS buffer of tile t when double-buffered)
+  auto step = [&](int t, auto par_c) {
+    constexpr int par = decltype(par_c)::value;
+    using SetNext = std::integral_constant<int, NSET == 2 ? (par ^ 1) : 0>;
+    using SlotLoad = std::integral_constant<int, (par + 1 + NSET) & 1>;   // tile t+1+NSET
+    using SlotFetch = std::integral_constant<int, (par + NSET) & 1>;      // tile t+2+NSET
+    const int buf = NBUF == 2 ? par : 0;
+    const __bf16* sK = tiles + buf * 2 * TILE;
+    const __bf16* sV = sK + TILE;
+    const int n0 = k_begin + t * BN;
 
     // this wave's 32 keys: S^T = K Q^T
     f32x16 s = zero_f32x16();
-    const __bf16* krow = &sK[(wave * 32 + c32) * KS + 8 * half];
+    {
+      const int key = wave * 32 + c32;
+      const __bf16* krow = sK + key * D;
 #pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc)
-      s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * cc), qf[cc], s);
-
+      for (int cc = 0; cc < D / 16; ++cc)
+        s = mfma32(*reinterpret_cast<const bf16x8*>(krow + dswz<D>(key, 2 * cc + half) * 8),
+                   qf[cc], s);
+    }
     if (n0 + BN > k_end) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -160,12 +227,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 
     float mt = kNegInf;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[v]);
+    for (int v = 0; v < 16; v += 2) mt = fmaxf(mt, fmaxf(s[v], s[v + 1]));
     mt = fmaxf(mt, xor32(mt));
     const float m_new = fmaxf(m_run, mt);
     const float ms = (m_new == kNegInf) ? 0.0f : m_new * c;
-    // exactly 1 when the max did not move (m_run - m_new == 0), exactly 0
-    // when nothing was visible before (m_run = -inf)
+    // exactly 1 when the max did not move, exactly 0 when nothing was seen
     const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2((m_run - m_new) * c);
     float rs = 0.0f;
 #pragma unroll
@@ -183,21 +249,38 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 
     bf16x8 pf[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int i0 = 2 * t;
-      pf[t] = cat(cvt4(s[4 * i0 + 0], s[4 * i0 + 1], s[4 * i0 + 2], s[4 * i0 + 3]),
-                  cvt4(s[4 * i0 + 4], s[4 * i0 + 5], s[4 * i0 + 6], s[4 * i0 + 7]));
+    for (int tt = 0; tt < 2; ++tt) {
+      const int i0 = 2 * tt;
+      pf[tt] = cat(cvt4(s[4 * i0 + 0], s[4 * i0 + 1], s[4 * i0 + 2], s[4 * i0 + 3]),
+                   cvt4(s[4 * i0 + 4], s[4 * i0 + 5], s[4 * i0 + 6], s[4 * i0 + 7]));
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const __bf16* vrow = &sV[(db * 32 + c32) * VS + wave * 32 + 4 * half];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vrow + 16 * t);
-        const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vrow + 16 * t + 8);
-        o[db] = mfma32(cat(v0, v1), pf[t], o[db]);
+      for (int tt = 0; tt < 2; ++tt) {
+        const int k0 = wave * 32 + 16 * tt + 4 * half + tr_key;
+        const int k1 = k0 + 8;
+        const int cc = 4 * db + tr_c;
+        const bf16x4 v0 = ds_read_tr16(sV + k0 * D + dswz<D>(k0, cc) * 8 + tr_e);
+        const bf16x4 v1 = ds_read_tr16(sV + k1 * D + dswz<D>(k1, cc) * 8 + tr_e);
+        o[db] = mfma32(cat(v0, v1), pf[tt], o[db]);
       }
     }
+
+    // unconditional (a past-the-end tile stores finite filler that is never
+    // read unmasked), so the compiler sees fixed load counts in the loop
+    if (NBUF == 1) lds_barrier();  // single buffer: everyone done reading
+    store_tile(SetNext{}, NBUF == 2 ? (par ^ 1) : 0);
+    lds_barrier();
+    // page ids two tiles ahead, then refill the drained register set
+    fetch_pages(t + 2 + NSET, SlotFetch{});
+    load_tile(t + 1 + NSET, SetNext{}, SlotLoad{});
+  };
+  // Steps run in pairs; with an odd tile count the last step covers keys
+  // >= k_end only, all masked, and leaves (m, l, O) unchanged.
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- merge the four waves' partial states through LDS
@@ -241,14 +324,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const float nan = __builtin_nanf("");
     const int64_t prow = (int64_t)b * a.hq + hq2;
-    float* op = a.o_part + (prow * a.num_splits + split) * D;
-#pragma unroll 4
-    for (int j = 0; j < DPT; ++j) {
-      const int d = dpart * DPT + j;
-      float acc = 0.0f;
+    float* op = a.o_part + (prow * a.num_splits + split) * D + dpart * DPT;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) acc += wgt[w] * sO[(w * D + d) * 32 + qcol];
-      op[d] = any_bad ? nan : acc * inv;
+    for (int j = 0; j < DPT; j += 4) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int d = dpart * DPT + j;
+        acc.x += wgt[w] * sO[(w * D + d + 0) * 32 + qcol];
+        acc.y += wgt[w] * sO[(w * D + d + 1) * 32 + qcol];
+        acc.z += wgt[w] * sO[(w * D + d + 2) * 32 + qcol];
+        acc.w += wgt[w] * sO[(w * D + d + 3) * 32 + qcol];
+      }
+      *reinterpret_cast<float4*>(op + j) =
+          any_bad ? make_float4(nan, nan, nan, nan)
+                  : make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
     if (dpart == 0) {
       const float lse = l > 0.0f ? m * a.scale + __logf(l) : kNegInf;
@@ -257,44 +347,67 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   }
 }
 
-// ---- combine: one wave per output row, head_dim / 64 elements per lane
+// ---- combine: one 64-lane workgroup per output row; split weights are
+// staged in LDS and the partial loads are issued eight splits at a time
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
-  constexpr int EPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
+__global__ __launch_bounds__(64) void combine_kernel(const CombineArgs a) {
+  constexpr int EPL = D / 64;  // head_dim elements per lane
+  __shared__ float sw[256];
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
   const int S = a.num_splits;
   const float* lp = a.lse_part + (int64_t)row * S;
-  const float* op = a.o_part + (int64_t)row * S * D;
+  const float* op = a.o_part + (int64_t)row * S * D + lane * EPL;
 
   float m = kNegInf;
-  for (int s = lane; s < S; s += 64) m = fmaxf(m, lp[s]);
+  int has_nan = 0;
+  for (int s = lane; s < S; s += 64) {
+    const float x = lp[s];
+    m = fmaxf(m, x);
+    has_nan |= (x != x);
+  }
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) m = fmaxf(m, __shfl_xor(m, w, 64));
-  // a NaN partial (bad page id) must reach the output
-  int has_nan = 0;
-  for (int s = lane; s < S; s += 64) has_nan |= (lp[s] != lp[s]);
   has_nan = __any(has_nan);
 
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
   float lse = kNegInf;
-  if (m != kNegInf && !has_nan) {
-    float tot = 0.0f;
-    for (int s = 0; s < S; ++s) tot += __expf(lp[s] - m);
-    lse = m + __logf(tot);
-    for (int s = 0; s < S; ++s) {
-      const float w = __expf(lp[s] - lse);
-      const float* src = op + (int64_t)s * D + lane * EPL;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += w * src[e];
-    }
-  } else if (has_nan) {
+  if (has_nan) {
+    // a NaN partial (bad page id) must reach the output
     lse = __builtin_nanf("");
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = lse;
+  } else if (m != kNegInf) {
+    float tot = 0.0f;
+    for (int s = lane; s < S; s += 64) {
+      const float w = __expf(lp[s] - m);  // -inf (empty split) -> 0
+      sw[s] = w;
+      tot += w;
+    }
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) tot += __shfl_xor(tot, w, 64);
+    lse = m + __logf(tot);
+    const float inv = 1.0f / tot;
+    __syncthreads();
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+      float x[8][EPL];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[i][e] = op[(int64_t)(s + i) * D + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += sw[s + i] * x[i][e];
+    }
+    for (; s < S; ++s)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += sw[s] * op[(int64_t)s * D + e];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= inv;
   }
   __bf16* dst = static_cast<__bf16*>(a.out) + (int64_t)row * a.out_row_stride + lane * EPL;
 #pragma unroll
@@ -313,7 +426,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel<D>, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel<D>, dim3((unsigned)a.rows), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -7,25 +7,34 @@
 //   for each K/V tile of 64 keys in the workgroup's visible range:
 //     S^T  = K * Q^T                         (bf16 MFMA, fp32 accumulate)
 //     mask keys outside [i+off-wl, i+off+wr] and beyond seqlen_k (edge tiles)
-//     m'   = max(m, rowmax S);  alpha = exp2((m - m') * c);  c = scale*log2e
+//     m'   = max(m, rowmax S) when it grew by more than 2^8 in P units, else m
+//     alpha = exp2((m - m') * c);  c = scale*log2e
 //     P    = exp2(S*c - m'*c)                (rounded to bf16 for the MFMA)
 //     l    = alpha*l + rowsum P;  O = alpha*O + P*V
 //   O /= l;  LSE = m*scale + ln(l);  rows with no visible key: O = 0, LSE = -inf.
+// Keeping a stale running max (the sm_120 PR page notes FA4's rescale
+// threshold: the max may lag by a few log2 units) changes no result: O and l
+// carry the same factor, and P stays below 2^8, far inside fp32/bf16 range.
 //
 // MI355X mapping:
-//   * 4 waves x 32 query rows. Rows are "packed": the r = Hq/Hkv query heads
-//     that share a KV head are folded into the row index (row = pos*r + head
-//     offset), so one K/V tile serves all of them (GQA packing, interface
-//     page `pack_gqa`; the sm_120 PR page's qhead-into-seqlen fold).
-//   * Both GEMMs are transposed (see attn_common.hpp) so each lane owns one
-//     query: row max needs one exchange with lane ^ 32, row sum none.
-//   * K tile row-major and V tile transposed in LDS; the next tile's global
-//     loads are issued into registers before the current tile's math.
-//   * Tiles wholly outside the causal/window band are never visited; only
-//     edge tiles pay for per-element masking.
-//   * Launch order: heaviest (latest) query blocks first, KV head fastest, so
-//     the 8 XCDs (round-robin workgroup placement) each keep a fixed subset
-//     of KV heads hot in their L2.
+//   * 4 waves x 32 packed query rows; rows fold the r = Hq/Hkv query heads of
+//     one KV head into the row index (row = pos*r + head offset), so each K/V
+//     tile serves all of them (interface page `pack_gqa`; sm_120 PR page's
+//     qhead-into-seqlen fold).
+//   * Both GEMMs transposed (attn_common.hpp): one lane owns one query.
+//   * K and V tiles are row-major in LDS with 16-byte chunks XOR-swizzled by
+//     key (chunk ^ 2*(key & 7)); global loads are fully coalesced (16 lanes
+//     per 256-byte row) and the 16-byte LDS stores, the K fragment reads and
+//     the transposing V fragment reads (ds_read_b64_tr_b16) are all free of
+//     bank conflicts.
+//   * Double-buffered LDS, next tile prefetched into registers during the
+//     current tile's math; one barrier per tile. D = 64/128 fit two waves per
+//     SIMD (two workgroups per CU), so one wave's softmax overlaps another's
+//     MFMAs.
+//   * Tiles wholly outside the causal/window band are never visited.
+//   * Grid order: heaviest (latest) query blocks first, KV head fastest, so
+//     round-robin placement keeps each KV head's K/V in a fixed subset of the
+//     8 XCD L2s.
 #include <climits>
 
 #include "attn_common.hpp"
@@ -34,22 +43,29 @@
 namespace mi_attn {
 
 template <int D>
-struct FwdTile {
-  static constexpr int BM = kFwdBlockM;
-  static constexpr int BN = kFwdBlockN;
-  static constexpr int KS = D + 8;        // K tile row stride (elements)
-  static constexpr int VS = BN + 4;       // V^T tile row stride (elements)
-  static constexpr int CPR = D / 8;       // 16-byte chunks per K/V row
-  static constexpr int NCH = BN * CPR / 256;  // chunks per thread per tensor
-  static_assert(NCH * 256 == BN * CPR, "tile must split evenly over 256 threads");
+struct FwdCfg {
+  static constexpr int BM = kFwdBlockM;      // 128 rows, 4 waves
+  static constexpr int BN = kFwdBlockN;      // 64 keys
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int ROWS_PER_LD = 64 / CPR;       // rows one wave instruction covers
+  static constexpr int NCH = BN * CPR / 256;         // chunks per thread per tensor
+  static constexpr int TILE = BN * D;                // elements per K (or V) tile
+  static constexpr int WAVES_PER_EU = D <= 128 ? 2 : 1;
+  static constexpr float RESCALE_LOG2 = 8.0f;        // lazy-rescale threshold
 };
 
+// position of chunk c of row `key` inside the swizzled tile row
 template <int D>
-__global__ __launch_bounds__(256) void fwd_kernel(const FwdArgs a) {
-  using T = FwdTile<D>;
-  constexpr int BM = T::BM, BN = T::BN, KS = T::KS, VS = T::VS, CPR = T::CPR, NCH = T::NCH;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[BN * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[D * VS];
+__device__ __forceinline__ int swz(int key, int c) {
+  return D >= 128 ? (c ^ ((key & 7) << 1)) : (c ^ ((key & 3) << 1));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_EU)))
+void fwd_kernel(const FwdArgs a) {
+  using C = FwdCfg<D>;
+  constexpr int BM = C::BM, BN = C::BN, CPR = C::CPR, NCH = C::NCH, TILE = C::TILE;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[4 * TILE];  // K0 V0 K1 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -113,10 +129,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(const FwdArgs a) {
   // ---- Q^T fragments (B operand), kept in registers for the whole loop
   const __bf16* qp = static_cast<const __bf16*>(a.q) + q_base + (int64_t)pos * a.q_rs +
                      (int64_t)hq * a.q_hs;
+  // branch-free: invalid lanes read row 0 of head hk*r and zero it afterwards
+  // (a load under a divergent branch makes every later wait drain all loads)
   bf16x8 qf[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c)
-    qf[c] = valid ? as_bf16x8(ld16(qp + 16 * c + 8 * half)) : zero_bf16x8();
+  for (int c = 0; c < D / 16; ++c) {
+    const bf16x8 x = as_bf16x8(ld16(qp + 16 * c + 8 * half));
+    qf[c] = valid ? x : zero_bf16x8();
+  }
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -124,59 +144,73 @@ __global__ __launch_bounds__(256) void fwd_kernel(const FwdArgs a) {
   float m_run = kNegInf;
   float l_run = 0.0f;
 
-  // ---- K/V tile staging: each wave instruction moves 32 rows x 2 chunks
+  // ---- K/V staging: wave instruction u covers ROWS_PER_LD whole rows,
+  // CPR lanes per row (16-byte chunk c = lane % CPR)
   const __bf16* kp = static_cast<const __bf16*>(a.k) + k_base + (int64_t)hk * a.k_hs;
   const __bf16* vp = static_cast<const __bf16*>(a.v) + v_base + (int64_t)hk * a.v_hs;
+  const int ld_c = lane % CPR;
+  const int ld_r = lane / CPR;
   uint4 kreg[NCH], vreg[NCH];
 
-  auto chunk_row = [&](int u) { return ((u * 4 + wave) & 1) * 32 + c32; };
-  auto chunk_col = [&](int u) { return (((u * 4 + wave) >> 1) * 2 + half) * 8; };
-
+  // branch-free loads: rows past seqlen_k re-read the last key (finite data
+  // whose scores are masked), so no divergent branch drains the prefetch
   auto load_tile = [&](int n0) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int key = n0 + chunk_row(u);
-      const int col = chunk_col(u);
-      if (key < sk) {
-        kreg[u] = ld16(kp + (int64_t)key * a.k_rs + col);
-        vreg[u] = ld16(vp + (int64_t)key * a.v_rs + col);
-      } else {
-        kreg[u] = make_uint4(0, 0, 0, 0);
-        vreg[u] = make_uint4(0, 0, 0, 0);
-      }
+      const int row = (u * 4 + wave) * C::ROWS_PER_LD + ld_r;
+      const int key = min(n0 + row, sk - 1);
+      kreg[u] = ld16(kp + (int64_t)key * a.k_rs + ld_c * 8);
+      vreg[u] = ld16(vp + (int64_t)key * a.v_rs + ld_c * 8);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](__bf16* sK, __bf16* sV) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int row = chunk_row(u);
-      const int col = chunk_col(u);
-      *reinterpret_cast<uint4*>(&sK[row * KS + col]) = kreg[u];
-      const bf16x8 vv = as_bf16x8(vreg[u]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sV[(col + e) * VS + row] = vv[e];
+      const int row = (u * 4 + wave) * C::ROWS_PER_LD + ld_r;
+      const int p = row * D + swz<D>(row, ld_c) * 8;
+      *reinterpret_cast<uint4*>(&sK[p]) = kreg[u];
+      *reinterpret_cast<uint4*>(&sV[p]) = vreg[u];
     }
   };
 
+  // per-lane constants for the fragment reads
+  // K (A operand of S^T): row kb*32 + c32, chunk 2*cc + half
+  // V (A operand of O^T, transposing read): 16-lane group g = lane/16 reads 4
+  // keys x 16 dims; lane j of the group points at key j/4, dims 4*(j%4)..+3
+  const int tr_g = lane >> 4;
+  const int tr_j = lane & 15;
+  const int tr_key = tr_j >> 2;                       // + key base
+  const int tr_c = (tr_g & 1) * 2 + ((tr_j & 3) >> 1);  // + 4*db
+  const int tr_e = (tr_j & 1) * 4;
+
   const float c = a.scale_log2;
-  if (n_begin < n_end) load_tile(n_begin * BN);
+  const float rescale_raw = C::RESCALE_LOG2 / fmaxf(c, 1e-30f);
+
+  if (n_begin < n_end) {
+    load_tile(n_begin * BN);
+    store_tile(smem, smem + TILE);
+    __syncthreads();
+  }
 
   for (int nb = n_begin; nb < n_end; ++nb) {
     const int n0 = nb * BN;
-    __syncthreads();  // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    if (nb + 1 < n_end) load_tile(n0 + BN);
+    const int cur = (nb - n_begin) & 1;
+    const __bf16* sK = smem + cur * 2 * TILE;
+    const __bf16* sV = sK + TILE;
+    const bool more = nb + 1 < n_end;
+    if (more) load_tile(n0 + BN);
 
     // S^T = K Q^T: two 32-key blocks
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = zero_f32x16();
-      const __bf16* krow = &sK[(kb * 32 + c32) * KS + 8 * half];
+      const int key = kb * 32 + c32;
+      const __bf16* krow = sK + key * D;
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * cc);
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(krow + swz<D>(key, 2 * cc + half) * 8);
         s[kb] = mfma32(kf, qf[cc], s[kb]);
       }
     }
@@ -192,18 +226,26 @@ __global__ __launch_bounds__(256) void fwd_kernel(const FwdArgs a) {
         }
     }
 
-    // online softmax (exp2 domain)
+    // online softmax with a lazily updated running max
     float mt = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][v]);
+      for (int v = 0; v < 16; v += 2) mt = fmaxf(mt, fmaxf(s[kb][v], s[kb][v + 1]));
     mt = fmaxf(mt, xor32(mt));
-    const float m_new = fmaxf(m_run, mt);
-    const float ms = (m_new == kNegInf) ? 0.0f : m_new * c;
-    // exactly 1 when the max did not move (m_run - m_new == 0), exactly 0
-    // when nothing was visible before (m_run = -inf)
-    const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2((m_run - m_new) * c);
+    const bool grow = (m_run == kNegInf) ? (mt != kNegInf) : (mt - m_run > rescale_raw);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = grow ? ((m_run == kNegInf) ? 0.0f : fast_exp2((m_run - m_new) * c))
+                               : 1.0f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    }
+    const float ms = (m_run == kNegInf) ? 0.0f : m_run * c;
     float rs = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -213,16 +255,11 @@ __global__ __launch_bounds__(256) void fwd_kernel(const FwdArgs a) {
         s[kb][v] = p;
         rs += p;
       }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    l_run += rs;
 
-    // P^T fragments: MFMA t covers keys 16t..16t+15 of the tile. Lane half h
-    // supplies keys {16t+4h+j, 16t+8+4h+j : j<4}; the V^T fragment below
-    // uses the same key order, so the contraction is unchanged.
+    // P^T fragments: MFMA t covers keys 16t..16t+15 of the tile; lane half h
+    // supplies keys {16t+4h+j, 16t+8+4h+j : j<4}; the V^T fragment below uses
+    // the same key order, so the contraction is unchanged.
     bf16x8 pf[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -232,17 +269,22 @@ __global__ __launch_bounds__(256) void fwd_kernel(const FwdArgs a) {
                   cvt4(s[kb][4 * i0 + 4], s[kb][4 * i0 + 5], s[kb][4 * i0 + 6], s[kb][4 * i0 + 7]));
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T, V^T fragments read transposed from row-major V
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const __bf16* vrow = &sV[(db * 32 + c32) * VS + 4 * half];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vrow + 16 * t);
-        const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vrow + 16 * t + 8);
+        const int k0 = 16 * t + 4 * half + tr_key;
+        const int k1 = k0 + 8;
+        const int cc = 4 * db + tr_c;
+        const bf16x4 v0 = ds_read_tr16(sV + k0 * D + swz<D>(k0, cc) * 8 + tr_e);
+        const bf16x4 v1 = ds_read_tr16(sV + k1 * D + swz<D>(k1, cc) * 8 + tr_e);
         o[db] = mfma32(cat(v0, v1), pf[t], o[db]);
       }
     }
+
+    if (more) store_tile(smem + (cur ^ 1) * 2 * TILE, smem + (cur ^ 1) * 2 * TILE + TILE);
+    lds_barrier();  // next buffer written; this buffer free for reuse
   }
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store
