@@ -41,6 +41,7 @@ void normalise_window(int causal, int wl_in, int wr_in, int* wl, int* wr) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kFwdRowsPerTile = mi_attn::kFwdBlockN;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Split count when the caller passes 0. Same shape as the interface page's
@@ -159,7 +160,7 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
     max_k = p->seqlen_k;
   }
   const int group = p->num_heads_q / p->num_heads_kv;
-  if ((int64_t)max_q * group > INT32_MAX - mi_attn::kFwdBlockM)
+  if ((int64_t)max_q * group > INT32_MAX - mi_attn::kFwdPPBlockM)
     return fail(MI_ATTN_EINVAL, "seqlen_q * (num_heads_q / num_heads_kv) overflows int32");
   if (p->batch == 0 || max_q == 0) return ok();
   if (!p->q || !p->k || !p->v || !p->out)
@@ -171,6 +172,11 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
   for (int64_t s : strides)
     if (!stride_ok(s))
       return fail(MI_ATTN_EINVAL, "row/head strides must be non-negative multiples of 8");
+  if (p->q_row_stride < p->head_dim || p->k_row_stride < p->head_dim ||
+      p->v_row_stride < p->head_dim || p->o_row_stride < p->head_dim)
+    return fail(MI_ATTN_EINVAL, "row strides must be >= head_dim (rows may not overlap)");
+  if ((int64_t)kFwdRowsPerTile * (p->k_row_stride + p->v_row_stride) * 2 > INT32_MAX)
+    return fail(MI_ATTN_EINVAL, "K/V row stride too large for 32-bit tile offsets");
   if (!varlen) {
     const int64_t bstr[] = {p->q_batch_stride, p->k_batch_stride, p->v_batch_stride,
                             p->o_batch_stride};
@@ -207,11 +213,12 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
   a.hkv = p->num_heads_kv;
   a.group = group;
   a.total_q = p->total_q;
-  a.num_m_blocks = (int)(((int64_t)max_q * group + mi_attn::kFwdBlockM - 1) / mi_attn::kFwdBlockM);
+  a.max_rows = max_q * group;
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   normalise_window(p->causal, p->window_left, p->window_right, &a.wl, &a.wr);
-  if ((int64_t)a.num_m_blocks * a.hkv * a.batch > INT32_MAX)
+  if (((int64_t)a.max_rows + mi_attn::kFwdBlockM - 1) / mi_attn::kFwdBlockM * a.hkv * a.batch >
+      INT32_MAX)
     return fail(MI_ATTN_EINVAL, "launch grid too large");
 
   hipStream_t s = static_cast<hipStream_t>(stream);

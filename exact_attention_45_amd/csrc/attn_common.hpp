@@ -38,6 +38,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Value of lane (l ^ 32). ds_bpermute based; well defined for every lane.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// IEEE 754-2019 maximum (NaN-propagating). gfx950 has it as v_maximum3_f32,
+// which needs no input quieting; fmaxf lowers in IEEE mode with a
+// canonicalising v_max_f32 in front of every input that is not the result of
+// ordinary arithmetic (MFMA outputs, lane shuffles), doubling the max cost.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
 __device__ __forceinline__ bf16x4 cvt4(float a, float b, float c, float d) {
   bf16x4 r;
   r[0] = (__bf16)a;
@@ -92,6 +99,40 @@ __device__ __forceinline__ bf16x4 ds_read_tr16(const __bf16* p) {
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
+}
+
+// A wave-uniform int the compiler computed in vector registers (e.g. after a
+// division), moved to a scalar register so loop counters and addresses
+// derived from it stay scalar.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// LDS tile layout shared by the kernels: rows of head_dim bf16 (16-byte
+// chunks), chunk c of row `key` stored at chunk position c ^ swz_key(key).
+// swz_key maps key & 7 onto 0,2,4,6,1,3,5,7: eight consecutive keys reading
+// the same chunk hit eight different 16-byte bank groups (16-byte fragment
+// reads), while the four keys of a transposing read, 4h..4h+3, keep each
+// 32-byte chunk pair together and spread over four pair slots.
+__device__ __forceinline__ int swz_key(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
+
+// Buffer resource over [base, base + num_bytes): raw buffer loads whose byte
+// offset falls outside return zero instead of touching memory. The third
+// descriptor dword 0x00020000 selects the 32-bit data format gfx9-family raw
+// buffer loads use.
+// Arguments must be wave-uniform; readfirstlane states that to the compiler
+// (otherwise it wraps each load in a loop over distinct descriptor values).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(num_bytes);
+  void* b = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // 16-byte global load / store of raw bits.

@@ -227,8 +227,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 
     float mt = kNegInf;
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) mt = fmaxf(mt, fmaxf(s[v], s[v + 1]));
-    mt = fmaxf(mt, xor32(mt));
+    for (int v = 0; v < 16; v += 2) mt = vmax3(mt, s[v], s[v + 1]);
+    mt = vmax(mt, xor32(mt));
     const float m_new = fmaxf(m_run, mt);
     const float ms = (m_new == kNegInf) ? 0.0f : m_new * c;
     // exactly 1 when the max did not move, exactly 0 when nothing was seen

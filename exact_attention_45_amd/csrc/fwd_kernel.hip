@@ -23,19 +23,25 @@
 //     qhead-into-seqlen fold).
 //   * Both GEMMs transposed (attn_common.hpp): one lane owns one query.
 //   * K and V tiles are row-major in LDS with 16-byte chunks XOR-swizzled by
-//     key (chunk ^ 2*(key & 7)); global loads are fully coalesced (16 lanes
-//     per 256-byte row) and the 16-byte LDS stores, the K fragment reads and
-//     the transposing V fragment reads (ds_read_b64_tr_b16) are all free of
-//     bank conflicts.
+//     key (swz_key); global loads are fully coalesced (16 lanes per 256-byte
+//     row) and the 16-byte LDS stores, the K fragment reads and the
+//     transposing V fragment reads (ds_read_b64_tr_b16) are bank-conflict
+//     free.
 //   * Double-buffered LDS, next tile prefetched into registers during the
 //     current tile's math; one barrier per tile. D = 64/128 fit two waves per
 //     SIMD (two workgroups per CU), so one wave's softmax overlaps another's
 //     MFMAs.
+//   * Few VALU instructions outside the softmax itself: the tile loop is
+//     unrolled by two so both LDS buffers sit at compile-time offsets, every
+//     fragment address is a per-lane constant plus an immediate, and K/V rows
+//     are fetched with buffer loads whose descriptor ends at seqlen_k (rows
+//     past it read as zero, no clamping).
 //   * Tiles wholly outside the causal/window band are never visited.
 //   * Grid order: heaviest (latest) query blocks first, KV head fastest, so
 //     round-robin placement keeps each KV head's K/V in a fixed subset of the
 //     8 XCD L2s.
 #include <climits>
+#include <type_traits>
 
 #include "attn_common.hpp"
 #include "kernels.hpp"
@@ -47,25 +53,22 @@ struct FwdCfg {
   static constexpr int BM = kFwdBlockM;      // 128 rows, 4 waves
   static constexpr int BN = kFwdBlockN;      // 64 keys
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
-  static constexpr int ROWS_PER_LD = 64 / CPR;       // rows one wave instruction covers
-  static constexpr int NCH = BN * CPR / 256;         // chunks per thread per tensor
-  static constexpr int TILE = BN * D;                // elements per K (or V) tile
+  static constexpr int RPL = 64 / CPR;       // rows one wave instruction covers
+  static constexpr int NCH = BN * CPR / 256; // chunks per thread per tensor
+  static constexpr int TILE_B = BN * D * 2;  // bytes per K (or V) tile
   static constexpr int WAVES_PER_EU = D <= 128 ? 2 : 1;
-  static constexpr float RESCALE_LOG2 = 8.0f;        // lazy-rescale threshold
+  static constexpr float RESCALE_LOG2 = 8.0f;  // lazy-rescale threshold
 };
-
-// position of chunk c of row `key` inside the swizzled tile row
-template <int D>
-__device__ __forceinline__ int swz(int key, int c) {
-  return D >= 128 ? (c ^ ((key & 7) << 1)) : (c ^ ((key & 3) << 1));
-}
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_EU)))
 void fwd_kernel(const FwdArgs a) {
   using C = FwdCfg<D>;
-  constexpr int BM = C::BM, BN = C::BN, CPR = C::CPR, NCH = C::NCH, TILE = C::TILE;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[4 * TILE];  // K0 V0 K1 V1
+  constexpr int BM = C::BM, BN = C::BN, CPR = C::CPR, RPL = C::RPL, NCH = C::NCH;
+  constexpr int TILE_B = C::TILE_B;
+  constexpr int ROW_B = D * 2;  // bytes per tile row
+  // K0 V0 K1 V1
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -99,6 +102,8 @@ void fwd_kernel(const FwdArgs a) {
     k_base = (int64_t)b * a.k_bs;
     v_base = (int64_t)b * a.v_bs;
   }
+  sq = uniform(sq);
+  sk = uniform(sk);
   const int r = a.group;
   const int rows = sq * r;
   const int row0 = mb * BM;
@@ -115,22 +120,22 @@ void fwd_kernel(const FwdArgs a) {
   const int hi = min(a.wr >= 0 ? pos + off + a.wr : INT_MAX / 2, sk - 1);
 
   // workgroup-wide visible key range
-  const int pos_min = row0 / r;
-  const int pos_max = (min(row0 + BM, rows) - 1) / r;
+  const int pos_min = uniform(row0 / r);
+  const int pos_max = uniform((min(row0 + BM, rows) - 1) / r);
   const int kv_lo = a.wl >= 0 ? max(0, pos_min + off - a.wl) : 0;
   const int kv_hi = a.wr >= 0 ? min(sk, pos_max + off + a.wr + 1) : sk;  // exclusive
-  const int n_begin = kv_lo / BN;
-  const int n_end = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : n_begin;
+  const int n_begin = uniform(kv_lo / BN);
+  const int n_end = uniform(kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : n_begin);
   // a tile [n0, n0+BN) is fully visible to every row iff
   //   n0 + BN <= sk, n0 + BN - 1 <= pos_min + off + wr, n0 >= pos_max + off - wl
   const int full_hi = a.wr >= 0 ? pos_min + off + a.wr : INT_MAX / 2;
   const int full_lo = a.wl >= 0 ? pos_max + off - a.wl : INT_MIN / 2;
 
-  // ---- Q^T fragments (B operand), kept in registers for the whole loop
+  // ---- Q^T fragments (B operand), kept in registers for the whole loop.
+  // Branch-free: invalid lanes read row 0 of head hk*r and zero it (a load
+  // under a divergent branch makes later waits drain every outstanding load).
   const __bf16* qp = static_cast<const __bf16*>(a.q) + q_base + (int64_t)pos * a.q_rs +
                      (int64_t)hq * a.q_hs;
-  // branch-free: invalid lanes read row 0 of head hk*r and zero it afterwards
-  // (a load under a divergent branch makes every later wait drain all loads)
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
@@ -144,77 +149,94 @@ void fwd_kernel(const FwdArgs a) {
   float m_run = kNegInf;
   float l_run = 0.0f;
 
-  // ---- K/V staging: wave instruction u covers ROWS_PER_LD whole rows,
-  // CPR lanes per row (16-byte chunk c = lane % CPR)
+  // ---- K/V staging. Wave instruction u covers RPL whole rows, CPR lanes per
+  // row (chunk ld_c = lane % CPR); row & 7 does not depend on u, so each
+  // lane's LDS store offset is one constant plus an immediate per u.
   const __bf16* kp = static_cast<const __bf16*>(a.k) + k_base + (int64_t)hk * a.k_hs;
   const __bf16* vp = static_cast<const __bf16*>(a.v) + v_base + (int64_t)hk * a.v_hs;
   const int ld_c = lane % CPR;
-  const int ld_r = lane / CPR;
+  const int ld_r = wave * RPL + lane / CPR;  // row within each 4*RPL-row slice u
+  const uint32_t koff = (uint32_t)(ld_r * a.k_rs * 2 + ld_c * 16);
+  const uint32_t voff = (uint32_t)(ld_r * a.v_rs * 2 + ld_c * 16);
+  const int st_off = ld_r * ROW_B + ((ld_c ^ swz_key(ld_r)) * 16);
   uint4 kreg[NCH], vreg[NCH];
 
-  // branch-free loads: rows past seqlen_k re-read the last key (finite data
-  // whose scores are masked), so no divergent branch drains the prefetch
+  // One buffer descriptor per slice u (rows n0 + 4*RPL*u ..), ending at the
+  // last row before seqlen_k: rows past it read as zero. Descriptors live in
+  // scalar registers; each lane keeps a single byte offset per tensor.
   auto load_tile = [&](int n0) {
+    const int nrows = min(sk - n0, BN);  // >= 1
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int row = (u * 4 + wave) * C::ROWS_PER_LD + ld_r;
-      const int key = min(n0 + row, sk - 1);
-      kreg[u] = ld16(kp + (int64_t)key * a.k_rs + ld_c * 8);
-      vreg[u] = ld16(vp + (int64_t)key * a.v_rs + ld_c * 8);
+      const int r0 = u * 4 * RPL;
+      const int left = nrows - r0;
+      const uint32_t kn = left > 0 ? (uint32_t)((left - 1) * a.k_rs * 2 + ROW_B) : 0u;
+      const uint32_t vn = left > 0 ? (uint32_t)((left - 1) * a.v_rs * 2 + ROW_B) : 0u;
+      kreg[u] = buf_ld16(make_rsrc(kp + (int64_t)(n0 + r0) * a.k_rs, kn), koff);
+      vreg[u] = buf_ld16(make_rsrc(vp + (int64_t)(n0 + r0) * a.v_rs, vn), voff);
     }
   };
-  auto store_tile = [&](__bf16* sK, __bf16* sV) {
+  auto store_tile = [&](auto buf_c) {
+    constexpr int KB = decltype(buf_c)::value * 2 * TILE_B;
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int row = (u * 4 + wave) * C::ROWS_PER_LD + ld_r;
-      const int p = row * D + swz<D>(row, ld_c) * 8;
-      *reinterpret_cast<uint4*>(&sK[p]) = kreg[u];
-      *reinterpret_cast<uint4*>(&sV[p]) = vreg[u];
+      *reinterpret_cast<uint4*>(smem + KB + st_off + u * 4 * RPL * ROW_B) = kreg[u];
+      *reinterpret_cast<uint4*>(smem + KB + TILE_B + st_off + u * 4 * RPL * ROW_B) = vreg[u];
     }
   };
 
-  // per-lane constants for the fragment reads
-  // K (A operand of S^T): row kb*32 + c32, chunk 2*cc + half
-  // V (A operand of O^T, transposing read): 16-lane group g = lane/16 reads 4
-  // keys x 16 dims; lane j of the group points at key j/4, dims 4*(j%4)..+3
+  // ---- fragment read offsets (bytes): a per-lane constant + an immediate.
+  // K (A operand of S^T): row kb*32 + c32, chunk 2*cc + half. With f = swz
+  // of the row (same for both 32-row blocks), the chunk lands at
+  // 8*(cc>>2) + ((2*(cc&3) + half) ^ f): four lane patterns.
+  const int fk = swz_key(c32);
+  int k_rd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) k_rd[i] = c32 * ROW_B + (((2 * i + half) ^ fk) * 16);
+  // V (A operand of O^T, transposing read): 16-lane group g reads 4 keys x 16
+  // dims; lane j points at key 4*half + j/4 (+16t, +8 part), dims
+  // 16*(g&1) + 4*(j&3) of d-block db: chunk 4*db + 2*(g&1) + (j&3)/2, lands
+  // at 8*(db>>1) + ((4*(db&1) + chunk%4) ^ f): two lane patterns.
   const int tr_g = lane >> 4;
   const int tr_j = lane & 15;
-  const int tr_key = tr_j >> 2;                       // + key base
-  const int tr_c = (tr_g & 1) * 2 + ((tr_j & 3) >> 1);  // + 4*db
-  const int tr_e = (tr_j & 1) * 4;
+  const int tr_row = 4 * half + (tr_j >> 2);
+  const int tr_c = (tr_g & 1) * 2 + ((tr_j & 3) >> 1);
+  const int fv = swz_key(tr_row);
+  int v_rd[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    v_rd[i] = tr_row * ROW_B + (((4 * i + tr_c) ^ fv) * 16) + (tr_j & 1) * 8;
 
   const float c = a.scale_log2;
   const float rescale_raw = C::RESCALE_LOG2 / fmaxf(c, 1e-30f);
 
-  if (n_begin < n_end) {
-    load_tile(n_begin * BN);
-    store_tile(smem, smem + TILE);
-    __syncthreads();
-  }
-
-  for (int nb = n_begin; nb < n_end; ++nb) {
+  // one tile: compute from LDS buffer `buf`, store the prefetched next tile
+  // into the other buffer, barrier
+  auto step = [&](int nb, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr int KB = buf * 2 * TILE_B;
+    constexpr int VB = KB + TILE_B;
     const int n0 = nb * BN;
-    const int cur = (nb - n_begin) & 1;
-    const __bf16* sK = smem + cur * 2 * TILE;
-    const __bf16* sV = sK + TILE;
     const bool more = nb + 1 < n_end;
     if (more) load_tile(n0 + BN);
 
-    // S^T = K Q^T: two 32-key blocks
+    // S^T = K Q^T: two 32-key blocks. Matrix phases run at raised wave
+    // priority so the SIMD keeps issuing this wave's MFMAs while the other
+    // resident wave's softmax fills the vector-ALU slots.
+    __builtin_amdgcn_s_setprio(1);
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = zero_f32x16();
-      const int key = kb * 32 + c32;
-      const __bf16* krow = sK + key * D;
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(krow + swz<D>(key, 2 * cc + half) * 8);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            smem + KB + kb * 32 * ROW_B + (cc >> 2) * 128 + k_rd[cc & 3]);
         s[kb] = mfma32(kf, qf[cc], s[kb]);
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     const bool full = (n0 + BN <= sk) && (n0 + BN - 1 <= full_hi) && (n0 >= full_lo);
     if (!full) {
 #pragma unroll
@@ -231,8 +253,8 @@ void fwd_kernel(const FwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) mt = fmaxf(mt, fmaxf(s[kb][v], s[kb][v + 1]));
-    mt = fmaxf(mt, xor32(mt));
+      for (int v = 0; v < 16; v += 2) mt = vmax3(mt, s[kb][v], s[kb][v + 1]);
+    mt = vmax(mt, xor32(mt));
     const bool grow = (m_run == kNegInf) ? (mt != kNegInf) : (mt - m_run > rescale_raw);
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = grow ? mt : m_run;
@@ -270,21 +292,31 @@ void fwd_kernel(const FwdArgs a) {
     }
 
     // O^T += V^T P^T, V^T fragments read transposed from row-major V
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int k0 = 16 * t + 4 * half + tr_key;
-        const int k1 = k0 + 8;
-        const int cc = 4 * db + tr_c;
-        const bf16x4 v0 = ds_read_tr16(sV + k0 * D + swz<D>(k0, cc) * 8 + tr_e);
-        const bf16x4 v1 = ds_read_tr16(sV + k1 * D + swz<D>(k1, cc) * 8 + tr_e);
+        const char* vb = smem + VB + (16 * t) * ROW_B + (db >> 1) * 128 + v_rd[db & 1];
+        const bf16x4 v0 = ds_read_tr16(reinterpret_cast<const __bf16*>(vb));
+        const bf16x4 v1 = ds_read_tr16(reinterpret_cast<const __bf16*>(vb + 8 * ROW_B));
         o[db] = mfma32(cat(v0, v1), pf[t], o[db]);
       }
     }
 
-    if (more) store_tile(smem + (cur ^ 1) * 2 * TILE, smem + (cur ^ 1) * 2 * TILE + TILE);
+    __builtin_amdgcn_s_setprio(0);
+    if (more) store_tile(std::integral_constant<int, buf ^ 1>{});
     lds_barrier();  // next buffer written; this buffer free for reuse
+  };
+
+  if (n_begin < n_end) {
+    load_tile(n_begin * BN);
+    store_tile(std::integral_constant<int, 0>{});
+    lds_barrier();
+  }
+  for (int nb = n_begin; nb < n_end; nb += 2) {
+    step(nb, std::integral_constant<int, 0>{});
+    if (nb + 1 < n_end) step(nb + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store
@@ -312,12 +344,21 @@ void fwd_kernel(const FwdArgs a) {
   }
 }
 
+// head_dim 64/128 run the eight-wave ping-pong kernel (fwd_pp_kernel.hip);
+// head_dim 256 needs all 512 registers of a lane for one wave's accumulators,
+// so it runs this four-wave kernel at one wave per SIMD.
 template <int D>
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
-  const int64_t grid = (int64_t)a.num_m_blocks * a.hkv * a.batch;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_kernel<D>, dim3((unsigned)grid), dim3(256), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_fwd(const FwdArgs& args, hipStream_t s) {
+  if constexpr (D <= 128) {
+    return launch_fwd_pp<D>(args, s);
+  } else {
+    FwdArgs a = args;
+    a.num_m_blocks = (int)(((int64_t)a.max_rows + kFwdBlockM - 1) / kFwdBlockM);
+    const int64_t grid = (int64_t)a.num_m_blocks * a.hkv * a.batch;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fwd_kernel<D>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
 }
 
 template hipError_t launch_fwd<64>(const FwdArgs&, hipStream_t);

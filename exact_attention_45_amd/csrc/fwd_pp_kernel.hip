@@ -1,0 +1,385 @@
+// Prefill forward for head_dim 64/128: eight waves in two ping-pong groups.
+//
+// Same method as fwd_kernel.hip (mslk flash_attn interface.py page,
+// `_flash_attn_fwd`: exact attention with online softmax in the exp2 domain
+// and a natural-log LSE; lazily updated running max). What differs is the
+// schedule. A workgroup owns 256 packed query rows: group A = waves 0-3
+// (rows 0-127), group B = waves 4-7 (rows 128-255). Wave w and wave w+4
+// share SIMD w, and the two groups run the same per-tile work offset by half
+// a tile, separated by workgroup barriers:
+//
+//   half-step 2k  : A: MFMA item k      B: softmax of tile k-1
+//   half-step 2k+1: A: softmax of tile k  B: MFMA item k
+//   MFMA item k   = O += P(k-1) V(k-1)  and  S(k) = K(k) Q^T   (32 MFMAs)
+//
+// so on every SIMD one wave keeps the matrix cores busy while the other runs
+// its exponentials; neither waits for the other's phase.
+//
+// K/V tiles (64 keys) rotate through three LDS buffers: tile k is read in
+// half-steps 2k..2k+3, so tile k+1 is stored during half-step 2k into the
+// buffer tile k-2 vacated, and tile k+2 is fetched into registers right
+// after, a full tile ahead of its store. Every load and store is issued
+// unconditionally (tiles past the end re-read the last tile), which keeps the
+// compiler's load-wait counts static.
+#include <climits>
+#include <type_traits>
+
+#include "attn_common.hpp"
+#include "kernels.hpp"
+
+namespace mi_attn {
+
+template <int D>
+struct PPCfg {
+  static constexpr int BM = kFwdPPBlockM;      // 256 packed rows
+  static constexpr int BN = kFwdBlockN;        // 64 keys
+  static constexpr int NT = 512;               // 8 waves
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int RPL = 64 / CPR;         // rows per wave load instruction
+  static constexpr int SLICE = 8 * RPL;        // rows per slice (all 8 waves)
+  static constexpr int NCH = BN * CPR / NT;    // chunks per thread per tensor
+  static constexpr int TILE_B = BN * D * 2;    // bytes per K (or V) tile
+  static constexpr int NBUF = 3;
+  static constexpr float RESCALE_LOG2 = 8.0f;
+  static_assert(NCH * NT == BN * CPR, "tile must split evenly over the workgroup");
+};
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_pp_kernel(const FwdArgs a) {
+  using C = PPCfg<D>;
+  constexpr int BM = C::BM, BN = C::BN, CPR = C::CPR, RPL = C::RPL, NCH = C::NCH;
+  constexpr int TILE_B = C::TILE_B, SLICE = C::SLICE;
+  constexpr int ROW_B = D * 2;
+  constexpr int BUF_B = 2 * TILE_B;  // K then V
+  __shared__ __attribute__((aligned(16))) char smem[C::NBUF * BUF_B];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = wave >> 2;  // 0: group A, 1: group B
+  const int wig = wave & 3;   // wave in group
+  const int c32 = lane & 31;
+  const int half = lane >> 5;
+
+  // ---- work item: heavy query blocks first, (KV head, sequence) fastest
+  const int nhb = a.hkv * a.batch;
+  const int lin = blockIdx.x;
+  const int hb = lin % nhb;
+  const int mb = a.num_m_blocks - 1 - lin / nhb;
+  const int hk = hb % a.hkv;
+  const int b = hb / a.hkv;
+
+  int sq = a.seqlen_q, sk = a.seqlen_k;
+  int64_t q_base, k_base, v_base, o_base;
+  int q_tok0 = 0;
+  if (a.cu_q != nullptr) {
+    q_tok0 = a.cu_q[b];
+    sq = a.cu_q[b + 1] - q_tok0;
+    const int k_tok0 = a.cu_k[b];
+    sk = a.cu_k[b + 1] - k_tok0;
+    q_base = (int64_t)q_tok0 * a.q_rs;
+    o_base = (int64_t)q_tok0 * a.o_rs;
+    k_base = (int64_t)k_tok0 * a.k_rs;
+    v_base = (int64_t)k_tok0 * a.v_rs;
+  } else {
+    q_base = (int64_t)b * a.q_bs;
+    o_base = (int64_t)b * a.o_bs;
+    k_base = (int64_t)b * a.k_bs;
+    v_base = (int64_t)b * a.v_bs;
+  }
+  sq = uniform(sq);
+  sk = uniform(sk);
+  const int r = a.group;
+  const int rows = sq * r;
+  const int row0 = mb * BM;
+  if (row0 >= rows) return;  // uniform over the workgroup
+
+  // ---- this lane's query row
+  const int prow = row0 + grp * 128 + wig * 32 + c32;
+  const bool valid = prow < rows;
+  const int pos = valid ? prow / r : 0;
+  const int hq = hk * r + (valid ? prow - (prow / r) * r : 0);
+
+  const int off = sk - sq;  // bottom-right alignment
+  const int lo = a.wl >= 0 ? pos + off - a.wl : INT_MIN / 2;
+  const int hi = min(a.wr >= 0 ? pos + off + a.wr : INT_MAX / 2, sk - 1);
+
+  // workgroup-wide visible key range (both groups walk the same tiles)
+  const int pos_min = uniform(row0 / r);
+  const int pos_max = uniform((min(row0 + BM, rows) - 1) / r);
+  const int kv_lo = a.wl >= 0 ? max(0, pos_min + off - a.wl) : 0;
+  const int kv_hi = a.wr >= 0 ? min(sk, pos_max + off + a.wr + 1) : sk;  // exclusive
+  const int n_begin = uniform(kv_lo / BN);
+  const int n_end = uniform(kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : n_begin);
+  const int T = n_end - n_begin;
+  // per-group "tile fully visible" bounds (group rows [g0, g1))
+  const int g0 = min(row0 + grp * 128, rows - 1);
+  const int g1 = min(row0 + grp * 128 + 128, rows) - 1;
+  const int gpos_min = uniform(g0 / r);
+  const int gpos_max = uniform(max(g0, g1) / r);
+  const int full_hi = a.wr >= 0 ? gpos_min + off + a.wr : INT_MAX / 2;
+  const int full_lo = a.wl >= 0 ? gpos_max + off - a.wl : INT_MIN / 2;
+
+  // ---- Q^T fragments (B operand). Branch-free: invalid lanes read row 0 of
+  // head hk*r and zero it (a load under a divergent branch makes later waits
+  // drain every outstanding load).
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + q_base + (int64_t)pos * a.q_rs +
+                     (int64_t)hq * a.q_hs;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const bf16x8 x = as_bf16x8(ld16(qp + 16 * c + 8 * half));
+    qf[c] = valid ? x : zero_bf16x8();
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = zero_f32x16();
+  float m_run = kNegInf;
+  float l_run = 0.0f;
+
+  // ---- K/V staging: slice u = rows [u*SLICE, (u+1)*SLICE); within a slice
+  // wave w covers rows w*RPL.., CPR lanes per row. row & 7 is the same in
+  // every slice, so the swizzled store offset is one per-lane constant.
+  const __bf16* kp = static_cast<const __bf16*>(a.k) + k_base + (int64_t)hk * a.k_hs;
+  const __bf16* vp = static_cast<const __bf16*>(a.v) + v_base + (int64_t)hk * a.v_hs;
+  const int ld_c = lane % CPR;
+  const int ld_r = wave * RPL + lane / CPR;
+  uint32_t koff[NCH], voff[NCH];
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    koff[u] = (uint32_t)((ld_r + u * SLICE) * a.k_rs * 2 + ld_c * 16);
+    voff[u] = (uint32_t)((ld_r + u * SLICE) * a.v_rs * 2 + ld_c * 16);
+  }
+  const int st_off = ld_r * ROW_B + ((ld_c ^ swz_key(ld_r)) * 16);
+  uint4 kreg[NCH], vreg[NCH];
+
+  // One buffer descriptor per tensor per tile, ending at the last row before
+  // seqlen_k (rows past it read as zero); its base is the tile's first row.
+  auto load_tile = [&](int n0) {
+    const int nrows = min(sk - n0, BN);  // >= 1
+    const auto kr = make_rsrc(kp + (int64_t)n0 * a.k_rs, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
+    const auto vr = make_rsrc(vp + (int64_t)n0 * a.v_rs, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      kreg[u] = buf_ld16(kr, koff[u]);
+      vreg[u] = buf_ld16(vr, voff[u]);
+    }
+  };
+  auto store_tile = [&](int boff) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      *reinterpret_cast<uint4*>(smem + boff + st_off + u * SLICE * ROW_B) = kreg[u];
+      *reinterpret_cast<uint4*>(smem + boff + TILE_B + st_off + u * SLICE * ROW_B) = vreg[u];
+    }
+  };
+
+  // ---- fragment read offsets: per-lane constant + immediate (see
+  // fwd_kernel.hip for the derivation of the four K and two V patterns)
+  const int fk = swz_key(c32);
+  int k_rd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) k_rd[i] = c32 * ROW_B + (((2 * i + half) ^ fk) * 16);
+  const int tr_g = lane >> 4;
+  const int tr_j = lane & 15;
+  const int tr_row = 4 * half + (tr_j >> 2);
+  const int tr_c = (tr_g & 1) * 2 + ((tr_j & 3) >> 1);
+  const int fv = swz_key(tr_row);
+  int v_rd[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    v_rd[i] = tr_row * ROW_B + (((4 * i + tr_c) ^ fv) * 16) + (tr_j & 1) * 8;
+
+  const float c = a.scale_log2;
+  const float rescale_raw = C::RESCALE_LOG2 / fmaxf(c, 1e-30f);
+
+  f32x16 s[2];
+  bf16x8 pf[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) pf[t] = zero_bf16x8();
+
+  // S(k) = K(k) Q^T into s[]
+  auto s_part = [&](int k) {
+    const char* kb0 = smem + (k % 3) * BUF_B;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = zero_f32x16();
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            kb0 + kb * 32 * ROW_B + (cc >> 2) * 128 + k_rd[cc & 3]);
+        s[kb] = mfma32(kf, qf[cc], s[kb]);
+      }
+    }
+  };
+  // O += P(k) V(k)
+  auto pv_part = [&](int k) {
+    const char* vb = smem + (k % 3) * BUF_B + TILE_B;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const char* p = vb + (16 * t) * ROW_B + (db >> 1) * 128 + v_rd[db & 1];
+        const bf16x4 v0 = ds_read_tr16(reinterpret_cast<const __bf16*>(p));
+        const bf16x4 v1 = ds_read_tr16(reinterpret_cast<const __bf16*>(p + 8 * ROW_B));
+        o[db] = mfma32(cat(v0, v1), pf[t], o[db]);
+      }
+    }
+  };
+  // Issue order for one matrix phase: keep several LDS fragment reads in
+  // flight ahead of the MFMAs that consume them (the default schedule issues
+  // each read right before its MFMA and stalls on LDS latency).
+  constexpr int NMF = D / 16 * 2;  // MFMAs per part (S and P V alike)
+  auto sched_part = [&](auto rpm_c) {
+    constexpr int RPM = decltype(rpm_c)::value;  // LDS reads per MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * RPM, 0);
+#pragma unroll
+    for (int i = 0; i < NMF - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+
+  // MFMA item k: O += P(k-1) V(k-1) (k >= 1), then S(k) = K(k) Q^T (k < T)
+  auto mfma_item = [&](int k) {
+    if (k >= 1) {
+      pv_part(k - 1);
+      sched_part(std::integral_constant<int, 2>{});
+    }
+    if (k < T) {
+      s_part(k);
+      sched_part(std::integral_constant<int, 1>{});
+    }
+  };
+
+  // softmax of S(k) into P(k): mask edge tiles, lazy running max, exp2
+  auto sm_item = [&](int k) {
+    const int n0 = (n_begin + k) * BN;
+    const bool full = (n0 + BN <= sk) && (n0 + BN - 1 <= full_hi) && (n0 >= full_lo);
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = n0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (key < lo || key > hi) s[kb][v] = kNegInf;
+        }
+    }
+    float mt = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) mt = vmax3(mt, s[kb][v], s[kb][v + 1]);
+    mt = vmax(mt, xor32(mt));
+    const bool grow = (m_run == kNegInf) ? (mt != kNegInf) : (mt - m_run > rescale_raw);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = grow ? ((m_run == kNegInf) ? 0.0f : fast_exp2((m_run - m_new) * c))
+                               : 1.0f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    }
+    const float ms = (m_run == kNegInf) ? 0.0f : m_run * c;
+    float rs = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = fast_exp2(fmaf(s[kb][v], c, -ms));
+        s[kb][v] = p;
+        rs += p;
+      }
+    l_run += rs;
+    // P^T fragments in the key order of the V^T fragments (fwd_kernel.hip)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kb = t >> 1;
+      const int i0 = 2 * (t & 1);
+      pf[t] = cat(cvt4(s[kb][4 * i0 + 0], s[kb][4 * i0 + 1], s[kb][4 * i0 + 2], s[kb][4 * i0 + 3]),
+                  cvt4(s[kb][4 * i0 + 4], s[kb][4 * i0 + 5], s[kb][4 * i0 + 6], s[kb][4 * i0 + 7]));
+    }
+  };
+
+  if (T > 0) {
+    // prologue: tile 0 in buffer 0, tile 1 (or a re-read of tile 0) in flight
+    load_tile(n_begin * BN);
+    store_tile(0);
+    load_tile(min(n_begin + 1, n_end - 1) * BN);
+    lds_barrier();
+    for (int k = 0; k < T; ++k) {
+      // half-step 2k: everyone stages tile k+1 into the buffer tile k-2 left
+      // (its last reader finished before the previous barrier) and fetches
+      // tile k+2; the stores drain under this half-step's work. Then A does
+      // matrix work and B the softmax.
+      store_tile(((k + 1) % 3) * BUF_B);
+      load_tile(min(n_begin + k + 2, n_end - 1) * BN);
+      if (grp == 0) {
+        __builtin_amdgcn_s_setprio(1);
+        mfma_item(k);
+        __builtin_amdgcn_s_setprio(0);
+      } else if (k >= 1) {
+        sm_item(k - 1);
+      }
+      lds_barrier();
+      // half-step 2k+1: A softmax, B matrix work
+      if (grp == 0) {
+        sm_item(k);
+      } else {
+        __builtin_amdgcn_s_setprio(1);
+        mfma_item(k);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      lds_barrier();
+    }
+    // tail: the last P V products
+    if (grp == 0) mfma_item(T);
+    else sm_item(T - 1);
+    lds_barrier();
+    if (grp == 1) mfma_item(T);
+  }
+
+  // ---- epilogue: combine the two lane halves' row sums, normalise, store
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (valid) {
+    __bf16* op = static_cast<__bf16*>(a.out) + o_base + (int64_t)pos * a.o_rs +
+                 (int64_t)hq * a.o_hs;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * half;
+        *reinterpret_cast<bf16x4*>(op + d0) =
+            cvt4(o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
+                 o[db][4 * i + 3] * inv);
+      }
+    if (half == 0 && a.lse != nullptr) {
+      const float lse = l_tot > 0.0f ? m_run * a.scale + __logf(l_tot) : kNegInf;
+      const int64_t li = a.cu_q != nullptr
+                             ? (int64_t)hq * a.total_q + q_tok0 + pos
+                             : ((int64_t)b * a.hq + hq) * sq + pos;
+      a.lse[li] = lse;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_fwd_pp(const FwdArgs& args, hipStream_t s) {
+  FwdArgs a = args;
+  a.num_m_blocks = (int)(((int64_t)a.max_rows + kFwdPPBlockM - 1) / kFwdPPBlockM);
+  const int64_t grid = (int64_t)a.num_m_blocks * a.hkv * a.batch;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fwd_pp_kernel<D>, dim3((unsigned)grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_fwd_pp<64>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd_pp<128>(const FwdArgs&, hipStream_t);
+
+}  // namespace mi_attn

@@ -23,7 +23,8 @@ struct FwdArgs {
   int32_t batch, seqlen_q, seqlen_k;
   int32_t hq, hkv, group;  // group = hq / hkv
   int32_t total_q;
-  int32_t num_m_blocks;    // ceil(max_seqlen_q * group / BLOCK_M)
+  int32_t max_rows;        // max_seqlen_q * group (packed rows of the longest sequence)
+  int32_t num_m_blocks;    // set by each launcher: ceil(max_rows / its BLOCK_M)
   float scale;             // softmax_scale
   float scale_log2;        // softmax_scale * log2(e)
   int32_t wl, wr;
@@ -57,11 +58,13 @@ struct CombineArgs {
   int32_t rows, num_splits;
 };
 
-constexpr int kFwdBlockM = 128;   // packed query rows per workgroup (4 waves x 32)
+constexpr int kFwdBlockM = 128;   // packed query rows per workgroup (4 waves x 32), D = 256
+constexpr int kFwdPPBlockM = 256; // ping-pong kernel, D = 64/128 (8 waves x 32)
 constexpr int kFwdBlockN = 64;    // keys per K/V tile
 constexpr int kDecBlockN = 128;   // keys per decode tile (4 waves x 32)
 
 template <int D> hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
+template <int D> hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t s);
 template <int D> hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 template <int D> hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
