@@ -32,6 +32,50 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "exact_attention_45_amd", "csrc")
+# sources whose compiled code the counted kernels consist of
+KERNEL_SOURCES = {
+    "fwd_pp_kernel<128>": ["fwd_pp_kernel.hip", "attn_common.hpp", "kernels.hpp"],
+    "decode_split_kernel<128>": ["decode_kernel.hip", "attn_common.hpp", "kernels.hpp"],
+    "combine_kernel<128>": ["decode_kernel.hip", "attn_common.hpp", "kernels.hpp"],
+}
+COUNTER_SUMMARY = os.path.join(
+    HERE, "profiles", "hbm_counters_prefill_s4096_d128_and_paged_decode_sk32768.md")
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(*kernels: str):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch, summed over `kernels`,
+    read from the committed counter summary; None when the summary has no
+    line for one of them or its sources changed since the counters were taken."""
+    try:
+        with open(COUNTER_SUMMARY) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    found = {}
+    for ln in lines:
+        if ln.startswith("traffic: "):
+            kv = dict(t.split("=", 1) for t in ln[len("traffic: "):].split())
+            found[kv.get("kernel")] = kv
+    total = 0
+    for k in kernels:
+        kv = found.get(k)
+        if kv is None or kv.get("source_sha256") != source_digest(k):
+            return None
+        total += int(kv["fetch_bytes"]) + int(kv["write_bytes"])
+    return total
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -280,14 +324,16 @@ def main():
         },
         "roofline": {
             "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-            "kernel": "fwd_kernel<128>", "avg_launch_us": round(pre_avg * 1e3, 2),
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": counter_traffic("fwd_pp_kernel<128>"),
+            "kernel": "fwd_pp_kernel<128>", "avg_launch_us": round(pre_avg * 1e3, 2),
         },
         "cpu_baseline": cpu,
         "decode": {
             "value": round(gbs, 1), "unit": "GB/s", "avg_launch_us": round(dec_avg * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": counter_traffic("decode_split_kernel<128>", "combine_kernel<128>"),
                          "kernel": "decode_split_kernel<128> + combine_kernel<128>"},
         },
     }
