@@ -36,7 +36,18 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Value of lane (l ^ 32). ds_bpermute based; well defined for every lane.
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Reductions over the lane pair (l, l ^ 32) without LDS traffic:
+// v_permlane32_swap with both operands x leaves, in every lane l, x of lane
+// l % 32 in the first result and x of lane l % 32 + 32 in the second (both
+// halves then combine the same two values in the same order).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // IEEE 754-2019 maximum (NaN-propagating). gfx950 has it as v_maximum3_f32,
 // which needs no input quieting; fmaxf lowers in IEEE mode with a
@@ -133,6 +144,50 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t byt
   typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// LDS byte address (offset within the workgroup's LDS) of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Direct global-to-LDS load (gfx950 buffer_load_dwordx4 ... lds): lane i's 16
+// bytes at buffer offset voff land at LDS address lds_base + 16 * i, with
+// lds_base wave-uniform (it goes through M0). No registers are staged.
+// Issued as inline asm: the compiler cannot tell which LDS buffer such a load
+// writes when buffers rotate at run time, and for its own builtin it would
+// then wait for every outstanding load before each later LDS read. Loads the
+// compiler does not count only make its own vmcnt waits stricter; the caller
+// waits for these itself (vmcnt_wait, then a barrier for other waves' loads).
+// The kernels keep nothing in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(lds_base)
+      : "memory", "m0");
+}
+// Same load without touching M0 (it must still hold the LDS base of an
+// earlier dma16): the immediate OFF shifts both the LDS destination and the
+// global offset; soff (wave-uniform) adds to the global offset only.
+template <int OFF>
+__device__ __forceinline__ void dma16_same_m0(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
+               :
+               : "v"(voff), "s"(r), "s"(soff), "i"(OFF)
+               : "memory");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 // 16-byte global load / store of raw bits.

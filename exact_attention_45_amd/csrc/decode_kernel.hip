@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     float mt = kNegInf;
 #pragma unroll
     for (int v = 0; v < 16; v += 2) mt = vmax3(mt, s[v], s[v + 1]);
-    mt = vmax(mt, xor32(mt));
+    mt = pair_max(mt);
     const float m_new = fmaxf(m_run, mt);
     const float ms = (m_new == kNegInf) ? 0.0f : m_new * c;
     // exactly 1 when the max did not move, exactly 0 when nothing was seen
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   }
 
   // ---- merge the four waves' partial states through LDS
-  const float l_wave = l_run + xor32(l_run);
+  const float l_wave = pair_sum(l_run);
   const int any_bad = __syncthreads_or(bad_page ? 1 : 0);
   float* sO = reinterpret_cast<float*>(smem);          // [wave][d][32]
   float* sM = sO + 4 * D * 32;                          // [wave][32]

@@ -254,7 +254,7 @@ void fwd_kernel(const FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; v += 2) mt = vmax3(mt, s[kb][v], s[kb][v + 1]);
-    mt = vmax(mt, xor32(mt));
+    mt = pair_max(mt);
     const bool grow = (m_run == kNegInf) ? (mt != kNegInf) : (mt - m_run > rescale_raw);
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = grow ? mt : m_run;
@@ -320,7 +320,7 @@ void fwd_kernel(const FwdArgs a) {
   }
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (valid) {
     __bf16* op = static_cast<__bf16*>(a.out) + o_base + (int64_t)pos * a.o_rs +

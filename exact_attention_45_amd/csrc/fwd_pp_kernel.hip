@@ -35,21 +35,18 @@ struct PPCfg {
   static constexpr int BN = kFwdBlockN;        // 64 keys
   static constexpr int NT = 512;               // 8 waves
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
-  static constexpr int RPL = 64 / CPR;         // rows per wave load instruction
-  static constexpr int SLICE = 8 * RPL;        // rows per slice (all 8 waves)
-  static constexpr int NCH = BN * CPR / NT;    // chunks per thread per tensor
   static constexpr int TILE_B = BN * D * 2;    // bytes per K (or V) tile
-  static constexpr int NBUF = 3;
+  static constexpr int NBUF = 4;
   static constexpr float RESCALE_LOG2 = 8.0f;
-  static_assert(NCH * NT == BN * CPR, "tile must split evenly over the workgroup");
+  static_assert(BN == 64 && (CPR == 8 || CPR == 16), "staging assumes 64-key tiles, D 64/128");
 };
 
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_pp_kernel(const FwdArgs a) {
   using C = PPCfg<D>;
-  constexpr int BM = C::BM, BN = C::BN, CPR = C::CPR, RPL = C::RPL, NCH = C::NCH;
-  constexpr int TILE_B = C::TILE_B, SLICE = C::SLICE;
+  constexpr int BM = C::BM, BN = C::BN, CPR = C::CPR;
+  constexpr int TILE_B = C::TILE_B;
   constexpr int ROW_B = D * 2;
   constexpr int BUF_B = 2 * TILE_B;  // K then V
   __shared__ __attribute__((aligned(16))) char smem[C::NBUF * BUF_B];
@@ -139,40 +136,49 @@ void fwd_pp_kernel(const FwdArgs a) {
   float m_run = kNegInf;
   float l_run = 0.0f;
 
-  // ---- K/V staging: slice u = rows [u*SLICE, (u+1)*SLICE); within a slice
-  // wave w covers rows w*RPL.., CPR lanes per row. row & 7 is the same in
-  // every slice, so the swizzled store offset is one per-lane constant.
+  // ---- K/V tiles go global -> LDS directly (dma16), 1 KB per wave
+  // instruction, nothing staged in registers. For each tensor, instruction i
+  // of wave w fills LDS rows RPI*(NI*w + i) .. +RPI-1: lane j lands at row
+  // offset j / CPR, physical chunk j % CPR, so it loads the logical chunk
+  // (j % CPR) ^ swz_key(row) of that row.
+  constexpr int RPI = 1024 / ROW_B;  // rows per DMA instruction
+  constexpr int NI = BN / RPI / 8;   // DMA instructions per wave per tensor
+  static_assert(NI * RPI * 8 == BN, "a tile splits evenly over eight waves");
   const __bf16* kp = static_cast<const __bf16*>(a.k) + k_base + (int64_t)hk * a.k_hs;
   const __bf16* vp = static_cast<const __bf16*>(a.v) + v_base + (int64_t)hk * a.v_hs;
-  const int ld_c = lane % CPR;
-  const int ld_r = wave * RPL + lane / CPR;
-  uint32_t koff[NCH], voff[NCH];
+  uint32_t kdo[NI], vdo[NI];
 #pragma unroll
-  for (int u = 0; u < NCH; ++u) {
-    koff[u] = (uint32_t)((ld_r + u * SLICE) * a.k_rs * 2 + ld_c * 16);
-    voff[u] = (uint32_t)((ld_r + u * SLICE) * a.v_rs * 2 + ld_c * 16);
+  for (int i = 0; i < NI; ++i) {
+    const int row = RPI * (NI * wave + i) + lane / CPR;
+    const int ch = (lane % CPR) ^ swz_key(row);
+    kdo[i] = (uint32_t)(row * a.k_rs * 2 + ch * 16);
+    vdo[i] = (uint32_t)(row * a.v_rs * 2 + ch * 16);
   }
-  const int st_off = ld_r * ROW_B + ((ld_c ^ swz_key(ld_r)) * 16);
-  uint4 kreg[NCH], vreg[NCH];
+  const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
 
   // One buffer descriptor per tensor per tile, ending at the last row before
   // seqlen_k (rows past it read as zero); its base is the tile's first row.
-  auto load_tile = [&](int n0) {
+  auto k_rsrc = [&](int n0) {
     const int nrows = min(sk - n0, BN);  // >= 1
-    const auto kr = make_rsrc(kp + (int64_t)n0 * a.k_rs, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
-    const auto vr = make_rsrc(vp + (int64_t)n0 * a.v_rs, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
-#pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      kreg[u] = buf_ld16(kr, koff[u]);
-      vreg[u] = buf_ld16(vr, voff[u]);
-    }
+    return make_rsrc(kp + (int64_t)n0 * a.k_rs, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
   };
-  auto store_tile = [&](int boff) {
+  auto v_rsrc = [&](int n0) {
+    const int nrows = min(sk - n0, BN);
+    return make_rsrc(vp + (int64_t)n0 * a.v_rs, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
+  };
+  // this wave's loads of the tile at key n0 into LDS buffer buf: K parts
+  // i = 0..NI-1, then V parts
+  auto dma_k = [&](int n0, int buf, int i) {
+    dma16(k_rsrc(n0), kdo[i], lds_w + (uint32_t)(buf * BUF_B + i * 1024));
+  };
+  auto dma_v = [&](int n0, int buf, int i) {
+    dma16(v_rsrc(n0), vdo[i], lds_w + (uint32_t)(buf * BUF_B + TILE_B + i * 1024));
+  };
+  auto issue_tile = [&](int n0, int buf) {
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      *reinterpret_cast<uint4*>(smem + boff + st_off + u * SLICE * ROW_B) = kreg[u];
-      *reinterpret_cast<uint4*>(smem + boff + TILE_B + st_off + u * SLICE * ROW_B) = vreg[u];
-    }
+    for (int i = 0; i < NI; ++i) dma_k(n0, buf, i);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma_v(n0, buf, i);
   };
 
   // ---- fragment read offsets: per-lane constant + immediate (see
@@ -201,7 +207,7 @@ void fwd_pp_kernel(const FwdArgs a) {
 
   // S(k) = K(k) Q^T into s[]
   auto s_part = [&](int k) {
-    const char* kb0 = smem + (k % 3) * BUF_B;
+    const char* kb0 = smem + (k & 3) * BUF_B;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = zero_f32x16();
@@ -213,9 +219,9 @@ void fwd_pp_kernel(const FwdArgs a) {
       }
     }
   };
-  // O += P(k) V(k)
+  // O += P(k) V(k); V^T fragments from row-major V by transposing reads
   auto pv_part = [&](int k) {
-    const char* vb = smem + (k % 3) * BUF_B + TILE_B;
+    const char* vb = smem + (k & 3) * BUF_B + TILE_B;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -232,12 +238,12 @@ void fwd_pp_kernel(const FwdArgs a) {
   // each read right before its MFMA and stalls on LDS latency).
   constexpr int NMF = D / 16 * 2;  // MFMAs per part (S and P V alike)
   auto sched_part = [&](auto rpm_c) {
-    constexpr int RPM = decltype(rpm_c)::value;  // LDS reads per MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * RPM, 0);
+    constexpr int R = decltype(rpm_c)::value;  // LDS reads per MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * R, 0);
 #pragma unroll
     for (int i = 0; i < NMF - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
@@ -267,12 +273,14 @@ void fwd_pp_kernel(const FwdArgs a) {
           if (key < lo || key > hi) s[kb][v] = kNegInf;
         }
     }
-    float mt = kNegInf;
+    // two independent max chains (one per 32-key half), then the lane pair
+    float m0 = kNegInf, m1 = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) mt = vmax3(mt, s[kb][v], s[kb][v + 1]);
-    mt = vmax(mt, xor32(mt));
+    for (int v = 0; v < 16; v += 2) {
+      m0 = vmax3(m0, s[0][v], s[0][v + 1]);
+      m1 = vmax3(m1, s[1][v], s[1][v + 1]);
+    }
+    const float mt = pair_max(vmax(m0, m1));
     const bool grow = (m_run == kNegInf) ? (mt != kNegInf) : (mt - m_run > rescale_raw);
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = grow ? mt : m_run;
@@ -286,16 +294,18 @@ void fwd_pp_kernel(const FwdArgs a) {
         for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
     }
     const float ms = (m_run == kNegInf) ? 0.0f : m_run * c;
-    float rs = 0.0f;
+    // four partial row sums keep the adds off one serial chain
+    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float p = fast_exp2(fmaf(s[kb][v], c, -ms));
         s[kb][v] = p;
-        rs += p;
+        rs[v & 3] += p;
       }
-    l_run += rs;
+    }
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     // P^T fragments in the key order of the V^T fragments (fwd_kernel.hip)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -307,18 +317,22 @@ void fwd_pp_kernel(const FwdArgs a) {
   };
 
   if (T > 0) {
-    // prologue: tile 0 in buffer 0, tile 1 (or a re-read of tile 0) in flight
-    load_tile(n_begin * BN);
-    store_tile(0);
-    load_tile(min(n_begin + 1, n_end - 1) * BN);
+    // prologue: tiles 0 and 1 (or a re-read of tile 0) in flight; wait for
+    // tile 0 (this wave's part), then the barrier makes all parts visible
+    issue_tile(n_begin * BN, 0);
+    issue_tile(min(n_begin + 1, n_end - 1) * BN, 1);
+    vmcnt_wait<2 * NI>();
     lds_barrier();
     for (int k = 0; k < T; ++k) {
-      // half-step 2k: everyone stages tile k+1 into the buffer tile k-2 left
-      // (its last reader finished before the previous barrier) and fetches
-      // tile k+2; the stores drain under this half-step's work. Then A does
-      // matrix work and B the softmax.
-      store_tile(((k + 1) % 3) * BUF_B);
-      load_tile(min(n_begin + k + 2, n_end - 1) * BN);
+      // tile k+2 goes into the buffer tile k-2 left (its last reader finished
+      // before the previous barrier). Each group issues its loads at the
+      // start of its softmax half-step (B: 2k, A: 2k+1): loads issued by all
+      // eight waves at the same instant queue behind each other in the CU's
+      // load path.
+      const int dn0 = min(n_begin + k + 2, n_end - 1) * BN;
+      const int dbuf = (k + 2) & 3;
+      // half-step 2k: A matrix work, B softmax
+      if (grp == 1) issue_tile(dn0, dbuf);
       if (grp == 0) {
         __builtin_amdgcn_s_setprio(1);
         mfma_item(k);
@@ -327,7 +341,9 @@ void fwd_pp_kernel(const FwdArgs a) {
         sm_item(k - 1);
       }
       lds_barrier();
-      // half-step 2k+1: A softmax, B matrix work
+      // half-step 2k+1: A softmax, B matrix work; then tile k+1 must have
+      // landed (only tile k+2's loads may still be in flight)
+      if (grp == 0) issue_tile(dn0, dbuf);
       if (grp == 0) {
         sm_item(k);
       } else {
@@ -335,17 +351,24 @@ void fwd_pp_kernel(const FwdArgs a) {
         mfma_item(k);
         __builtin_amdgcn_s_setprio(0);
       }
+      vmcnt_wait<2 * NI>();
       lds_barrier();
     }
     // tail: the last P V products
-    if (grp == 0) mfma_item(T);
-    else sm_item(T - 1);
+    if (grp == 0) {
+      mfma_item(T);
+    } else {
+      sm_item(T - 1);
+    }
     lds_barrier();
     if (grp == 1) mfma_item(T);
+    // the last re-read tiles may still be landing; none may outlive the
+    // workgroup's LDS
+    vmcnt_wait<0>();
   }
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (valid) {
     __bf16* op = static_cast<__bf16*>(a.out) + o_base + (int64_t)pos * a.o_rs +
