@@ -140,19 +140,27 @@ void fwd_pp_kernel(const FwdArgs a) {
   // instruction, nothing staged in registers. For each tensor, instruction i
   // of wave w fills LDS rows RPI*(NI*w + i) .. +RPI-1: lane j lands at row
   // offset j / CPR, physical chunk j % CPR, so it loads the logical chunk
-  // (j % CPR) ^ swz_key(row) of that row.
+  // (j % CPR) ^ swizzle(row) of that row.
+  // K has its own swizzle, conflict-free for the 16-byte fragment reads (the
+  // 16 lanes an LDS cycle serves read one logical chunk of 16 consecutive
+  // keys): D = 128 (16 chunks per 256-byte row): kswz(key) = swz_key(key)
+  // with bit 3 = key bit 3, covering all 16 positions; D = 64 (two 128-byte
+  // rows per bank window): kswz(key) = (key >> 1) & 7. V keeps swz_key for
+  // its transposing reads.
   constexpr int RPI = 1024 / ROW_B;  // rows per DMA instruction
   constexpr int NI = BN / RPI / 8;   // DMA instructions per wave per tensor
   static_assert(NI * RPI * 8 == BN, "a tile splits evenly over eight waves");
   const __bf16* kp = static_cast<const __bf16*>(a.k) + k_base + (int64_t)hk * a.k_hs;
   const __bf16* vp = static_cast<const __bf16*>(a.v) + v_base + (int64_t)hk * a.v_hs;
+  auto kswz = [](int key) {
+    return D == 128 ? (swz_key(key) | (((key >> 3) & 1) << 3)) : ((key >> 1) & 7);
+  };
   uint32_t kdo[NI], vdo[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int row = RPI * (NI * wave + i) + lane / CPR;
-    const int ch = (lane % CPR) ^ swz_key(row);
-    kdo[i] = (uint32_t)(row * a.k_rs * 2 + ch * 16);
-    vdo[i] = (uint32_t)(row * a.v_rs * 2 + ch * 16);
+    kdo[i] = (uint32_t)(row * a.k_rs * 2 + ((lane % CPR) ^ kswz(row)) * 16);
+    vdo[i] = (uint32_t)(row * a.v_rs * 2 + ((lane % CPR) ^ swz_key(row)) * 16);
   }
   const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
 
@@ -181,12 +189,14 @@ void fwd_pp_kernel(const FwdArgs a) {
     for (int i = 0; i < NI; ++i) dma_v(n0, buf, i);
   };
 
-  // ---- fragment read offsets: per-lane constant + immediate (see
-  // fwd_kernel.hip for the derivation of the four K and two V patterns)
-  const int fk = swz_key(c32);
-  int k_rd[4];
+  // ---- fragment read offsets. K: lane (c32, half) reads logical chunk
+  // 2*cc + half of key c32 (+32 for the second key block, which has the same
+  // swizzle). V: per-lane constant + immediate (see fwd_kernel.hip for the
+  // derivation of the two transposing-read patterns).
+  const int fk = kswz(c32);
+  int k_rd[D / 16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) k_rd[i] = c32 * ROW_B + (((2 * i + half) ^ fk) * 16);
+  for (int cc = 0; cc < D / 16; ++cc) k_rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ fk) * 16);
   const int tr_g = lane >> 4;
   const int tr_j = lane & 15;
   const int tr_row = 4 * half + (tr_j >> 2);
@@ -213,8 +223,7 @@ void fwd_pp_kernel(const FwdArgs a) {
       s[kb] = zero_f32x16();
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            kb0 + kb * 32 * ROW_B + (cc >> 2) * 128 + k_rd[cc & 3]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb0 + kb * 32 * ROW_B + k_rd[cc]);
         s[kb] = mfma32(kf, qf[cc], s[kb]);
       }
     }
