@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmiattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "fwd_kernel.hip", "fwd_pp_kernel.hip", "decode_kernel.hip"]
+SOURCES = ["api.hip", "fwd_kernel.hip", "fwd_pp_kernel.hip", "decode_kernel.hip",
+           "decode_stream_kernel.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code; scalar/float2 math

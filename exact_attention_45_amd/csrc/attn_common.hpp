@@ -55,6 +55,23 @@ __device__ __forceinline__ float pair_sum(float x) {
 // ordinary arithmetic (MFMA outputs, lane shuffles), doubling the max cost.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+__device__ __forceinline__ float vmin(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+
+// Masking without vector compares (each compare result takes a scalar
+// register pair, and unrolled over a tile they exhaust the scalar file).
+// vis64 sets bit l for the local key offsets l in [r0, r1] of a 64-key
+// window; mask_by_bit keeps x when bit `bit` of `word` is set and otherwise
+// returns -inf, as min(x, +inf) or min(x, -inf).
+__device__ __forceinline__ uint64_t vis64(int r0, int r1) {
+  const int a0 = r0 < 0 ? 0 : r0;
+  const int a1 = r1 > 63 ? 63 : r1;
+  if (a0 > a1) return 0;
+  return (~0ull >> (63 - a1)) & (~0ull << a0);
+}
+__device__ __forceinline__ float mask_by_bit(float x, uint32_t word, int bit) {
+  const uint32_t keep = (word >> bit) & 1u;
+  return vmin(x, __uint_as_float(0xFF800000u ^ (keep << 31)));
+}
 
 __device__ __forceinline__ bf16x4 cvt4(float a, float b, float c, float d) {
   bf16x4 r;

@@ -1,0 +1,345 @@
+// Split-KV decode over a paged K/V cache: per-wave streaming variant, used
+// when every aligned 32-key slice lies inside one page (page_size a multiple
+// of 32) and head_dim is 64 or 128.
+//
+// Same method as decode_kernel.hip (split-K decoding page, triton_splitk.py
+// `FwOp.apply`; interface page, the num_splits path of `_flash_attn_fwd`):
+// each split writes a normalised fp32 partial O_s and its LSE_s, and the
+// combine kernel merges them by LSE weights. What differs is how the bytes
+// move. Decode reads every K/V byte once, so the kernel is a streaming
+// kernel whose speed is the number of bytes it keeps in flight:
+//   * A workgroup (4 waves) owns one (sequence, KV head, 32-head row block,
+//     split). The split's keys are cut into 32-key slices aligned to absolute
+//     key multiples of 32; wave w takes slices w, w+4, w+8, ... and keeps its
+//     own running (max, sum, O). Waves never wait for each other until the
+//     final merge: no barrier in the loop.
+//   * K and V of a slice are loaded into registers with 16-byte loads in row
+//     order (each instruction reads four whole 256-byte rows: measured on
+//     MI355X, reading a head's rows this way streams at ~6.5 TB/s, while the
+//     MFMA-fragment order, 32 rows x 32 bytes per instruction, manages ~3.9).
+//     Both go to a wave-private LDS slot just before use; K is read back as
+//     MFMA fragments, V with transposing reads. NS register sets per wave:
+//     slice i+NS-1 is requested while slice i is computed, 16 KB per wave in
+//     flight per set (registers, not LDS, are the large buffer here: a wave
+//     may hold 512 of them).
+//   * The slot loop is unrolled NS times so every register set is named at
+//     compile time and the compiler derives each load-count wait itself.
+//   * A slice sits in one page, so its page id is one scalar load and its K
+//     and V rows are reached through one buffer descriptor per tensor whose
+//     bound ends at the last key before seqused_k: rows past it read as zero.
+//   * A page id outside [0, num_pages), or a seqused_k outside [0, capacity],
+//     is never dereferenced and turns the split's partial into NaN.
+#include <climits>
+#include <type_traits>
+
+#include "attn_common.hpp"
+#include "kernels.hpp"
+
+namespace mi_attn {
+
+template <int D>
+struct StreamCfg {
+  static constexpr int NS = 3;                  // K/V register sets per wave
+  static constexpr int SLICE = 32;              // keys per slice
+  static constexpr int ROW_B = D * 2;           // bytes per K/V row
+  static constexpr int SLICE_B = SLICE * ROW_B; // bytes per K (or V) slice
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int RPL = 64 / CPR;          // rows per load instruction
+  static constexpr int NLD = SLICE / RPL;       // load instructions per tensor per slice
+  static constexpr int SLOT_B = 4 * 2 * SLICE_B; // K and V slots of the four waves
+  static constexpr int MERGE_B = (4 * D * 32 + 2 * 4 * 32) * 4;  // end-of-split merge
+  static constexpr int LDS_B = SLOT_B > MERGE_B ? SLOT_B : MERGE_B;
+};
+
+// LDS chunk position of logical 16-byte chunk c of V row `key`. The XOR
+// spreads the eight keys of a transposing read over distinct bank groups; it
+// is an involution, so it also maps a physical position back to its chunk.
+template <int D>
+__device__ __forceinline__ int vswz(int key, int c) {
+  return D >= 128 ? (c ^ ((key & 7) << 1)) : (c ^ ((key & 3) << 1));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) {
+  using C = StreamCfg<D>;
+  constexpr int NS = C::NS, ROW_B = C::ROW_B, SLICE_B = C::SLICE_B, CPR = C::CPR;
+  constexpr int RPL = C::RPL, NLD = C::NLD;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_B];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int c32 = lane & 31;
+  const int half = lane >> 5;
+
+  // ---- work item: split fastest, then row block, KV head, sequence
+  int lin = blockIdx.x;
+  const int split = lin % a.num_splits;
+  lin /= a.num_splits;
+  const int rb = lin % a.row_blocks;
+  lin /= a.row_blocks;
+  const int hk = lin % a.hkv;
+  const int b = lin / a.hkv;
+
+  const int cap = a.max_pages * a.page_size;
+  int sk = a.seqused_k != nullptr ? a.seqused_k[b] : cap;
+  bool bad = sk < 0 || sk > cap;  // would index past the page-table row
+  sk = uniform(min(max(sk, 0), cap));
+  // the query sits at position sk - 1; a left window keeps the last wl+1 keys
+  const int kv_lo = uniform(a.wl >= 0 ? max(0, sk - 1 - a.wl) : 0);
+  // this split's slices [m_lo, m_hi) of the visible ones
+  const int m_first = kv_lo / 32;
+  const int n_sl = sk > kv_lo ? (sk - 1) / 32 - m_first + 1 : 0;
+  const int per = (n_sl + a.num_splits - 1) / a.num_splits;
+  const int m_lo = uniform(m_first + min(n_sl, split * per));
+  const int m_hi = uniform(m_first + min(n_sl, (split + 1) * per));
+  // this wave's slices m_lo + wave + 4i, i < n_w; padded to a multiple of NS
+  const int n_w = uniform(m_hi - m_lo > wave ? (m_hi - m_lo - wave + 3) / 4 : 0);
+  const int n_pad = (n_w + NS - 1) / NS * NS;
+
+  // ---- this lane's query head (MFMA B operand)
+  const int col = rb * 32 + c32;
+  const bool valid = col < a.group;
+  const int hq = hk * a.group + (valid ? col : 0);
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + (int64_t)b * a.q_bs + (int64_t)hq * a.q_hs;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) {
+    const bf16x8 x = as_bf16x8(ld16(qp + 16 * cc + 8 * half));
+    qf[cc] = valid ? x : zero_bf16x8();
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = zero_f32x16();
+  float m_run = kNegInf;
+  float l_run = 0.0f;
+  const float c = a.scale_log2;
+
+  // ---- slice addressing
+  const int64_t ts2 = (int64_t)a.hkv * ROW_B;  // bytes between consecutive tokens
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)hk * ROW_B;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)hk * ROW_B;
+  const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
+  // loads: instruction u covers slice rows RPL*u .. +RPL-1, lane j row
+  // RPL*u + j / CPR at chunk j % CPR
+  const int ld_r = lane / CPR;
+  const int ld_c = lane % CPR;
+  const uint32_t ld_off = (uint32_t)(ld_r * ts2 + ld_c * 16);
+  // K slot: chunk c of row r at position c ^ kswz(r), conflict-free for the
+  // fragment reads (16 lanes read one logical chunk of 16 consecutive keys);
+  // V slot: chunk c at vswz(r, c), for the transposing reads
+  auto kswz = [](int key) {
+    return D == 128 ? (((key & 3) << 1) | ((key >> 2) & 1) | (((key >> 3) & 1) << 3)) : ((key >> 1) & 7);
+  };
+  char* kslot = smem + wave * 2 * SLICE_B;
+  char* vslot = kslot + SLICE_B;
+  // over the load instructions u, kswz(row) repeats with period 4 and
+  // vswz(row, .) with period 2
+  int k_st[4], v_st[2];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int row = RPL * p + ld_r;
+    k_st[p] = row * ROW_B + ((ld_c ^ kswz(row)) * 16);
+    if (p < 2) v_st[p] = row * ROW_B + vswz<D>(row, ld_c) * 16;
+  }
+  const int fk = kswz(c32);
+  int k_rd[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) k_rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ fk) * 16);
+
+  uint4 kreg[NS][NLD];
+  uint4 vreg[NS][NLD];
+  // request slice i of this wave into register set `slot` (compile time)
+  auto issue = [&](int i, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    const int m = m_lo + wave + 4 * i;
+    const int key0 = 32 * m;
+    const int nvalid = (i < n_w) ? min(32, sk - key0) : 0;
+    const int pidx = min(key0 / a.page_size, a.max_pages - 1);
+    int page = nvalid > 0 ? ptab[pidx] : 0;
+    const bool ok = page >= 0 && page < a.num_pages;
+    bad |= !ok;
+    page = ok ? page : 0;
+    const int64_t row0 = (int64_t)page * a.page_size + key0 % a.page_size;
+    const uint32_t nrec = nvalid > 0 && ok ? (uint32_t)((nvalid - 1) * ts2 + ROW_B) : 0u;
+    const auto kr = make_rsrc(kbase + row0 * ts2, nrec);
+    const auto vr = make_rsrc(vbase + row0 * ts2, nrec);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      kreg[slot][u] = buf_ld16(kr, ld_off + (uint32_t)(RPL * u * ts2));
+      vreg[slot][u] = buf_ld16(vr, ld_off + (uint32_t)(RPL * u * ts2));
+    }
+  };
+
+  // transposing V reads: lane j of 16-lane group g points at key j/4
+  const int tr_g = lane >> 4;
+  const int tr_j = lane & 15;
+  const int tr_key = tr_j >> 2;
+  const int tr_c = (tr_g & 1) * 2 + ((tr_j & 3) >> 1);
+  const int tr_e = (tr_j & 1) * 8;
+
+  // compute slice i from slot `slot`
+  auto consume = [&](int i, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    // K and V rows into this wave's slots (LDS operations of one wave
+    // complete in order, so the previous slice's reads are done first)
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      *reinterpret_cast<uint4*>(kslot + k_st[u & 3] + (u >> 2) * 4 * RPL * ROW_B) = kreg[slot][u];
+      *reinterpret_cast<uint4*>(vslot + v_st[u & 1] + (u >> 1) * 2 * RPL * ROW_B) = vreg[slot][u];
+    }
+    const char* vs = vslot;
+    f32x16 s = zero_f32x16();
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc)
+      s = mfma32(*reinterpret_cast<const bf16x8*>(kslot + k_rd[cc]), qf[cc], s);
+    // keys outside [kv_lo, sk) (first and last slices, and padding)
+    const int key0 = 32 * (m_lo + wave + 4 * i);
+    if (i >= n_w || key0 < kv_lo || key0 + 32 > sk) {
+      const uint32_t w = (uint32_t)vis64(kv_lo - key0 - 4 * half, sk - 1 - key0 - 4 * half);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = mask_by_bit(s[v], i < n_w ? w : 0u, 8 * (v >> 2) + (v & 3));
+    }
+    float m0 = kNegInf, m1 = kNegInf;
+#pragma unroll
+    for (int v = 0; v < 16; v += 4) {
+      m0 = vmax3(m0, s[v], s[v + 1]);
+      m1 = vmax3(m1, s[v + 2], s[v + 3]);
+    }
+    const float mt = pair_max(vmax(m0, m1));
+    const float m_new = vmax(m_run, mt);
+    const float ms = (m_new == kNegInf) ? 0.0f : m_new * c;
+    // exactly 1 when the max did not move or nothing was seen yet
+    const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2((m_run - m_new) * c);
+    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s[v] = fast_exp2(fmaf(s[v], c, -ms));
+      rs[v & 3] += s[v];
+    }
+    l_run = l_run * alpha + ((rs[0] + rs[1]) + (rs[2] + rs[3]));
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int i0 = 2 * tt;
+      pf[tt] = cat(cvt4(s[4 * i0 + 0], s[4 * i0 + 1], s[4 * i0 + 2], s[4 * i0 + 3]),
+                   cvt4(s[4 * i0 + 4], s[4 * i0 + 5], s[4 * i0 + 6], s[4 * i0 + 7]));
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int k0 = 16 * tt + 4 * half + tr_key;
+        const int k1 = k0 + 8;
+        const int cc = 4 * db + tr_c;
+        const bf16x4 v0 = ds_read_tr16(
+            reinterpret_cast<const __bf16*>(vs + k0 * ROW_B + vswz<D>(k0, cc) * 16 + tr_e));
+        const bf16x4 v1 = ds_read_tr16(
+            reinterpret_cast<const __bf16*>(vs + k1 * ROW_B + vswz<D>(k1, cc) * 16 + tr_e));
+        o[db] = mfma32(cat(v0, v1), pf[tt], o[db]);
+      }
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  static_assert(NS == 3, "the unrolled loop below names three register sets");
+  if (n_pad > 0) {
+    issue(0, S0{});
+    issue(1, S1{});
+    for (int i = 0; i < n_pad; i += 3) {
+      issue(i + 2, S2{});
+      consume(i, S0{});
+      issue(i + 3, S0{});
+      consume(i + 1, S1{});
+      issue(i + 4, S1{});
+      consume(i + 2, S2{});
+    }
+  }
+  // the last requests (past the end, all-zero rows) must land before the
+  // workgroup's registers and LDS are released
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- merge the four waves' states through LDS (the V slots are reused)
+  const float l_wave = pair_sum(l_run);
+  const int any_bad = __syncthreads_or(bad ? 1 : 0);
+  float* sO = reinterpret_cast<float*>(smem);  // [wave][d][32]
+  float* sM = sO + 4 * D * 32;                 // [wave][32]
+  float* sL = sM + 4 * 32;                     // [wave][32]
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int d = db * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      sO[(wave * D + d) * 32 + c32] = o[db][v];
+    }
+  if (half == 0) {
+    sM[wave * 32 + c32] = m_run;
+    sL[wave * 32 + c32] = l_wave;
+  }
+  __syncthreads();
+
+  // thread -> (query column, slice of head_dim)
+  const int qcol = tid & 31;
+  const int dpart = tid >> 5;  // 0..7
+  constexpr int DPT = D / 8;
+  const int hcol = rb * 32 + qcol;
+  if (hcol < a.group) {
+    const int hq2 = hk * a.group + hcol;
+    float mw[4], m = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = sM[w * 32 + qcol];
+      m = vmax(m, mw[w]);
+    }
+    float wgt[4], l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wgt[w] = (m == kNegInf) ? 0.0f : fast_exp2((mw[w] - m) * c);
+      l += wgt[w] * sL[w * 32 + qcol];
+    }
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float nan = __builtin_nanf("");
+    const int64_t prow = (int64_t)b * a.hq + hq2;
+    float* op = a.o_part + (prow * a.num_splits + split) * D + dpart * DPT;
+#pragma unroll
+    for (int j = 0; j < DPT; j += 4) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int d = dpart * DPT + j;
+        acc.x += wgt[w] * sO[(w * D + d + 0) * 32 + qcol];
+        acc.y += wgt[w] * sO[(w * D + d + 1) * 32 + qcol];
+        acc.z += wgt[w] * sO[(w * D + d + 2) * 32 + qcol];
+        acc.w += wgt[w] * sO[(w * D + d + 3) * 32 + qcol];
+      }
+      *reinterpret_cast<float4*>(op + j) =
+          any_bad ? make_float4(nan, nan, nan, nan)
+                  : make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (dpart == 0) {
+      const float lse = l > 0.0f ? m * a.scale + __logf(l) : kNegInf;
+      a.lse_part[prow * a.num_splits + split] = any_bad ? nan : lse;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t s) {
+  const int64_t grid = (int64_t)a.batch * a.hkv * a.row_blocks * a.num_splits;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_stream_kernel<D>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_decode_stream<64>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode_stream<128>(const DecodeArgs&, hipStream_t);
+
+}  // namespace mi_attn

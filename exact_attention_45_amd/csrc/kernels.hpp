@@ -66,6 +66,7 @@ constexpr int kDecBlockN = 128;   // keys per decode tile (4 waves x 32)
 template <int D> hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
 template <int D> hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t s);
 template <int D> hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+template <int D> hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t s);
 template <int D> hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 }  // namespace mi_attn
