@@ -37,7 +37,7 @@ CSRC = os.path.join(HERE, "exact_attention_45_amd", "csrc")
 # sources whose compiled code the counted kernels consist of
 KERNEL_SOURCES = {
     "fwd_pp_kernel<128>": ["fwd_pp_kernel.hip", "attn_common.hpp", "kernels.hpp"],
-    "decode_split_kernel<128>": ["decode_kernel.hip", "attn_common.hpp", "kernels.hpp"],
+    "decode_stream_kernel<128>": ["decode_stream_kernel.hip", "attn_common.hpp", "kernels.hpp"],
     "combine_kernel<128>": ["decode_kernel.hip", "attn_common.hpp", "kernels.hpp"],
 }
 COUNTER_SUMMARY = os.path.join(
@@ -333,8 +333,8 @@ def main():
             "value": round(gbs, 1), "unit": "GB/s", "avg_launch_us": round(dec_avg * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": counter_traffic("decode_split_kernel<128>", "combine_kernel<128>"),
-                         "kernel": "decode_split_kernel<128> + combine_kernel<128>"},
+                         "traffic": counter_traffic("decode_stream_kernel<128>", "combine_kernel<128>"),
+                         "kernel": "decode_stream_kernel<128> + combine_kernel<128>"},
         },
     }
     if extra:

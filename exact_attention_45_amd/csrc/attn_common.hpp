@@ -124,9 +124,14 @@ __device__ __forceinline__ bf16x4 ds_read_tr16(const __bf16* p) {
 // later tiles stay in flight across it. (__syncthreads also waits vmcnt = 0.)
 // s_waitcnt encoding (gfx9): vmcnt[3:0]|expcnt[6:4]|lgkmcnt[11:8]|vmcnt_hi[15:14];
 // 0xC07F = vmcnt 63, expcnt 7, lgkmcnt 0.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier (the barrier intrinsic itself is declared not to touch
+// memory); they emit no instructions.
 __device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // A wave-uniform int the compiler computed in vector registers (e.g. after a
@@ -204,7 +209,9 @@ __device__ __forceinline__ void dma16_same_m0(__amdgpu_buffer_rsrc_t r, uint32_t
 template <int N>
 __device__ __forceinline__ void vmcnt_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  asm volatile("" ::: "memory");
 }
 
 // 16-byte global load / store of raw bits.
