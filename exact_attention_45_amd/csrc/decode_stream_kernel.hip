@@ -40,6 +40,7 @@ namespace mi_attn {
 template <int D>
 struct StreamCfg {
   static constexpr int NS = 3;                  // K/V register sets per wave
+  static constexpr float RESCALE_LOG2 = 8.0f;   // lazy-rescale threshold
   static constexpr int SLICE = 32;              // keys per slice
   static constexpr int ROW_B = D * 2;           // bytes per K/V row
   static constexpr int SLICE_B = SLICE * ROW_B; // bytes per K (or V) slice
@@ -115,6 +116,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   float m_run = kNegInf;
   float l_run = 0.0f;
   const float c = a.scale_log2;
+  const float rescale_raw = C::RESCALE_LOG2 / fmaxf(c, 1e-30f);
 
   // ---- slice addressing
   const int64_t ts2 = (int64_t)a.hkv * ROW_B;  // bytes between consecutive tokens
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
       s = mfma32(*reinterpret_cast<const bf16x8*>(kslot + k_rd[cc]), qf[cc], s);
     // keys outside [kv_lo, sk) (first and last slices, and padding)
     const int key0 = 32 * (m_lo + wave + 4 * i);
-    if (i >= n_w || key0 < kv_lo || key0 + 32 > sk) {
+    if (i >= n_w || key0 < kv_lo || key0 + 32 > sk) [[unlikely]] {
       const uint32_t w = (uint32_t)vis64(kv_lo - key0 - 4 * half, sk - 1 - key0 - 4 * half);
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = mask_by_bit(s[v], i < n_w ? w : 0u, 8 * (v >> 2) + (v & 3));
@@ -208,22 +210,30 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
       m1 = vmax3(m1, s[v + 2], s[v + 3]);
     }
     const float mt = pair_max(vmax(m0, m1));
-    const float m_new = vmax(m_run, mt);
-    const float ms = (m_new == kNegInf) ? 0.0f : m_new * c;
-    // exactly 1 when the max did not move or nothing was seen yet
-    const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2((m_run - m_new) * c);
+    // lazy rescale (as in the prefill kernels): the running max moves only
+    // when a slice max exceeds it by more than 2^RESCALE_LOG2 in exp2 units,
+    // so the O accumulators (which live in accumulation registers that vector
+    // arithmetic must copy out and back) are rarely touched; alpha is exactly
+    // 1 for lanes whose max stays
+    const bool grow = (m_run == kNegInf) ? (mt != kNegInf) : (mt - m_run > rescale_raw);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = grow ? ((m_run == kNegInf) ? 0.0f : fast_exp2((m_run - m_new) * c)) : 1.0f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    }
+    const float ms = (m_run == kNegInf) ? 0.0f : m_run * c;
     float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       s[v] = fast_exp2(fmaf(s[v], c, -ms));
       rs[v & 3] += s[v];
     }
-    l_run = l_run * alpha + ((rs[0] + rs[1]) + (rs[2] + rs[3]));
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     bf16x8 pf[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
