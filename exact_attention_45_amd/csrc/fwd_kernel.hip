@@ -239,22 +239,25 @@ void fwd_kernel(const FwdArgs a) {
     __builtin_amdgcn_s_setprio(0);
     const bool full = (n0 + BN <= sk) && (n0 + BN - 1 <= full_hi) && (n0 >= full_lo);
     if (!full) {
+      // element (kb, v) holds key n0 + 4*half + l, l = 32*kb + 8*(v>>2) + (v&3)
+      const uint64_t vis = vis64(lo - n0 - 4 * half, hi - n0 - 4 * half);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t w = (uint32_t)(vis >> (32 * kb));
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = n0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          if (key < lo || key > hi) s[kb][v] = kNegInf;
-        }
+        for (int v = 0; v < 16; ++v) s[kb][v] = mask_by_bit(s[kb][v], w, 8 * (v >> 2) + (v & 3));
+      }
     }
 
-    // online softmax with a lazily updated running max
-    float mt = kNegInf;
+    // online softmax with a lazily updated running max; the max and the row
+    // sum run on two and four independent chains
+    float m0 = kNegInf, m1 = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) mt = vmax3(mt, s[kb][v], s[kb][v + 1]);
-    mt = pair_max(mt);
+    for (int v = 0; v < 16; v += 2) {
+      m0 = vmax3(m0, s[0][v], s[0][v + 1]);
+      m1 = vmax3(m1, s[1][v], s[1][v + 1]);
+    }
+    const float mt = pair_max(vmax(m0, m1));
     const bool grow = (m_run == kNegInf) ? (mt != kNegInf) : (mt - m_run > rescale_raw);
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = grow ? mt : m_run;
@@ -268,16 +271,16 @@ void fwd_kernel(const FwdArgs a) {
         for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
     }
     const float ms = (m_run == kNegInf) ? 0.0f : m_run * c;
-    float rs = 0.0f;
+    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float p = fast_exp2(fmaf(s[kb][v], c, -ms));
         s[kb][v] = p;
-        rs += p;
+        rs[v & 3] += p;
       }
-    l_run += rs;
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
     // P^T fragments: MFMA t covers keys 16t..16t+15 of the tile; lane half h
     // supplies keys {16t+4h+j, 16t+8+4h+j : j<4}; the V^T fragment below uses

@@ -274,13 +274,14 @@ void fwd_pp_kernel(const FwdArgs a) {
     const int n0 = (n_begin + k) * BN;
     const bool full = (n0 + BN <= sk) && (n0 + BN - 1 <= full_hi) && (n0 >= full_lo);
     if (!full) {
+      // element (kb, v) holds key n0 + 4*half + l, l = 32*kb + 8*(v>>2) + (v&3)
+      const uint64_t vis = vis64(lo - n0 - 4 * half, hi - n0 - 4 * half);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t w = (uint32_t)(vis >> (32 * kb));
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = n0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          if (key < lo || key > hi) s[kb][v] = kNegInf;
-        }
+        for (int v = 0; v < 16; ++v) s[kb][v] = mask_by_bit(s[kb][v], w, 8 * (v >> 2) + (v & 3));
+      }
     }
     // two independent max chains (one per 32-key half), then the lane pair
     float m0 = kNegInf, m1 = kNegInf;
