@@ -47,7 +47,10 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Split count when the caller passes 0. Same shape as the interface page's
 // `num_splits_heuristic` (no split for <= 4 key blocks; otherwise enough
 // splits to give every compute unit work, capped at 128 and at the number
-// of key blocks), counting one workgroup per (sequence, KV head, row block).
+// of key blocks). The streaming kernel runs one wave per (sequence, KV head,
+// row block, split) and aims at one wave per SIMD (four per compute unit);
+// the tile kernel runs one workgroup per (sequence, KV head, row block,
+// split) and aims at two workgroups per compute unit.
 int split_heuristic(const mi_attn_decode_params* p) {
   const int cap = p->max_pages_per_seq * p->page_size;
   const int n_blocks = (cap + mi_attn::kDecBlockN - 1) / mi_attn::kDecBlockN;
@@ -62,8 +65,8 @@ int split_heuristic(const mi_attn_decode_params* p) {
   }
   const int group = p->num_heads_q / p->num_heads_kv;
   const long work = (long)p->batch * p->num_heads_kv * ((group + 31) / 32);
-  // two resident workgroups per compute unit keep enough loads in flight
-  const long want = std::max(1L, (2L * cus) / std::max(1L, work));
+  const long per_cu = mi_attn::decode_streams(p->head_dim, p->page_size) ? 4L : 2L;
+  const long want = std::max(1L, (per_cu * cus) / std::max(1L, work));
   return (int)std::max(1L, std::min<long>({want, 128L, (long)n_blocks}));
 }
 

@@ -417,9 +417,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombineArgs a) {
 
 template <int D>
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  // per-wave streaming kernel when every aligned 32-key slice is in one page
   if constexpr (D <= 128) {
-    if (a.page_size % 32 == 0) return launch_decode_stream<D>(a, s);
+    if (decode_streams(D, a.page_size)) return launch_decode_stream<D>(a, s);
   }
   const int64_t grid = (int64_t)a.batch * a.hkv * a.row_blocks * a.num_splits;
   if (grid <= 0) return hipSuccess;

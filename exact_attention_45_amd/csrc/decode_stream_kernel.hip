@@ -8,11 +8,14 @@
 // combine kernel merges them by LSE weights. What differs is how the bytes
 // move. Decode reads every K/V byte once, so the kernel is a streaming
 // kernel whose speed is the number of bytes it keeps in flight:
-//   * A workgroup (4 waves) owns one (sequence, KV head, 32-head row block,
-//     split). The split's keys are cut into 32-key slices aligned to absolute
-//     key multiples of 32; wave w takes slices w, w+4, w+8, ... and keeps its
-//     own running (max, sum, O). Waves never wait for each other until the
-//     final merge: no barrier in the loop.
+//   * A workgroup (4 waves) owns one (sequence, 32-head row block, split)
+//     for four consecutive KV heads, one head per wave. The heads of a token
+//     share its cache row (Hkv x D x 2 bytes), so the four waves read whole
+//     rows between them at about the same time. Each wave streams the whole
+//     split for its head: the split's keys cut into 32-key slices aligned to
+//     absolute key multiples of 32, one running (max, sum, O), and at the end
+//     it writes its normalised partial straight from registers. The waves
+//     never synchronise.
 //   * K and V of a slice are loaded into registers with 16-byte loads in row
 //     order (each instruction reads four whole 256-byte rows: measured on
 //     MI355X, reading a head's rows this way streams at ~6.5 TB/s, while the
@@ -48,8 +51,7 @@ struct StreamCfg {
   static constexpr int RPL = 64 / CPR;          // rows per load instruction
   static constexpr int NLD = SLICE / RPL;       // load instructions per tensor per slice
   static constexpr int SLOT_B = 4 * 2 * SLICE_B; // K and V slots of the four waves
-  static constexpr int MERGE_B = (4 * D * 32 + 2 * 4 * 32) * 4;  // end-of-split merge
-  static constexpr int LDS_B = SLOT_B > MERGE_B ? SLOT_B : MERGE_B;
+  static constexpr int LDS_B = SLOT_B;
 };
 
 // LDS chunk position of logical 16-byte chunk c of V row `key`. The XOR
@@ -73,14 +75,18 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   const int c32 = lane & 31;
   const int half = lane >> 5;
 
-  // ---- work item: split fastest, then row block, KV head, sequence
+  // ---- work item: (sequence, 32-head row block, split) for four consecutive
+  // KV heads, one per wave; split fastest
+  const int n_hg = (a.hkv + 3) / 4;
   int lin = blockIdx.x;
   const int split = lin % a.num_splits;
   lin /= a.num_splits;
+  const int hg = lin % n_hg;
+  lin /= n_hg;
   const int rb = lin % a.row_blocks;
-  lin /= a.row_blocks;
-  const int hk = lin % a.hkv;
-  const int b = lin / a.hkv;
+  const int b = lin / a.row_blocks;
+  const int hk = hg * 4 + wave;
+  if (hk >= a.hkv) return;  // wave-uniform; the waves never synchronise
 
   const int cap = a.max_pages * a.page_size;
   int sk = a.seqused_k != nullptr ? a.seqused_k[b] : cap;
@@ -94,8 +100,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   const int per = (n_sl + a.num_splits - 1) / a.num_splits;
   const int m_lo = uniform(m_first + min(n_sl, split * per));
   const int m_hi = uniform(m_first + min(n_sl, (split + 1) * per));
-  // this wave's slices m_lo + wave + 4i, i < n_w; padded to a multiple of NS
-  const int n_w = uniform(m_hi - m_lo > wave ? (m_hi - m_lo - wave + 3) / 4 : 0);
+  // this wave's slices m_lo + i, i < n_w (all of the split, for its head);
+  // padded to a multiple of NS
+  const int n_w = uniform(m_hi - m_lo);
   const int n_pad = (n_w + NS - 1) / NS * NS;
 
   // ---- this lane's query head (MFMA B operand)
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   // request slice i of this wave into register set `slot` (compile time)
   auto issue = [&](int i, auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
-    const int m = m_lo + wave + 4 * i;
+    const int m = m_lo + i;
     const int key0 = 32 * m;
     const int nvalid = (i < n_w) ? min(32, sk - key0) : 0;
     const int pidx = min(key0 / a.page_size, a.max_pages - 1);
@@ -181,23 +188,27 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   const int tr_c = (tr_g & 1) * 2 + ((tr_j & 3) >> 1);
   const int tr_e = (tr_j & 1) * 8;
 
-  // compute slice i from slot `slot`
-  auto consume = [&](int i, auto slot_c) {
+  // K and V rows of register set `slot` into this wave's LDS slots (LDS
+  // operations of one wave complete in order, so the previous slice's reads
+  // are done first); the set is free for the next request afterwards
+  auto stage = [&](auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
-    // K and V rows into this wave's slots (LDS operations of one wave
-    // complete in order, so the previous slice's reads are done first)
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       *reinterpret_cast<uint4*>(kslot + k_st[u & 3] + (u >> 2) * 4 * RPL * ROW_B) = kreg[slot][u];
       *reinterpret_cast<uint4*>(vslot + v_st[u & 1] + (u >> 1) * 2 * RPL * ROW_B) = vreg[slot][u];
     }
+  };
+
+  // compute slice i from the LDS slots
+  auto consume = [&](int i) {
     const char* vs = vslot;
     f32x16 s = zero_f32x16();
 #pragma unroll
     for (int cc = 0; cc < D / 16; ++cc)
       s = mfma32(*reinterpret_cast<const bf16x8*>(kslot + k_rd[cc]), qf[cc], s);
     // keys outside [kv_lo, sk) (first and last slices, and padding)
-    const int key0 = 32 * (m_lo + wave + 4 * i);
+    const int key0 = 32 * (m_lo + i);
     if (i >= n_w || key0 < kv_lo || key0 + 32 > sk) [[unlikely]] {
       const uint32_t w = (uint32_t)vis64(kv_lo - key0 - 4 * half, sk - 1 - key0 - 4 * half);
 #pragma unroll
@@ -261,89 +272,56 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   static_assert(NS == 3, "the unrolled loop below names three register sets");
+  // three slices stay requested while one is computed
   if (n_pad > 0) {
     issue(0, S0{});
     issue(1, S1{});
+    issue(2, S2{});
     for (int i = 0; i < n_pad; i += 3) {
-      issue(i + 2, S2{});
-      consume(i, S0{});
+      stage(S0{});
       issue(i + 3, S0{});
-      consume(i + 1, S1{});
+      consume(i);
+      stage(S1{});
       issue(i + 4, S1{});
-      consume(i + 2, S2{});
+      consume(i + 1);
+      stage(S2{});
+      issue(i + 5, S2{});
+      consume(i + 2);
     }
   }
   // the last requests (past the end, all-zero rows) must land before the
   // workgroup's registers and LDS are released
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- merge the four waves' states through LDS (the V slots are reused)
-  const float l_wave = pair_sum(l_run);
-  const int any_bad = __syncthreads_or(bad ? 1 : 0);
-  float* sO = reinterpret_cast<float*>(smem);  // [wave][d][32]
-  float* sM = sO + 4 * D * 32;                 // [wave][32]
-  float* sL = sM + 4 * 32;                     // [wave][32]
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int d = db * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-      sO[(wave * D + d) * 32 + c32] = o[db][v];
-    }
-  if (half == 0) {
-    sM[wave * 32 + c32] = m_run;
-    sL[wave * 32 + c32] = l_wave;
-  }
-  __syncthreads();
-
-  // thread -> (query column, slice of head_dim)
-  const int qcol = tid & 31;
-  const int dpart = tid >> 5;  // 0..7
-  constexpr int DPT = D / 8;
-  const int hcol = rb * 32 + qcol;
-  if (hcol < a.group) {
-    const int hq2 = hk * a.group + hcol;
-    float mw[4], m = kNegInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      mw[w] = sM[w * 32 + qcol];
-      m = vmax(m, mw[w]);
-    }
-    float wgt[4], l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      wgt[w] = (m == kNegInf) ? 0.0f : fast_exp2((mw[w] - m) * c);
-      l += wgt[w] * sL[w * 32 + qcol];
-    }
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  // ---- this wave owns its head's whole split: normalise and write the
+  // partial straight from registers (lane: query column c32, head dims
+  // 32*db + 8*i + 4*half .. +3)
+  const float l_tot = pair_sum(l_run);
+  if (valid) {
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float nan = __builtin_nanf("");
-    const int64_t prow = (int64_t)b * a.hq + hq2;
-    float* op = a.o_part + (prow * a.num_splits + split) * D + dpart * DPT;
+    const int64_t prow = (int64_t)b * a.hq + hq;
+    float* op = a.o_part + (prow * a.num_splits + split) * D;
 #pragma unroll
-    for (int j = 0; j < DPT; j += 4) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int d = dpart * DPT + j;
-        acc.x += wgt[w] * sO[(w * D + d + 0) * 32 + qcol];
-        acc.y += wgt[w] * sO[(w * D + d + 1) * 32 + qcol];
-        acc.z += wgt[w] * sO[(w * D + d + 2) * 32 + qcol];
-        acc.w += wgt[w] * sO[(w * D + d + 3) * 32 + qcol];
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * half;
+        *reinterpret_cast<float4*>(op + d0) =
+            bad ? make_float4(nan, nan, nan, nan)
+                : make_float4(o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
+                              o[db][4 * i + 3] * inv);
       }
-      *reinterpret_cast<float4*>(op + j) =
-          any_bad ? make_float4(nan, nan, nan, nan)
-                  : make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
-    if (dpart == 0) {
-      const float lse = l > 0.0f ? m * a.scale + __logf(l) : kNegInf;
-      a.lse_part[prow * a.num_splits + split] = any_bad ? nan : lse;
+    if (half == 0) {
+      const float lse = l_tot > 0.0f ? m_run * a.scale + __logf(l_tot) : kNegInf;
+      a.lse_part[prow * a.num_splits + split] = bad ? nan : lse;
     }
   }
 }
 
 template <int D>
 hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t s) {
-  const int64_t grid = (int64_t)a.batch * a.hkv * a.row_blocks * a.num_splits;
+  const int64_t grid = (int64_t)a.batch * ((a.hkv + 3) / 4) * a.row_blocks * a.num_splits;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(decode_stream_kernel<D>, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
