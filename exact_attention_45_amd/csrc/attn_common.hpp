@@ -168,6 +168,14 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t byt
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Same, marked non-temporal (data read once, e.g. a decode step's KV cache
+// stream).
+__device__ __forceinline__ uint4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // LDS byte address (offset within the workgroup's LDS) of a __shared__ pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;

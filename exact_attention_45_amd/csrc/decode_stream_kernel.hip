@@ -176,8 +176,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
     const auto vr = make_rsrc(vbase + row0 * ts2, nrec);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      kreg[slot][u] = buf_ld16(kr, ld_off + (uint32_t)(RPL * u * ts2));
-      vreg[slot][u] = buf_ld16(vr, ld_off + (uint32_t)(RPL * u * ts2));
+      kreg[slot][u] = buf_ld16_nt(kr, ld_off + (uint32_t)(RPL * u * ts2));
+      vreg[slot][u] = buf_ld16_nt(vr, ld_off + (uint32_t)(RPL * u * ts2));
     }
   };
 
