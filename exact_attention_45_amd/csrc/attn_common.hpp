@@ -224,6 +224,11 @@ __device__ __forceinline__ void vmcnt_wait() {
 
 // 16-byte global load / store of raw bits.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   return __builtin_bit_cast(bf16x8, u);

@@ -147,8 +147,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
       const int page = ok ? pid[slot][u] : 0;
       const int64_t off =
           ((int64_t)page * a.page_size + key % a.page_size) * tok_stride + ld_c * 8;
-      kreg[set][u] = ld16(kc + off);
-      vreg[set][u] = ld16(vc + off);
+      kreg[set][u] = ld16_nt(kc + off);  // the cache is read once per step
+      vreg[set][u] = ld16_nt(vc + off);
     }
   };
   auto store_tile = [&](auto set_c, int buf) {
@@ -347,67 +347,82 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   }
 }
 
-// ---- combine: one 64-lane workgroup per output row; split weights are
-// staged in LDS and the partial loads are issued eight splits at a time
+// ---- combine: one 64-lane workgroup per output row. The first 16 splits'
+// partial rows are requested together with the split LSEs, so a step with
+// at most 16 splits waits for memory once; larger split counts stream in
+// chunks of 16 with the next chunk requested before the current one is
+// summed. Split weights go through LDS (zero past the last split, so the
+// clamped loads of a ragged last chunk add nothing).
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(const CombineArgs a) {
   constexpr int EPL = D / 64;  // head_dim elements per lane
-  __shared__ float sw[256];
+  constexpr int CH = 16;       // splits per chunk
+  typedef float vecE __attribute__((ext_vector_type(EPL)));
+  __shared__ float sw[256 + CH];
   const int lane = threadIdx.x;
   const int row = blockIdx.x;
   const int S = a.num_splits;
   const float* lp = a.lse_part + (int64_t)row * S;
   const float* op = a.o_part + (int64_t)row * S * D + lane * EPL;
+  auto load_chunk = [&](int s0, vecE (&x)[CH]) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      x[i] = *reinterpret_cast<const vecE*>(op + (int64_t)min(s0 + i, S - 1) * D);
+  };
+
+  // straight-line code up to the sum, so that the compiler issues every
+  // load before the first wait
+  float xl[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sj = lane + 64 * j;
+    const float v = lp[min(sj, S - 1)];
+    xl[j] = sj < S ? v : kNegInf;
+  }
+  vecE x[CH];
+  load_chunk(0, x);
 
   float m = kNegInf;
   int has_nan = 0;
-  for (int s = lane; s < S; s += 64) {
-    const float x = lp[s];
-    m = fmaxf(m, x);
-    has_nan |= (x != x);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m = fmaxf(m, xl[j]);
+    has_nan |= (xl[j] != xl[j]);
   }
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) m = fmaxf(m, __shfl_xor(m, w, 64));
   has_nan = __any(has_nan);
-
-  float acc[EPL];
+  const float mm = m == kNegInf ? 0.0f : m;
+  float tot = 0.0f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  float lse = kNegInf;
+  for (int j = 0; j < 4; ++j) {
+    const float w = __expf(xl[j] - mm);  // -inf (empty or absent split) -> 0
+    sw[lane + 64 * j] = w;
+    tot += w;
+  }
+  if (lane < CH) sw[256 + lane] = 0.0f;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) tot += __shfl_xor(tot, w, 64);
+  __syncthreads();
+  vecE acc = {};
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    vecE y[CH];
+    const bool more = s0 + CH < S;
+    if (more) load_chunk(s0 + CH, y);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) acc += sw[s0 + i] * x[i];
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) x[i] = y[i];
+    }
+  }
+  // every split empty: zero output and lse -inf; a NaN partial (bad page
+  // id) must reach the output
+  float lse = tot > 0.0f ? mm + __logf(tot) : kNegInf;
+  acc = tot > 0.0f ? acc * (1.0f / tot) : vecE{};
   if (has_nan) {
-    // a NaN partial (bad page id) must reach the output
     lse = __builtin_nanf("");
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = lse;
-  } else if (m != kNegInf) {
-    float tot = 0.0f;
-    for (int s = lane; s < S; s += 64) {
-      const float w = __expf(lp[s] - m);  // -inf (empty split) -> 0
-      sw[s] = w;
-      tot += w;
-    }
-#pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) tot += __shfl_xor(tot, w, 64);
-    lse = m + __logf(tot);
-    const float inv = 1.0f / tot;
-    __syncthreads();
-    int s = 0;
-    for (; s + 8 <= S; s += 8) {
-      float x[8][EPL];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) x[i][e] = op[(int64_t)(s + i) * D + e];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += sw[s + i] * x[i][e];
-    }
-    for (; s < S; ++s)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += sw[s] * op[(int64_t)s * D + e];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] *= inv;
+    acc = lse;
   }
   __bf16* dst = static_cast<__bf16*>(a.out) + (int64_t)row * a.out_row_stride + lane * EPL;
 #pragma unroll
