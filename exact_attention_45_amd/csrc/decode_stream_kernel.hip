@@ -21,10 +21,12 @@
 //     MI355X, reading a head's rows this way streams at ~6.5 TB/s, while the
 //     MFMA-fragment order, 32 rows x 32 bytes per instruction, manages ~3.9).
 //     Both go to a wave-private LDS slot just before use; K is read back as
-//     MFMA fragments, V with transposing reads. NS register sets per wave:
-//     slice i+NS-1 is requested while slice i is computed, 16 KB per wave in
-//     flight per set (registers, not LDS, are the large buffer here: a wave
-//     may hold 512 of them).
+//     MFMA fragments, V with transposing reads. NS register sets per wave: a
+//     set is refilled with slice i+NS as soon as slice i has moved to LDS, so
+//     NS slices (16 KB each at D = 128) stay requested while slice i is
+//     computed (registers, not LDS, are the large buffer here: a wave may
+//     hold 512 of them). The loads are marked non-temporal: the cache is
+//     read once per step.
 //   * The slot loop is unrolled NS times so every register set is named at
 //     compile time and the compiler derives each load-count wait itself.
 //   * A slice sits in one page, so its page id is one scalar load and its K
@@ -100,10 +102,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   const int per = (n_sl + a.num_splits - 1) / a.num_splits;
   const int m_lo = uniform(m_first + min(n_sl, split * per));
   const int m_hi = uniform(m_first + min(n_sl, (split + 1) * per));
-  // this wave's slices m_lo + i, i < n_w (all of the split, for its head);
-  // padded to a multiple of NS
+  // this wave's slices m_lo + i, i < n_w (all of the split, for its head)
   const int n_w = uniform(m_hi - m_lo);
-  const int n_pad = (n_w + NS - 1) / NS * NS;
 
   // ---- this lane's query head (MFMA B operand)
   const int col = rb * 32 + c32;
@@ -272,12 +272,14 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   static_assert(NS == 3, "the unrolled loop below names three register sets");
-  // three slices stay requested while one is computed
-  if (n_pad > 0) {
+  // three slices stay requested while one is computed; requests past the
+  // last slice load nothing (zero-length descriptor)
+  if (n_w > 0) {
     issue(0, S0{});
     issue(1, S1{});
     issue(2, S2{});
-    for (int i = 0; i < n_pad; i += 3) {
+    int i = 0;
+    for (; i + 3 <= n_w; i += 3) {
       stage(S0{});
       issue(i + 3, S0{});
       consume(i);
@@ -287,6 +289,15 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
       stage(S2{});
       issue(i + 5, S2{});
       consume(i + 2);
+    }
+    // one or two slices left (in sets 0 and 1)
+    if (i < n_w) {
+      stage(S0{});
+      consume(i);
+      if (i + 1 < n_w) {
+        stage(S1{});
+        consume(i + 1);
+      }
     }
   }
   // the last requests (past the end, all-zero rows) must land before the
