@@ -15,12 +15,14 @@
 // so on every SIMD one wave keeps the matrix cores busy while the other runs
 // its exponentials; neither waits for the other's phase.
 //
-// K/V tiles (64 keys) rotate through three LDS buffers: tile k is read in
-// half-steps 2k..2k+3, so tile k+1 is stored during half-step 2k into the
-// buffer tile k-2 vacated, and tile k+2 is fetched into registers right
-// after, a full tile ahead of its store. Every load and store is issued
-// unconditionally (tiles past the end re-read the last tile), which keeps the
-// compiler's load-wait counts static.
+// K/V tiles (64 keys) rotate through four LDS buffers and go there straight
+// from global memory (direct-to-LDS buffer loads, nothing staged in
+// registers). Tile k is read in half-steps 2k..2k+3; tile k+2 is requested
+// during iteration k into the buffer tile k-2 vacated (each group issues its
+// share at the start of its softmax half-step), and an explicit load-count
+// wait plus a barrier at the end of iteration k make tile k+1 visible. Every
+// request is issued unconditionally (tiles past the end re-read the last
+// tile), which keeps the wait counts static.
 #include <climits>
 #include <type_traits>
 
