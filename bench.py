@@ -15,6 +15,11 @@ second (plus Q, O, LSE and page-table bytes). Progress goes to stderr.
 Flags: --gpus N (only 1 is supported: the path is single-GPU), --steps K,
 --warmup W, --no-cpu-baseline, --cpu-seconds S (oracle sample budget),
 --all-configs (also time the other benchmark workloads; stderr only).
+
+The default warmup is 200 steps (~70 ms of GPU work): on MI355X the core
+clock climbs for the first few tens of milliseconds of sustained matrix-core
+load, and a handful of warmup steps times the prefill ~20% slower than it
+runs in steady state.
 """
 from __future__ import annotations
 
@@ -83,8 +88,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--all-configs", action="store_true")

@@ -248,15 +248,16 @@ void fwd_pp_kernel(const FwdArgs a) {
   // flight ahead of the MFMAs that consume them (the default schedule issues
   // each read right before its MFMA and stalls on LDS latency).
   constexpr int NMF = D / 16 * 2;  // MFMAs per part (S and P V alike)
+  constexpr int LEAD = 8;          // MFMAs' worth of fragment reads issued ahead
   auto sched_part = [&](auto rpm_c) {
     constexpr int R = decltype(rpm_c)::value;  // LDS reads per MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, LEAD * R, 0);
 #pragma unroll
-    for (int i = 0; i < NMF - 4; ++i) {
+    for (int i = 0; i < NMF - LEAD; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
   };
 
   // MFMA item k: O += P(k-1) V(k-1) (k >= 1), then S(k) = K(k) Q^T (k < T)
