@@ -76,13 +76,9 @@ void fwd_kernel(const FwdArgs a) {
   const int c32 = lane & 31;
   const int half = lane >> 5;
 
-  // ---- work item: heavy query blocks first, (KV head, sequence) fastest
-  const int nhb = a.hkv * a.batch;
-  const int lin = blockIdx.x;
-  const int hb = lin % nhb;
-  const int mb = a.num_m_blocks - 1 - lin / nhb;
-  const int hk = hb % a.hkv;
-  const int b = hb / a.hkv;
+  // ---- work item (heavy query blocks first; see fwd_work_item)
+  int hk, b, mb;
+  if (!fwd_work_item<BM>(a, hk, b, mb)) return;
 
   int sq = a.seqlen_q, sk = a.seqlen_k;
   int64_t q_base, k_base, v_base, o_base;
@@ -357,7 +353,7 @@ hipError_t launch_fwd(const FwdArgs& args, hipStream_t s) {
   } else {
     FwdArgs a = args;
     a.num_m_blocks = (int)(((int64_t)a.max_rows + kFwdBlockM - 1) / kFwdBlockM);
-    const int64_t grid = (int64_t)a.num_m_blocks * a.hkv * a.batch;
+    const int64_t grid = fwd_blocks_per_head(a, kFwdBlockM) * a.hkv;
     if (grid <= 0) return hipSuccess;
     hipLaunchKernelGGL(fwd_kernel<D>, dim3((unsigned)grid), dim3(256), 0, s, a);
     return hipGetLastError();

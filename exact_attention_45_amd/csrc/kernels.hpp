@@ -30,6 +30,59 @@ struct FwdArgs {
   int32_t wl, wr;
 };
 
+// Query blocks (of BM packed rows) a prefill launch covers per KV head.
+// Dense batches: every sequence has num_m_blocks of them. Packed varlen
+// batches: the sum over sequences of ceil(rows_b / BM) is at most
+// total_rows / BM + batch, so the grid holds about as many workgroups as
+// there are real blocks (not num_m_blocks per sequence).
+inline int64_t fwd_blocks_per_head(const FwdArgs& a, int bm) {
+  const int64_t dense = (int64_t)a.num_m_blocks * a.batch;
+  if (a.cu_q == nullptr) return dense;
+  const int64_t packed = ((int64_t)a.total_q * a.group + bm - 1) / bm + a.batch;
+  return packed < dense ? packed : dense;
+}
+
+// Work item (KV head hk, sequence b, query block mb) of prefill workgroup
+// blockIdx.x. Dense batches: heavy (late) query blocks first, (KV head,
+// sequence) fastest. Packed varlen batches: KV head fastest, then block g of
+// the concatenation of every sequence's blocks, each sequence's last
+// (heaviest) block first; the sequence lengths are read eight at a time
+// (independent scalar loads, one memory latency per eight sequences).
+// Returns false for a workgroup past the last block.
+template <int BM>
+__device__ __forceinline__ bool fwd_work_item(const FwdArgs& a, int& hk, int& b, int& mb) {
+  // every quantity here is the same in all lanes: keep it in scalar registers
+  const auto scalar = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  const int lin = (int)blockIdx.x;
+  if (a.cu_q == nullptr) {
+    const int nhb = a.hkv * a.batch;
+    const int hb = scalar(lin % nhb);
+    mb = scalar(a.num_m_blocks - 1 - lin / nhb);
+    hk = scalar(hb % a.hkv);
+    b = scalar(hb / a.hkv);
+    return true;
+  }
+  hk = scalar(lin % a.hkv);
+  int g = scalar(lin / a.hkv);
+  for (int j0 = 0; j0 < a.batch; j0 += 8) {
+    int cu[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) cu[i] = a.cu_q[min(j0 + i, a.batch)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int len = cu[i + 1] - cu[i];  // 0 past the last sequence
+      const int nb = len > 0 ? (int)(((int64_t)len * a.group + BM - 1) / BM) : 0;
+      if (g < nb) {
+        b = scalar(j0 + i);
+        mb = scalar(nb - 1 - g);
+        return true;
+      }
+      g -= nb;
+    }
+  }
+  return false;
+}
+
 // Paged split-KV decode arguments.
 struct DecodeArgs {
   const void* q;

@@ -89,8 +89,9 @@ typedef enum {
  *   q   [total_q, num_heads_q, head_dim]
  *   k,v [total_k, num_heads_kv, head_dim]
  *   lse [num_heads_q, total_q] float32, contiguous, or NULL.
- *   max_seqlen_q / max_seqlen_k must bound every sequence's length (they
- *   size the launch grid); seqlen_q / seqlen_k are ignored.
+ *   total_q must equal cu_seqlens_q[batch]; max_seqlen_q / max_seqlen_k
+ *   must bound every sequence's length (together they size the launch
+ *   grid); seqlen_q / seqlen_k are ignored.
  *
  * num_heads_q must be a multiple of num_heads_kv. Query heads sharing a KV
  * head are processed together (GQA packing), so one K/V tile load serves all
@@ -109,7 +110,9 @@ typedef struct {
   int32_t batch, seqlen_q, seqlen_k;
   int32_t num_heads_q, num_heads_kv, head_dim;
   const int32_t *cu_seqlens_q, *cu_seqlens_k; /* device, [batch+1], or NULL  */
-  int32_t total_q;                            /* varlen: rows of q and lse   */
+  int32_t total_q;                            /* varlen: cu_seqlens_q[batch],
+                                                 the rows of q and lse; it
+                                                 also sizes the launch grid */
   int32_t max_seqlen_q, max_seqlen_k;         /* varlen: host upper bounds   */
   const int32_t *page_table;                  /* must be NULL                */
   float softmax_scale;
