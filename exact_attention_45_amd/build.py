@@ -17,8 +17,14 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmiattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "fwd_kernel.hip", "fwd_pp_kernel.hip", "decode_kernel.hip",
-           "decode_stream_kernel.hip"]
+SOURCES = ["api.hip", "fwd_kernel.hip", "fwd_pp_kernel.hip", "fwd_sp_kernel.hip",
+           "decode_kernel.hip", "decode_stream_kernel.hip"]
+# Per-source extra flags. fwd_sp_kernel runs one wave per SIMD with more than
+# 256 registers; by default the compiler then places every MFMA accumulator in
+# accumulation registers, and the vector instructions that rescale O force
+# copies of all of O at every loop iteration. The VGPR form keeps O and S in
+# vector registers (other values still use accumulation registers).
+SOURCE_FLAGS = {"fwd_sp_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code; scalar/float2 math
@@ -47,7 +53,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
 
         def compile_one(src):
             obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
-            cmd = [cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *flags, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             r = subprocess.run(cmd, capture_output=True, text=True)

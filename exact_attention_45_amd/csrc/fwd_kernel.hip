@@ -351,12 +351,7 @@ hipError_t launch_fwd(const FwdArgs& args, hipStream_t s) {
   if constexpr (D <= 128) {
     return launch_fwd_pp<D>(args, s);
   } else {
-    FwdArgs a = args;
-    a.num_m_blocks = (int)(((int64_t)a.max_rows + kFwdBlockM - 1) / kFwdBlockM);
-    const int64_t grid = fwd_blocks_per_head(a, kFwdBlockM) * a.hkv;
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(fwd_kernel<D>, dim3((unsigned)grid), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_fwd_sp<D, 1>(args, s);
   }
 }
 

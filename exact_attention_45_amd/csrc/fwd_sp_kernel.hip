@@ -1,0 +1,487 @@
+// Prefill forward with one wave per SIMD and software pipelining inside the
+// wave: the matrix cores compute the next tile's scores while the same wave
+// runs the current tile's exponentials. Serves head_dim 256, whose O
+// accumulators alone take 128 registers per lane.
+//
+// Method as in fwd_pp_kernel.hip (mslk flash_attn interface.py page,
+// `_flash_attn_fwd`): exact attention, online softmax in the exp2 domain with
+// a lazily updated running max, natural-log LSE, empty rows O = 0 and
+// LSE = -inf. Same MFMA conventions (attn_common.hpp: both GEMMs transposed so
+// a lane owns one query), the same packed GQA rows, tile skipping, edge masks
+// and grid order.
+//
+// Schedule. A workgroup is four waves, one per SIMD, each with the whole
+// 512-entry register file; wave w owns 32*QB consecutive packed rows (QB query
+// blocks of 32 MFMA columns), so every K or V fragment read from LDS feeds QB
+// MFMAs. Iteration k of the key-tile loop:
+//   top     : wait until K(k+1) and V(k) have landed, barrier; request
+//             K(k+2) and V(k+1) straight into LDS (direct-to-LDS buffer loads)
+//   softmax : mask S(k) on edge tiles, running max, lazy rescale of O
+//   phase 1 : S(k+1) = K(k+1) Q^T on the matrix cores, its MFMAs interleaved
+//             with the exponentials, row sums and bf16 packing of P(k)
+//   phase 2 : O += P(k) V(k), the transposing V reads issued several MFMAs
+//             ahead and held there by scheduling barriers
+// K runs one tile ahead of V; each has two LDS buffers (tile j in buffer
+// j & 1). The loop is unrolled by two so buffer offsets and the two score
+// register sets are fixed at compile time.
+//
+// With one wave per SIMD nothing hides LDS latency but the wave's own
+// read-ahead: with each read issued just before its MFMA (the compiler's
+// choice when left alone) the long-context D256 workload ran 2.85 ms; with
+// six MFMAs of read-ahead in phase 2, 2.4 ms.
+//
+// Register classes: this source is compiled with MFMA results in vector
+// registers (the build's per-file flag), so O and S stay where the softmax
+// and the rescale read them, and the Q fragments, which are only MFMA
+// operands, are placed in the accumulation registers.
+#include <climits>
+#include <type_traits>
+#include <utility>
+
+#include "attn_common.hpp"
+#include "kernels.hpp"
+
+#ifndef FWD_SP_LEAD1
+#define FWD_SP_LEAD1 4
+#endif
+#ifndef FWD_SP_LEAD2
+#define FWD_SP_LEAD2 6
+#endif
+
+namespace mi_attn {
+
+template <int D, int QB>
+struct SPCfg {
+  static constexpr int BM = 128 * QB;          // packed rows per workgroup
+  static constexpr int BN = kFwdBlockN;        // 64 keys per tile
+  static constexpr int ROW_B = D * 2;          // bytes per K/V row
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int TILE_B = BN * ROW_B;    // bytes per K (or V) tile
+  static constexpr int RPI = 1024 / ROW_B;     // rows per direct-to-LDS wave instruction
+  static constexpr int NI = BN / RPI / 4;      // such instructions per wave per tensor
+  static constexpr float RESCALE_LOG2 = 8.0f;  // lazy-rescale threshold
+  static_assert(NI * RPI * 4 == BN, "a tile splits evenly over four waves");
+  static_assert(D == 128 || D == 256, "16-byte-chunk swizzles assume 256- or 512-byte rows");
+};
+
+// K tile swizzle: chunk c of key row `key` sits at chunk c ^ kswz16(key). The
+// 16 lanes an LDS cycle serves read one logical chunk of 16 consecutive keys;
+// kswz16 takes 16 distinct values over any 16 consecutive keys, and rows are a
+// multiple of 256 bytes, so those reads hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int kswz16(int key) { return swz_key(key) | (((key >> 3) & 1) << 3); }
+
+// Scheduling-group pattern for a run of NMF MFMAs fed by NRD LDS fragment
+// reads: the reads of the first LEAD MFMAs go first, then after each MFMA the
+// reads that keep LEAD MFMAs' worth in flight, and VALU vector instructions.
+template <int NMF, int NRD, int LEAD, int VALU, int I>
+__device__ __forceinline__ void sched_reads_step() {
+  constexpr int AHEAD = (LEAD * NRD) / NMF;
+  constexpr int b0 = AHEAD + (I * NRD) / NMF;
+  constexpr int b1 = AHEAD + ((I + 1) * NRD) / NMF;
+  constexpr int before = b0 < NRD ? b0 : NRD;
+  constexpr int after = b1 < NRD ? b1 : NRD;
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if constexpr (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
+  if constexpr (after > before) __builtin_amdgcn_sched_group_barrier(0x100, after - before, 0);
+}
+template <int NMF, int NRD, int LEAD, int VALU, int... I>
+__device__ __forceinline__ void sched_reads_impl(std::integer_sequence<int, I...>) {
+  constexpr int AHEAD = (LEAD * NRD) / NMF < NRD ? (LEAD * NRD) / NMF : NRD;
+  if constexpr (AHEAD > 0) __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+  (sched_reads_step<NMF, NRD, LEAD, VALU, I>(), ...);
+}
+template <int NMF, int NRD, int LEAD, int VALU>
+__device__ __forceinline__ void sched_reads() {
+  sched_reads_impl<NMF, NRD, LEAD, VALU>(std::make_integer_sequence<int, NMF>{});
+}
+
+template <int D, int QB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_sp_kernel(const FwdArgs a) {
+  using C = SPCfg<D, QB>;
+  constexpr int BM = C::BM, BN = C::BN, ROW_B = C::ROW_B, CPR = C::CPR, TILE_B = C::TILE_B;
+  constexpr int RPI = C::RPI, NI = C::NI;
+  constexpr int NKC = D / 16;  // 16-deep contraction steps of S over head_dim
+  constexpr int NDB = D / 32;  // 32-row blocks of O^T
+  // K0 K1 V0 V1
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE_B];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c32 = lane & 31;
+  const int half = lane >> 5;
+
+  // ---- work item (heavy query blocks first; see fwd_work_item)
+  int hk, b, mb;
+  if (!fwd_work_item<BM>(a, hk, b, mb)) return;
+
+  int sq = a.seqlen_q, sk = a.seqlen_k;
+  int64_t q_base, k_base, v_base, o_base;
+  int q_tok0 = 0;
+  if (a.cu_q != nullptr) {
+    q_tok0 = a.cu_q[b];
+    sq = a.cu_q[b + 1] - q_tok0;
+    const int k_tok0 = a.cu_k[b];
+    sk = a.cu_k[b + 1] - k_tok0;
+    q_base = (int64_t)q_tok0 * a.q_rs;
+    o_base = (int64_t)q_tok0 * a.o_rs;
+    k_base = (int64_t)k_tok0 * a.k_rs;
+    v_base = (int64_t)k_tok0 * a.v_rs;
+  } else {
+    q_base = (int64_t)b * a.q_bs;
+    o_base = (int64_t)b * a.o_bs;
+    k_base = (int64_t)b * a.k_bs;
+    v_base = (int64_t)b * a.v_bs;
+  }
+  sq = uniform(sq);
+  sk = uniform(sk);
+  const int r = a.group;
+  const int rows = sq * r;
+  const int row0 = mb * BM;
+  if (row0 >= rows) return;  // uniform over the workgroup
+
+  // ---- this lane's query rows, one per query block
+  const int off = sk - sq;  // bottom-right alignment
+  bool valid[QB];
+  int pos[QB], hq[QB], lo[QB], hi[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int prow = row0 + wave * 32 * QB + qb * 32 + c32;
+    valid[qb] = prow < rows;
+    pos[qb] = valid[qb] ? prow / r : 0;
+    hq[qb] = hk * r + (valid[qb] ? prow - (prow / r) * r : 0);
+    lo[qb] = a.wl >= 0 ? pos[qb] + off - a.wl : INT_MIN / 2;
+    hi[qb] = min(a.wr >= 0 ? pos[qb] + off + a.wr : INT_MAX / 2, sk - 1);
+  }
+
+  // workgroup-wide visible key range and "tile fully visible" bounds
+  const int pos_min = uniform(row0 / r);
+  const int pos_max = uniform((min(row0 + BM, rows) - 1) / r);
+  const int kv_lo = a.wl >= 0 ? max(0, pos_min + off - a.wl) : 0;
+  const int kv_hi = a.wr >= 0 ? min(sk, pos_max + off + a.wr + 1) : sk;  // exclusive
+  const int n_begin = uniform(kv_lo / BN);
+  const int n_end = uniform(kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : n_begin);
+  const int T = n_end - n_begin;
+  const int full_hi = a.wr >= 0 ? pos_min + off + a.wr : INT_MAX / 2;
+  const int full_lo = a.wl >= 0 ? pos_max + off - a.wl : INT_MIN / 2;
+
+  // ---- Q^T fragments (B operand of S), in registers for the whole loop.
+  // Branch-free: invalid lanes read a valid row and zero it.
+  bf16x8 qf[QB][NKC];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + q_base + (int64_t)pos[qb] * a.q_rs +
+                       (int64_t)hq[qb] * a.q_hs;
+#pragma unroll
+    for (int cc = 0; cc < NKC; ++cc) {
+      const bf16x8 x = as_bf16x8(ld16(qp + 16 * cc + 8 * half));
+      qf[qb][cc] = valid[qb] ? x : zero_bf16x8();
+    }
+  }
+  // Register classes: the Q fragments are only ever MFMA operands, so they
+  // can live in accumulation registers; O is rescaled by vector
+  // instructions, which read only vector registers. Left to itself the
+  // allocator keeps O in accumulation registers and copies all of it out at
+  // every loop iteration for the (rarely taken) rescale. The empty asm
+  // statements state the intended classes and emit no instructions.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int cc = 0; cc < NKC; ++cc) asm volatile("" : "+a"(qf[qb][cc]));
+
+  f32x16 o[NDB][QB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) o[db][qb] = zero_f32x16();
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.0f;
+  }
+
+  // ---- K/V tiles go global -> LDS directly, 1 KB per wave instruction.
+  // Instruction i of wave w fills tile rows RPI*(NI*w + i) .. +RPI-1: lane j
+  // lands at row offset j / CPR, physical chunk j % CPR, so it loads logical
+  // chunk (j % CPR) ^ swizzle(row). K uses kswz16, V swz_key (the pattern its
+  // transposing reads need).
+  const __bf16* kp = static_cast<const __bf16*>(a.k) + k_base + (int64_t)hk * a.k_hs;
+  const __bf16* vp = static_cast<const __bf16*>(a.v) + v_base + (int64_t)hk * a.v_hs;
+  uint32_t kdo[NI], vdo[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = RPI * (NI * wave + i) + lane / CPR;
+    kdo[i] = (uint32_t)(row * a.k_rs * 2 + ((lane % CPR) ^ kswz16(row)) * 16);
+    vdo[i] = (uint32_t)(row * a.v_rs * 2 + ((lane % CPR) ^ swz_key(row)) * 16);
+  }
+  const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
+  // one buffer descriptor per tensor per tile, ending at the last row before
+  // seqlen_k (rows past it read as zero)
+  auto issue_k = [&](int j, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const int n0 = (n_begin + j) * BN;
+    const int nrows = min(sk - n0, BN);  // >= 1
+    const auto rs = make_rsrc(kp + (int64_t)n0 * a.k_rs, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(rs, kdo[i], lds_w + (uint32_t)(buf * TILE_B + i * 1024));
+  };
+  auto issue_v = [&](int j, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const int n0 = (n_begin + j) * BN;
+    const int nrows = min(sk - n0, BN);
+    const auto rs = make_rsrc(vp + (int64_t)n0 * a.v_rs, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      dma16(rs, vdo[i], lds_w + (uint32_t)((2 + buf) * TILE_B + i * 1024));
+  };
+
+  // ---- fragment read offsets. K: lane (c32, half) reads logical chunk
+  // 2*cc + half of key c32 (+32 for the second key block, same swizzle); for
+  // cc >= 8 (D = 256) the chunk lies 16 chunks = 256 bytes further. V: the
+  // transposing-read pattern of fwd_kernel.hip.
+  const int fk = kswz16(c32);
+  int k_rd[8];
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) k_rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ fk) * 16);
+  const int tr_g = lane >> 4;
+  const int tr_j = lane & 15;
+  const int tr_row = 4 * half + (tr_j >> 2);
+  const int tr_c = (tr_g & 1) * 2 + ((tr_j & 3) >> 1);
+  const int fv = swz_key(tr_row);
+  int v_rd[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    v_rd[i] = 2 * TILE_B + tr_row * ROW_B + (((4 * i + tr_c) ^ fv) * 16) + (tr_j & 1) * 8;
+
+  const float c = a.scale_log2;
+  const float rescale_raw = C::RESCALE_LOG2 / fmaxf(c, 1e-30f);
+
+  typedef f32x16 STile[2][QB];  // S^T accumulators: key block x query block
+  bf16x8 pf[QB][4];             // P^T fragments of the current tile
+  float ms[QB];                 // running max in exp2 units, per query block
+
+  // S = K(tile in buffer buf) Q^T. Contraction step outermost, so consecutive
+  // MFMAs accumulate into different registers.
+  auto s_tile = [&](auto buf_c, STile& s) {
+    constexpr int buf = decltype(buf_c)::value;
+    const char* kb0 = smem + buf * TILE_B;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = zero_f32x16();
+#pragma unroll
+    for (int cc = 0; cc < NKC; ++cc) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb0 + kb * 32 * ROW_B + (cc >> 3) * 256 +
+                                                           k_rd[cc & 7]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(kf, qf[qb][cc], s[kb][qb]);
+      }
+    }
+  };
+
+  // mask (edge tiles), running max, lazy rescale of O and l
+  auto sm_max = [&](STile& s, int j) {
+    const int n0 = (n_begin + j) * BN;
+    const bool full = (n0 + BN <= sk) && (n0 + BN - 1 <= full_hi) && (n0 >= full_lo);
+    if (!full) {
+      // element (kb, v) holds key n0 + 4*half + l, l = 32*kb + 8*(v>>2) + (v&3)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const uint64_t vis = vis64(lo[qb] - n0 - 4 * half, hi[qb] - n0 - 4 * half);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t w = (uint32_t)(vis >> (32 * kb));
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            s[kb][qb][v] = mask_by_bit(s[kb][qb][v], w, 8 * (v >> 2) + (v & 3));
+        }
+      }
+    }
+    bool grow[QB];
+    float mt[QB];
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float m0 = kNegInf, m1 = kNegInf;
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        m0 = vmax3(m0, s[0][qb][v], s[0][qb][v + 1]);
+        m1 = vmax3(m1, s[1][qb][v], s[1][qb][v + 1]);
+      }
+      mt[qb] = pair_max(vmax(m0, m1));
+      grow[qb] = (m_run[qb] == kNegInf) ? (mt[qb] != kNegInf) : (mt[qb] - m_run[qb] > rescale_raw);
+      any = any || grow[qb];
+    }
+    if (__builtin_amdgcn_ballot_w64(any) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = grow[qb] ? mt[qb] : m_run[qb];
+        const float alpha = grow[qb]
+                                ? ((m_run[qb] == kNegInf) ? 0.0f : fast_exp2((m_run[qb] - m_new) * c))
+                                : 1.0f;
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[db][qb][v] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ms[qb] = (m_run[qb] == kNegInf) ? 0.0f : m_run[qb] * c;
+  };
+
+  // P = exp2(S*c - m*c), row sums, P^T fragments in the key order of the V^T
+  // fragments (fwd_kernel.hip)
+  auto sm_exp = [&](STile& s) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(fmaf(s[kb][qb][v], c, -ms[qb]));
+          s[kb][qb][v] = p;
+          rs[v & 3] += p;
+        }
+      }
+      l_run[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kb = t >> 1;
+        const int i0 = 2 * (t & 1);
+        pf[qb][t] = cat(cvt4(s[kb][qb][4 * i0 + 0], s[kb][qb][4 * i0 + 1], s[kb][qb][4 * i0 + 2],
+                             s[kb][qb][4 * i0 + 3]),
+                        cvt4(s[kb][qb][4 * i0 + 4], s[kb][qb][4 * i0 + 5], s[kb][qb][4 * i0 + 6],
+                             s[kb][qb][4 * i0 + 7]));
+      }
+    }
+  };
+
+  // O += P V(tile in buffer buf): each V^T fragment pair feeds QB MFMAs;
+  // d-block innermost so consecutive MFMAs use different accumulators
+  // O += P V(tile in buffer buf); MFMA i covers key step t = i / NDB and
+  // d-block db = i % NDB (consecutive MFMAs use different accumulators). The
+  // V^T fragments are read LEAD2 MFMAs ahead, in source order, and scheduling
+  // barriers (nothing may cross them) between the {read i + LEAD2, MFMA i}
+  // groups keep that order: left free, the scheduler issues each read right
+  // before its MFMA, which then waits out the whole LDS latency.
+  auto pv_tile = [&](auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr int N = 4 * NDB;
+    constexpr int LEAD2 = FWD_SP_LEAD2;
+    auto read = [&](int i) __attribute__((always_inline)) {
+      const int t = i / NDB, db = i % NDB;
+      const char* p = smem + v_rd[db & 1] + (buf * TILE_B + (16 * t) * ROW_B + (db >> 1) * 128);
+      const bf16x4 v0 = ds_read_tr16(reinterpret_cast<const __bf16*>(p));
+      const bf16x4 v1 = ds_read_tr16(reinterpret_cast<const __bf16*>(p + 8 * ROW_B));
+      return cat(v0, v1);
+    };
+    bf16x8 ring[LEAD2];
+#pragma unroll
+    for (int i = 0; i < LEAD2; ++i) ring[i] = read(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int t = i / NDB, db = i % NDB;
+      const bf16x8 vf = ring[i % LEAD2];
+      if (i + LEAD2 < N) ring[i % LEAD2] = read(i + LEAD2);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma32(vf, pf[qb][t], o[db][qb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Phase-1 issue order: the S MFMAs spread through the softmax's vector
+  // instructions, K fragment reads LEAD1 MFMAs ahead.
+  constexpr int NMF = 2 * NKC * QB;     // MFMAs of one S tile
+  constexpr int NRD1 = 2 * NKC;         // K fragment reads of one S tile
+  constexpr int VPM = QB == 1 ? 4 : 7;  // vector instructions per phase-1 MFMA
+  constexpr int LEAD1 = FWD_SP_LEAD1;
+
+  STile sA, sB;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // iteration k: cur holds S(k); nxt receives S(k+1). par = k & 1.
+  auto step = [&](int k, auto par_c, STile& cur, STile& nxt) {
+    constexpr int par = decltype(par_c)::value;
+    using PN = std::integral_constant<int, par ^ 1>;
+    vmcnt_wait<0>();  // K(k+1), V(k) (this wave's parts)
+    lds_barrier();    // everyone's parts landed; K(k), V(k-1) no longer read
+    if (k + 2 < T) issue_k(k + 2, par_c);  // into the buffer K(k) left
+    if (k + 1 < T) issue_v(k + 1, PN{});   // into the buffer V(k-1) left
+    sm_max(cur, k);
+    if (k + 1 < T) {
+      s_tile(PN{}, nxt);
+      sm_exp(cur);
+      sched_reads<NMF, NRD1, LEAD1, VPM>();
+    } else {
+      sm_exp(cur);
+    }
+    pv_tile(par_c);
+  };
+
+  if (T > 0) {
+    // prologue: K(0), V(0), K(1) requested (K(0) re-read when T == 1); wait
+    // for K(0), compute S(0)
+    issue_k(0, I0{});
+    issue_v(0, I0{});
+    issue_k(min(1, T - 1), I1{});
+    vmcnt_wait<2 * NI>();
+    lds_barrier();
+    s_tile(I0{}, sA);
+    for (int k = 0; k < T; k += 2) {
+      step(k, I0{}, sA, sB);
+      if (k + 1 < T) step(k + 1, I1{}, sB, sA);
+    }
+    vmcnt_wait<0>();
+  }
+
+  // ---- epilogue: combine the two lane halves' row sums, normalise, store
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = pair_sum(l_run[qb]);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (valid[qb]) {
+      __bf16* op = static_cast<__bf16*>(a.out) + o_base + (int64_t)pos[qb] * a.o_rs +
+                   (int64_t)hq[qb] * a.o_hs;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = db * 32 + 8 * i + 4 * half;
+          *reinterpret_cast<bf16x4*>(op + d0) =
+              cvt4(o[db][qb][4 * i] * inv, o[db][qb][4 * i + 1] * inv, o[db][qb][4 * i + 2] * inv,
+                   o[db][qb][4 * i + 3] * inv);
+        }
+      if (half == 0 && a.lse != nullptr) {
+        const float lse = l_tot > 0.0f ? m_run[qb] * a.scale + __logf(l_tot) : kNegInf;
+        const int64_t li = a.cu_q != nullptr
+                               ? (int64_t)hq[qb] * a.total_q + q_tok0 + pos[qb]
+                               : ((int64_t)b * a.hq + hq[qb]) * sq + pos[qb];
+        a.lse[li] = lse;
+      }
+    }
+  }
+}
+
+template <int D, int QB>
+hipError_t launch_fwd_sp(const FwdArgs& args, hipStream_t s) {
+  constexpr int BM = SPCfg<D, QB>::BM;
+  FwdArgs a = args;
+  a.num_m_blocks = (int)(((int64_t)a.max_rows + BM - 1) / BM);
+  const int64_t grid = fwd_blocks_per_head(a, BM) * a.hkv;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_sp_kernel<D, QB>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_fwd_sp<256, 1>(const FwdArgs&, hipStream_t);
+
+}  // namespace mi_attn

@@ -124,6 +124,7 @@ constexpr bool decode_streams(int head_dim, int page_size) {
 
 template <int D> hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
 template <int D> hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t s);
+template <int D, int QB> hipError_t launch_fwd_sp(const FwdArgs& a, hipStream_t s);
 template <int D> hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 template <int D> hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t s);
 template <int D> hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
