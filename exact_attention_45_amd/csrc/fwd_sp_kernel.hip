@@ -17,10 +17,13 @@
 //   top     : wait until K(k+1) and V(k) have landed, barrier; request
 //             K(k+2) and V(k+1) straight into LDS (direct-to-LDS buffer loads)
 //   softmax : mask S(k) on edge tiles, running max, lazy rescale of O
-//   phase 1 : S(k+1) = K(k+1) Q^T on the matrix cores, its MFMAs interleaved
-//             with the exponentials, row sums and bf16 packing of P(k)
+//   phase 1 : S(k+1) = K(k+1) Q^T on the matrix cores, each MFMA issued
+//             together with exponentials, row-sum adds and bf16 packing of
+//             P(k), K fragment reads a few MFMAs ahead
 //   phase 2 : O += P(k) V(k), the transposing V reads issued several MFMAs
-//             ahead and held there by scheduling barriers
+//             ahead
+// Both phases are written in the intended issue order and held there by
+// scheduling barriers.
 // K runs one tile ahead of V; each has two LDS buffers (tile j in buffer
 // j & 1). The loop is unrolled by two so buffer offsets and the two score
 // register sets are fixed at compile time.
@@ -28,7 +31,8 @@
 // With one wave per SIMD nothing hides LDS latency but the wave's own
 // read-ahead: with each read issued just before its MFMA (the compiler's
 // choice when left alone) the long-context D256 workload ran 2.85 ms; with
-// six MFMAs of read-ahead in phase 2, 2.4 ms.
+// six MFMAs of read-ahead in phase 2, 2.35 ms; with phase 1 also written out
+// group by group, 2.07 ms.
 //
 // Register classes: this source is compiled with MFMA results in vector
 // registers (the build's per-file flag), so O and S stay where the softmax
@@ -36,7 +40,6 @@
 // operands, are placed in the accumulation registers.
 #include <climits>
 #include <type_traits>
-#include <utility>
 
 #include "attn_common.hpp"
 #include "kernels.hpp"
@@ -69,31 +72,6 @@ struct SPCfg {
 // kswz16 takes 16 distinct values over any 16 consecutive keys, and rows are a
 // multiple of 256 bytes, so those reads hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int kswz16(int key) { return swz_key(key) | (((key >> 3) & 1) << 3); }
-
-// Scheduling-group pattern for a run of NMF MFMAs fed by NRD LDS fragment
-// reads: the reads of the first LEAD MFMAs go first, then after each MFMA the
-// reads that keep LEAD MFMAs' worth in flight, and VALU vector instructions.
-template <int NMF, int NRD, int LEAD, int VALU, int I>
-__device__ __forceinline__ void sched_reads_step() {
-  constexpr int AHEAD = (LEAD * NRD) / NMF;
-  constexpr int b0 = AHEAD + (I * NRD) / NMF;
-  constexpr int b1 = AHEAD + ((I + 1) * NRD) / NMF;
-  constexpr int before = b0 < NRD ? b0 : NRD;
-  constexpr int after = b1 < NRD ? b1 : NRD;
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  if constexpr (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
-  if constexpr (after > before) __builtin_amdgcn_sched_group_barrier(0x100, after - before, 0);
-}
-template <int NMF, int NRD, int LEAD, int VALU, int... I>
-__device__ __forceinline__ void sched_reads_impl(std::integer_sequence<int, I...>) {
-  constexpr int AHEAD = (LEAD * NRD) / NMF < NRD ? (LEAD * NRD) / NMF : NRD;
-  if constexpr (AHEAD > 0) __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
-  (sched_reads_step<NMF, NRD, LEAD, VALU, I>(), ...);
-}
-template <int NMF, int NRD, int LEAD, int VALU>
-__device__ __forceinline__ void sched_reads() {
-  sched_reads_impl<NMF, NRD, LEAD, VALU>(std::make_integer_sequence<int, NMF>{});
-}
 
 template <int D, int QB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -363,8 +341,55 @@ void fwd_sp_kernel(const FwdArgs a) {
     }
   };
 
-  // O += P V(tile in buffer buf): each V^T fragment pair feeds QB MFMAs;
-  // d-block innermost so consecutive MFMAs use different accumulators
+  // Phase 1 for one query block per wave: S(next) = K(tile in buffer buf)
+  // Q^T fused with the exponentials of S(cur). MFMA i (contraction step
+  // i / 2, key block i % 2) is issued with the K fragment read LEAD1 MFMAs
+  // ahead and with the exponentials, row-sum adds and bf16 packing of
+  // 32 / N_MF score elements of the current tile, in that source order, held
+  // by scheduling barriers between the groups.
+  auto phase1 = [&](auto buf_c, STile& cur, STile& nxt) __attribute__((always_inline)) {
+    static_assert(QB == 1, "fused phase 1 handles one query block per wave");
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr int N = 2 * NKC;   // MFMAs and K fragment reads
+    constexpr int EPM = 32 / N;  // score elements per MFMA
+    constexpr int L1 = FWD_SP_LEAD1;
+    auto kread = [&](int i) __attribute__((always_inline)) {
+      const int cc = i >> 1, kb = i & 1;
+      return *reinterpret_cast<const bf16x8*>(smem + k_rd[cc & 7] +
+                                              (buf * TILE_B + kb * 32 * ROW_B + (cc >> 3) * 256));
+    };
+    bf16x8 ring[L1];
+#pragma unroll
+    for (int i = 0; i < L1; ++i) ring[i] = kread(i);
+    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int cc = i >> 1, kb = i & 1;
+      const bf16x8 kf = ring[i % L1];
+      if (i + L1 < N) ring[i % L1] = kread(i + L1);
+      nxt[kb][0] = mfma32(kf, qf[0][cc], cc == 0 ? zero_f32x16() : nxt[kb][0]);
+#pragma unroll
+      for (int e = 0; e < EPM; ++e) {
+        const int j = i * EPM + e;  // element: key block j / 16, register j % 16
+        const int jb = j >> 4, jv = j & 15;
+        const float x = fast_exp2(fmaf(cur[jb][0][jv], c, -ms[0]));
+        cur[jb][0][jv] = x;
+        rs[jv & 3] += x;
+        if ((j & 7) == 7) {
+          // P^T fragment t holds elements 8t .. 8t+7 (see sm_exp)
+          const int t = j >> 3, tb = t >> 1, t0 = 8 * (t & 1);
+          pf[0][t] = cat(cvt4(cur[tb][0][t0 + 0], cur[tb][0][t0 + 1], cur[tb][0][t0 + 2],
+                              cur[tb][0][t0 + 3]),
+                         cvt4(cur[tb][0][t0 + 4], cur[tb][0][t0 + 5], cur[tb][0][t0 + 6],
+                              cur[tb][0][t0 + 7]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run[0] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  };
+
   // O += P V(tile in buffer buf); MFMA i covers key step t = i / NDB and
   // d-block db = i % NDB (consecutive MFMAs use different accumulators). The
   // V^T fragments are read LEAD2 MFMAs ahead, in source order, and scheduling
@@ -397,12 +422,6 @@ void fwd_sp_kernel(const FwdArgs a) {
     }
   };
 
-  // Phase-1 issue order: the S MFMAs spread through the softmax's vector
-  // instructions, K fragment reads LEAD1 MFMAs ahead.
-  constexpr int NMF = 2 * NKC * QB;     // MFMAs of one S tile
-  constexpr int NRD1 = 2 * NKC;         // K fragment reads of one S tile
-  constexpr int VPM = QB == 1 ? 4 : 7;  // vector instructions per phase-1 MFMA
-  constexpr int LEAD1 = FWD_SP_LEAD1;
 
   STile sA, sB;
   using I0 = std::integral_constant<int, 0>;
@@ -418,9 +437,7 @@ void fwd_sp_kernel(const FwdArgs a) {
     if (k + 1 < T) issue_v(k + 1, PN{});   // into the buffer V(k-1) left
     sm_max(cur, k);
     if (k + 1 < T) {
-      s_tile(PN{}, nxt);
-      sm_exp(cur);
-      sched_reads<NMF, NRD1, LEAD1, VPM>();
+      phase1(PN{}, cur, nxt);
     } else {
       sm_exp(cur);
     }
