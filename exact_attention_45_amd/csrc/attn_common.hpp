@@ -112,6 +112,19 @@ __device__ __forceinline__ f32x16 zero_f32x16() {
 // row-major (key, dim) in LDS and lane j pointing at key j/4, dims 4*(j%4),
 // lane i gets dim i of four consecutive keys: an MFMA operand fragment whose
 // contraction index is the key. (Semantics measured on gfx950.)
+//
+// Fragment orders used by the P V product (O^T += V^T P^T), 16 keys per MFMA:
+//   * V^T fragment (A operand): two transposing reads. 16-lane group g reads
+//     4 keys x 16 dims; lane j points at key 4*half + j/4 (+16t for MFMA t,
+//     +8 for the second read), dims 16*(g&1) + 4*(j&3) of d-block db, i.e.
+//     16-byte chunk 4*db + 2*(g&1) + (j&3)/2 of that key row, which sits at
+//     8*(db>>1) + ((4*(db&1) + chunk%4) ^ swz_key(key)) in the swizzled tile:
+//     two lane patterns (db even / odd) plus immediates.
+//   * P^T fragment (B operand): MFMA t covers keys 16t..16t+15 of the tile;
+//     lane half h supplies keys {16t+4h+j, 16t+8+4h+j : j<4}, the key order of
+//     the V^T fragment above, taken from S^T accumulator registers
+//     8*(t&1) .. 8*(t&1)+7 of key block t>>1. The contraction is over the
+//     same 16 keys in the same order on both sides, so the product is exact.
 __device__ __forceinline__ bf16x4 ds_read_tr16(const __bf16* p) {
   typedef __attribute__((ext_vector_type(4))) short s16x4;
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;

@@ -1,6 +1,6 @@
 // Prefill forward for head_dim 64/128: eight waves in two ping-pong groups.
 //
-// Same method as fwd_kernel.hip (mslk flash_attn interface.py page,
+// Same method as in fwd_kernel.hip (mslk flash_attn interface.py page,
 // `_flash_attn_fwd`: exact attention with online softmax in the exp2 domain
 // and a natural-log LSE; lazily updated running max). What differs is the
 // schedule. A workgroup owns 256 packed query rows: group A = waves 0-3
@@ -189,8 +189,8 @@ void fwd_pp_kernel(const FwdArgs a) {
 
   // ---- fragment read offsets. K: lane (c32, half) reads logical chunk
   // 2*cc + half of key c32 (+32 for the second key block, which has the same
-  // swizzle). V: per-lane constant + immediate (see fwd_kernel.hip for the
-  // derivation of the two transposing-read patterns).
+  // swizzle). V: per-lane constant + immediate (the two transposing-read patterns
+  // of attn_common.hpp).
   const int fk = kswz(c32);
   int k_rd[D / 16];
 #pragma unroll
@@ -315,7 +315,7 @@ void fwd_pp_kernel(const FwdArgs a) {
       }
     }
     l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-    // P^T fragments in the key order of the V^T fragments (fwd_kernel.hip)
+    // P^T fragments in the key order of the V^T fragments (attn_common.hpp)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kb = t >> 1;

@@ -3,7 +3,7 @@
 // runs the current tile's exponentials. Serves head_dim 256, whose O
 // accumulators alone take 128 registers per lane.
 //
-// Method as in fwd_pp_kernel.hip (mslk flash_attn interface.py page,
+// Method as in fwd_kernel.hip (mslk flash_attn interface.py page,
 // `_flash_attn_fwd`): exact attention, online softmax in the exp2 domain with
 // a lazily updated running max, natural-log LSE, empty rows O = 0 and
 // LSE = -inf. Same MFMA conventions (attn_common.hpp: both GEMMs transposed so
@@ -218,7 +218,7 @@ void fwd_sp_kernel(const FwdArgs a) {
   // ---- fragment read offsets. K: lane (c32, half) reads logical chunk
   // 2*cc + half of key c32 (+32 for the second key block, same swizzle); for
   // cc >= 8 (D = 256) the chunk lies 16 chunks = 256 bytes further. V: the
-  // transposing-read pattern of fwd_kernel.hip.
+  // transposing-read pattern of attn_common.hpp.
   const int fk = kswz16(c32);
   int k_rd[8];
 #pragma unroll
@@ -314,7 +314,7 @@ void fwd_sp_kernel(const FwdArgs a) {
   };
 
   // P = exp2(S*c - m*c), row sums, P^T fragments in the key order of the V^T
-  // fragments (fwd_kernel.hip)
+  // fragments (attn_common.hpp)
   auto sm_exp = [&](STile& s) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
