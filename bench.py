@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "fwd_pp_kernel<128>": ["fwd_pp_kernel.hip", "attn_common.hpp", "kernels.hpp"],
     "decode_stream_kernel<128>": ["decode_stream_kernel.hip", "attn_common.hpp", "kernels.hpp"],
     "combine_kernel<128>": ["decode_kernel.hip", "attn_common.hpp", "kernels.hpp"],
+    "fwd_sp_kernel<256,1>": ["fwd_sp_kernel.hip", "attn_common.hpp", "kernels.hpp"],
 }
 COUNTER_SUMMARY = os.path.join(
     HERE, "profiles", "hbm_counters_prefill_s4096_d128_and_paged_decode_sk32768.md")
