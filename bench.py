@@ -119,6 +119,14 @@ def prefill_flops(w) -> float:
             lq = int(w.cu_seqlens_q[b + 1] - w.cu_seqlens_q[b])
             lk = int(w.cu_seqlens_k[b + 1] - w.cu_seqlens_k[b])
             pairs += _pairs(lq, lk, w.causal, w.window_left, w.window_right)
+    elif w.kind == "paged_prefill":
+        cap = w.page_table.shape[1] * w.page_size
+        pairs = 0
+        for b in range(w.batch):
+            lk = cap if w.seqused_k is None else int(w.seqused_k[b])
+            lq = (int(w.cu_seqlens_q[b + 1] - w.cu_seqlens_q[b]) if w.cu_seqlens_q is not None
+                  else w.seqlen_q)
+            pairs += _pairs(lq, lk, w.causal, w.window_left, w.window_right)
     else:
         pairs = w.batch * _pairs(w.seqlen_q, w.seqlen_k, w.causal, w.window_left, w.window_right)
     return 4.0 * w.head_dim * w.num_heads_q * pairs
@@ -156,6 +164,9 @@ class Prefill:
         if w.kind == "varlen":
             self.kw.update(cu_seqlens_q=dev_i32(w.cu_seqlens_q), cu_seqlens_k=dev_i32(w.cu_seqlens_k),
                            max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k)
+        if w.kind == "paged_prefill":
+            self.kw.update(page_table=dev_i32(w.page_table),
+                           seqused_k=None if w.seqused_k is None else dev_i32(w.seqused_k))
         self.out, self.lse = mi.mi_attn_fwd(self.q, self.k, self.v, **self.kw)
 
     def __call__(self):
@@ -288,8 +299,12 @@ def main():
 
     extra = {}
     if args.all_configs:
-        for i in (1, 3, 4):
-            wi = W.standard_config(i)
+        # the three other prefill workloads, then the causal GQA S4096 D128 one
+        # with K/V in a cache of 256-token pages behind a permuted page table
+        paged = W.paged_prefill_case(1002, 1, 32, 4, 128, 256, 16, None, seqlen_q=4096,
+                                     causal=True, name="paged256_causal_gqa32x4_s4096_d128")
+        for i in (1, 3, 4, paged):
+            wi = W.standard_config(i) if isinstance(i, int) else i
             p = Prefill(mi, wi, torch)
             for _ in range(3):
                 p()

@@ -72,6 +72,8 @@ class FwdParams(ctypes.Structure):
         ("page_table", _vp),
         ("softmax_scale", ctypes.c_float),
         ("causal", _i32), ("window_left", _i32), ("window_right", _i32),
+        ("seqused_k", _vp),
+        ("page_size", _i32), ("num_pages", _i32), ("max_pages_per_seq", _i32),
     ]
 
 
@@ -174,26 +176,60 @@ def mi_attn_fwd(q, k, v, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=Non
                 max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
                 softmax_scale: Optional[float] = None, causal: bool = False,
                 window_left: Optional[int] = None, window_right: Optional[int] = None,
-                return_lse: bool = True) -> Tuple:
+                return_lse: bool = True, page_table=None, seqused_k=None,
+                check_bounds: bool = False) -> Tuple:
     """Exact attention forward (interface page, `_flash_attn_fwd` contract).
 
     Dense: q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D); lse (B, Hq, Sq).
     Varlen: q (Tq, Hq, D), k/v (Tk, Hkv, D), cu_seqlens_q/k int32 (B+1,);
     lse (Hq, Tq). max_seqlen_q/k default to the token totals (no device sync).
+    Paged: page_table int32 (B, max_pages) with k/v caches
+    (num_pages, page_size, Hkv, D), page_size a multiple of 64, seqused_k int32
+    (B,) or None (every sequence max_pages * page_size keys); q dense or packed
+    by cu_seqlens_q (cu_seqlens_k must be None). check_bounds validates the
+    page ids and seqused_k on the host first (one device-to-host copy).
     """
     import torch
     lib = load()
     dev = q.device
     for n, t in (("q", q), ("k", k), ("v", v)):
         _req_bf16(n, t, dev)
+    paged = page_table is not None
+    if paged and cu_seqlens_k is not None:
+        raise MiAttnError(MI_ATTN_EINVAL, "page_table is not supported with cu_seqlens_k")
+    if not paged and seqused_k is not None:
+        raise MiAttnError(MI_ATTN_EINVAL, "seqused_k is only used with a page_table")
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
-    if varlen and (cu_seqlens_q is None or cu_seqlens_k is None):
+    if varlen and not paged and (cu_seqlens_q is None or cu_seqlens_k is None):
         raise MiAttnError(MI_ATTN_EINVAL, "cu_seqlens_q and cu_seqlens_k go together")
     hq, d = q.shape[-2], q.shape[-1]
     hkv = k.shape[-2]
     if v.shape[-1] != d or k.shape[-1] != d:
         raise MiAttnError(MI_ATTN_EUNSUPPORTED, "head_dim of q, k and v must match")
-    if varlen:
+    if paged:
+        if k.dim() != 4 or k.shape != v.shape:
+            raise MiAttnError(MI_ATTN_EINVAL, "paged k/v must be (num_pages, page_size, Hkv, D)")
+        if varlen:
+            if q.dim() != 3:
+                raise MiAttnError(MI_ATTN_EINVAL, "varlen q must be (tokens, heads, head_dim)")
+            batch = cu_seqlens_q.shape[0] - 1
+            _req_i32("cu_seqlens_q", cu_seqlens_q, (batch + 1,), dev)
+            total_q = q.shape[0]
+            max_q = total_q if max_seqlen_q is None else int(max_seqlen_q)
+            seq_shape, lse_shape = (total_q,), (hq, total_q)
+        else:
+            if q.dim() != 4:
+                raise MiAttnError(MI_ATTN_EINVAL, "dense q must be (batch, seqlen, heads, head_dim)")
+            batch, sq = q.shape[0], q.shape[1]
+            total_q, max_q = batch * sq, sq
+            seq_shape, lse_shape = (batch, sq), (batch, hq, sq)
+        _req_i32("page_table", page_table, (batch, page_table.shape[1]), dev)
+        if seqused_k is not None:
+            _req_i32("seqused_k", seqused_k, (batch,), dev)
+        if check_bounds:
+            check_paged_bounds(page_table, seqused_k, k.shape[0], k.shape[1])
+        max_k = page_table.shape[1] * k.shape[1]
+    elif varlen:
         if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape:
             raise MiAttnError(MI_ATTN_EINVAL, "varlen q/k/v must be (tokens, heads, head_dim)")
         batch = cu_seqlens_q.shape[0] - 1
@@ -229,7 +265,21 @@ def mi_attn_fwd(q, k, v, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=Non
 
     p = FwdParams()
     p.q, p.k, p.v, p.out, p.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse)
-    if varlen:
+    if paged:
+        if varlen:
+            p.q_row_stride, p.q_head_stride = q.stride(0), q.stride(1)
+            p.o_row_stride, p.o_head_stride = out.stride(0), out.stride(1)
+            p.cu_seqlens_q = cu_seqlens_q.data_ptr()
+        else:
+            p.q_batch_stride, p.q_row_stride, p.q_head_stride = q.stride(0), q.stride(1), q.stride(2)
+            p.o_batch_stride, p.o_row_stride, p.o_head_stride = (out.stride(0), out.stride(1),
+                                                                 out.stride(2))
+            p.seqlen_q = max_q
+        p.k_batch_stride, p.k_row_stride, p.k_head_stride = k.stride(0), k.stride(1), k.stride(2)
+        p.v_batch_stride, p.v_row_stride, p.v_head_stride = v.stride(0), v.stride(1), v.stride(2)
+        p.page_table, p.seqused_k = page_table.data_ptr(), _ptr(seqused_k)
+        p.num_pages, p.page_size, p.max_pages_per_seq = k.shape[0], k.shape[1], page_table.shape[1]
+    elif varlen:
         p.q_row_stride, p.q_head_stride = q.stride(0), q.stride(1)
         p.k_row_stride, p.k_head_stride = k.stride(0), k.stride(1)
         p.v_row_stride, p.v_head_stride = v.stride(0), v.stride(1)

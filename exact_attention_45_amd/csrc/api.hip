@@ -135,11 +135,22 @@ const char* mi_attn_version(void) { return "mi_attn 0.1.0 gfx950"; }
 
 int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
   if (p == nullptr) return fail(MI_ATTN_EINVAL, "params is NULL");
-  if (p->page_table != nullptr)
-    return fail(MI_ATTN_EUNSUPPORTED, "paged K/V in the prefill forward is not supported; "
-                                      "use mi_attn_decode_splitkv");
-  const bool varlen = p->cu_seqlens_q != nullptr || p->cu_seqlens_k != nullptr;
-  if (varlen && (p->cu_seqlens_q == nullptr || p->cu_seqlens_k == nullptr))
+  const bool paged = p->page_table != nullptr;
+  if (paged) {
+    // interface page: the page_table branch rejects cu_seqlens_k
+    if (p->cu_seqlens_k != nullptr)
+      return fail(MI_ATTN_EINVAL, "page_table is not supported with cu_seqlens_k");
+    if (p->page_size <= 0 || p->num_pages <= 0 || p->max_pages_per_seq <= 0)
+      return fail(MI_ATTN_EINVAL, "page_size, num_pages and max_pages_per_seq must be > 0");
+    if (p->page_size % mi_attn::kFwdBlockN != 0)
+      return fail(MI_ATTN_EUNSUPPORTED, "page_size %d must be a multiple of %d for the prefill "
+                  "forward", p->page_size, mi_attn::kFwdBlockN);
+    if ((int64_t)p->page_size * p->max_pages_per_seq > INT32_MAX ||
+        (int64_t)p->batch * p->max_pages_per_seq > INT32_MAX)
+      return fail(MI_ATTN_EINVAL, "page table too large for 32-bit indexing");
+  }
+  const bool varlen = p->cu_seqlens_q != nullptr || (!paged && p->cu_seqlens_k != nullptr);
+  if (varlen && !paged && (p->cu_seqlens_q == nullptr || p->cu_seqlens_k == nullptr))
     return fail(MI_ATTN_EINVAL, "cu_seqlens_q and cu_seqlens_k must both be given");
   if (p->batch < 0 || p->num_heads_q <= 0 || p->num_heads_kv <= 0)
     return fail(MI_ATTN_EINVAL, "batch must be >= 0 and head counts > 0");
@@ -152,12 +163,12 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
     return fail(MI_ATTN_EUNSUPPORTED, "softmax_scale must be finite and >= 0");
   int max_q, max_k;
   if (varlen) {
-    if (p->max_seqlen_q < 0 || p->max_seqlen_k < 0 || p->total_q < 0)
+    if (p->max_seqlen_q < 0 || (!paged && p->max_seqlen_k < 0) || p->total_q < 0)
       return fail(MI_ATTN_EINVAL, "max_seqlen_q/k and total_q must be >= 0 for varlen");
     max_q = p->max_seqlen_q;
     max_k = p->max_seqlen_k;
   } else {
-    if (p->seqlen_q < 0 || p->seqlen_k < 0)
+    if (p->seqlen_q < 0 || (!paged && p->seqlen_k < 0))
       return fail(MI_ATTN_EINVAL, "seqlen_q and seqlen_k must be >= 0");
     max_q = p->seqlen_q;
     max_k = p->seqlen_k;
@@ -181,11 +192,15 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
   if ((int64_t)kFwdRowsPerTile * (p->k_row_stride + p->v_row_stride) * 2 > INT32_MAX)
     return fail(MI_ATTN_EINVAL, "K/V row stride too large for 32-bit tile offsets");
   if (!varlen) {
-    const int64_t bstr[] = {p->q_batch_stride, p->k_batch_stride, p->v_batch_stride,
-                            p->o_batch_stride};
+    const int64_t bstr[] = {p->q_batch_stride, p->o_batch_stride};
     for (int64_t s : bstr)
       if (!stride_ok(s))
         return fail(MI_ATTN_EINVAL, "batch strides must be non-negative multiples of 8");
+  }
+  if (!varlen || paged) {
+    // dense: batch strides; paged: page strides
+    if (!stride_ok(p->k_batch_stride) || !stride_ok(p->v_batch_stride))
+      return fail(MI_ATTN_EINVAL, "K/V batch (or page) strides must be non-negative multiples of 8");
   }
   (void)max_k;
 
@@ -208,10 +223,15 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
   a.o_rs = p->o_row_stride;
   a.o_hs = p->o_head_stride;
   a.cu_q = p->cu_seqlens_q;
-  a.cu_k = p->cu_seqlens_k;
+  a.cu_k = paged ? nullptr : p->cu_seqlens_k;
   a.batch = p->batch;
   a.seqlen_q = varlen ? 0 : p->seqlen_q;
-  a.seqlen_k = varlen ? 0 : p->seqlen_k;
+  a.seqlen_k = (varlen || paged) ? 0 : p->seqlen_k;
+  a.page_table = p->page_table;
+  a.seqused_k = paged ? p->seqused_k : nullptr;
+  a.page_size = paged ? p->page_size : 0;
+  a.num_pages = paged ? p->num_pages : 0;
+  a.max_pages = paged ? p->max_pages_per_seq : 0;
   a.hq = p->num_heads_q;
   a.hkv = p->num_heads_kv;
   a.group = group;

@@ -23,6 +23,12 @@
 //   * K and V tiles row-major in LDS with XOR-swizzled 16-byte chunks, filled
 //     by direct-to-LDS buffer loads whose descriptor ends at seqlen_k (rows
 //     past it read as zero);
+//   * with a paged K/V cache (interface page, page_table branch) a 64-key tile
+//     lies in one page (page_size is a multiple of 64), so the tile's
+//     descriptor is based at page_table[b][n0 / page_size] * page stride +
+//     (n0 % page_size) rows; a workgroup first checks every page id it will
+//     read and writes NaN instead when one is outside [0, num_pages). Paging
+//     is a template parameter: the dense kernels carry none of it;
 //   * tiles wholly outside the causal/window band are never visited;
 //   * grid order: heaviest (latest) query blocks first, KV head fastest, so
 //     round-robin placement keeps each KV head's K/V in a fixed subset of the

@@ -43,7 +43,7 @@ struct PPCfg {
   static_assert(BN == 64 && (CPR == 8 || CPR == 16), "staging assumes 64-key tiles, D 64/128");
 };
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_pp_kernel(const FwdArgs a) {
   using C = PPCfg<D>;
@@ -71,18 +71,13 @@ void fwd_pp_kernel(const FwdArgs a) {
   if (a.cu_q != nullptr) {
     q_tok0 = a.cu_q[b];
     sq = a.cu_q[b + 1] - q_tok0;
-    const int k_tok0 = a.cu_k[b];
-    sk = a.cu_k[b + 1] - k_tok0;
     q_base = (int64_t)q_tok0 * a.q_rs;
     o_base = (int64_t)q_tok0 * a.o_rs;
-    k_base = (int64_t)k_tok0 * a.k_rs;
-    v_base = (int64_t)k_tok0 * a.v_rs;
   } else {
     q_base = (int64_t)b * a.q_bs;
     o_base = (int64_t)b * a.o_bs;
-    k_base = (int64_t)b * a.k_bs;
-    v_base = (int64_t)b * a.v_bs;
   }
+  fwd_kv_extent<PAGED>(a, b, sk, k_base, v_base);
   sq = uniform(sq);
   sk = uniform(sk);
   const int r = a.group;
@@ -107,7 +102,11 @@ void fwd_pp_kernel(const FwdArgs a) {
   const int kv_hi = a.wr >= 0 ? min(sk, pos_max + off + a.wr + 1) : sk;  // exclusive
   const int n_begin = uniform(kv_lo / BN);
   const int n_end = uniform(kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : n_begin);
-  const int T = n_end - n_begin;
+  int T = n_end - n_begin;
+  // a paged cache with a page id outside [0, num_pages) in this range: no
+  // tile is read and every row of the workgroup gets NaN
+  const bool poison = fwd_bad_pages<PAGED>(a, b, n_begin * BN, min(sk, n_end * BN), lane);
+  if (poison) T = 0;
   // per-group "tile fully visible" bounds (group rows [g0, g1))
   const int g0 = min(row0 + grp * 128, rows - 1);
   const int g1 = min(row0 + grp * 128 + 128, rows) - 1;
@@ -163,28 +162,19 @@ void fwd_pp_kernel(const FwdArgs a) {
   const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
 
   // One buffer descriptor per tensor per tile, ending at the last row before
-  // seqlen_k (rows past it read as zero); its base is the tile's first row.
-  auto k_rsrc = [&](int n0) {
+  // seqlen_k (rows past it read as zero); its base is the tile's first row,
+  // ko / vo elements from the sequence's K / V base (contiguous, or in the
+  // page that holds it). This wave's loads of the tile at key n0 into LDS
+  // buffer buf: K parts i = 0..NI-1, then V parts.
+  auto issue_tile = [&](int n0, int buf, int64_t ko, int64_t vo) {
     const int nrows = min(sk - n0, BN);  // >= 1
-    return make_rsrc(kp + (int64_t)n0 * a.k_rs, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
-  };
-  auto v_rsrc = [&](int n0) {
-    const int nrows = min(sk - n0, BN);
-    return make_rsrc(vp + (int64_t)n0 * a.v_rs, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
-  };
-  // this wave's loads of the tile at key n0 into LDS buffer buf: K parts
-  // i = 0..NI-1, then V parts
-  auto dma_k = [&](int n0, int buf, int i) {
-    dma16(k_rsrc(n0), kdo[i], lds_w + (uint32_t)(buf * BUF_B + i * 1024));
-  };
-  auto dma_v = [&](int n0, int buf, int i) {
-    dma16(v_rsrc(n0), vdo[i], lds_w + (uint32_t)(buf * BUF_B + TILE_B + i * 1024));
-  };
-  auto issue_tile = [&](int n0, int buf) {
+    const auto kr = make_rsrc(kp + ko, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
+    const auto vr = make_rsrc(vp + vo, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma_k(n0, buf, i);
+    for (int i = 0; i < NI; ++i) dma16(kr, kdo[i], lds_w + (uint32_t)(buf * BUF_B + i * 1024));
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma_v(n0, buf, i);
+    for (int i = 0; i < NI; ++i)
+      dma16(vr, vdo[i], lds_w + (uint32_t)(buf * BUF_B + TILE_B + i * 1024));
   };
 
   // ---- fragment read offsets. K: lane (c32, half) reads logical chunk
@@ -328,8 +318,11 @@ void fwd_pp_kernel(const FwdArgs a) {
   if (T > 0) {
     // prologue: tiles 0 and 1 (or a re-read of tile 0) in flight; wait for
     // tile 0 (this wave's part), then the barrier makes all parts visible
-    issue_tile(n_begin * BN, 0);
-    issue_tile(min(n_begin + 1, n_end - 1) * BN, 1);
+    int64_t ko, vo;
+    fwd_tile_rows<PAGED>(a, b, n_begin * BN, ko, vo);
+    issue_tile(n_begin * BN, 0, ko, vo);
+    fwd_tile_rows<PAGED>(a, b, min(n_begin + 1, n_end - 1) * BN, ko, vo);
+    issue_tile(min(n_begin + 1, n_end - 1) * BN, 1, ko, vo);
     vmcnt_wait<2 * NI>();
     lds_barrier();
     for (int k = 0; k < T; ++k) {
@@ -340,8 +333,10 @@ void fwd_pp_kernel(const FwdArgs a) {
       // load path.
       const int dn0 = min(n_begin + k + 2, n_end - 1) * BN;
       const int dbuf = (k + 2) & 3;
+      int64_t dko, dvo;
+      fwd_tile_rows<PAGED>(a, b, dn0, dko, dvo);
       // half-step 2k: A matrix work, B softmax
-      if (grp == 1) issue_tile(dn0, dbuf);
+      if (grp == 1) issue_tile(dn0, dbuf, dko, dvo);
       if (grp == 0) {
         __builtin_amdgcn_s_setprio(1);
         mfma_item(k);
@@ -352,7 +347,7 @@ void fwd_pp_kernel(const FwdArgs a) {
       lds_barrier();
       // half-step 2k+1: A softmax, B matrix work; then tile k+1 must have
       // landed (only tile k+2's loads may still be in flight)
-      if (grp == 0) issue_tile(dn0, dbuf);
+      if (grp == 0) issue_tile(dn0, dbuf, dko, dvo);
       if (grp == 0) {
         sm_item(k);
       } else {
@@ -378,7 +373,7 @@ void fwd_pp_kernel(const FwdArgs a) {
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store
   const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float inv = poison ? __builtin_nanf("") : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
   if (valid) {
     __bf16* op = static_cast<__bf16*>(a.out) + o_base + (int64_t)pos * a.o_rs +
                  (int64_t)hq * a.o_hs;
@@ -392,7 +387,8 @@ void fwd_pp_kernel(const FwdArgs a) {
                  o[db][4 * i + 3] * inv);
       }
     if (half == 0 && a.lse != nullptr) {
-      const float lse = l_tot > 0.0f ? m_run * a.scale + __logf(l_tot) : kNegInf;
+      const float lse = poison ? __builtin_nanf("")
+                               : (l_tot > 0.0f ? m_run * a.scale + __logf(l_tot) : kNegInf);
       const int64_t li = a.cu_q != nullptr
                              ? (int64_t)hq * a.total_q + q_tok0 + pos
                              : ((int64_t)b * a.hq + hq) * sq + pos;
@@ -407,7 +403,10 @@ hipError_t launch_fwd_pp(const FwdArgs& args, hipStream_t s) {
   a.num_m_blocks = (int)(((int64_t)a.max_rows + kFwdPPBlockM - 1) / kFwdPPBlockM);
   const int64_t grid = fwd_blocks_per_head(a, kFwdPPBlockM) * a.hkv;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_pp_kernel<D>, dim3((unsigned)grid), dim3(512), 0, s, a);
+  if (a.page_table != nullptr)
+    hipLaunchKernelGGL((fwd_pp_kernel<D, true>), dim3((unsigned)grid), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_pp_kernel<D, false>), dim3((unsigned)grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

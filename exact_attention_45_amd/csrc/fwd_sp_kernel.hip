@@ -73,7 +73,7 @@ struct SPCfg {
 // multiple of 256 bytes, so those reads hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int kswz16(int key) { return swz_key(key) | (((key >> 3) & 1) << 3); }
 
-template <int D, int QB>
+template <int D, int QB, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_sp_kernel(const FwdArgs a) {
   using C = SPCfg<D, QB>;
@@ -100,18 +100,13 @@ void fwd_sp_kernel(const FwdArgs a) {
   if (a.cu_q != nullptr) {
     q_tok0 = a.cu_q[b];
     sq = a.cu_q[b + 1] - q_tok0;
-    const int k_tok0 = a.cu_k[b];
-    sk = a.cu_k[b + 1] - k_tok0;
     q_base = (int64_t)q_tok0 * a.q_rs;
     o_base = (int64_t)q_tok0 * a.o_rs;
-    k_base = (int64_t)k_tok0 * a.k_rs;
-    v_base = (int64_t)k_tok0 * a.v_rs;
   } else {
     q_base = (int64_t)b * a.q_bs;
     o_base = (int64_t)b * a.o_bs;
-    k_base = (int64_t)b * a.k_bs;
-    v_base = (int64_t)b * a.v_bs;
   }
+  fwd_kv_extent<PAGED>(a, b, sk, k_base, v_base);
   sq = uniform(sq);
   sk = uniform(sk);
   const int r = a.group;
@@ -140,7 +135,11 @@ void fwd_sp_kernel(const FwdArgs a) {
   const int kv_hi = a.wr >= 0 ? min(sk, pos_max + off + a.wr + 1) : sk;  // exclusive
   const int n_begin = uniform(kv_lo / BN);
   const int n_end = uniform(kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : n_begin);
-  const int T = n_end - n_begin;
+  int T = n_end - n_begin;
+  // a paged cache with a page id outside [0, num_pages) in this range: no
+  // tile is read and every row of the workgroup gets NaN
+  const bool poison = fwd_bad_pages<PAGED>(a, b, n_begin * BN, min(sk, n_end * BN), lane);
+  if (poison) T = 0;
   const int full_hi = a.wr >= 0 ? pos_min + off + a.wr : INT_MAX / 2;
   const int full_lo = a.wl >= 0 ? pos_max + off - a.wl : INT_MIN / 2;
 
@@ -195,21 +194,23 @@ void fwd_sp_kernel(const FwdArgs a) {
     vdo[i] = (uint32_t)(row * a.v_rs * 2 + ((lane % CPR) ^ swz_key(row)) * 16);
   }
   const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
-  // one buffer descriptor per tensor per tile, ending at the last row before
-  // seqlen_k (rows past it read as zero)
-  auto issue_k = [&](int j, auto buf_c) {
+  // one buffer descriptor per tensor per tile, based at the tile's first row
+  // (ko / vo elements from the sequence's K / V base: contiguous, or in the
+  // page that holds it) and ending at the last row before seqlen_k (rows past
+  // it read as zero)
+  auto issue_k = [&](int j, auto buf_c, int64_t ko) {
     constexpr int buf = decltype(buf_c)::value;
     const int n0 = (n_begin + j) * BN;
     const int nrows = min(sk - n0, BN);  // >= 1
-    const auto rs = make_rsrc(kp + (int64_t)n0 * a.k_rs, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
+    const auto rs = make_rsrc(kp + ko, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
 #pragma unroll
     for (int i = 0; i < NI; ++i) dma16(rs, kdo[i], lds_w + (uint32_t)(buf * TILE_B + i * 1024));
   };
-  auto issue_v = [&](int j, auto buf_c) {
+  auto issue_v = [&](int j, auto buf_c, int64_t vo) {
     constexpr int buf = decltype(buf_c)::value;
     const int n0 = (n_begin + j) * BN;
     const int nrows = min(sk - n0, BN);
-    const auto rs = make_rsrc(vp + (int64_t)n0 * a.v_rs, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
+    const auto rs = make_rsrc(vp + vo, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       dma16(rs, vdo[i], lds_w + (uint32_t)((2 + buf) * TILE_B + i * 1024));
@@ -428,13 +429,21 @@ void fwd_sp_kernel(const FwdArgs a) {
   using I1 = std::integral_constant<int, 1>;
 
   // iteration k: cur holds S(k); nxt receives S(k+1). par = k & 1.
+  // row offsets of tile j (clamped to the last tile) from the sequence's K/V
+  auto rows_of = [&](int j, int64_t& ko, int64_t& vo) __attribute__((always_inline)) {
+    fwd_tile_rows<PAGED>(a, b, (n_begin + min(j, T - 1)) * BN, ko, vo);
+  };
+
   auto step = [&](int k, auto par_c, STile& cur, STile& nxt) {
     constexpr int par = decltype(par_c)::value;
     using PN = std::integral_constant<int, par ^ 1>;
     vmcnt_wait<0>();  // K(k+1), V(k) (this wave's parts)
     lds_barrier();    // everyone's parts landed; K(k), V(k-1) no longer read
-    if (k + 2 < T) issue_k(k + 2, par_c);  // into the buffer K(k) left
-    if (k + 1 < T) issue_v(k + 1, PN{});   // into the buffer V(k-1) left
+    int64_t k_nx, v_nx, unused;
+    rows_of(k + 2, k_nx, unused);
+    rows_of(k + 1, unused, v_nx);
+    if (k + 2 < T) issue_k(k + 2, par_c, k_nx);  // into the buffer K(k) left
+    if (k + 1 < T) issue_v(k + 1, PN{}, v_nx);   // into the buffer V(k-1) left
     sm_max(cur, k);
     if (k + 1 < T) {
       phase1(PN{}, cur, nxt);
@@ -447,9 +456,12 @@ void fwd_sp_kernel(const FwdArgs a) {
   if (T > 0) {
     // prologue: K(0), V(0), K(1) requested (K(0) re-read when T == 1); wait
     // for K(0), compute S(0)
-    issue_k(0, I0{});
-    issue_v(0, I0{});
-    issue_k(min(1, T - 1), I1{});
+    int64_t ko, vo;
+    rows_of(0, ko, vo);
+    issue_k(0, I0{}, ko);
+    issue_v(0, I0{}, vo);
+    rows_of(1, ko, vo);
+    issue_k(min(1, T - 1), I1{}, ko);
     vmcnt_wait<2 * NI>();
     lds_barrier();
     s_tile(I0{}, sA);
@@ -464,7 +476,7 @@ void fwd_sp_kernel(const FwdArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = pair_sum(l_run[qb]);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float inv = poison ? __builtin_nanf("") : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
     if (valid[qb]) {
       __bf16* op = static_cast<__bf16*>(a.out) + o_base + (int64_t)pos[qb] * a.o_rs +
                    (int64_t)hq[qb] * a.o_hs;
@@ -478,7 +490,8 @@ void fwd_sp_kernel(const FwdArgs a) {
                    o[db][qb][4 * i + 3] * inv);
         }
       if (half == 0 && a.lse != nullptr) {
-        const float lse = l_tot > 0.0f ? m_run[qb] * a.scale + __logf(l_tot) : kNegInf;
+        const float lse = poison ? __builtin_nanf("")
+                                 : (l_tot > 0.0f ? m_run[qb] * a.scale + __logf(l_tot) : kNegInf);
         const int64_t li = a.cu_q != nullptr
                                ? (int64_t)hq[qb] * a.total_q + q_tok0 + pos[qb]
                                : ((int64_t)b * a.hq + hq[qb]) * sq + pos[qb];
@@ -495,7 +508,10 @@ hipError_t launch_fwd_sp(const FwdArgs& args, hipStream_t s) {
   a.num_m_blocks = (int)(((int64_t)a.max_rows + BM - 1) / BM);
   const int64_t grid = fwd_blocks_per_head(a, BM) * a.hkv;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_sp_kernel<D, QB>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  if (a.page_table != nullptr)
+    hipLaunchKernelGGL((fwd_sp_kernel<D, QB, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_sp_kernel<D, QB, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -28,6 +28,12 @@ struct FwdArgs {
   float scale;             // softmax_scale
   float scale_log2;        // softmax_scale * log2(e)
   int32_t wl, wr;
+  // Paged K/V (page_table non-NULL): k/v point at the caches, k_bs/v_bs are
+  // the page strides, cu_k is NULL, sequence b has seqused_k[b] keys (or
+  // max_pages * page_size), page_size is a multiple of the 64-key tile.
+  const int32_t* page_table;
+  const int32_t* seqused_k;
+  int32_t page_size, num_pages, max_pages;
 };
 
 // Query blocks (of BM packed rows) a prefill launch covers per KV head.
@@ -81,6 +87,68 @@ __device__ __forceinline__ bool fwd_work_item(const FwdArgs& a, int& hk, int& b,
     }
   }
   return false;
+}
+
+// Keys of sequence b and the element offset of its K/V rows from a.k / a.v
+// for a prefill launch: packed (cu_k), paged (rows are located per tile, so
+// the base is 0) or dense. A paged sequence's key count is clamped to the
+// capacity of its page-table row, so no page lookup leaves that row.
+// PAGED is a compile-time copy of (a.page_table != nullptr): the dense
+// kernels carry no paging code.
+template <bool PAGED>
+__device__ __forceinline__ void fwd_kv_extent(const FwdArgs& a, int b, int& sk, int64_t& k_base,
+                                              int64_t& v_base) {
+  if constexpr (PAGED) {
+    const int cap = a.max_pages * a.page_size;
+    sk = a.seqused_k != nullptr ? min(max(a.seqused_k[b], 0), cap) : cap;
+    k_base = 0;
+    v_base = 0;
+  } else if (a.cu_k != nullptr) {
+    const int k_tok0 = a.cu_k[b];
+    sk = a.cu_k[b + 1] - k_tok0;
+    k_base = (int64_t)k_tok0 * a.k_rs;
+    v_base = (int64_t)k_tok0 * a.v_rs;
+  } else {
+    sk = a.seqlen_k;
+    k_base = (int64_t)b * a.k_bs;
+    v_base = (int64_t)b * a.v_bs;
+  }
+}
+
+// Row offsets (elements from the sequence's K/V base) of the key tile that
+// starts at key n0: contiguous rows, or for a paged cache the page that holds
+// key n0 (page_table row b, entry n0 / page_size; a tile never straddles a
+// page) plus the slot within it.
+template <bool PAGED>
+__device__ __forceinline__ void fwd_tile_rows(const FwdArgs& a, int b, int n0, int64_t& k_off,
+                                              int64_t& v_off) {
+  if constexpr (PAGED) {
+    const int pi = n0 / a.page_size;
+    const int pid = __builtin_amdgcn_readfirstlane(a.page_table[(int64_t)b * a.max_pages + pi]);
+    const int slot = n0 - pi * a.page_size;
+    k_off = (int64_t)pid * a.k_bs + (int64_t)slot * a.k_rs;
+    v_off = (int64_t)pid * a.v_bs + (int64_t)slot * a.v_rs;
+  } else {
+    k_off = (int64_t)n0 * a.k_rs;
+    v_off = (int64_t)n0 * a.v_rs;
+  }
+}
+
+// For a paged cache: true when any page id covering keys [k_lo, k_hi) of
+// sequence b lies outside [0, num_pages). Each lane checks every 64th page;
+// the answer is the same in every wave of the workgroup.
+template <bool PAGED>
+__device__ __forceinline__ bool fwd_bad_pages(const FwdArgs& a, int b, int k_lo, int k_hi,
+                                              int lane) {
+  if constexpr (!PAGED) return false;
+  if (k_hi <= k_lo) return false;
+  const int p_lo = k_lo / a.page_size, p_hi = (k_hi - 1) / a.page_size;
+  bool bad = false;
+  for (int pi = p_lo + lane; pi <= p_hi; pi += 64) {
+    const int pid = a.page_table[(int64_t)b * a.max_pages + pi];
+    bad = bad || (unsigned)pid >= (unsigned)a.num_pages;
+  }
+  return __builtin_amdgcn_ballot_w64(bad) != 0;
 }
 
 // Paged split-KV decode arguments.

@@ -93,11 +93,33 @@ typedef enum {
  *   must bound every sequence's length (together they size the launch
  *   grid); seqlen_q / seqlen_k are ignored.
  *
+ * Paged K/V (page_table non-NULL; interface page, the page_table branch of
+ * `_flash_attn_fwd`: a KV cache in pages, e.g. prefill of new tokens after a
+ * cached prefix): cu_seqlens_k must be NULL; queries are dense or packed by
+ * cu_seqlens_q as above.
+ *   k,v [num_pages, page_size, num_heads_kv, head_dim]: k_batch_stride /
+ *       v_batch_stride are the strides between pages, row and head strides
+ *       as above
+ *   page_table [batch, max_pages_per_seq] int32, row-contiguous: key t of
+ *       sequence b lives in page page_table[b * max_pages_per_seq +
+ *       t / page_size], slot t % page_size
+ *   seqused_k [batch] int32 keys of each sequence, or NULL for
+ *       max_pages_per_seq * page_size; each must be in
+ *       [0, max_pages_per_seq * page_size]
+ *   seqlen_k and max_seqlen_k are ignored; queries are aligned bottom-right
+ *   to each sequence's seqused_k keys.
+ * page_size must be a positive multiple of 64 (a 64-key tile never straddles
+ * pages; other sizes return MI_ATTN_EUNSUPPORTED) and num_pages,
+ * max_pages_per_seq positive. The kernel checks every page id a workgroup
+ * will read against [0, num_pages) before touching the cache; a workgroup
+ * that finds one outside writes NaN to its rows of out and lse instead.
+ * For dense K/V, page_table must be NULL and the four paging fields are
+ * ignored.
+ *
  * num_heads_q must be a multiple of num_heads_kv. Query heads sharing a KV
  * head are processed together (GQA packing), so one K/V tile load serves all
  * of them. softmax_scale must be finite; the Python binding passes
  * 1/sqrt(head_dim) when the caller gives none (interface page default).
- * page_table must be NULL: paged K/V is served by mi_attn_decode_splitkv.
  * --------------------------------------------------------------------- */
 typedef struct {
   const void *q, *k, *v;
@@ -114,9 +136,11 @@ typedef struct {
                                                  the rows of q and lse; it
                                                  also sizes the launch grid */
   int32_t max_seqlen_q, max_seqlen_k;         /* varlen: host upper bounds   */
-  const int32_t *page_table;                  /* must be NULL                */
+  const int32_t *page_table;                  /* device, paged K/V, or NULL  */
   float softmax_scale;
   int32_t causal, window_left, window_right;
+  const int32_t *seqused_k;                   /* device [batch], paged only  */
+  int32_t page_size, num_pages, max_pages_per_seq; /* paged only           */
 } mi_attn_fwd_params;
 
 int mi_attn_fwd(const mi_attn_fwd_params *p, void *stream);

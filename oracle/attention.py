@@ -250,6 +250,47 @@ def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1
     return out, lse, o_parts, lse_parts
 
 
+def paged_prefill(q, k_cache, v_cache, page_table, seqused_k, scale, causal=False,
+                  window_left=None, window_right=None, cu_seqlens_q=None):
+    """Queries against a paged K/V cache (interface page, the page_table branch
+    of `_flash_attn_fwd`: caches (num_pages, page_size, Hkv, D), a
+    (B, max_pages) page table, per-sequence key counts seqused_k).
+
+    q is dense (B, Sq, Hq, D), or packed (Tq, Hq, D) with cu_seqlens_q. The keys
+    of sequence b are its seqused_k[b] cached tokens (None: the capacity of its
+    page-table row, max_pages * page_size) gathered through the page table;
+    the definition then applies with the queries aligned bottom-right to those
+    keys. Returns O shaped like q and LSE (B, Hq, Sq) dense or (Hq, Tq) packed.
+    """
+    B = page_table.shape[0]
+    cap = page_table.shape[1] * k_cache.shape[1]
+    Hq, Hkv = q.shape[-2], k_cache.shape[2]
+    r = Hq // Hkv
+    packed = cu_seqlens_q is not None
+    out = np.zeros(q.shape[:-1] + (v_cache.shape[-1],))
+    lse = np.full((Hq, q.shape[0]) if packed else (B, Hq, q.shape[1]), NEG_INF)
+    for b in range(B):
+        sk = cap if seqused_k is None else int(seqused_k[b])
+        kb = paged_gather(k_cache, page_table[b], sk)
+        vb = paged_gather(v_cache, page_table[b], sk)
+        if packed:
+            q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+            qb = q[q0:q1]
+        else:
+            qb = q[b]
+        if qb.shape[0] == 0:
+            continue
+        vis = visible_mask(qb.shape[0], sk, causal, window_left, window_right)
+        for h in range(Hq):
+            g = h // r
+            o, l = attention_head(qb[:, h], kb[:, g], vb[:, g], scale, vis)
+            if packed:
+                out[q0:q1, h], lse[h, q0:q1] = o, l
+            else:
+                out[b, :, h], lse[b, h] = o, l
+    return out, lse
+
+
 # ------------------------------------------------------- accounting --------
 
 def visible_pairs(seqlen_q: int, seqlen_k: int, causal=False, window_left=None,

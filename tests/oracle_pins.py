@@ -18,6 +18,9 @@ What each pin rests on:
   split_combine  combining split partials equals the unsplit result,
                  including empty splits
   paged          paged gather equals the contiguous layout
+  paged_prefill  queries (dense and packed) against a paged cache equal the
+                 scalar loops run on contiguous copies built token by token,
+                 with ragged seqused_k, Sq < Sk, empty sequences and masks
   torch_sdpa     torch's float64 scaled_dot_product_attention on CPU, with
                  an explicit boolean mask built from the closed-form interval
 """
@@ -296,6 +299,68 @@ def pin_paged():
     return True, "ok"
 
 
+def pin_paged_prefill():
+    rng = _rng(21)
+    B, Hq, Hkv, D, ps, pps = 3, 4, 2, 3, 4, 3
+    num_pages = B * pps + 1
+    kc = rng.standard_normal((num_pages, ps, Hkv, D))
+    vc = rng.standard_normal((num_pages, ps, Hkv, D))
+    table = rng.permutation(num_pages)[:B * pps].reshape(B, pps)
+    used = np.array([10, 0, 12])
+    masks = [dict(causal=True), dict(window_left=2, window_right=1), dict()]
+
+    def contiguous(cache, b):
+        return np.stack([cache[table[b, t // ps], t % ps] for t in range(used[b])]) \
+            if used[b] else np.zeros((0, Hkv, D))
+
+    # dense queries: Sq = 5 new tokens after a cached prefix (Sq < Sk), one
+    # sequence with no keys
+    Sq = 5
+    q = rng.standard_normal((B, Sq, Hq, D))
+    for mk in masks:
+        o, l = A.paged_prefill(q, kc, vc, table, used, 0.6, **mk)
+        for b in range(B):
+            kb, vb = contiguous(kc, b), contiguous(vc, b)
+            if used[b] == 0:
+                if not (np.all(o[b] == 0) and np.all(l[b] == -np.inf)):
+                    return False, f"{mk} seq {b}: no keys must give O = 0, LSE = -inf"
+                continue
+            ob, lb = BR.attention_loops(q[b][None], kb[None], vb[None], 0.6, **mk)
+            ok1, d1 = _close(o[b], np.array(ob[0]))
+            ok2, d2 = _close(l[b], np.array(lb[0]))
+            if not (ok1 and ok2):
+                return False, f"dense {mk} seq {b}: O {d1} LSE {d2}"
+    # packed queries of lengths 2, 0, 6 (one longer than its keys: leading
+    # rows see nothing under causal)
+    lens = [2, 0, 6]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    qp = rng.standard_normal((int(cu[-1]), Hq, D))
+    used_p = np.array([7, 3, 4])
+    for mk in masks:
+        o, l = A.paged_prefill(qp, kc, vc, table, used_p, 0.6, cu_seqlens_q=cu, **mk)
+        for b in range(B):
+            q0, q1 = int(cu[b]), int(cu[b + 1])
+            if q1 == q0:
+                continue
+            kb = np.stack([kc[table[b, t // ps], t % ps] for t in range(used_p[b])])
+            vb = np.stack([vc[table[b, t // ps], t % ps] for t in range(used_p[b])])
+            ob, lb = BR.attention_loops(qp[q0:q1][None], kb[None], vb[None], 0.6, **mk)
+            ok1, d1 = _close(o[q0:q1], np.array(ob[0]))
+            ok2, d2 = _close(l[:, q0:q1], np.array(lb[0]))
+            if not (ok1 and ok2):
+                return False, f"packed {mk} seq {b}: O {d1} LSE {d2}"
+    # seqused_k = None means the whole page-table row
+    o, l = A.paged_prefill(q, kc, vc, table, None, 0.6, causal=True)
+    kb = np.stack([kc[table[0, t // ps], t % ps] for t in range(pps * ps)])
+    vb = np.stack([vc[table[0, t // ps], t % ps] for t in range(pps * ps)])
+    ob, lb = BR.attention_loops(q[0][None], kb[None], vb[None], 0.6, causal=True)
+    ok1, d1 = _close(o[0], np.array(ob[0]))
+    ok2, d2 = _close(l[0], np.array(lb[0]))
+    if not (ok1 and ok2):
+        return False, f"seqused None: O {d1} LSE {d2}"
+    return True, "ok"
+
+
 def pin_torch_sdpa():
     import torch
     import torch.nn.functional as F
@@ -359,6 +424,7 @@ ALL_PINS = {
     "gqa_as_mha": pin_gqa_as_mha,
     "split_combine": pin_split_combine,
     "paged": pin_paged,
+    "paged_prefill": pin_paged_prefill,
     "torch_sdpa": pin_torch_sdpa,
     "rows_match_full": pin_rows_match_full,
 }

@@ -107,7 +107,15 @@ def _call_fwd(lib, p):
     (dict(out=FAKE + 2), mi.MI_ATTN_EINVAL),
     (dict(q_row_stride=100), mi.MI_ATTN_EINVAL),
     (dict(k_batch_stride=-8), mi.MI_ATTN_EINVAL),
-    (dict(page_table=FAKE), mi.MI_ATTN_EUNSUPPORTED),
+    (dict(page_table=FAKE), mi.MI_ATTN_EINVAL),  # paging sizes missing
+    (dict(page_table=FAKE, page_size=32, num_pages=8, max_pages_per_seq=2),
+     mi.MI_ATTN_EUNSUPPORTED),  # page_size not a multiple of the 64-key tile
+    (dict(page_table=FAKE, page_size=64, num_pages=8, max_pages_per_seq=2,
+          cu_seqlens_k=FAKE), mi.MI_ATTN_EINVAL),  # interface page: no cu_seqlens_k with pages
+    (dict(page_table=FAKE, page_size=64, num_pages=8, max_pages_per_seq=2,
+          k_batch_stride=-8), mi.MI_ATTN_EINVAL),  # page stride
+    (dict(page_table=FAKE, page_size=64, num_pages=8, max_pages_per_seq=1 << 30),
+     mi.MI_ATTN_EINVAL),  # table capacity overflows int32
     (dict(cu_seqlens_q=FAKE), mi.MI_ATTN_EINVAL),
     (dict(softmax_scale=float("nan")), mi.MI_ATTN_EUNSUPPORTED),
     (dict(softmax_scale=-1.0), mi.MI_ATTN_EUNSUPPORTED),

@@ -41,6 +41,14 @@ MUTANTS = [
     ("paged_gather", "pages = [cache[int(page_table_row[p])] for p in range(n_pages)]",
      "pages = [cache[p] for p in range(n_pages)]", "page table ignored"),
     ("paged_decode", "g = h // r", "g = h % Hkv", "interleaved GQA grouping (paged)"),
+    ("paged_prefill", "g = h // r", "g = h % Hkv", "interleaved GQA grouping (paged prefill)"),
+    ("paged_prefill", "sk = cap if seqused_k is None else int(seqused_k[b])", "sk = cap",
+     "seqused_k ignored (paged prefill)"),
+    ("paged_prefill", "vis = visible_mask(qb.shape[0], sk, causal, window_left, window_right)",
+     "vis = visible_mask(qb.shape[0], qb.shape[0], causal, window_left, window_right)",
+     "queries aligned to their own length, not the cached keys"),
+    ("paged_prefill", "kb = paged_gather(k_cache, page_table[b], sk)",
+     "kb = paged_gather(k_cache, page_table[0], sk)", "every sequence reads row 0 of the table"),
 ]
 
 

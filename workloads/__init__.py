@@ -77,7 +77,7 @@ def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
 class Workload:
     """One synthetic attention problem.
 
-    kind is "dense", "varlen" or "paged". Tensors hold bf16 bit patterns
+    kind is "dense", "varlen", "paged" (decode) or "paged_prefill". Tensors hold bf16 bit patterns
     (uint16) or int32 index arrays. Mask parameters follow the front end's
     convention: causal flag plus window sizes, where None means unbounded.
     """
@@ -178,6 +178,48 @@ def paged_decode_case(seed: int, batch: int, hq: int, hkv: int, d: int, page_siz
                     seqlen_k=pages_per_seq * page_size, max_seqlen_q=1,
                     max_seqlen_k=int(seqused.max(initial=0)), page_table=page_table,
                     seqused_k=seqused, page_size=page_size, num_splits=num_splits, seed=seed)
+
+
+def paged_prefill_case(seed: int, batch: int, hq: int, hkv: int, d: int, page_size: int,
+                       pages_per_seq: int, seqused_k, seqlen_q: Optional[int] = None,
+                       seqlens_q=None, num_pages: Optional[int] = None, causal: bool = False,
+                       window_left: Optional[int] = None, window_right: Optional[int] = None,
+                       softmax_scale: Optional[float] = None,
+                       name: str = "paged_prefill") -> Workload:
+    """New query tokens against a paged K/V cache (e.g. prefill after a cached
+    prefix). Queries are dense (batch, seqlen_q, hq, d) or, with seqlens_q,
+    packed (sum, hq, d) with cu_seqlens_q. Draw order: Q, K cache, V cache,
+    then the page permutation (page_table[b, p] = perm[b * pages_per_seq + p]).
+    seqused_k (keys per sequence) may be None for full page-table rows.
+    """
+    rng = np.random.default_rng(seed)
+    if num_pages is None:
+        num_pages = batch * pages_per_seq
+    assert num_pages >= batch * pages_per_seq
+    if seqlens_q is not None:
+        seqlens_q = [int(x) for x in seqlens_q]
+        assert len(seqlens_q) == batch
+        cu_q = _cu(seqlens_q)
+        q = _normal_bf16(rng, (int(cu_q[-1]), hq, d))
+        max_q = max(seqlens_q, default=0)
+    else:
+        cu_q = None
+        q = _normal_bf16(rng, (batch, seqlen_q, hq, d))
+        max_q = seqlen_q
+    k = _normal_bf16(rng, (num_pages, page_size, hkv, d))
+    v = _normal_bf16(rng, (num_pages, page_size, hkv, d))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    page_table = np.ascontiguousarray(perm[:batch * pages_per_seq].reshape(batch, pages_per_seq))
+    seqused = None if seqused_k is None else np.asarray(seqused_k, dtype=np.int32).reshape(batch)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    cap = pages_per_seq * page_size
+    return Workload(name=name, kind="paged_prefill", q=q, k=k, v=v, num_heads_q=hq,
+                    num_heads_kv=hkv, head_dim=d, softmax_scale=scale, causal=causal,
+                    window_left=window_left, window_right=window_right, batch=batch,
+                    seqlen_q=0 if seqlens_q is not None else seqlen_q, seqlen_k=cap,
+                    cu_seqlens_q=cu_q, max_seqlen_q=max_q,
+                    max_seqlen_k=cap if seqused is None else int(seqused.max(initial=0)),
+                    page_table=page_table, seqused_k=seqused, page_size=page_size, seed=seed)
 
 
 STANDARD_CONFIGS = {
