@@ -26,7 +26,7 @@ __all__ = [
     "mi_attn_combine", "mi_attn_decode_workspace_bytes", "mi_attn_decode_num_splits",
     "mi_attn_last_error", "mi_attn_version", "FwdParams", "DecodeParams",
     "MI_ATTN_OK", "MI_ATTN_EINVAL", "MI_ATTN_EUNSUPPORTED", "MI_ATTN_EBOUNDS",
-    "MI_ATTN_EWORKSPACE", "MI_ATTN_EHIP",
+    "MI_ATTN_EWORKSPACE", "MI_ATTN_EHIP", "MI_ATTN_KV_BF16", "MI_ATTN_KV_FP8_E4M3",
 ]
 
 MI_ATTN_OK = 0
@@ -35,6 +35,8 @@ MI_ATTN_EUNSUPPORTED = -2
 MI_ATTN_EBOUNDS = -3
 MI_ATTN_EWORKSPACE = -4
 MI_ATTN_EHIP = -5
+MI_ATTN_KV_BF16 = 0
+MI_ATTN_KV_FP8_E4M3 = 1
 _STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EBOUNDS", -4: "EWORKSPACE",
            -5: "EHIP"}
 
@@ -90,6 +92,7 @@ class DecodeParams(ctypes.Structure):
         ("causal", _i32), ("window_left", _i32), ("window_right", _i32),
         ("num_splits", _i32),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("kv_dtype", _i32), ("k_descale", _vp), ("v_descale", _vp),
     ]
 
 
@@ -317,7 +320,24 @@ def _decode_params(q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax
     p.num_splits = int(num_splits)
     if workspace is not None:
         p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    p.kv_dtype = MI_ATTN_KV_FP8_E4M3 if _is_fp8(k_cache) else MI_ATTN_KV_BF16
     return p
+
+
+def _is_fp8(t) -> bool:
+    import torch
+    return t.dtype in (torch.float8_e4m3fn, torch.uint8)
+
+
+def _req_kv(name, t, device, fp8: bool):
+    """bf16 cache, or fp8 e4m3 (torch.float8_e4m3fn, or its raw bytes as uint8)."""
+    if not fp8:
+        return _req_bf16(name, t, device)
+    if not _is_fp8(t):
+        raise MiAttnError(MI_ATTN_EINVAL, f"{name} must be float8_e4m3fn or uint8 like k_cache "
+                                          f"(got {t.dtype})")
+    if not t.is_cuda or t.device != device:
+        raise MiAttnError(MI_ATTN_EINVAL, f"{name} must be a device tensor on {device}")
 
 
 def mi_attn_decode_workspace_bytes(q, k_cache, v_cache, page_table, num_splits: int = 0) -> int:
@@ -326,7 +346,10 @@ def mi_attn_decode_workspace_bytes(q, k_cache, v_cache, page_table, num_splits: 
                        None)
     n = lib.mi_attn_decode_workspace_bytes(ctypes.byref(p))
     if n == 0:
-        raise MiAttnError(MI_ATTN_EINVAL, mi_attn_last_error())
+        # the size query only says "invalid"; the split-count query returns
+        # the status itself for the same validation
+        rc = lib.mi_attn_decode_num_splits(ctypes.byref(p))
+        raise MiAttnError(rc if rc < 0 else MI_ATTN_EINVAL, mi_attn_last_error())
     return n
 
 
@@ -363,18 +386,23 @@ def check_paged_bounds(page_table, seqused_k, num_pages: int, page_size: int):
 def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=None, lse=None,
                            softmax_scale: Optional[float] = None, num_splits: int = 0,
                            window_left: Optional[int] = None, workspace=None,
-                           return_lse: bool = True, check_bounds: bool = False):
+                           return_lse: bool = True, check_bounds: bool = False,
+                           k_descale=None, v_descale=None):
     """One query token per sequence against a paged cache, split along keys.
 
-    q (B, Hq, D); k/v cache (num_pages, page_size, Hkv, D) contiguous;
-    page_table int32 (B, max_pages); seqused_k int32 (B,) or None.
+    q (B, Hq, D); k/v cache (num_pages, page_size, Hkv, D) contiguous, bf16 or
+    fp8 e4m3 (float8_e4m3fn or uint8 bytes; then k_descale / v_descale are
+    float32 (B, Hkv) or None for 1); page_table int32 (B, max_pages);
+    seqused_k int32 (B,) or None.
     Returns out (B, Hq, D) bf16 and lse (B, Hq) float32.
     """
     import torch
     lib = load()
     dev = q.device
-    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
-        _req_bf16(n, t, dev)
+    _req_bf16("q", q, dev)
+    fp8 = _is_fp8(k_cache)
+    _req_kv("k_cache", k_cache, dev, fp8)
+    _req_kv("v_cache", v_cache, dev, fp8)
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise MiAttnError(MI_ATTN_EINVAL, "q must be (B, Hq, D) and caches (pages, page_size, Hkv, D)")
     if not k_cache.is_contiguous() or not v_cache.is_contiguous():
@@ -396,6 +424,15 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     p = _decode_params(q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
                        num_splits, window_left, workspace)
+    for n, t in (("k_descale", k_descale), ("v_descale", v_descale)):
+        if t is None:
+            continue
+        if not fp8:
+            raise MiAttnError(MI_ATTN_EINVAL, f"{n} applies to an fp8 cache only")
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, k_cache.shape[2]) \
+                or t.device != dev:
+            raise MiAttnError(MI_ATTN_EINVAL, f"{n} must be contiguous float32 {(B, k_cache.shape[2])}")
+    p.k_descale, p.v_descale = _ptr(k_descale), _ptr(v_descale)
     _check(lib.mi_attn_decode_splitkv(ctypes.byref(p), _stream_ptr(dev)))
     return out, lse
 

@@ -34,27 +34,50 @@
 //     bound ends at the last key before seqused_k: rows past it read as zero.
 //   * A page id outside [0, num_pages), or a seqused_k outside [0, capacity],
 //     is never dereferenced and turns the split's partial into NaN.
+//   * fp8 cache (FP8 = true; sm_120 PR page, fp8 KV-cache decode: OCP e4m3
+//     K/V with a per-(batch, KV head) k_descale / v_descale and bf16 compute):
+//     a row is head_dim bytes, so a 16-byte load covers twice the keys and a
+//     slice half the bytes. Staging converts each byte to bf16 (exact: e4m3
+//     values are bf16 values) into the same LDS layout, so the fragment reads,
+//     MFMAs and softmax are those of the bf16 path. k_descale multiplies the
+//     score scale (S = scale * ks * q.k8); v_descale multiplies the
+//     normalised partial (O = vs * sum p v8).
 #include <climits>
 #include <type_traits>
+#include <utility>
 
 #include "attn_common.hpp"
 #include "kernels.hpp"
 
 namespace mi_attn {
 
-template <int D>
+template <int D, bool FP8>
 struct StreamCfg {
-  static constexpr int NS = 3;                  // K/V register sets per wave
+  // K/V register sets per wave. Three for fp8 as well: with half the bytes
+  // per slice, 4 or 6 sets in flight measured slower (110 and 128 us against
+  // 96 us for the B16 Sk32768 fp8 workload).
+  static constexpr int NS = 3;
   static constexpr float RESCALE_LOG2 = 8.0f;   // lazy-rescale threshold
   static constexpr int SLICE = 32;              // keys per slice
-  static constexpr int ROW_B = D * 2;           // bytes per K/V row
-  static constexpr int SLICE_B = SLICE * ROW_B; // bytes per K (or V) slice
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int ROW_B = D * 2;           // bytes per bf16 K/V row (LDS)
+  static constexpr int SLICE_B = SLICE * ROW_B; // bytes per K (or V) slice in LDS
+  static constexpr int GROW_B = FP8 ? D : D * 2; // bytes per K/V row in the cache
+  static constexpr int CPR = GROW_B / 16;       // 16-byte chunks per cache row
   static constexpr int RPL = 64 / CPR;          // rows per load instruction
   static constexpr int NLD = SLICE / RPL;       // load instructions per tensor per slice
   static constexpr int SLOT_B = 4 * 2 * SLICE_B; // K and V slots of the four waves
   static constexpr int LDS_B = SLOT_B;
 };
+
+// Four OCP e4m3 bytes (little-endian in w) -> four bf16 values (exact): the
+// hardware conversion gives fp32, the bf16 rounding of which is exact.
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  const bf16x4 r = cvt4(lo[0], lo[1], hi[0], hi[1]);
+  return __builtin_bit_cast(uint2, r);
+}
 
 // LDS chunk position of logical 16-byte chunk c of V row `key`. The XOR
 // spreads the eight keys of a transposing read over distinct bank groups; it
@@ -64,11 +87,28 @@ __device__ __forceinline__ int vswz(int key, int c) {
   return D >= 128 ? (c ^ ((key & 7) << 1)) : (c ^ ((key & 3) << 1));
 }
 
-template <int D>
+// The slot loop of one wave over its n_w slices with NS = sizeof...(J)
+// register sets: request slices 0..NS-1, then per round, for each set J in
+// order, move slice i+J to LDS, refill set J with slice i+J+NS and compute
+// slice i+J; the last fewer-than-NS slices sit in sets 0, 1, ...
+template <class Issue, class Stage, class Consume, int... J>
+__device__ __forceinline__ void stream_slices(int n_w, Issue& issue, Stage& stage, Consume& consume,
+                                              std::integer_sequence<int, J...>) {
+  constexpr int NS = sizeof...(J);
+  (issue(J, std::integral_constant<int, J>{}), ...);
+  int i = 0;
+  for (; i + NS <= n_w; i += NS)
+    ((stage(std::integral_constant<int, J>{}), issue(i + NS + J, std::integral_constant<int, J>{}),
+      consume(i + J)),
+     ...);
+  ((i + J < n_w ? (stage(std::integral_constant<int, J>{}), consume(i + J), 0) : 0), ...);
+}
+
+template <int D, bool FP8>
 __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) {
-  using C = StreamCfg<D>;
+  using C = StreamCfg<D, FP8>;
   constexpr int NS = C::NS, ROW_B = C::ROW_B, SLICE_B = C::SLICE_B, CPR = C::CPR;
-  constexpr int RPL = C::RPL, NLD = C::NLD;
+  constexpr int RPL = C::RPL, NLD = C::NLD, GROW_B = C::GROW_B;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_B];
 
   const int tid = threadIdx.x;
@@ -122,13 +162,19 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   for (int i = 0; i < D / 32; ++i) o[i] = zero_f32x16();
   float m_run = kNegInf;
   float l_run = 0.0f;
-  const float c = a.scale_log2;
+  // fp8: the key descale joins the score scale, the value descale the output
+  float kds = 1.0f, vds = 1.0f;
+  if constexpr (FP8) {
+    if (a.k_descale != nullptr) kds = a.k_descale[(int64_t)b * a.hkv + hk];
+    if (a.v_descale != nullptr) vds = a.v_descale[(int64_t)b * a.hkv + hk];
+  }
+  const float c = a.scale_log2 * kds;
   const float rescale_raw = C::RESCALE_LOG2 / fmaxf(c, 1e-30f);
 
   // ---- slice addressing
-  const int64_t ts2 = (int64_t)a.hkv * ROW_B;  // bytes between consecutive tokens
-  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)hk * ROW_B;
-  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)hk * ROW_B;
+  const int64_t ts2 = (int64_t)a.hkv * GROW_B;  // bytes between consecutive tokens
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)hk * GROW_B;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)hk * GROW_B;
   const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
   // loads: instruction u covers slice rows RPL*u .. +RPL-1, lane j row
   // RPL*u + j / CPR at chunk j % CPR
@@ -171,7 +217,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
     bad |= !ok;
     page = ok ? page : 0;
     const int64_t row0 = (int64_t)page * a.page_size + key0 % a.page_size;
-    const uint32_t nrec = nvalid > 0 && ok ? (uint32_t)((nvalid - 1) * ts2 + ROW_B) : 0u;
+    const uint32_t nrec = nvalid > 0 && ok ? (uint32_t)((nvalid - 1) * ts2 + GROW_B) : 0u;
     const auto kr = make_rsrc(kbase + row0 * ts2, nrec);
     const auto vr = make_rsrc(vbase + row0 * ts2, nrec);
 #pragma unroll
@@ -193,10 +239,30 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   // are done first); the set is free for the next request afterwards
   auto stage = [&](auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
+    if constexpr (!FP8) {
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      *reinterpret_cast<uint4*>(kslot + k_st[u & 3] + (u >> 2) * 4 * RPL * ROW_B) = kreg[slot][u];
-      *reinterpret_cast<uint4*>(vslot + v_st[u & 1] + (u >> 1) * 2 * RPL * ROW_B) = vreg[slot][u];
+      for (int u = 0; u < NLD; ++u) {
+        *reinterpret_cast<uint4*>(kslot + k_st[u & 3] + (u >> 2) * 4 * RPL * ROW_B) = kreg[slot][u];
+        *reinterpret_cast<uint4*>(vslot + v_st[u & 1] + (u >> 1) * 2 * RPL * ROW_B) = vreg[slot][u];
+      }
+    } else {
+      // 16 fp8 values = dims 16*ld_c .. +15 of row RPL*u + ld_r: bf16
+      // chunks 2*ld_c and 2*ld_c + 1 of that row, each at its swizzled place
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        const int row = RPL * u + ld_r;
+        const uint4 kx = kreg[slot][u], vx = vreg[slot][u];
+        const uint2 k0 = fp8x4_to_bf16x4(kx.x), k1 = fp8x4_to_bf16x4(kx.y);
+        const uint2 k2 = fp8x4_to_bf16x4(kx.z), k3 = fp8x4_to_bf16x4(kx.w);
+        const uint2 v0 = fp8x4_to_bf16x4(vx.x), v1 = fp8x4_to_bf16x4(vx.y);
+        const uint2 v2 = fp8x4_to_bf16x4(vx.z), v3 = fp8x4_to_bf16x4(vx.w);
+        char* kr = kslot + row * ROW_B;
+        char* vr = vslot + row * ROW_B;
+        *reinterpret_cast<uint4*>(kr + (((2 * ld_c) ^ kswz(row)) * 16)) = make_uint4(k0.x, k0.y, k1.x, k1.y);
+        *reinterpret_cast<uint4*>(kr + (((2 * ld_c + 1) ^ kswz(row)) * 16)) = make_uint4(k2.x, k2.y, k3.x, k3.y);
+        *reinterpret_cast<uint4*>(vr + vswz<D>(row, 2 * ld_c) * 16) = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        *reinterpret_cast<uint4*>(vr + vswz<D>(row, 2 * ld_c + 1) * 16) = make_uint4(v2.x, v2.y, v3.x, v3.y);
+      }
     }
   };
 
@@ -268,38 +334,11 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
     }
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  static_assert(NS == 3, "the unrolled loop below names three register sets");
-  // three slices stay requested while one is computed; requests past the
-  // last slice load nothing (zero-length descriptor)
-  if (n_w > 0) {
-    issue(0, S0{});
-    issue(1, S1{});
-    issue(2, S2{});
-    int i = 0;
-    for (; i + 3 <= n_w; i += 3) {
-      stage(S0{});
-      issue(i + 3, S0{});
-      consume(i);
-      stage(S1{});
-      issue(i + 4, S1{});
-      consume(i + 1);
-      stage(S2{});
-      issue(i + 5, S2{});
-      consume(i + 2);
-    }
-    // one or two slices left (in sets 0 and 1)
-    if (i < n_w) {
-      stage(S0{});
-      consume(i);
-      if (i + 1 < n_w) {
-        stage(S1{});
-        consume(i + 1);
-      }
-    }
-  }
+  // NS slices stay requested while one is computed; requests past the last
+  // slice load nothing (zero-length descriptor). The slot loop is unrolled NS
+  // times (a fold over the slots) so every register set is named at compile
+  // time.
+  if (n_w > 0) stream_slices(n_w, issue, stage, consume, std::make_integer_sequence<int, NS>{});
   // the last requests (past the end, all-zero rows) must land before the
   // workgroup's registers and LDS are released
   __builtin_amdgcn_s_waitcnt(0);
@@ -309,7 +348,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   // 32*db + 8*i + 4*half .. +3)
   const float l_tot = pair_sum(l_run);
   if (valid) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float inv = l_tot > 0.0f ? vds / l_tot : 0.0f;
     const float nan = __builtin_nanf("");
     const int64_t prow = (int64_t)b * a.hq + hq;
     float* op = a.o_part + (prow * a.num_splits + split) * D;
@@ -324,21 +363,32 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
                               o[db][4 * i + 3] * inv);
       }
     if (half == 0) {
-      const float lse = l_tot > 0.0f ? m_run * a.scale + __logf(l_tot) : kNegInf;
+      const float lse = l_tot > 0.0f ? m_run * (a.scale * kds) + __logf(l_tot) : kNegInf;
       a.lse_part[prow * a.num_splits + split] = bad ? nan : lse;
     }
   }
 }
 
-template <int D>
-hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t s) {
+template <int D, bool FP8>
+hipError_t launch_stream(const DecodeArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.batch * ((a.hkv + 3) / 4) * a.row_blocks * a.num_splits;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_stream_kernel<D>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_stream_kernel<D, FP8>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t s) {
+  return launch_stream<D, false>(a, s);
+}
+template <int D>
+hipError_t launch_decode_stream_fp8(const DecodeArgs& a, hipStream_t s) {
+  return launch_stream<D, true>(a, s);
 }
 
 template hipError_t launch_decode_stream<64>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream<128>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode_stream_fp8<64>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode_stream_fp8<128>(const DecodeArgs&, hipStream_t);
 
 }  // namespace mi_attn

@@ -168,6 +168,11 @@ struct DecodeArgs {
   float scale;
   float scale_log2;
   int32_t wl;                // < 0 unbounded
+  // fp8 (OCP e4m3) cache: one byte per element, real value = descale[b][kv
+  // head] * decoded byte; descales NULL = 1
+  int32_t kv_fp8;
+  const float* k_descale;    // [batch][hkv] or NULL
+  const float* v_descale;
 };
 
 struct CombineArgs {
@@ -195,6 +200,7 @@ template <int D> hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t s);
 template <int D, int QB> hipError_t launch_fwd_sp(const FwdArgs& a, hipStream_t s);
 template <int D> hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 template <int D> hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t s);
+template <int D> hipError_t launch_decode_stream_fp8(const DecodeArgs& a, hipStream_t s);
 template <int D> hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 }  // namespace mi_attn

@@ -178,7 +178,19 @@ int mi_attn_fwd(const mi_attn_fwd_params *p, void *stream);
  * workspace: caller-allocated device memory of at least
  * mi_attn_decode_workspace_bytes(p) bytes, 256-byte aligned. Two launches
  * on `stream`; concurrent calls must use distinct workspaces.
+ *
+ * fp8 cache (kv_dtype == MI_ATTN_KV_FP8_E4M3; sm_120 PR page, fp8 KV-cache
+ * decode): k_cache and v_cache hold one OCP e4m3 byte per element, same
+ * [num_pages, page_size, num_heads_kv, head_dim] layout; the cached value is
+ * k_descale[b * num_heads_kv + g] * e4m3(byte) (likewise V), with
+ * k_descale / v_descale device float32 [batch, num_heads_kv], or NULL for 1.
+ * The query stays bf16 and the arithmetic is the bf16 path's (each byte is
+ * widened to bf16 exactly). Supported for head_dim 64/128 with page_size a
+ * multiple of 32; other combinations return MI_ATTN_EUNSUPPORTED. With
+ * kv_dtype == MI_ATTN_KV_BF16 the descale pointers are ignored.
  * --------------------------------------------------------------------- */
+enum { MI_ATTN_KV_BF16 = 0, MI_ATTN_KV_FP8_E4M3 = 1 };
+
 typedef struct {
   const void *q;
   const void *k_cache, *v_cache;
@@ -195,6 +207,8 @@ typedef struct {
   int32_t num_splits;
   void *workspace;
   size_t workspace_bytes;
+  int32_t kv_dtype;                     /* MI_ATTN_KV_BF16 or MI_ATTN_KV_FP8_E4M3 */
+  const float *k_descale, *v_descale;   /* fp8 only: [batch, num_heads_kv] or NULL */
 } mi_attn_decode_params;
 
 /* The split count mi_attn_decode_splitkv will use for *p (resolves

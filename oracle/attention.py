@@ -220,14 +220,37 @@ def paged_gather(cache: np.ndarray, page_table_row: np.ndarray, seqlen: int) -> 
     return np.concatenate(pages, axis=0)[:seqlen]
 
 
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Values of OCP 8-bit floating point E4M3 codes (the fp8 e4m3 format the
+    sm_120 PR page's fp8 KV-cache decode stores), as float64.
+
+    Bit 7 is the sign, bits 6..3 the exponent field e (bias 7), bits 2..0 the
+    mantissa m: e > 0 gives (1 + m/8) * 2**(e - 7), e = 0 the subnormal
+    (m/8) * 2**-6; the two codes with e = 15 and m = 7 are NaN, and there are
+    no infinities (largest finite magnitude 448).
+    """
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
 def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1,
-                 causal=False, window_left=None, window_right=None, heads=None):
+                 causal=False, window_left=None, window_right=None, heads=None,
+                 k_descale=None, v_descale=None):
     """One query per sequence over a paged cache.
 
     q (B, Hq, D) float64. Returns O (B, Hq, Dv), LSE (B, Hq), and the split
     partials (S, B, Hq, Dv), (S, B, Hq) of the contiguous-range partition used
     by split_bounds, combined with `combine` to form O and LSE. `heads` limits
     the work to a subset of query heads (others are left at zero / -inf).
+    k_descale / v_descale (B, Hkv), for a quantized cache (sm_120 PR page, fp8
+    KV-cache decode with per-(batch, kv_head) descales): sequence b's keys of
+    KV head g are k_descale[b, g] times the cached values (likewise V); the
+    caches are then the decoded values (e4m3_decode of the stored codes).
     """
     B, Hq, _ = q.shape
     Hkv = k_cache.shape[2]
@@ -239,6 +262,10 @@ def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1
         sk = int(seqused_k[b])
         kb = paged_gather(k_cache, page_table[b], sk)
         vb = paged_gather(v_cache, page_table[b], sk)
+        if k_descale is not None:
+            kb = kb * np.asarray(k_descale, dtype=np.float64)[b][None, :, None]
+        if v_descale is not None:
+            vb = vb * np.asarray(v_descale, dtype=np.float64)[b][None, :, None]
         vis = visible_mask(1, sk, causal, window_left, window_right)
         bounds = split_bounds(sk, num_splits)
         for h in heads:

@@ -18,6 +18,10 @@ What each pin rests on:
   split_combine  combining split partials equals the unsplit result,
                  including empty splits
   paged          paged gather equals the contiguous layout
+  e4m3           all 256 fp8 codes decode as torch's float8_e4m3fn does, and
+                 closed-form values (1, 448, 2**-6, 2**-9, -0, NaN codes)
+  descale        per-(batch, KV head) descales equal decoding a cache whose
+                 pages were scaled beforehand, page by page
   paged_prefill  queries (dense and packed) against a paged cache equal the
                  scalar loops run on contiguous copies built token by token,
                  with ragged seqused_k, Sq < Sk, empty sequences and masks
@@ -361,6 +365,50 @@ def pin_paged_prefill():
     return True, "ok"
 
 
+def pin_e4m3():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    mine = A.e4m3_decode(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    if not same.all():
+        bad = np.flatnonzero(~same)[:4]
+        return False, f"codes {bad.tolist()}: {mine[bad].tolist()} vs torch {ref[bad].tolist()}"
+    closed = {0x38: 1.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0xB8: -1.0, 0x3C: 1.5}
+    for c, v in closed.items():
+        if A.e4m3_decode(np.array([c]))[0] != v:
+            return False, f"code {c:#x} != {v}"
+    if not (np.isnan(mine[0x7F]) and np.isnan(mine[0xFF]) and np.signbit(mine[0x80])):
+        return False, "NaN codes / negative zero"
+    return True, "ok"
+
+
+def pin_descale():
+    rng = _rng(23)
+    B, Hq, Hkv, D, ps, pps = 2, 4, 2, 3, 4, 2
+    num_pages = B * pps
+    q = rng.standard_normal((B, Hq, D))
+    kc = rng.standard_normal((num_pages, ps, Hkv, D))
+    vc = rng.standard_normal((num_pages, ps, Hkv, D))
+    table = rng.permutation(num_pages).reshape(B, pps)
+    used = np.array([7, 8])
+    ks = rng.uniform(0.5, 2.0, (B, Hkv))
+    vs = rng.uniform(0.5, 2.0, (B, Hkv))
+    o, l, _, _ = A.paged_decode(q, kc, vc, table, used, 0.4, num_splits=2,
+                                k_descale=ks, v_descale=vs)
+    # every page belongs to one sequence: scale that page's heads by its owner's descales
+    kc2, vc2 = kc.copy(), vc.copy()
+    for b in range(B):
+        for p_ in table[b]:
+            for g in range(Hkv):
+                kc2[p_, :, g] *= ks[b, g]
+                vc2[p_, :, g] *= vs[b, g]
+    o2, l2, _, _ = A.paged_decode(q, kc2, vc2, table, used, 0.4, num_splits=1)
+    ok1, d1 = _close(o, o2)
+    ok2, d2 = _close(l, l2)
+    return (ok1 and ok2), f"O {d1} LSE {d2}"
+
+
 def pin_torch_sdpa():
     import torch
     import torch.nn.functional as F
@@ -425,6 +473,8 @@ ALL_PINS = {
     "split_combine": pin_split_combine,
     "paged": pin_paged,
     "paged_prefill": pin_paged_prefill,
+    "e4m3": pin_e4m3,
+    "descale": pin_descale,
     "torch_sdpa": pin_torch_sdpa,
     "rows_match_full": pin_rows_match_full,
 }

@@ -42,6 +42,12 @@ MUTANTS = [
      "pages = [cache[p] for p in range(n_pages)]", "page table ignored"),
     ("paged_decode", "g = h // r", "g = h % Hkv", "interleaved GQA grouping (paged)"),
     ("paged_prefill", "g = h // r", "g = h % Hkv", "interleaved GQA grouping (paged prefill)"),
+    ("e4m3_decode", "np.exp2(e - 7.0)", "np.exp2(e - 8.0)", "e4m3 exponent bias 8 (the FNUZ bias)"),
+    ("e4m3_decode", "(m / 8.0) * 2.0 ** -6", "(m / 8.0) * 2.0 ** -7", "e4m3 subnormal scale"),
+    ("paged_decode", "kb = kb * np.asarray(k_descale, dtype=np.float64)[b][None, :, None]",
+     "kb = kb * np.asarray(v_descale, dtype=np.float64)[b][None, :, None]", "K scaled by the V descale"),
+    ("paged_decode", "vb = vb * np.asarray(v_descale, dtype=np.float64)[b][None, :, None]",
+     "vb = vb * np.asarray(v_descale, dtype=np.float64)[0][None, :, None]", "V descale of sequence 0 for all"),
     ("paged_prefill", "sk = cap if seqused_k is None else int(seqused_k[b])", "sk = cap",
      "seqused_k ignored (paged prefill)"),
     ("paged_prefill", "vis = visible_mask(qb.shape[0], sk, causal, window_left, window_right)",

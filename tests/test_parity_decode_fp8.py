@@ -1,0 +1,117 @@
+"""GPU parity of the fp8 (OCP e4m3) KV-cache decode with per-(batch, KV head)
+descales (mi_attn_decode_splitkv through the C ABI) against the float64
+oracle run on the decoded cache values."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as OA
+import workloads as W
+from tests.gpu_util import check, dev_bf16, dev_i32, f64, host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def dev_u8(codes: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).cuda()
+
+
+def dev_f32(x):
+    return None if x is None else torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def run_fp8(mi, w, num_splits=None, window_left=None, as_float8=False):
+    kc, vc = dev_u8(w.k), dev_u8(w.v)
+    if as_float8:
+        kc, vc = kc.view(torch.float8_e4m3fn), vc.view(torch.float8_e4m3fn)
+    out, lse = mi.mi_attn_decode_splitkv(
+        dev_bf16(w.q), kc, vc, dev_i32(w.page_table), seqused_k=dev_i32(w.seqused_k),
+        softmax_scale=w.softmax_scale,
+        num_splits=w.num_splits if num_splits is None else num_splits,
+        window_left=window_left, k_descale=dev_f32(w.k_descale), v_descale=dev_f32(w.v_descale),
+        check_bounds=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_fp8(w, window_left=None, heads=None):
+    o, l, _, _ = OA.paged_decode(f64(w.q), OA.e4m3_decode(w.k), OA.e4m3_decode(w.v), w.page_table,
+                                 w.seqused_k, w.softmax_scale, num_splits=1,
+                                 window_left=window_left, heads=heads,
+                                 k_descale=w.k_descale, v_descale=w.v_descale)
+    return o, l
+
+
+CASES = [
+    # (name, B, Hq, Hkv, D, page_size, pages_per_seq, extra_pages, seqused, splits, wl, descale)
+    ("gqa8_page256_ragged", 3, 16, 2, 128, 256, 5, 3, [1, 700, 1280], 4, None, True),
+    ("gqa4_page64_d64", 2, 16, 4, 64, 64, 10, 2, [600, 65], 6, None, True),
+    ("mha_page32_no_descale", 2, 4, 4, 128, 32, 12, 0, [384, 200], 5, None, False),
+    ("gqa32_heuristic_splits", 2, 32, 1, 128, 128, 8, 1, [1024, 333], 0, None, True),
+    ("window_left", 2, 8, 2, 128, 256, 4, 0, [900, 300], 3, 150, True),
+    ("empty_and_tiny", 4, 8, 2, 64, 64, 3, 0, [0, 1, 64, 65], 8, None, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fp8_decode_elementwise(gpu_lib, case):
+    name, B, Hq, Hkv, D, ps, pps, extra, used, splits, wl, ds = case
+    print(f"[case] fp8 decode {name}", flush=True)
+    w = W.paged_decode_fp8_case(zlib.crc32(name.encode()) % 10000, B, Hq, Hkv, D, ps, pps,
+                                num_pages=B * pps + extra, seqused_k=used, num_splits=splits,
+                                descale=ds)
+    out, lse = run_fp8(gpu_lib, w, window_left=wl)
+    o_ref, l_ref = oracle_fp8(w, window_left=wl)
+    print(name, check(host_f64(out), o_ref, host_f64(lse), l_ref, what=name))
+
+
+def test_fp8_every_code_decodes_exactly(gpu_lib):
+    """One key per sequence: O is that key's V row times its descale, so every
+    finite e4m3 code placed in V must come back exactly (vs = 1, the value is
+    a bf16 value); the float8_e4m3fn tensor dtype is accepted as well."""
+    B, Hq, Hkv, D, ps = 2, 4, 4, 128, 64
+    w = W.paged_decode_fp8_case(77, B, Hq, Hkv, D, ps, 1, seqused_k=[1, 1], num_splits=1,
+                                descale=False)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    codes = np.resize(finite, (B, Hkv, D))  # cycles through all 254 finite codes
+    for b in range(B):
+        w.v[w.page_table[b, 0], 0] = codes[b]
+    out, lse = run_fp8(gpu_lib, w, as_float8=True)
+    got = host_f64(out).reshape(B, Hkv, Hq // Hkv, D)
+    want = OA.e4m3_decode(codes)[:, :, None, :]
+    assert np.array_equal(got, np.broadcast_to(want, got.shape))
+    o_ref, l_ref = oracle_fp8(w)
+    check(host_f64(out), o_ref, host_f64(lse), l_ref, what="one key")
+
+
+def test_fp8_full_size_decode_sampled(gpu_lib):
+    """The paged decode workload's shape with an fp8 cache (B16, GQA 32/4,
+    D128, Sk 32768, 256-token pages, 16 splits); the oracle checks four
+    sequences' heads 0, 13, 31."""
+    w = W.paged_decode_fp8_case(1005, 16, 32, 4, 128, 256, 128, num_splits=16,
+                                name="paged_fp8_b16_sk32768")
+    out, lse = run_fp8(gpu_lib, w)
+    o_all, l_all = host_f64(out), host_f64(lse)
+    heads = [0, 13, 31]
+    for b in (0, 5, 10, 15):
+        # only sequence b's pages, behind an identity table (the oracle decodes
+        # what it is given to float64)
+        pages = w.page_table[b]
+        wb = W.Workload(name="b", kind="paged", q=w.q[b:b + 1], k=w.k[pages], v=w.v[pages],
+                        num_heads_q=32, num_heads_kv=4, head_dim=128,
+                        softmax_scale=w.softmax_scale,
+                        page_table=np.arange(len(pages), dtype=np.int32)[None],
+                        seqused_k=w.seqused_k[b:b + 1],
+                        k_descale=w.k_descale[b:b + 1], v_descale=w.v_descale[b:b + 1])
+        o_ref, l_ref = oracle_fp8(wb, heads=heads)
+        for h in heads:
+            check(o_all[b, h], o_ref[0, h], l_all[b, h], l_ref[0, h], what=f"seq {b} head {h}")
+
+
+def test_fp8_unsupported_shapes_rejected(gpu_lib):
+    w = W.paged_decode_fp8_case(9, 1, 4, 2, 128, 16, 4)  # page_size 16: not a multiple of 32
+    with pytest.raises(gpu_lib.MiAttnError) as e:
+        run_fp8(gpu_lib, w)
+    assert e.value.code == gpu_lib.MI_ATTN_EUNSUPPORTED

@@ -105,6 +105,9 @@ class Workload:
     page_size: int = 0
     num_splits: int = 0
     seed: int = 0
+    kv_dtype: str = "bf16"                  # "bf16", or "fp8_e4m3": k/v hold uint8 codes
+    k_descale: Optional[np.ndarray] = None  # fp8: float32 (B, Hkv), or None for 1
+    v_descale: Optional[np.ndarray] = None
 
 
 def dense_case(seed: int, batch: int, seqlen_q: int, seqlen_k: int, hq: int, hkv: int,
@@ -178,6 +181,64 @@ def paged_decode_case(seed: int, batch: int, hq: int, hkv: int, d: int, page_siz
                     seqlen_k=pages_per_seq * page_size, max_seqlen_q=1,
                     max_seqlen_k=int(seqused.max(initial=0)), page_table=page_table,
                     seqused_k=seqused, page_size=page_size, num_splits=num_splits, seed=seed)
+
+
+def _e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float32 values -> OCP e4m3 codes (uint8), round to nearest even, via
+    torch's float8_e4m3fn cast. Callers keep |x| well below 448."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def paged_decode_fp8_case(seed: int, batch: int, hq: int, hkv: int, d: int, page_size: int,
+                          pages_per_seq: int, num_pages: Optional[int] = None, seqused_k=None,
+                          num_splits: int = 0, descale: bool = True,
+                          softmax_scale: Optional[float] = None,
+                          name: str = "paged_fp8") -> Workload:
+    """paged_decode_case with an fp8 e4m3 K/V cache and per-(batch, KV head)
+    descales. Draw order: Q (bf16), K and V values (float32 N(0,1)), the page
+    permutation, then the K and V descale factors f ~ U[0.5, 2]. Descale =
+    f / 16; a page owned by sequence b stores codes of value / descale[b, g]
+    (|value / descale| < 200, far from e4m3's 448); pages no sequence uses
+    are stored with descale 1/16. descale=False stores every page with 1 and
+    passes no descales (the kernel's default)."""
+    rng = np.random.default_rng(seed)
+    if num_pages is None:
+        num_pages = batch * pages_per_seq
+    assert num_pages >= batch * pages_per_seq
+    q = _normal_bf16(rng, (batch, hq, d))
+    kx = rng.standard_normal((num_pages, page_size, hkv, d), dtype=np.float32)
+    vx = rng.standard_normal((num_pages, page_size, hkv, d), dtype=np.float32)
+    perm = rng.permutation(num_pages).astype(np.int32)
+    page_table = np.ascontiguousarray(perm[:batch * pages_per_seq].reshape(batch, pages_per_seq))
+    if descale:
+        kd = (rng.uniform(0.5, 2.0, (batch, hkv)) / 16.0).astype(np.float32)
+        vd = (rng.uniform(0.5, 2.0, (batch, hkv)) / 16.0).astype(np.float32)
+        kpage = np.full((num_pages, hkv), 1.0 / 16.0, dtype=np.float32)
+        vpage = np.full((num_pages, hkv), 1.0 / 16.0, dtype=np.float32)
+        for b in range(batch):
+            kpage[page_table[b]] = kd[b]
+            vpage[page_table[b]] = vd[b]
+        kx /= kpage[:, None, :, None]
+        vx /= vpage[:, None, :, None]
+    else:
+        kd = vd = None
+    k = _e4m3_codes(kx)
+    del kx
+    v = _e4m3_codes(vx)
+    del vx
+    if seqused_k is None:
+        seqused = np.full(batch, pages_per_seq * page_size, dtype=np.int32)
+    else:
+        seqused = np.asarray(seqused_k, dtype=np.int32).reshape(batch)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    return Workload(name=name, kind="paged", q=q, k=k, v=v, num_heads_q=hq, num_heads_kv=hkv,
+                    head_dim=d, softmax_scale=scale, batch=batch, seqlen_q=1,
+                    seqlen_k=pages_per_seq * page_size, max_seqlen_q=1,
+                    max_seqlen_k=int(seqused.max(initial=0)), page_table=page_table,
+                    seqused_k=seqused, page_size=page_size, num_splits=num_splits, seed=seed,
+                    kv_dtype="fp8_e4m3", k_descale=kd, v_descale=vd)
 
 
 def paged_prefill_case(seed: int, batch: int, hq: int, hkv: int, d: int, page_size: int,
