@@ -76,6 +76,7 @@ class FwdParams(ctypes.Structure):
         ("causal", _i32), ("window_left", _i32), ("window_right", _i32),
         ("seqused_k", _vp),
         ("page_size", _i32), ("num_pages", _i32), ("max_pages_per_seq", _i32),
+        ("learnable_sink", _vp),
     ]
 
 
@@ -93,6 +94,7 @@ class DecodeParams(ctypes.Structure):
         ("num_splits", _i32),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("kv_dtype", _i32), ("k_descale", _vp), ("v_descale", _vp),
+        ("learnable_sink", _vp),
     ]
 
 
@@ -180,7 +182,7 @@ def mi_attn_fwd(q, k, v, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=Non
                 softmax_scale: Optional[float] = None, causal: bool = False,
                 window_left: Optional[int] = None, window_right: Optional[int] = None,
                 return_lse: bool = True, page_table=None, seqused_k=None,
-                check_bounds: bool = False) -> Tuple:
+                check_bounds: bool = False, learnable_sink=None) -> Tuple:
     """Exact attention forward (interface page, `_flash_attn_fwd` contract).
 
     Dense: q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D); lse (B, Hq, Sq).
@@ -191,6 +193,7 @@ def mi_attn_fwd(q, k, v, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=Non
     (B,) or None (every sequence max_pages * page_size keys); q dense or packed
     by cu_seqlens_q (cu_seqlens_k must be None). check_bounds validates the
     page ids and seqused_k on the host first (one device-to-host copy).
+    learnable_sink: bf16 (Hq,) per-head sink logits (see include/mi_attn.h).
     """
     import torch
     lib = load()
@@ -299,6 +302,7 @@ def mi_attn_fwd(q, k, v, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=Non
     p.total_q, p.max_seqlen_q, p.max_seqlen_k = total_q, max_q, max_k
     p.softmax_scale = scale
     p.causal, p.window_left, p.window_right = int(bool(causal)), _win(window_left), _win(window_right)
+    p.learnable_sink = _req_sink(learnable_sink, hq, dev)
     _check(lib.mi_attn_fwd(ctypes.byref(p), _stream_ptr(dev)))
     return out, lse
 
@@ -322,6 +326,16 @@ def _decode_params(q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax
         p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     p.kv_dtype = MI_ATTN_KV_FP8_E4M3 if _is_fp8(k_cache) else MI_ATTN_KV_BF16
     return p
+
+
+def _req_sink(sink, hq: int, device):
+    """learnable_sink: bf16 (num_heads_q,) device tensor, or None."""
+    if sink is None:
+        return None
+    _req_bf16("learnable_sink", sink, device)
+    if tuple(sink.shape) != (hq,) or not sink.is_contiguous():
+        raise MiAttnError(MI_ATTN_EINVAL, f"learnable_sink must be contiguous ({hq},)")
+    return sink.data_ptr()
 
 
 def _is_fp8(t) -> bool:
@@ -387,7 +401,7 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
                            softmax_scale: Optional[float] = None, num_splits: int = 0,
                            window_left: Optional[int] = None, workspace=None,
                            return_lse: bool = True, check_bounds: bool = False,
-                           k_descale=None, v_descale=None):
+                           k_descale=None, v_descale=None, learnable_sink=None):
     """One query token per sequence against a paged cache, split along keys.
 
     q (B, Hq, D); k/v cache (num_pages, page_size, Hkv, D) contiguous, bf16 or
@@ -433,6 +447,7 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
                 or t.device != dev:
             raise MiAttnError(MI_ATTN_EINVAL, f"{n} must be contiguous float32 {(B, k_cache.shape[2])}")
     p.k_descale, p.v_descale = _ptr(k_descale), _ptr(v_descale)
+    p.learnable_sink = _req_sink(learnable_sink, hq, dev)
     _check(lib.mi_attn_decode_splitkv(ctypes.byref(p), _stream_ptr(dev)))
     return out, lse
 

@@ -237,6 +237,7 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
   a.page_size = paged ? p->page_size : 0;
   a.num_pages = paged ? p->num_pages : 0;
   a.max_pages = paged ? p->max_pages_per_seq : 0;
+  a.sink = static_cast<const __bf16*>(p->learnable_sink);
   a.hq = p->num_heads_q;
   a.hkv = p->num_heads_kv;
   a.group = group;
@@ -321,6 +322,8 @@ int mi_attn_decode_splitkv(const mi_attn_decode_params* p, void* stream) {
   cb.lse = p->lse;
   cb.rows = (int)rows;
   cb.num_splits = splits;
+  cb.sink = static_cast<const __bf16*>(p->learnable_sink);
+  cb.hq = p->num_heads_q;
   // out rows are (batch, head): require the (b, h) -> row map to be affine
   if (p->o_batch_stride != (int64_t)p->num_heads_q * p->o_head_stride)
     return fail(MI_ATTN_EINVAL, "out must have o_batch_stride == num_heads_q * o_head_stride");

@@ -132,6 +132,23 @@ __device__ __forceinline__ bf16x4 ds_read_tr16(const __bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// Learnable sink (interface page, `learnable_sink`, one logit per query
+// head), read as one more term of the softmax denominator that carries no
+// value. Given a row's log-sum-exp over its keys, lse_keys (-inf when it has
+// none), returns the row's LSE with the sink, log(exp(lse_keys) +
+// exp(sink)), and sets *w = exp(lse_keys - that), the factor that rescales
+// the row's normalised output (0 when the row has no key).
+__device__ __forceinline__ float merge_sink(float lse_keys, float sink, float* w) {
+  if (sink == kNegInf) {  // no sink term
+    *w = 1.0f;
+    return lse_keys;
+  }
+  const float hi = vmax(lse_keys, sink);
+  const float lse = hi + __logf(__expf(lse_keys - hi) + __expf(sink - hi));
+  *w = lse_keys == kNegInf ? 0.0f : __expf(lse_keys - lse);
+  return lse;
+}
+
 // Workgroup barrier that waits only for this wave's LDS operations
 // (lgkmcnt = 0), not for outstanding global loads: register prefetches for
 // later tiles stay in flight across it. (__syncthreads also waits vmcnt = 0.)

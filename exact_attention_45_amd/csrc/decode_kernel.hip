@@ -419,7 +419,13 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombineArgs a) {
   // every split empty: zero output and lse -inf; a NaN partial (bad page
   // id) must reach the output
   float lse = tot > 0.0f ? mm + __logf(tot) : kNegInf;
-  acc = tot > 0.0f ? acc * (1.0f / tot) : vecE{};
+  float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+  if (a.sink != nullptr) {
+    float w;
+    lse = merge_sink(lse, (float)a.sink[row % a.hq], &w);
+    inv *= w;
+  }
+  acc = acc * inv;
   if (has_nan) {
     lse = __builtin_nanf("");
     acc = lse;

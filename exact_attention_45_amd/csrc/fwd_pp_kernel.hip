@@ -373,7 +373,13 @@ void fwd_pp_kernel(const FwdArgs a) {
 
   // ---- epilogue: combine the two lane halves' row sums, normalise, store
   const float l_tot = pair_sum(l_run);
-  const float inv = poison ? __builtin_nanf("") : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
+  float inv = poison ? __builtin_nanf("") : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
+  float lse_row = l_tot > 0.0f ? m_run * a.scale + __logf(l_tot) : kNegInf;
+  if (a.sink != nullptr) {
+    float w;
+    lse_row = merge_sink(lse_row, (float)a.sink[hq], &w);
+    inv *= w;
+  }
   if (valid) {
     __bf16* op = static_cast<__bf16*>(a.out) + o_base + (int64_t)pos * a.o_rs +
                  (int64_t)hq * a.o_hs;
@@ -387,8 +393,7 @@ void fwd_pp_kernel(const FwdArgs a) {
                  o[db][4 * i + 3] * inv);
       }
     if (half == 0 && a.lse != nullptr) {
-      const float lse = poison ? __builtin_nanf("")
-                               : (l_tot > 0.0f ? m_run * a.scale + __logf(l_tot) : kNegInf);
+      const float lse = poison ? __builtin_nanf("") : lse_row;
       const int64_t li = a.cu_q != nullptr
                              ? (int64_t)hq * a.total_q + q_tok0 + pos
                              : ((int64_t)b * a.hq + hq) * sq + pos;

@@ -476,7 +476,13 @@ void fwd_sp_kernel(const FwdArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = pair_sum(l_run[qb]);
-    const float inv = poison ? __builtin_nanf("") : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
+    float inv = poison ? __builtin_nanf("") : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
+    float lse_row = l_tot > 0.0f ? m_run[qb] * a.scale + __logf(l_tot) : kNegInf;
+    if (a.sink != nullptr) {
+      float w;
+      lse_row = merge_sink(lse_row, (float)a.sink[hq[qb]], &w);
+      inv *= w;
+    }
     if (valid[qb]) {
       __bf16* op = static_cast<__bf16*>(a.out) + o_base + (int64_t)pos[qb] * a.o_rs +
                    (int64_t)hq[qb] * a.o_hs;
@@ -490,8 +496,7 @@ void fwd_sp_kernel(const FwdArgs a) {
                    o[db][qb][4 * i + 3] * inv);
         }
       if (half == 0 && a.lse != nullptr) {
-        const float lse = poison ? __builtin_nanf("")
-                                 : (l_tot > 0.0f ? m_run[qb] * a.scale + __logf(l_tot) : kNegInf);
+        const float lse = poison ? __builtin_nanf("") : lse_row;
         const int64_t li = a.cu_q != nullptr
                                ? (int64_t)hq[qb] * a.total_q + q_tok0 + pos[qb]
                                : ((int64_t)b * a.hq + hq[qb]) * sq + pos[qb];

@@ -34,6 +34,7 @@ struct FwdArgs {
   const int32_t* page_table;
   const int32_t* seqused_k;
   int32_t page_size, num_pages, max_pages;
+  const __bf16* sink;  // learnable-sink logits [hq], or NULL
 };
 
 // Query blocks (of BM packed rows) a prefill launch covers per KV head.
@@ -182,6 +183,8 @@ struct CombineArgs {
   int64_t out_row_stride;
   float* lse;
   int32_t rows, num_splits;
+  const __bf16* sink;  // learnable-sink logits [hq] (row = b * hq + h), or NULL
+  int32_t hq;
 };
 
 constexpr int kFwdBlockM = 128;   // packed query rows per workgroup (4 waves x 32), D = 256

@@ -120,6 +120,12 @@ typedef enum {
  * head are processed together (GQA packing), so one K/V tile load serves all
  * of them. softmax_scale must be finite; the Python binding passes
  * 1/sqrt(head_dim) when the caller gives none (interface page default).
+ *
+ * learnable_sink (interface page, `learnable_sink`: bf16, one per query head),
+ * or NULL: head h's logit s_h joins every row's softmax denominator without a
+ * value, so LSE = log(exp(s_h) + sum_j exp(scale * q.k_j)) and
+ * O = sum_j exp(scale * q.k_j - LSE) v_j; a row with no visible key gets
+ * O = 0 and LSE = s_h; s_h = -inf is no sink.
  * --------------------------------------------------------------------- */
 typedef struct {
   const void *q, *k, *v;
@@ -141,6 +147,7 @@ typedef struct {
   int32_t causal, window_left, window_right;
   const int32_t *seqused_k;                   /* device [batch], paged only  */
   int32_t page_size, num_pages, max_pages_per_seq; /* paged only           */
+  const void *learnable_sink;                 /* device bf16 [num_heads_q], or NULL */
 } mi_attn_fwd_params;
 
 int mi_attn_fwd(const mi_attn_fwd_params *p, void *stream);
@@ -209,6 +216,8 @@ typedef struct {
   size_t workspace_bytes;
   int32_t kv_dtype;                     /* MI_ATTN_KV_BF16 or MI_ATTN_KV_FP8_E4M3 */
   const float *k_descale, *v_descale;   /* fp8 only: [batch, num_heads_kv] or NULL */
+  const void *learnable_sink;           /* device bf16 [num_heads_q], or NULL; as for
+                                           mi_attn_fwd, merged in the combine step */
 } mi_attn_decode_params;
 
 /* The split count mi_attn_decode_splitkv will use for *p (resolves

@@ -72,10 +72,14 @@ def visible_mask(seqlen_q: int, seqlen_k: int, causal: bool = False,
 
 # ------------------------------------------------------------- one head ----
 
-def softmax_lse_rows(s: np.ndarray, vis: np.ndarray):
+def softmax_lse_rows(s: np.ndarray, vis: np.ndarray, sink: Optional[float] = None):
     """Row-wise log-sum-exp and probabilities of masked scores.
 
     s, vis: (n, Sk). Returns (P (n, Sk), LSE (n,)). Empty rows: P = 0, LSE = -inf.
+    sink: a learnable-sink logit (interface page, `learnable_sink`, one per
+    query head), read as one more term of every row's softmax denominator that
+    carries no value: LSE = log(exp(sink) + sum_j exp(s_j)), P_j = exp(s_j - LSE).
+    A row with no visible key then has P = 0 and LSE = sink.
     """
     s = np.where(vis, s, NEG_INF)
     nonempty = vis.any(axis=1)
@@ -84,23 +88,33 @@ def softmax_lse_rows(s: np.ndarray, vis: np.ndarray):
     lsum = e.sum(axis=1)
     lse = np.full(s.shape[0], NEG_INF)
     lse[nonempty] = m[nonempty] + np.log(lsum[nonempty])
+    if sink is not None and sink != NEG_INF:
+        hi = np.maximum(lse, sink)
+        lse = hi + np.log(np.exp(lse - hi) + np.exp(sink - hi))
     p = np.zeros_like(e)
     p[nonempty] = np.where(vis[nonempty], np.exp(s[nonempty] - lse[nonempty, None]), 0.0)
     return p, lse
 
 
 def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                   vis: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Single head. q (Sq, D), k (Sk, D), v (Sk, Dv), vis (Sq, Sk) -> O (Sq, Dv), LSE (Sq,)."""
+                   vis: np.ndarray, sink: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Single head. q (Sq, D), k (Sk, D), v (Sk, Dv), vis (Sq, Sk) -> O (Sq, Dv), LSE (Sq,).
+    sink: this head's learnable-sink logit or None (softmax_lse_rows)."""
     s = scale * (q @ k.T)
-    p, lse = softmax_lse_rows(s, vis)
+    p, lse = softmax_lse_rows(s, vis, sink)
     return p @ v, lse
+
+
+def _sink_of(sink, h):
+    return None if sink is None else float(sink[h])
 
 
 # ------------------------------------------------------- dense / varlen ----
 
-def attention_dense(q, k, v, scale, causal=False, window_left=None, window_right=None):
-    """q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D) float64 -> O (B, Sq, Hq, Dv), LSE (B, Hq, Sq)."""
+def attention_dense(q, k, v, scale, causal=False, window_left=None, window_right=None,
+                    sink=None):
+    """q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D) float64 -> O (B, Sq, Hq, Dv), LSE (B, Hq, Sq).
+    sink: per-query-head learnable-sink logits (Hq,) or None."""
     B, Sq, Hq, _ = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
     assert Hq % Hkv == 0
@@ -111,12 +125,13 @@ def attention_dense(q, k, v, scale, causal=False, window_left=None, window_right
     for b in range(B):
         for h in range(Hq):
             g = h // r
-            out[b, :, h], lse[b, h] = attention_head(q[b, :, h], k[b, :, g], v[b, :, g], scale, vis)
+            out[b, :, h], lse[b, h] = attention_head(q[b, :, h], k[b, :, g], v[b, :, g], scale, vis,
+                                                     _sink_of(sink, h))
     return out, lse
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
-                     window_left=None, window_right=None):
+                     window_left=None, window_right=None, sink=None):
     """Packed sequences. q (Tq, Hq, D), k/v (Tk, Hkv, D) -> O (Tq, Hq, Dv), LSE (Hq, Tq).
 
     The LSE layout (num_heads, total_q) is the interface page's varlen layout.
@@ -134,7 +149,8 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
         for h in range(Hq):
             g = h // r
             out[q0:q1, h], lse[h, q0:q1] = attention_head(q[q0:q1, h], k[k0:k1, g],
-                                                          v[k0:k1, g], scale, vis)
+                                                          v[k0:k1, g], scale, vis,
+                                                          _sink_of(sink, h))
     return out, lse
 
 
@@ -238,9 +254,22 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return sign * mag
 
 
+def with_sink(out, lse, sink):
+    """Adds learnable-sink logits to a finished (O, LSE): LSE' = log(exp(LSE)
+    + exp(sink)), O' = O * exp(LSE - LSE'). out[..., :] rows line up with lse
+    (out has lse's shape plus the value axis); sink broadcasts against lse.
+    Equal to putting the sink into the softmax (softmax_lse_rows); used where
+    the keys were split."""
+    sink = np.broadcast_to(np.asarray(sink, dtype=np.float64), lse.shape)
+    hi = np.maximum(lse, sink)
+    new = hi + np.log(np.exp(lse - hi) + np.exp(sink - hi))
+    w = np.where(np.isfinite(lse), np.exp(lse - new), 0.0)
+    return out * w[..., None], new
+
+
 def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1,
                  causal=False, window_left=None, window_right=None, heads=None,
-                 k_descale=None, v_descale=None):
+                 k_descale=None, v_descale=None, sink=None):
     """One query per sequence over a paged cache.
 
     q (B, Hq, D) float64. Returns O (B, Hq, Dv), LSE (B, Hq), and the split
@@ -251,6 +280,8 @@ def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1
     KV-cache decode with per-(batch, kv_head) descales): sequence b's keys of
     KV head g are k_descale[b, g] times the cached values (likewise V); the
     caches are then the decoded values (e4m3_decode of the stored codes).
+    sink: per-query-head learnable-sink logits (Hq,), merged after the split
+    combine (with_sink).
     """
     B, Hq, _ = q.shape
     Hkv = k_cache.shape[2]
@@ -274,11 +305,13 @@ def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1
             o_parts[:, b, h] = o[:, 0]
             lse_parts[:, b, h] = l[:, 0]
     out, lse = combine(o_parts, lse_parts)
+    if sink is not None:
+        out, lse = with_sink(out, lse, np.asarray(sink, dtype=np.float64)[None, :])
     return out, lse, o_parts, lse_parts
 
 
 def paged_prefill(q, k_cache, v_cache, page_table, seqused_k, scale, causal=False,
-                  window_left=None, window_right=None, cu_seqlens_q=None):
+                  window_left=None, window_right=None, cu_seqlens_q=None, sink=None):
     """Queries against a paged K/V cache (interface page, the page_table branch
     of `_flash_attn_fwd`: caches (num_pages, page_size, Hkv, D), a
     (B, max_pages) page table, per-sequence key counts seqused_k).
@@ -310,7 +343,7 @@ def paged_prefill(q, k_cache, v_cache, page_table, seqused_k, scale, causal=Fals
         vis = visible_mask(qb.shape[0], sk, causal, window_left, window_right)
         for h in range(Hq):
             g = h // r
-            o, l = attention_head(qb[:, h], kb[:, g], vb[:, g], scale, vis)
+            o, l = attention_head(qb[:, h], kb[:, g], vb[:, g], scale, vis, _sink_of(sink, h))
             if packed:
                 out[q0:q1, h], lse[h, q0:q1] = o, l
             else:

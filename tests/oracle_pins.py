@@ -22,6 +22,12 @@ What each pin rests on:
                  closed-form values (1, 448, 2**-6, 2**-9, -0, NaN codes)
   descale        per-(batch, KV head) descales equal decoding a cache whose
                  pages were scaled beforehand, page by page
+  sink_as_key    a learnable sink equals one more key whose score is the sink
+                 (an extra head-dim coordinate makes it exact for every query)
+                 and whose value is zero, run through the no-sink path
+  sink_merge     the sink put into the softmax equals merging it into a
+                 finished (O, LSE) in the log domain; sink = -inf changes
+                 nothing; a row with no visible key gets O = 0, LSE = sink
   paged_prefill  queries (dense and packed) against a paged cache equal the
                  scalar loops run on contiguous copies built token by token,
                  with ragged seqused_k, Sq < Sk, empty sequences and masks
@@ -409,6 +415,60 @@ def pin_descale():
     return (ok1 and ok2), f"O {d1} LSE {d2}"
 
 
+def pin_sink_as_key():
+    rng = _rng(25)
+    B, S, Hq, Hkv, D = 2, 7, 4, 2, 3
+    scale = 0.5
+    q = rng.standard_normal((B, S, Hq, D))
+    k = rng.standard_normal((B, S, Hkv, D))
+    v = rng.standard_normal((B, S, Hkv, D))
+    sink = rng.uniform(-2.0, 3.0, Hq)
+    o, l = A.attention_dense(q, k, v, scale, sink=sink)
+    # per query head h: q' = [q, 1], real keys [k, 0], the sink key
+    # [0, sink_h / scale] (score exactly sink_h), value 0, visible to all
+    r = Hq // Hkv
+    for h in range(Hq):
+        g = h // r
+        for b in range(B):
+            q2 = np.concatenate([q[b, :, h], np.ones((S, 1))], axis=1)
+            k2 = np.concatenate([np.concatenate([k[b, :, g], np.zeros((S, 1))], axis=1),
+                                 np.concatenate([np.zeros((1, D)), [[sink[h] / scale]]], axis=1)])
+            v2 = np.concatenate([v[b, :, g], np.zeros((1, D))])
+            o2, l2 = A.attention_head(q2, k2, v2, scale, np.ones((S, S + 1), dtype=bool))
+            ok1, d1 = _close(o[b, :, h], o2)
+            ok2, d2 = _close(l[b, h], l2)
+            if not (ok1 and ok2):
+                return False, f"b {b} h {h}: O {d1} LSE {d2}"
+    return True, "ok"
+
+
+def pin_sink_merge():
+    rng = _rng(26)
+    Sq, Sk, Hq, D = 6, 9, 2, 4
+    q = rng.standard_normal((1, Sq, Hq, D))
+    k = rng.standard_normal((1, Sk, 1, D))
+    v = rng.standard_normal((1, Sk, 1, D))
+    sink = np.array([0.7, -1.3])
+    for mk in [dict(causal=True), dict(window_left=2, window_right=0), dict()]:
+        o, l = A.attention_dense(q, k, v, 0.6, sink=sink, **mk)
+        o0, l0 = A.attention_dense(q, k, v, 0.6, **mk)
+        # with_sink wants O's leading axes in LSE's order: (B, Hq, Sq, D)
+        om, lm = A.with_sink(o0.transpose(0, 2, 1, 3), l0, sink[None, :, None])
+        om = om.transpose(0, 2, 1, 3)
+        ok1, d1 = _close(o, om)
+        ok2, d2 = _close(l, lm)
+        if not (ok1 and ok2):
+            return False, f"{mk}: O {d1} LSE {d2}"
+        on, ln_ = A.attention_dense(q, k, v, 0.6, sink=np.full(Hq, -np.inf), **mk)
+        if not (np.array_equal(on, o0) and np.array_equal(ln_, l0)):
+            return False, f"{mk}: sink -inf changed the result"
+    # Sq > Sk causal: the first rows see no key
+    o, l = A.attention_dense(q, k[:, :3], v[:, :3], 0.6, causal=True, sink=sink)
+    if not (np.all(o[0, :3] == 0) and np.allclose(l[0, :, :3], sink[:, None], rtol=0, atol=0)):
+        return False, "row with no key: O must be 0 and LSE the sink"
+    return True, "ok"
+
+
 def pin_torch_sdpa():
     import torch
     import torch.nn.functional as F
@@ -474,6 +534,8 @@ ALL_PINS = {
     "paged": pin_paged,
     "paged_prefill": pin_paged_prefill,
     "e4m3": pin_e4m3,
+    "sink_as_key": pin_sink_as_key,
+    "sink_merge": pin_sink_merge,
     "descale": pin_descale,
     "torch_sdpa": pin_torch_sdpa,
     "rows_match_full": pin_rows_match_full,

@@ -43,6 +43,12 @@ MUTANTS = [
     ("paged_decode", "g = h // r", "g = h % Hkv", "interleaved GQA grouping (paged)"),
     ("paged_prefill", "g = h // r", "g = h % Hkv", "interleaved GQA grouping (paged prefill)"),
     ("e4m3_decode", "np.exp2(e - 7.0)", "np.exp2(e - 8.0)", "e4m3 exponent bias 8 (the FNUZ bias)"),
+    ("softmax_lse_rows", "lse = hi + np.log(np.exp(lse - hi) + np.exp(sink - hi))",
+     "lse = hi + np.log(np.exp(lse - hi) + np.exp(-sink - hi))", "sink sign flipped"),
+    ("softmax_lse_rows", "lse = hi + np.log(np.exp(lse - hi) + np.exp(sink - hi))",
+     "lse = hi", "sink replaces the log-sum instead of adding to it"),
+    ("with_sink", "w = np.where(np.isfinite(lse), np.exp(lse - new), 0.0)",
+     "w = np.where(np.isfinite(lse), 1.0, 0.0)", "sink merge leaves O unscaled"),
     ("e4m3_decode", "(m / 8.0) * 2.0 ** -6", "(m / 8.0) * 2.0 ** -7", "e4m3 subnormal scale"),
     ("paged_decode", "kb = kb * np.asarray(k_descale, dtype=np.float64)[b][None, :, None]",
      "kb = kb * np.asarray(v_descale, dtype=np.float64)[b][None, :, None]", "K scaled by the V descale"),
