@@ -203,59 +203,61 @@ void fwd_pp_kernel(const FwdArgs a) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) pf[t] = zero_bf16x8();
 
-  // S(k) = K(k) Q^T into s[]
-  auto s_part = [&](int k) {
+  // Both parts of a matrix phase are written in issue order: a ring of LDS
+  // fragments read LEAD MFMAs ahead, consecutive MFMAs on different
+  // accumulators, and scheduling barriers between the {read i + LEAD,
+  // MFMA i} groups so the compiler keeps that order.
+  constexpr int LEAD = 8;
+  // S(k) = K(k) Q^T into s[]; MFMA i: contraction step i / 2, key block i % 2
+  auto s_part = [&](int k) __attribute__((always_inline)) {
     const char* kb0 = smem + (k & 3) * BUF_B;
+    constexpr int N = 2 * (D / 16);  // i -> cc = i / 2, kb = i % 2
+    auto rd = [&](int i) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(kb0 + (i & 1) * 32 * ROW_B + k_rd[i >> 1]);
+    };
+    bf16x8 ring[LEAD];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero_f32x16();
+    for (int i = 0; i < LEAD; ++i) ring[i] = rd(i);
+    s[0] = zero_f32x16();
+    s[1] = zero_f32x16();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int cc = 0; cc < D / 16; ++cc) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb0 + kb * 32 * ROW_B + k_rd[cc]);
-        s[kb] = mfma32(kf, qf[cc], s[kb]);
-      }
+    for (int i = 0; i < N; ++i) {
+      const bf16x8 kf = ring[i % LEAD];
+      if (i + LEAD < N) ring[i % LEAD] = rd(i + LEAD);
+      s[i & 1] = mfma32(kf, qf[i >> 1], s[i & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // O += P(k) V(k); V^T fragments from row-major V by transposing reads
-  auto pv_part = [&](int k) {
+  // O += P(k) V(k); V^T fragments from row-major V by transposing reads;
+  // MFMA i: 16-key step i / NDB, d-block i % NDB
+  auto pv_part = [&](int k) __attribute__((always_inline)) {
     const char* vb = smem + (k & 3) * BUF_B + TILE_B;
+    constexpr int NDB = D / 32, N = 4 * NDB;  // i -> t = i / NDB, db = i % NDB
+    auto rd = [&](int i) __attribute__((always_inline)) {
+      const int t = i / NDB, db = i % NDB;
+      const char* p = vb + (16 * t) * ROW_B + (db >> 1) * 128 + v_rd[db & 1];
+      const bf16x4 v0 = ds_read_tr16(reinterpret_cast<const __bf16*>(p));
+      const bf16x4 v1 = ds_read_tr16(reinterpret_cast<const __bf16*>(p + 8 * ROW_B));
+      return cat(v0, v1);
+    };
+    bf16x8 ring[LEAD];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int i = 0; i < LEAD; ++i) ring[i] = rd(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const char* p = vb + (16 * t) * ROW_B + (db >> 1) * 128 + v_rd[db & 1];
-        const bf16x4 v0 = ds_read_tr16(reinterpret_cast<const __bf16*>(p));
-        const bf16x4 v1 = ds_read_tr16(reinterpret_cast<const __bf16*>(p + 8 * ROW_B));
-        o[db] = mfma32(cat(v0, v1), pf[t], o[db]);
-      }
+    for (int i = 0; i < N; ++i) {
+      const bf16x8 vf = ring[i % LEAD];
+      if (i + LEAD < N) ring[i % LEAD] = rd(i + LEAD);
+      o[i % NDB] = mfma32(vf, pf[i / NDB], o[i % NDB]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  // Issue order for one matrix phase: keep several LDS fragment reads in
-  // flight ahead of the MFMAs that consume them (the default schedule issues
-  // each read right before its MFMA and stalls on LDS latency).
-  constexpr int NMF = D / 16 * 2;  // MFMAs per part (S and P V alike)
-  constexpr int LEAD = 8;          // MFMAs' worth of fragment reads issued ahead
-  auto sched_part = [&](auto rpm_c) {
-    constexpr int R = decltype(rpm_c)::value;  // LDS reads per MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, LEAD * R, 0);
-#pragma unroll
-    for (int i = 0; i < NMF - LEAD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
   };
 
   // MFMA item k: O += P(k-1) V(k-1) (k >= 1), then S(k) = K(k) Q^T (k < T)
   auto mfma_item = [&](int k) {
-    if (k >= 1) {
-      pv_part(k - 1);
-      sched_part(std::integral_constant<int, 2>{});
-    }
-    if (k < T) {
-      s_part(k);
-      sched_part(std::integral_constant<int, 1>{});
-    }
+    if (k >= 1) pv_part(k - 1);
+    if (k < T) s_part(k);
   };
 
   // softmax of S(k) into P(k): mask edge tiles, lazy running max, exp2
