@@ -254,6 +254,24 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return sign * mag
 
 
+def e5m2_decode(codes: np.ndarray) -> np.ndarray:
+    """Values of OCP 8-bit floating point E5M2 codes (the other fp8 KV-cache
+    format the sm_120 PR page's decode accepts), as float64.
+
+    Bit 7 is the sign, bits 6..2 the exponent field e (bias 15), bits 1..0 the
+    mantissa m: 0 < e < 31 gives (1 + m/4) * 2**(e - 15), e = 0 the subnormal
+    (m/4) * 2**-14; e = 31 is infinity when m = 0 and NaN otherwise (largest
+    finite magnitude 57344).
+    """
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    m = (c & 0x3).astype(np.float64)
+    mag = np.where(e == 0, (m / 4.0) * 2.0 ** -14, (1.0 + m / 4.0) * np.exp2(e - 15.0))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
 def with_sink(out, lse, sink):
     """Adds learnable-sink logits to a finished (O, LSE): LSE' = log(exp(LSE)
     + exp(sink)), O' = O * exp(LSE - LSE'). out[..., :] rows line up with lse
@@ -279,7 +297,8 @@ def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1
     k_descale / v_descale (B, Hkv), for a quantized cache (sm_120 PR page, fp8
     KV-cache decode with per-(batch, kv_head) descales): sequence b's keys of
     KV head g are k_descale[b, g] times the cached values (likewise V); the
-    caches are then the decoded values (e4m3_decode of the stored codes).
+    caches are then the decoded values (e4m3_decode or e5m2_decode of the
+    stored codes).
     sink: per-query-head learnable-sink logits (Hq,), merged after the split
     combine (with_sink).
     """

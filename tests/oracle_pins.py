@@ -20,6 +20,8 @@ What each pin rests on:
   paged          paged gather equals the contiguous layout
   e4m3           all 256 fp8 codes decode as torch's float8_e4m3fn does, and
                  closed-form values (1, 448, 2**-6, 2**-9, -0, NaN codes)
+  e5m2           all 256 fp8 codes decode as torch's float8_e5m2 does, and
+                 closed-form values (1, 57344, 2**-14, 2**-16, +-inf, NaN codes)
   descale        per-(batch, KV head) descales equal decoding a cache whose
                  pages were scaled beforehand, page by page
   sink_as_key    a learnable sink equals one more key whose score is the sink
@@ -389,6 +391,25 @@ def pin_e4m3():
     return True, "ok"
 
 
+def pin_e5m2():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    mine = A.e5m2_decode(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e5m2).to(torch.float64).numpy()
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    if not same.all():
+        bad = np.flatnonzero(~same)[:4]
+        return False, f"codes {bad.tolist()}: {mine[bad].tolist()} vs torch {ref[bad].tolist()}"
+    closed = {0x3C: 1.0, 0x7B: 57344.0, 0x04: 2.0 ** -14, 0x01: 2.0 ** -16, 0xBC: -1.0,
+              0x3E: 1.5, 0x7C: math.inf, 0xFC: -math.inf}
+    for c, v in closed.items():
+        if A.e5m2_decode(np.array([c]))[0] != v:
+            return False, f"code {c:#x} != {v}"
+    if not (np.isnan(mine[[0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF]]).all() and np.signbit(mine[0x80])):
+        return False, "NaN codes / negative zero"
+    return True, "ok"
+
+
 def pin_descale():
     rng = _rng(23)
     B, Hq, Hkv, D, ps, pps = 2, 4, 2, 3, 4, 2
@@ -534,6 +555,7 @@ ALL_PINS = {
     "paged": pin_paged,
     "paged_prefill": pin_paged_prefill,
     "e4m3": pin_e4m3,
+    "e5m2": pin_e5m2,
     "sink_as_key": pin_sink_as_key,
     "sink_merge": pin_sink_merge,
     "descale": pin_descale,

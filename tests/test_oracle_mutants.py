@@ -50,6 +50,9 @@ MUTANTS = [
     ("with_sink", "w = np.where(np.isfinite(lse), np.exp(lse - new), 0.0)",
      "w = np.where(np.isfinite(lse), 1.0, 0.0)", "sink merge leaves O unscaled"),
     ("e4m3_decode", "(m / 8.0) * 2.0 ** -6", "(m / 8.0) * 2.0 ** -7", "e4m3 subnormal scale"),
+    ("e5m2_decode", "np.exp2(e - 15.0)", "np.exp2(e - 16.0)", "e5m2 exponent bias 16 (the FNUZ bias)"),
+    ("e5m2_decode", "(m / 4.0) * 2.0 ** -14", "(m / 4.0) * 2.0 ** -15", "e5m2 subnormal scale"),
+    ("e5m2_decode", "e = (c >> 2) & 0x1F", "e = (c >> 3) & 0x1F", "e5m2 read with e4m3's field split"),
     ("paged_decode", "kb = kb * np.asarray(k_descale, dtype=np.float64)[b][None, :, None]",
      "kb = kb * np.asarray(v_descale, dtype=np.float64)[b][None, :, None]", "K scaled by the V descale"),
     ("paged_decode", "vb = vb * np.asarray(v_descale, dtype=np.float64)[b][None, :, None]",

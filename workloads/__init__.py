@@ -105,7 +105,7 @@ class Workload:
     page_size: int = 0
     num_splits: int = 0
     seed: int = 0
-    kv_dtype: str = "bf16"                  # "bf16", or "fp8_e4m3": k/v hold uint8 codes
+    kv_dtype: str = "bf16"                  # "bf16", "fp8_e4m3" or "fp8_e5m2": k/v hold uint8 codes
     k_descale: Optional[np.ndarray] = None  # fp8: float32 (B, Hkv), or None for 1
     v_descale: Optional[np.ndarray] = None
 
@@ -183,21 +183,23 @@ def paged_decode_case(seed: int, batch: int, hq: int, hkv: int, d: int, page_siz
                     seqused_k=seqused, page_size=page_size, num_splits=num_splits, seed=seed)
 
 
-def _e4m3_codes(x: np.ndarray) -> np.ndarray:
-    """float32 values -> OCP e4m3 codes (uint8), round to nearest even, via
-    torch's float8_e4m3fn cast. Callers keep |x| well below 448."""
+def _fp8_codes(x: np.ndarray, fmt: str) -> np.ndarray:
+    """float32 values -> OCP fp8 codes (uint8) of format fmt ("e4m3" or
+    "e5m2"), round to nearest even, via torch's float8 casts. Callers keep |x|
+    well below the format's largest finite value (448, 57344)."""
     import torch
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
-        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    dt = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[fmt]
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dt).view(
+        torch.uint8).numpy()
 
 
 def paged_decode_fp8_case(seed: int, batch: int, hq: int, hkv: int, d: int, page_size: int,
                           pages_per_seq: int, num_pages: Optional[int] = None, seqused_k=None,
                           num_splits: int = 0, descale: bool = True,
                           softmax_scale: Optional[float] = None,
-                          name: str = "paged_fp8") -> Workload:
-    """paged_decode_case with an fp8 e4m3 K/V cache and per-(batch, KV head)
-    descales. Draw order: Q (bf16), K and V values (float32 N(0,1)), the page
+                          name: str = "paged_fp8", fmt: str = "e4m3") -> Workload:
+    """paged_decode_case with an fp8 K/V cache (OCP e4m3, or e5m2 with
+    fmt="e5m2") and per-(batch, KV head) descales. Draw order: Q (bf16), K and V values (float32 N(0,1)), the page
     permutation, then the K and V descale factors f ~ U[0.5, 2]. Descale =
     f / 16; a page owned by sequence b stores codes of value / descale[b, g]
     (|value / descale| < 200, far from e4m3's 448); pages no sequence uses
@@ -224,9 +226,9 @@ def paged_decode_fp8_case(seed: int, batch: int, hq: int, hkv: int, d: int, page
         vx /= vpage[:, None, :, None]
     else:
         kd = vd = None
-    k = _e4m3_codes(kx)
+    k = _fp8_codes(kx, fmt)
     del kx
-    v = _e4m3_codes(vx)
+    v = _fp8_codes(vx, fmt)
     del vx
     if seqused_k is None:
         seqused = np.full(batch, pages_per_seq * page_size, dtype=np.int32)
@@ -238,7 +240,7 @@ def paged_decode_fp8_case(seed: int, batch: int, hq: int, hkv: int, d: int, page
                     seqlen_k=pages_per_seq * page_size, max_seqlen_q=1,
                     max_seqlen_k=int(seqused.max(initial=0)), page_table=page_table,
                     seqused_k=seqused, page_size=page_size, num_splits=num_splits, seed=seed,
-                    kv_dtype="fp8_e4m3", k_descale=kd, v_descale=vd)
+                    kv_dtype="fp8_" + fmt, k_descale=kd, v_descale=vd)
 
 
 def paged_prefill_case(seed: int, batch: int, hq: int, hkv: int, d: int, page_size: int,
