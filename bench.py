@@ -146,7 +146,7 @@ def _pairs(sq, sk, causal, wl, wr) -> int:
 
 
 def decode_bytes(w) -> int:
-    elem = 1 if w.kv_dtype == "fp8_e4m3" else 2
+    elem = 1 if w.kv_dtype.startswith("fp8") else 2
     kv = 2 * int(w.seqused_k.sum()) * w.num_heads_kv * w.head_dim * elem
     q = w.batch * w.num_heads_q * w.head_dim * 2
     o = q
@@ -181,9 +181,10 @@ class Decode:
         self.mi, self.w = mi, w
         self.q = dev_bf16(w.q)
         self.kd = self.vd = None
-        if w.kv_dtype == "fp8_e4m3":
-            self.kc = torch.from_numpy(w.k).to("cuda").view(torch.float8_e4m3fn)
-            self.vc = torch.from_numpy(w.v).to("cuda").view(torch.float8_e4m3fn)
+        if w.kv_dtype.startswith("fp8"):
+            dt = {"fp8_e4m3": torch.float8_e4m3fn, "fp8_e5m2": torch.float8_e5m2}[w.kv_dtype]
+            self.kc = torch.from_numpy(w.k).to("cuda").view(dt)
+            self.vc = torch.from_numpy(w.v).to("cuda").view(dt)
             if w.k_descale is not None:
                 self.kd = torch.from_numpy(w.k_descale).to("cuda")
                 self.vd = torch.from_numpy(w.v_descale).to("cuda")
@@ -340,22 +341,24 @@ def main():
             log(f"[bench] {wi.name}: {med * 1e3:.1f} us, {extra[wi.name]['tflops']:.1f} TFLOP/s")
             del p
             torch.cuda.empty_cache()
-        # the paged decode workload with an fp8 e4m3 cache (per-(batch, KV
-        # head) descales): half the K/V bytes
+        # the paged decode workload with an fp8 cache, e4m3 then e5m2
+        # (per-(batch, KV head) descales): half the K/V bytes
         del dec
         torch.cuda.empty_cache()
-        w8 = W.paged_decode_fp8_case(1005, 16, 32, 4, 128, 256, 128, num_splits=16,
-                                     name="paged_decode_fp8_b16_sk32768")
-        d8 = Decode(mi, w8, torch)
-        warm_up(torch, d8)
-        ms = sorted(time_launches(torch, d8, max(5, args.steps)))
-        med = ms[len(ms) // 2]
-        gb = decode_bytes(w8) / (med * 1e-3) / 1e9
-        extra[w8.name] = {"median_us": med * 1e3, "gbs": gb, "frac": gb / PEAK_HBM_GBS,
-                          "bytes_per_launch": decode_bytes(w8)}
-        log(f"[bench] {w8.name}: {med * 1e3:.1f} us, {gb:.0f} GB/s")
-        del d8, w8
-        torch.cuda.empty_cache()
+        for fmt, wname in (("e4m3", "paged_decode_fp8_b16_sk32768"),
+                           ("e5m2", "paged_decode_fp8_e5m2_b16_sk32768")):
+            w8 = W.paged_decode_fp8_case(1005, 16, 32, 4, 128, 256, 128, num_splits=16,
+                                         name=wname, fmt=fmt)
+            d8 = Decode(mi, w8, torch)
+            warm_up(torch, d8)
+            ms = sorted(time_launches(torch, d8, max(5, args.steps)))
+            med = ms[len(ms) // 2]
+            gb = decode_bytes(w8) / (med * 1e-3) / 1e9
+            extra[w8.name] = {"median_us": med * 1e3, "gbs": gb, "frac": gb / PEAK_HBM_GBS,
+                              "bytes_per_launch": decode_bytes(w8)}
+            log(f"[bench] {w8.name}: {med * 1e3:.1f} us, {gb:.0f} GB/s")
+            del d8, w8
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:

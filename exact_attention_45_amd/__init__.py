@@ -26,7 +26,7 @@ __all__ = [
     "mi_attn_combine", "mi_attn_decode_workspace_bytes", "mi_attn_decode_num_splits",
     "mi_attn_last_error", "mi_attn_version", "FwdParams", "DecodeParams",
     "MI_ATTN_OK", "MI_ATTN_EINVAL", "MI_ATTN_EUNSUPPORTED", "MI_ATTN_EBOUNDS",
-    "MI_ATTN_EWORKSPACE", "MI_ATTN_EHIP", "MI_ATTN_KV_BF16", "MI_ATTN_KV_FP8_E4M3",
+    "MI_ATTN_EWORKSPACE", "MI_ATTN_EHIP", "MI_ATTN_KV_BF16", "MI_ATTN_KV_FP8_E4M3", "MI_ATTN_KV_FP8_E5M2",
 ]
 
 MI_ATTN_OK = 0
@@ -37,6 +37,7 @@ MI_ATTN_EWORKSPACE = -4
 MI_ATTN_EHIP = -5
 MI_ATTN_KV_BF16 = 0
 MI_ATTN_KV_FP8_E4M3 = 1
+MI_ATTN_KV_FP8_E5M2 = 2
 _STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EBOUNDS", -4: "EWORKSPACE",
            -5: "EHIP"}
 
@@ -324,7 +325,7 @@ def _decode_params(q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax
     p.num_splits = int(num_splits)
     if workspace is not None:
         p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    p.kv_dtype = MI_ATTN_KV_FP8_E4M3 if _is_fp8(k_cache) else MI_ATTN_KV_BF16
+    p.kv_dtype = _kv_dtype(k_cache)
     return p
 
 
@@ -338,17 +339,27 @@ def _req_sink(sink, hq: int, device):
     return sink.data_ptr()
 
 
-def _is_fp8(t) -> bool:
+def _kv_dtype(t) -> int:
+    """Cache type code from the tensor dtype: float8_e4m3fn (or raw uint8
+    bytes, read as e4m3) and float8_e5m2 are fp8 caches, bfloat16 is bf16."""
     import torch
-    return t.dtype in (torch.float8_e4m3fn, torch.uint8)
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return MI_ATTN_KV_FP8_E4M3
+    if t.dtype == torch.float8_e5m2:
+        return MI_ATTN_KV_FP8_E5M2
+    return MI_ATTN_KV_BF16
+
+
+def _is_fp8(t) -> bool:
+    return _kv_dtype(t) != MI_ATTN_KV_BF16
 
 
 def _req_kv(name, t, device, fp8: bool):
-    """bf16 cache, or fp8 e4m3 (torch.float8_e4m3fn, or its raw bytes as uint8)."""
+    """bf16 cache, or fp8 (float8_e4m3fn, raw uint8 e4m3 bytes, or float8_e5m2)."""
     if not fp8:
         return _req_bf16(name, t, device)
     if not _is_fp8(t):
-        raise MiAttnError(MI_ATTN_EINVAL, f"{name} must be float8_e4m3fn or uint8 like k_cache "
+        raise MiAttnError(MI_ATTN_EINVAL, f"{name} must be an fp8 tensor like k_cache "
                                           f"(got {t.dtype})")
     if not t.is_cuda or t.device != device:
         raise MiAttnError(MI_ATTN_EINVAL, f"{name} must be a device tensor on {device}")
@@ -405,7 +416,7 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
     """One query token per sequence against a paged cache, split along keys.
 
     q (B, Hq, D); k/v cache (num_pages, page_size, Hkv, D) contiguous, bf16 or
-    fp8 e4m3 (float8_e4m3fn or uint8 bytes; then k_descale / v_descale are
+    fp8 (float8_e4m3fn, raw uint8 e4m3 bytes, or float8_e5m2; then k_descale / v_descale are
     float32 (B, Hkv) or None for 1); page_table int32 (B, max_pages);
     seqused_k int32 (B,) or None.
     Returns out (B, Hq, D) bf16 and lse (B, Hq) float32.
@@ -417,6 +428,8 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
     fp8 = _is_fp8(k_cache)
     _req_kv("k_cache", k_cache, dev, fp8)
     _req_kv("v_cache", v_cache, dev, fp8)
+    if fp8 and _kv_dtype(v_cache) != _kv_dtype(k_cache):
+        raise MiAttnError(MI_ATTN_EINVAL, "k_cache and v_cache must have the same fp8 format")
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise MiAttnError(MI_ATTN_EINVAL, "q must be (B, Hq, D) and caches (pages, page_size, Hkv, D)")
     if not k_cache.is_contiguous() or not v_cache.is_contiguous():

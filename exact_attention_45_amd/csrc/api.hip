@@ -90,9 +90,11 @@ int check_decode(const mi_attn_decode_params* p) {
     return fail(MI_ATTN_EINVAL, "num_splits must be in 0..256 (got %d)", p->num_splits);
   if (!isfinite(p->softmax_scale) || p->softmax_scale < 0.0f)
     return fail(MI_ATTN_EUNSUPPORTED, "softmax_scale must be finite and >= 0");
-  if (p->kv_dtype != MI_ATTN_KV_BF16 && p->kv_dtype != MI_ATTN_KV_FP8_E4M3)
-    return fail(MI_ATTN_EUNSUPPORTED, "kv_dtype %d not supported (bf16, fp8 e4m3)", p->kv_dtype);
-  if (p->kv_dtype == MI_ATTN_KV_FP8_E4M3 && !mi_attn::decode_streams(p->head_dim, p->page_size))
+  if (p->kv_dtype != MI_ATTN_KV_BF16 && p->kv_dtype != MI_ATTN_KV_FP8_E4M3 &&
+      p->kv_dtype != MI_ATTN_KV_FP8_E5M2)
+    return fail(MI_ATTN_EUNSUPPORTED, "kv_dtype %d not supported (bf16, fp8 e4m3, fp8 e5m2)",
+                p->kv_dtype);
+  if (p->kv_dtype != MI_ATTN_KV_BF16 && !mi_attn::decode_streams(p->head_dim, p->page_size))
     return fail(MI_ATTN_EUNSUPPORTED, "fp8 K/V needs head_dim 64/128 and page_size a multiple "
                 "of 32 (got %d, %d)", p->head_dim, p->page_size);
   return MI_ATTN_OK;
@@ -309,7 +311,7 @@ int mi_attn_decode_splitkv(const mi_attn_decode_params* p, void* stream) {
   int wl, wr;
   normalise_window(p->causal, p->window_left, p->window_right, &wl, &wr);
   a.wl = wl;
-  a.kv_fp8 = p->kv_dtype == MI_ATTN_KV_FP8_E4M3;
+  a.kv_fp8 = p->kv_dtype == MI_ATTN_KV_FP8_E4M3 ? 1 : p->kv_dtype == MI_ATTN_KV_FP8_E5M2 ? 2 : 0;
   a.k_descale = a.kv_fp8 ? p->k_descale : nullptr;
   a.v_descale = a.kv_fp8 ? p->v_descale : nullptr;
   if ((int64_t)a.batch * a.hkv * a.row_blocks * splits > INT32_MAX)

@@ -34,8 +34,9 @@
 //     bound ends at the last key before seqused_k: rows past it read as zero.
 //   * A page id outside [0, num_pages), or a seqused_k outside [0, capacity],
 //     is never dereferenced and turns the split's partial into NaN.
-//   * fp8 cache (FP8 = true; sm_120 PR page, fp8 KV-cache decode: OCP e4m3
-//     K/V with a per-(batch, KV head) k_descale / v_descale and bf16 compute):
+//   * fp8 cache (KV = 1 e4m3, 2 e5m2; sm_120 PR page, fp8 KV-cache decode:
+//     OCP e4m3 / e5m2 K/V with a per-(batch, KV head) k_descale / v_descale and
+//     bf16 compute):
 //     a row is head_dim bytes, so a 16-byte load covers twice the keys and a
 //     slice half the bytes. Staging converts each byte to bf16 (exact: e4m3
 //     values are bf16 values) into the same LDS layout, so the fragment reads,
@@ -51,8 +52,9 @@
 
 namespace mi_attn {
 
-template <int D, bool FP8>
+template <int D, int KV>
 struct StreamCfg {
+  static constexpr bool FP8 = KV != 0;
   // K/V register sets per wave. Three for fp8 as well: with half the bytes
   // per slice, 4 or 6 sets in flight measured slower (110 and 128 us against
   // 96 us for the B16 Sk32768 fp8 workload).
@@ -69,12 +71,20 @@ struct StreamCfg {
   static constexpr int LDS_B = SLOT_B;
 };
 
-// Four OCP e4m3 bytes (little-endian in w) -> four bf16 values (exact): the
-// hardware conversion gives fp32, the bf16 rounding of which is exact.
+// Four OCP fp8 bytes (little-endian in w; e4m3, or e5m2 when E5M2) -> four
+// bf16 values (exact): the hardware conversion gives fp32, and every e4m3 and
+// e5m2 value is a bf16 value.
+template <bool E5M2>
 __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
   typedef __attribute__((ext_vector_type(2))) float f32x2;
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f32x2 lo, hi;
+  if constexpr (E5M2) {
+    lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+  } else {
+    lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  }
   const bf16x4 r = cvt4(lo[0], lo[1], hi[0], hi[1]);
   return __builtin_bit_cast(uint2, r);
 }
@@ -104,9 +114,11 @@ __device__ __forceinline__ void stream_slices(int n_w, Issue& issue, Stage& stag
   ((i + J < n_w ? (stage(std::integral_constant<int, J>{}), consume(i + J), 0) : 0), ...);
 }
 
-template <int D, bool FP8>
+// KV: 0 = bf16 cache, 1 = fp8 e4m3, 2 = fp8 e5m2
+template <int D, int KV>
 __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) {
-  using C = StreamCfg<D, FP8>;
+  constexpr bool FP8 = KV != 0;
+  using C = StreamCfg<D, KV>;
   constexpr int NS = C::NS, ROW_B = C::ROW_B, SLICE_B = C::SLICE_B, CPR = C::CPR;
   constexpr int RPL = C::RPL, NLD = C::NLD, GROW_B = C::GROW_B;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_B];
@@ -252,10 +264,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
       for (int u = 0; u < NLD; ++u) {
         const int row = RPL * u + ld_r;
         const uint4 kx = kreg[slot][u], vx = vreg[slot][u];
-        const uint2 k0 = fp8x4_to_bf16x4(kx.x), k1 = fp8x4_to_bf16x4(kx.y);
-        const uint2 k2 = fp8x4_to_bf16x4(kx.z), k3 = fp8x4_to_bf16x4(kx.w);
-        const uint2 v0 = fp8x4_to_bf16x4(vx.x), v1 = fp8x4_to_bf16x4(vx.y);
-        const uint2 v2 = fp8x4_to_bf16x4(vx.z), v3 = fp8x4_to_bf16x4(vx.w);
+        const uint2 k0 = fp8x4_to_bf16x4<KV == 2>(kx.x), k1 = fp8x4_to_bf16x4<KV == 2>(kx.y);
+        const uint2 k2 = fp8x4_to_bf16x4<KV == 2>(kx.z), k3 = fp8x4_to_bf16x4<KV == 2>(kx.w);
+        const uint2 v0 = fp8x4_to_bf16x4<KV == 2>(vx.x), v1 = fp8x4_to_bf16x4<KV == 2>(vx.y);
+        const uint2 v2 = fp8x4_to_bf16x4<KV == 2>(vx.z), v3 = fp8x4_to_bf16x4<KV == 2>(vx.w);
         char* kr = kslot + row * ROW_B;
         char* vr = vslot + row * ROW_B;
         *reinterpret_cast<uint4*>(kr + (((2 * ld_c) ^ kswz(row)) * 16)) = make_uint4(k0.x, k0.y, k1.x, k1.y);
@@ -369,21 +381,21 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   }
 }
 
-template <int D, bool FP8>
+template <int D, int KV>
 hipError_t launch_stream(const DecodeArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.batch * ((a.hkv + 3) / 4) * a.row_blocks * a.num_splits;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_stream_kernel<D, FP8>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_stream_kernel<D, KV>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t s) {
-  return launch_stream<D, false>(a, s);
+  return launch_stream<D, 0>(a, s);
 }
 template <int D>
 hipError_t launch_decode_stream_fp8(const DecodeArgs& a, hipStream_t s) {
-  return launch_stream<D, true>(a, s);
+  return a.kv_fp8 == 2 ? launch_stream<D, 2>(a, s) : launch_stream<D, 1>(a, s);
 }
 
 template hipError_t launch_decode_stream<64>(const DecodeArgs&, hipStream_t);

@@ -169,8 +169,8 @@ struct DecodeArgs {
   float scale;
   float scale_log2;
   int32_t wl;                // < 0 unbounded
-  // fp8 (OCP e4m3) cache: one byte per element, real value = descale[b][kv
-  // head] * decoded byte; descales NULL = 1
+  // fp8 cache (1 = OCP e4m3, 2 = OCP e5m2; 0 = bf16): one byte per element,
+  // real value = descale[b][kv head] * decoded byte; descales NULL = 1
   int32_t kv_fp8;
   const float* k_descale;    // [batch][hkv] or NULL
   const float* v_descale;

@@ -186,17 +186,18 @@ int mi_attn_fwd(const mi_attn_fwd_params *p, void *stream);
  * mi_attn_decode_workspace_bytes(p) bytes, 256-byte aligned. Two launches
  * on `stream`; concurrent calls must use distinct workspaces.
  *
- * fp8 cache (kv_dtype == MI_ATTN_KV_FP8_E4M3; sm_120 PR page, fp8 KV-cache
- * decode): k_cache and v_cache hold one OCP e4m3 byte per element, same
+ * fp8 cache (kv_dtype == MI_ATTN_KV_FP8_E4M3 or MI_ATTN_KV_FP8_E5M2; sm_120
+ * PR page, fp8 KV-cache decode, e4m3/e5m2): k_cache and v_cache hold one OCP
+ * e4m3 (or e5m2) byte per element, same
  * [num_pages, page_size, num_heads_kv, head_dim] layout; the cached value is
- * k_descale[b * num_heads_kv + g] * e4m3(byte) (likewise V), with
+ * k_descale[b * num_heads_kv + g] * fp8(byte) (likewise V), with
  * k_descale / v_descale device float32 [batch, num_heads_kv], or NULL for 1.
  * The query stays bf16 and the arithmetic is the bf16 path's (each byte is
  * widened to bf16 exactly). Supported for head_dim 64/128 with page_size a
  * multiple of 32; other combinations return MI_ATTN_EUNSUPPORTED. With
  * kv_dtype == MI_ATTN_KV_BF16 the descale pointers are ignored.
  * --------------------------------------------------------------------- */
-enum { MI_ATTN_KV_BF16 = 0, MI_ATTN_KV_FP8_E4M3 = 1 };
+enum { MI_ATTN_KV_BF16 = 0, MI_ATTN_KV_FP8_E4M3 = 1, MI_ATTN_KV_FP8_E5M2 = 2 };
 
 typedef struct {
   const void *q;
@@ -214,7 +215,7 @@ typedef struct {
   int32_t num_splits;
   void *workspace;
   size_t workspace_bytes;
-  int32_t kv_dtype;                     /* MI_ATTN_KV_BF16 or MI_ATTN_KV_FP8_E4M3 */
+  int32_t kv_dtype;                     /* MI_ATTN_KV_BF16, _FP8_E4M3 or _FP8_E5M2 */
   const float *k_descale, *v_descale;   /* fp8 only: [batch, num_heads_kv] or NULL */
   const void *learnable_sink;           /* device bf16 [num_heads_q], or NULL; as for
                                            mi_attn_fwd, merged in the combine step */

@@ -170,7 +170,7 @@ def test_decode_workspace_size(lib):
     (dict(page_table=0), mi.MI_ATTN_EINVAL),
     (dict(k_cache=FAKE + 4), mi.MI_ATTN_EINVAL),
     (dict(max_pages_per_seq=1 << 24, page_size=1 << 10), mi.MI_ATTN_EBOUNDS),
-    (dict(kv_dtype=2), mi.MI_ATTN_EUNSUPPORTED),                      # no such cache type
+    (dict(kv_dtype=3), mi.MI_ATTN_EUNSUPPORTED),                      # no such cache type
     (dict(kv_dtype=mi.MI_ATTN_KV_FP8_E4M3, head_dim=256), mi.MI_ATTN_EUNSUPPORTED),
     (dict(kv_dtype=mi.MI_ATTN_KV_FP8_E4M3, page_size=48), mi.MI_ATTN_EUNSUPPORTED),
 ])
@@ -183,9 +183,10 @@ def test_decode_invalid_arguments(lib, kw, code):
     assert (n > 0) if pointer_only else (n == 0)
 
 
-def test_decode_fp8_params_accepted_by_validation(lib):
-    # fp8 e4m3 with head_dim 128 and 256-token pages sizes like the bf16 cache
-    p = _dec(kv_dtype=mi.MI_ATTN_KV_FP8_E4M3)
+@pytest.mark.parametrize("kv", [mi.MI_ATTN_KV_FP8_E4M3, mi.MI_ATTN_KV_FP8_E5M2])
+def test_decode_fp8_params_accepted_by_validation(lib, kv):
+    # fp8 (either format) with head_dim 128 and 256-token pages sizes like the bf16 cache
+    p = _dec(kv_dtype=kv)
     assert lib.mi_attn_decode_num_splits(ctypes.byref(p)) == 16
     assert lib.mi_attn_decode_workspace_bytes(ctypes.byref(p)) == \
         lib.mi_attn_decode_workspace_bytes(ctypes.byref(_dec()))

@@ -1,4 +1,4 @@
-"""GPU parity of the fp8 (OCP e4m3) KV-cache decode with per-(batch, KV head)
+"""GPU parity of the fp8 (OCP e4m3 and e5m2) KV-cache decode with per-(batch, KV head)
 descales (mi_attn_decode_splitkv through the C ABI) against the float64
 oracle run on the decoded cache values."""
 import zlib
@@ -24,7 +24,9 @@ def dev_f32(x):
 
 def run_fp8(mi, w, num_splits=None, window_left=None, as_float8=False):
     kc, vc = dev_u8(w.k), dev_u8(w.v)
-    if as_float8:
+    if w.kv_dtype == "fp8_e5m2":  # uint8 means e4m3 bytes: e5m2 needs its dtype
+        kc, vc = kc.view(torch.float8_e5m2), vc.view(torch.float8_e5m2)
+    elif as_float8:
         kc, vc = kc.view(torch.float8_e4m3fn), vc.view(torch.float8_e4m3fn)
     out, lse = mi.mi_attn_decode_splitkv(
         dev_bf16(w.q), kc, vc, dev_i32(w.page_table), seqused_k=dev_i32(w.seqused_k),
@@ -36,8 +38,12 @@ def run_fp8(mi, w, num_splits=None, window_left=None, as_float8=False):
     return out, lse
 
 
+def decode_codes(w, codes):
+    return OA.e5m2_decode(codes) if w.kv_dtype == "fp8_e5m2" else OA.e4m3_decode(codes)
+
+
 def oracle_fp8(w, window_left=None, heads=None):
-    o, l, _, _ = OA.paged_decode(f64(w.q), OA.e4m3_decode(w.k), OA.e4m3_decode(w.v), w.page_table,
+    o, l, _, _ = OA.paged_decode(f64(w.q), decode_codes(w, w.k), decode_codes(w, w.v), w.page_table,
                                  w.seqused_k, w.softmax_scale, num_splits=1,
                                  window_left=window_left, heads=heads,
                                  k_descale=w.k_descale, v_descale=w.v_descale)
@@ -65,6 +71,50 @@ def test_fp8_decode_elementwise(gpu_lib, case):
     out, lse = run_fp8(gpu_lib, w, window_left=wl)
     o_ref, l_ref = oracle_fp8(w, window_left=wl)
     print(name, check(host_f64(out), o_ref, host_f64(lse), l_ref, what=name))
+
+
+E5M2_CASES = [c for c in CASES if c[0] in ("gqa8_page256_ragged", "gqa4_page64_d64",
+                                            "window_left", "empty_and_tiny")]
+
+
+@pytest.mark.parametrize("case", E5M2_CASES, ids=[c[0] for c in E5M2_CASES])
+def test_e5m2_decode_elementwise(gpu_lib, case):
+    name, B, Hq, Hkv, D, ps, pps, extra, used, splits, wl, ds = case
+    print(f"[case] e5m2 decode {name}", flush=True)
+    w = W.paged_decode_fp8_case(zlib.crc32(name.encode()) % 10000 + 1, B, Hq, Hkv, D, ps, pps,
+                                num_pages=B * pps + extra, seqused_k=used, num_splits=splits,
+                                descale=ds, fmt="e5m2")
+    out, lse = run_fp8(gpu_lib, w, window_left=wl)
+    o_ref, l_ref = oracle_fp8(w, window_left=wl)
+    print(name, check(host_f64(out), o_ref, host_f64(lse), l_ref, what=name))
+
+
+def test_e5m2_every_finite_code_decodes_exactly(gpu_lib):
+    """As the e4m3 case below for e5m2: each of its 248 finite codes placed in
+    V comes back exactly (every e5m2 value is a bf16 value)."""
+    B, Hq, Hkv, D, ps = 2, 4, 4, 128, 64
+    w = W.paged_decode_fp8_case(78, B, Hq, Hkv, D, ps, 1, seqused_k=[1, 1], num_splits=1,
+                                descale=False, fmt="e5m2")
+    finite = np.array([c for c in range(256) if (c & 0x7C) != 0x7C], dtype=np.uint8)
+    codes = np.resize(finite, (B, Hkv, D))
+    for b in range(B):
+        w.v[w.page_table[b, 0], 0] = codes[b]
+    out, lse = run_fp8(gpu_lib, w)
+    got = host_f64(out).reshape(B, Hkv, Hq // Hkv, D)
+    want = OA.e5m2_decode(codes)[:, :, None, :]
+    assert np.array_equal(got, np.broadcast_to(want, got.shape))
+    o_ref, l_ref = oracle_fp8(w)
+    check(host_f64(out), o_ref, host_f64(lse), l_ref, what="one key e5m2")
+
+
+def test_fp8_mixed_formats_rejected(gpu_lib):
+    w = W.paged_decode_fp8_case(5, 1, 4, 2, 128, 64, 2)
+    kc = dev_u8(w.k).view(torch.float8_e4m3fn)
+    vc = dev_u8(w.v).view(torch.float8_e5m2)
+    with pytest.raises(gpu_lib.MiAttnError) as e:
+        gpu_lib.mi_attn_decode_splitkv(dev_bf16(w.q), kc, vc, dev_i32(w.page_table),
+                                       seqused_k=dev_i32(w.seqused_k))
+    assert e.value.code == gpu_lib.MI_ATTN_EINVAL
 
 
 def test_fp8_every_code_decodes_exactly(gpu_lib):
