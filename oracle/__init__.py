@@ -9,7 +9,8 @@ matrix, and uses numpy (BLAS) matmuls as its only library primitive.
 Modules:
   attention  full-matrix numpy implementation: masks, forward, varlen,
              split-KV partials and their combine, paged gather, paged prefill
-             and paged decode,
+             and paged decode, the backward (dQ, dK, dV) for dense and packed
+             sequences,
              and a per-row evaluator for sampling very large problems.
   brute      scalar Python loops over (batch, head, query, key, dim) for
              tiny shapes; an independent second reading of the definition.

@@ -154,6 +154,77 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
     return out, lse
 
 
+# -------------------------------------------------------------- backward ----
+
+def attention_head_backward(q, k, v, dout, scale, vis):
+    """Gradients of one head's attention output (backward page flash_bwd_sm100.py:
+    recompute P from S and LSE, dV = P^T dO, dP = dO V^T, dS = P * (dP - dPsum),
+    dQ = scale dS K, dK = scale dS^T Q; the interface page's backward
+    preprocess defines dPsum as the row sum of O * dO).
+
+    q (Sq, D), k (Sk, D), v (Sk, Dv), dout (Sq, Dv), vis (Sq, Sk) ->
+    dq (Sq, D), dk (Sk, D), dv (Sk, Dv). A query with no visible key has
+    P = 0 and so contributes nothing."""
+    s = scale * (q @ k.T)
+    p, _ = softmax_lse_rows(s, vis)
+    o = p @ v
+    dv = p.T @ dout
+    dp = dout @ v.T
+    dpsum = np.sum(o * dout, axis=1)
+    ds = p * (dp - dpsum[:, None])
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_dense_backward(q, k, v, dout, scale, causal=False, window_left=None,
+                             window_right=None):
+    """q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D), dout (B, Sq, Hq, Dv) float64 ->
+    dq, dk, dv shaped like q, k, v. With GQA, a KV head's dK and dV sum the
+    contributions of every query head that reads it (the interface page's
+    backward reduces them over the qhead_per_kvhead heads)."""
+    B, Sq, Hq, _ = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    assert Hq % Hkv == 0
+    r = Hq // Hkv
+    vis = visible_mask(Sq, Sk, causal, window_left, window_right)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // r
+            gq, gk, gv = attention_head_backward(q[b, :, h], k[b, :, g], v[b, :, g],
+                                                 dout[b, :, h], scale, vis)
+            dq[b, :, h] = gq
+            dk[b, :, g] += gk
+            dv[b, :, g] += gv
+    return dq, dk, dv
+
+
+def attention_varlen_backward(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
+                              window_left=None, window_right=None):
+    """Packed sequences: q (Tq, Hq, D), k/v (Tk, Hkv, D), dout (Tq, Hq, Dv) ->
+    dq, dk, dv shaped like q, k, v; each sequence as attention_dense_backward."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    r = Hq // Hkv
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(len(cu_seqlens_q) - 1):
+        q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
+        vis = visible_mask(q1 - q0, k1 - k0, causal, window_left, window_right)
+        for h in range(Hq):
+            g = h // r
+            gq, gk, gv = attention_head_backward(q[q0:q1, h], k[k0:k1, g], v[k0:k1, g],
+                                                 dout[q0:q1, h], scale, vis)
+            dq[q0:q1, h] = gq
+            dk[k0:k1, g] += gk
+            dv[k0:k1, g] += gv
+    return dq, dk, dv
+
+
 def attention_rows(q_rows: np.ndarray, row_index: np.ndarray, k: np.ndarray, v: np.ndarray,
                    scale: float, seqlen_q: int, causal=False, window_left=None,
                    window_right=None):

@@ -33,6 +33,14 @@ What each pin rests on:
   paged_prefill  queries (dense and packed) against a paged cache equal the
                  scalar loops run on contiguous copies built token by token,
                  with ragged seqused_k, Sq < Sk, empty sequences and masks
+  bwd_fd         backward gradients equal central finite differences of the
+                 scalar-loop forward (loss sum(O * G)), GQA, Sq != Sk, masks,
+                 rows with no visible key
+  bwd_varlen     packed-sequence gradients equal finite differences of the
+                 varlen forward, with different query and key lengths
+  bwd_closed     one key: dV = sum of dO over the group's heads and queries,
+                 dQ = dK = 0; sum over keys of dK is 0 (rows of dS sum to 0)
+  bwd_torch      torch float64 autograd through an explicit masked softmax
   torch_sdpa     torch's float64 scaled_dot_product_attention on CPU, with
                  an explicit boolean mask built from the closed-form interval
 """
@@ -524,6 +532,127 @@ def pin_torch_sdpa():
     return True, "ok"
 
 
+def _fd_grads(loss, arrays, h=1e-6):
+    """Central differences of loss(*arrays) with respect to every element."""
+    out = []
+    for n, x in enumerate(arrays):
+        g = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args = [a.copy() for a in arrays]
+            args[n][idx] += h
+            lp = loss(*args)
+            args[n][idx] -= 2 * h
+            lm = loss(*args)
+            g[idx] = (lp - lm) / (2 * h)
+        out.append(g)
+    return out
+
+
+def pin_bwd_fd():
+    rng = _rng(31)
+    cases = [((1, 4, 6, 4, 2, 3), MASKS[1]), ((1, 5, 5, 2, 1, 3), MASKS[2]),
+             ((2, 3, 4, 2, 2, 2), MASKS[0]), ((1, 6, 3, 2, 1, 2), MASKS[1]),
+             ((1, 5, 7, 4, 2, 2), MASKS[3])]
+    # (B, Sq, Sk, Hq, Hkv, D); Sq 6 > Sk 3 causal leaves rows with no key
+    for (B, Sq, Sk, Hq, Hkv, D), mk in cases:
+        q = rng.standard_normal((B, Sq, Hq, D))
+        k = rng.standard_normal((B, Sk, Hkv, D))
+        v = rng.standard_normal((B, Sk, Hkv, D))
+        g = rng.standard_normal((B, Sq, Hq, D))
+
+        def loss(q, k, v):
+            o, _ = BR.attention_loops(q, k, v, 0.6, **mk)
+            return float((np.array(o) * g).sum())
+        want = _fd_grads(loss, [q, k, v])
+        got = A.attention_dense_backward(q, k, v, g, 0.6, **mk)
+        for name, a, b in zip("qkv", got, want):
+            ok, d = _close(a, b, 1e-6)
+            if not ok:
+                return False, f"{(B, Sq, Sk, Hq, Hkv, D)} {mk} d{name}: {d}"
+    return True, "ok"
+
+
+def pin_bwd_varlen():
+    rng = _rng(32)
+    cu_q = np.array([0, 3, 3, 7])
+    cu_k = np.array([0, 2, 5, 11])
+    Hq, Hkv, D = 2, 1, 2
+    q = rng.standard_normal((7, Hq, D))
+    k = rng.standard_normal((11, Hkv, D))
+    v = rng.standard_normal((11, Hkv, D))
+    g = rng.standard_normal((7, Hq, D))
+    for mk in (MASKS[1], MASKS[2]):
+        def loss(q, k, v):
+            o, _ = A.attention_varlen(q, k, v, cu_q, cu_k, 0.8, **mk)
+            return float((o * g).sum())
+        want = _fd_grads(loss, [q, k, v])
+        got = A.attention_varlen_backward(q, k, v, g, cu_q, cu_k, 0.8, **mk)
+        for name, a, b in zip("qkv", got, want):
+            ok, d = _close(a, b, 1e-6)
+            if not ok:
+                return False, f"varlen {mk} d{name}: {d}"
+    return True, "ok"
+
+
+def pin_bwd_closed():
+    rng = _rng(33)
+    B, Sq, Hq, Hkv, D = 2, 5, 4, 2, 3
+    q = rng.standard_normal((B, Sq, Hq, D))
+    k = rng.standard_normal((B, 1, Hkv, D))
+    v = rng.standard_normal((B, 1, Hkv, D))
+    g = rng.standard_normal((B, Sq, Hq, D))
+    dq, dk, dv = A.attention_dense_backward(q, k, v, g, 0.9)
+    want_dv = g.reshape(B, Sq, Hkv, Hq // Hkv, D).sum(axis=(1, 3))[:, None]
+    for name, a, b in (("dv", dv, want_dv), ("dq", dq, np.zeros_like(dq)),
+                       ("dk", dk, np.zeros_like(dk))):
+        ok, d = _close(a, b, 1e-12)
+        if not ok:
+            return False, f"one key {name}: {d}"
+    Sk = 6
+    k = rng.standard_normal((B, Sk, Hkv, D))
+    v = rng.standard_normal((B, Sk, Hkv, D))
+    for mk in (MASKS[0], MASKS[1]):
+        _, dk, _ = A.attention_dense_backward(q, k, v, g, 0.9, **mk)
+        ok, d = _close(dk.sum(axis=1), np.zeros((B, Hkv, D)), 1e-12)
+        if not ok:
+            return False, f"sum of dK over keys {mk}: {d}"
+    return True, "ok"
+
+
+def pin_bwd_torch():
+    import torch
+    rng = _rng(34)
+    B, Sq, Sk, Hq, Hkv, D = 2, 6, 9, 4, 2, 5
+    r = Hq // Hkv
+    for mk in (MASKS[0], MASKS[1], MASKS[2]):
+        q = rng.standard_normal((B, Sq, Hq, D))
+        k = rng.standard_normal((B, Sk, Hkv, D))
+        v = rng.standard_normal((B, Sk, Hkv, D))
+        g = rng.standard_normal((B, Sq, Hq, D))
+        mask = np.zeros((Sq, Sk), dtype=bool)
+        for i in range(Sq):
+            n, lo, hi = interval_count(i, Sq, Sk, mk["causal"], mk["window_left"],
+                                       mk["window_right"])
+            if n > 0:
+                mask[i, lo:hi + 1] = True
+        tq = torch.from_numpy(q.copy()).requires_grad_()
+        tk = torch.from_numpy(k.copy()).requires_grad_()
+        tv = torch.from_numpy(v.copy()).requires_grad_()
+        qh = tq.permute(0, 2, 1, 3)
+        kh = tk.repeat_interleave(r, dim=2).permute(0, 2, 1, 3)
+        vh = tv.repeat_interleave(r, dim=2).permute(0, 2, 1, 3)
+        s = torch.matmul(qh, kh.transpose(-1, -2)) * 0.5
+        s = s.masked_fill(~torch.from_numpy(mask), float("-inf"))
+        o = torch.matmul(torch.softmax(s, dim=-1), vh).permute(0, 2, 1, 3)
+        (o * torch.from_numpy(g)).sum().backward()
+        got = A.attention_dense_backward(q, k, v, g, 0.5, **mk)
+        for name, a, t in zip("qkv", got, (tq, tk, tv)):
+            ok, d = _close(a, t.grad.numpy(), 1e-10)
+            if not ok:
+                return False, f"{mk} d{name}: {d}"
+    return True, "ok"
+
+
 def pin_rows_match_full():
     rng = _rng(20)
     Sq, Sk, D = 9, 13, 4
@@ -559,6 +688,10 @@ ALL_PINS = {
     "sink_as_key": pin_sink_as_key,
     "sink_merge": pin_sink_merge,
     "descale": pin_descale,
+    "bwd_fd": pin_bwd_fd,
+    "bwd_varlen": pin_bwd_varlen,
+    "bwd_closed": pin_bwd_closed,
+    "bwd_torch": pin_bwd_torch,
     "torch_sdpa": pin_torch_sdpa,
     "rows_match_full": pin_rows_match_full,
 }

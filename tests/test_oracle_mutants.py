@@ -57,6 +57,19 @@ MUTANTS = [
      "kb = kb * np.asarray(v_descale, dtype=np.float64)[b][None, :, None]", "K scaled by the V descale"),
     ("paged_decode", "vb = vb * np.asarray(v_descale, dtype=np.float64)[b][None, :, None]",
      "vb = vb * np.asarray(v_descale, dtype=np.float64)[0][None, :, None]", "V descale of sequence 0 for all"),
+    ("attention_head_backward", "ds = p * (dp - dpsum[:, None])", "ds = p * dp",
+     "backward drops the dPsum term"),
+    ("attention_head_backward", "dq = scale * (ds @ k)", "dq = ds @ k", "dQ without the scale"),
+    ("attention_head_backward", "dk = scale * (ds.T @ q)", "dk = scale * (p.T @ q)",
+     "dK from P instead of dS"),
+    ("attention_head_backward", "dv = p.T @ dout", "dv = p.T @ dout[::-1]", "dO rows reversed"),
+    ("attention_dense_backward", "dk[b, :, g] += gk", "dk[b, :, g] = gk",
+     "GQA dK keeps only the last query head"),
+    ("attention_dense_backward", "vis = visible_mask(Sq, Sk, causal, window_left, window_right)",
+     "vis = visible_mask(Sq, Sk, False, None, None)", "backward ignores the mask"),
+    ("attention_varlen_backward", "k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])",
+     "k0, k1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])",
+     "backward key offsets from query cu"),
     ("paged_prefill", "sk = cap if seqused_k is None else int(seqused_k[b])", "sk = cap",
      "seqused_k ignored (paged prefill)"),
     ("paged_prefill", "vis = visible_mask(qb.shape[0], sk, causal, window_left, window_right)",
