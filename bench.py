@@ -205,6 +205,30 @@ class Decode:
                                        k_descale=self.kd, v_descale=self.vd)
 
 
+class Backward:
+    """mi_attn_bwd on a dense workload: the forward's out and LSE are made
+    once, outside the timed calls; each call runs the three backward
+    launches (row sums of O dO, dQ, dK/dV)."""
+
+    def __init__(self, mi, w, torch):
+        import workloads as W
+        from tests.gpu_util import dev_bf16
+        self.mi, self.w = mi, w
+        self.q, self.k, self.v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+        self.kw = dict(softmax_scale=w.softmax_scale, causal=w.causal,
+                       window_left=w.window_left, window_right=w.window_right)
+        self.out, self.lse = mi.mi_attn_fwd(self.q, self.k, self.v, **self.kw)
+        self.g = dev_bf16(W.grad_output(w.seed, w.q.shape))
+        self.dq, self.dk, self.dv = (torch.empty_like(self.q), torch.empty_like(self.k),
+                                     torch.empty_like(self.v))
+        nb = mi.mi_attn_bwd_workspace_bytes(self.q, self.k, self.v, self.out, self.g, self.lse)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        self.mi.mi_attn_bwd(self.q, self.k, self.v, self.out, self.g, self.lse, dq=self.dq,
+                            dk=self.dk, dv=self.dv, workspace=self.ws, **self.kw)
+
+
 def time_launches(torch, fn, n):
     """Per-launch durations (ms) from HIP events on the launch stream."""
     stream = torch.cuda.current_stream()
@@ -341,6 +365,20 @@ def main():
             log(f"[bench] {wi.name}: {med * 1e3:.1f} us, {extra[wi.name]['tflops']:.1f} TFLOP/s")
             del p
             torch.cuda.empty_cache()
+        # backward of the causal GQA S4096 D128 workload; algorithmic flops
+        # 2.5x the forward's (five tile products per score tile against two)
+        wb = W.standard_config(2)
+        bw = Backward(mi, wb, torch)
+        warm_up(torch, bw)
+        ms = sorted(time_launches(torch, bw, max(5, args.steps // 2)))
+        med = ms[len(ms) // 2]
+        f = 2.5 * prefill_flops(wb)
+        name = "backward_" + wb.name
+        extra[name] = {"median_us": med * 1e3, "tflops": f / (med * 1e-3) / 1e12,
+                       "frac": f / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        log(f"[bench] {name}: {med * 1e3:.1f} us, {extra[name]['tflops']:.1f} TFLOP/s")
+        del bw
+        torch.cuda.empty_cache()
         # the paged decode workload with an fp8 cache, e4m3 then e5m2
         # (per-(batch, KV head) descales): half the K/V bytes
         del dec

@@ -10,6 +10,7 @@ to load, every call raises.
 
 Entry points (same names as the C ABI):
   mi_attn_fwd(q, k, v, ...)              -> (out, lse)
+  mi_attn_bwd(q, k, v, out, dout, lse, ...) -> (dq, dk, dv)
   mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, ...) -> (out, lse)
   mi_attn_combine(o_partial, lse_partial, ...) -> (out, lse)
   mi_attn_decode_workspace_bytes(...), mi_attn_decode_num_splits(...)
@@ -22,7 +23,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "MiAttnError", "load", "lib_path", "mi_attn_fwd", "mi_attn_decode_splitkv",
+    "MiAttnError", "load", "lib_path", "mi_attn_fwd", "mi_attn_bwd", "mi_attn_bwd_workspace_bytes",
+    "BwdParams", "mi_attn_decode_splitkv",
     "mi_attn_combine", "mi_attn_decode_workspace_bytes", "mi_attn_decode_num_splits",
     "mi_attn_last_error", "mi_attn_version", "FwdParams", "DecodeParams",
     "MI_ATTN_OK", "MI_ATTN_EINVAL", "MI_ATTN_EUNSUPPORTED", "MI_ATTN_EBOUNDS",
@@ -81,6 +83,23 @@ class FwdParams(ctypes.Structure):
     ]
 
 
+class BwdParams(ctypes.Structure):
+    """Mirror of mi_attn_bwd_params (field order and types must match the header)."""
+    _fields_ = [
+        ("q", _vp), ("k", _vp), ("v", _vp), ("out", _vp), ("dout", _vp), ("lse", _fp),
+        ("dq", _vp), ("dk", _vp), ("dv", _vp),
+        *[(f"{t}_{w}_stride", _i64) for t in ("q", "k", "v", "o", "do", "dq", "dk", "dv")
+          for w in ("batch", "row", "head")],
+        ("batch", _i32), ("seqlen_q", _i32), ("seqlen_k", _i32),
+        ("num_heads_q", _i32), ("num_heads_kv", _i32), ("head_dim", _i32),
+        ("cu_seqlens_q", _vp), ("cu_seqlens_k", _vp),
+        ("total_q", _i32), ("max_seqlen_q", _i32), ("max_seqlen_k", _i32),
+        ("softmax_scale", ctypes.c_float),
+        ("causal", _i32), ("window_left", _i32), ("window_right", _i32),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class DecodeParams(ctypes.Structure):
     """Mirror of mi_attn_decode_params."""
     _fields_ = [
@@ -121,6 +140,10 @@ def load(path: Optional[str] = None):
     lib.mi_attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.mi_attn_decode_num_splits.argtypes = [ctypes.POINTER(DecodeParams)]
     lib.mi_attn_decode_num_splits.restype = ctypes.c_int
+    lib.mi_attn_bwd.argtypes = [ctypes.POINTER(BwdParams), _vp]
+    lib.mi_attn_bwd.restype = ctypes.c_int
+    lib.mi_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(BwdParams)]
+    lib.mi_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.mi_attn_combine.argtypes = [_vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _vp]
     lib.mi_attn_combine.restype = ctypes.c_int
     lib.mi_attn_last_error.argtypes = []
@@ -306,6 +329,115 @@ def mi_attn_fwd(q, k, v, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=Non
     p.learnable_sink = _req_sink(learnable_sink, hq, dev)
     _check(lib.mi_attn_fwd(ctypes.byref(p), _stream_ptr(dev)))
     return out, lse
+
+
+def _bwd_params(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                max_seqlen_k, softmax_scale, causal, window_left, window_right):
+    """Checks shapes and fills BwdParams (no workspace yet)."""
+    import torch
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq),
+                 ("dk", dk), ("dv", dv)):
+        _req_bf16(n, t, dev)
+    varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
+    if varlen and (cu_seqlens_q is None or cu_seqlens_k is None):
+        raise MiAttnError(MI_ATTN_EINVAL, "cu_seqlens_q and cu_seqlens_k go together")
+    hq, d = q.shape[-2], q.shape[-1]
+    hkv = k.shape[-2]
+    if k.shape != v.shape or k.shape[-1] != d:
+        raise MiAttnError(MI_ATTN_EUNSUPPORTED, "k and v must match q's head_dim and each other")
+    for n, t, ref in (("out", out, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k),
+                      ("dv", dv, v)):
+        if t.shape != ref.shape:
+            raise MiAttnError(MI_ATTN_EINVAL, f"{n} must have shape {tuple(ref.shape)}")
+    p = BwdParams()
+    if varlen:
+        if q.dim() != 3 or k.dim() != 3:
+            raise MiAttnError(MI_ATTN_EINVAL, "varlen q/k/v must be (tokens, heads, head_dim)")
+        batch = cu_seqlens_q.shape[0] - 1
+        _req_i32("cu_seqlens_q", cu_seqlens_q, (batch + 1,), dev)
+        _req_i32("cu_seqlens_k", cu_seqlens_k, (batch + 1,), dev)
+        total_q = q.shape[0]
+        max_q = total_q if max_seqlen_q is None else int(max_seqlen_q)
+        max_k = k.shape[0] if max_seqlen_k is None else int(max_seqlen_k)
+        lse_shape = (hq, total_q)
+        p.cu_seqlens_q, p.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
+        p.total_q, p.max_seqlen_q, p.max_seqlen_k = total_q, max_q, max_k
+    else:
+        if q.dim() != 4 or k.dim() != 4:
+            raise MiAttnError(MI_ATTN_EINVAL, "dense q/k/v must be (batch, seqlen, heads, head_dim)")
+        batch, sq = q.shape[0], q.shape[1]
+        if k.shape[0] != batch:
+            raise MiAttnError(MI_ATTN_EINVAL, "q and k batch sizes differ")
+        lse_shape = (batch, hq, sq)
+        p.seqlen_q, p.seqlen_k = sq, k.shape[1]
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != lse_shape \
+            or lse.device != dev:
+        raise MiAttnError(MI_ATTN_EINVAL, f"lse must be contiguous float32 {lse_shape}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", out), ("do", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        st = t.stride()
+        if varlen:
+            setattr(p, f"{name}_row_stride", st[0])
+            setattr(p, f"{name}_head_stride", st[1])
+        else:
+            setattr(p, f"{name}_batch_stride", st[0])
+            setattr(p, f"{name}_row_stride", st[1])
+            setattr(p, f"{name}_head_stride", st[2])
+    p.q, p.k, p.v, p.out, p.dout, p.lse = (q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          out.data_ptr(), dout.data_ptr(), lse.data_ptr())
+    p.dq, p.dk, p.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    p.batch, p.num_heads_q, p.num_heads_kv, p.head_dim = batch, hq, hkv, d
+    p.softmax_scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    p.causal, p.window_left, p.window_right = int(bool(causal)), _win(window_left), _win(window_right)
+    return p
+
+
+def mi_attn_bwd_workspace_bytes(q, k, v, out, dout, lse, cu_seqlens_q=None, cu_seqlens_k=None,
+                                max_seqlen_q=None, max_seqlen_k=None, causal=False) -> int:
+    """Workspace bytes mi_attn_bwd needs for these tensors (raises if invalid)."""
+    lib = load()
+    p = _bwd_params(q, k, v, out, dout, lse, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                    max_seqlen_k, None, causal, None, None)
+    n = lib.mi_attn_bwd_workspace_bytes(ctypes.byref(p))
+    err = mi_attn_last_error()
+    if n == 0 and err:
+        raise MiAttnError(MI_ATTN_EINVAL if "supported" not in err else MI_ATTN_EUNSUPPORTED, err)
+    return int(n)
+
+
+def mi_attn_bwd(q, k, v, out, dout, lse, cu_seqlens_q=None, cu_seqlens_k=None,
+                max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                softmax_scale: Optional[float] = None, causal: bool = False,
+                window_left: Optional[int] = None, window_right: Optional[int] = None,
+                dq=None, dk=None, dv=None, workspace=None) -> Tuple:
+    """Backward of mi_attn_fwd (interface page, `_flash_attn_bwd` contract):
+    returns (dq, dk, dv) shaped like q, k, v, given the forward's out and lse
+    and the output gradient dout. Dense (B, S, H, D) or packed (T, H, D)
+    tensors with cu_seqlens_q/k as for mi_attn_fwd; head_dim 64 or 128; no
+    paged K/V or learnable sink. workspace: a uint8 device tensor of at least
+    mi_attn_bwd_workspace_bytes bytes, or None to allocate one.
+    """
+    import torch
+    lib = load()
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    p = _bwd_params(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                    max_seqlen_k, softmax_scale, causal, window_left, window_right)
+    need = lib.mi_attn_bwd_workspace_bytes(ctypes.byref(p))
+    err = mi_attn_last_error()
+    if need == 0 and err:
+        _check(lib.mi_attn_bwd(ctypes.byref(p), _stream_ptr(dev)))  # raises with the status
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda or workspace.device != dev:
+            raise MiAttnError(MI_ATTN_EINVAL, f"workspace must be a uint8 tensor on {dev}")
+        p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    _check(lib.mi_attn_bwd(ctypes.byref(p), _stream_ptr(dev)))
+    return dq, dk, dv
 
 
 def _decode_params(q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,

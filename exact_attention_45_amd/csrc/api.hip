@@ -8,6 +8,7 @@
 
 #include <algorithm>
 
+#include "bwd.hpp"
 #include "kernels.hpp"
 #include "mi_attn.h"
 
@@ -367,6 +368,156 @@ int mi_attn_combine(const float* o_partial, const float* lse_partial, void* out,
   hipError_t e = by_dim(head_dim, [&](auto dc) {
     return mi_attn::launch_combine<decltype(dc)::value>(cb, s);
   });
+  if (e != hipSuccess) return fail(MI_ATTN_EHIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Backward: shape, scalar and stride checks, then BwdArgs (enough to size
+// the workspace; pointers are checked only to launch).
+int check_bwd(const mi_attn_bwd_params* p, mi_attn::BwdArgs* a) {
+  if (p == nullptr) return fail(MI_ATTN_EINVAL, "params is NULL");
+  const bool varlen = p->cu_seqlens_q != nullptr || p->cu_seqlens_k != nullptr;
+  if (varlen && (p->cu_seqlens_q == nullptr || p->cu_seqlens_k == nullptr))
+    return fail(MI_ATTN_EINVAL, "cu_seqlens_q and cu_seqlens_k must both be given");
+  if (p->batch < 0 || p->num_heads_q <= 0 || p->num_heads_kv <= 0)
+    return fail(MI_ATTN_EINVAL, "batch must be >= 0 and head counts > 0");
+  if (p->num_heads_q % p->num_heads_kv != 0)
+    return fail(MI_ATTN_EINVAL, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
+                p->num_heads_q, p->num_heads_kv);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(MI_ATTN_EUNSUPPORTED, "backward head_dim %d not supported (64, 128)",
+                p->head_dim);
+  if (!isfinite(p->softmax_scale) || p->softmax_scale < 0.0f)
+    return fail(MI_ATTN_EUNSUPPORTED, "softmax_scale must be finite and >= 0");
+  int max_q, max_k;
+  if (varlen) {
+    if (p->max_seqlen_q < 0 || p->max_seqlen_k < 0 || p->total_q < 0)
+      return fail(MI_ATTN_EINVAL, "max_seqlen_q/k and total_q must be >= 0 for varlen");
+    max_q = p->max_seqlen_q;
+    max_k = p->max_seqlen_k;
+  } else {
+    if (p->seqlen_q < 0 || p->seqlen_k < 0)
+      return fail(MI_ATTN_EINVAL, "seqlen_q and seqlen_k must be >= 0");
+    max_q = p->seqlen_q;
+    max_k = p->seqlen_k;
+  }
+  const int group = p->num_heads_q / p->num_heads_kv;
+  if ((int64_t)max_q * group > INT32_MAX - mi_attn::kBwdBlockM ||
+      (int64_t)max_k > INT32_MAX - mi_attn::kBwdBlockN)
+    return fail(MI_ATTN_EINVAL, "sequence lengths overflow int32");
+  if (p->batch > 65535 || p->num_heads_kv > 65535)
+    return fail(MI_ATTN_EINVAL, "batch and num_heads_kv must be <= 65535");
+  const int64_t rs[] = {p->q_row_stride, p->k_row_stride, p->v_row_stride, p->o_row_stride,
+                        p->do_row_stride, p->dq_row_stride, p->dk_row_stride, p->dv_row_stride};
+  const int64_t hs[] = {p->q_head_stride, p->k_head_stride, p->v_head_stride,
+                        p->o_head_stride, p->do_head_stride, p->dq_head_stride,
+                        p->dk_head_stride, p->dv_head_stride};
+  for (int i = 0; i < 8; ++i) {
+    if (!stride_ok(rs[i]) || !stride_ok(hs[i]))
+      return fail(MI_ATTN_EINVAL, "row/head strides must be non-negative multiples of 8");
+    if (rs[i] < p->head_dim)
+      return fail(MI_ATTN_EINVAL, "row strides must be >= head_dim (rows may not overlap)");
+    if ((int64_t)mi_attn::kBwdTileM * rs[i] * 2 > INT32_MAX)
+      return fail(MI_ATTN_EINVAL, "row stride too large for 32-bit tile offsets");
+  }
+  if (!varlen) {
+    const int64_t bs[] = {p->q_batch_stride, p->k_batch_stride, p->v_batch_stride,
+                          p->o_batch_stride, p->do_batch_stride, p->dq_batch_stride,
+                          p->dk_batch_stride, p->dv_batch_stride};
+    for (int64_t s : bs)
+      if (!stride_ok(s))
+        return fail(MI_ATTN_EINVAL, "batch strides must be non-negative multiples of 8");
+  }
+  *a = mi_attn::BwdArgs{};
+  a->q = p->q;
+  a->k = p->k;
+  a->v = p->v;
+  a->o = p->out;
+  a->dout = p->dout;
+  a->lse = p->lse;
+  a->dq = p->dq;
+  a->dk = p->dk;
+  a->dv = p->dv;
+  a->q_bs = p->q_batch_stride;
+  a->q_rs = p->q_row_stride;
+  a->q_hs = p->q_head_stride;
+  a->k_bs = p->k_batch_stride;
+  a->k_rs = p->k_row_stride;
+  a->k_hs = p->k_head_stride;
+  a->v_bs = p->v_batch_stride;
+  a->v_rs = p->v_row_stride;
+  a->v_hs = p->v_head_stride;
+  a->o_bs = p->o_batch_stride;
+  a->o_rs = p->o_row_stride;
+  a->o_hs = p->o_head_stride;
+  a->do_bs = p->do_batch_stride;
+  a->do_rs = p->do_row_stride;
+  a->do_hs = p->do_head_stride;
+  a->dq_bs = p->dq_batch_stride;
+  a->dq_rs = p->dq_row_stride;
+  a->dq_hs = p->dq_head_stride;
+  a->dk_bs = p->dk_batch_stride;
+  a->dk_rs = p->dk_row_stride;
+  a->dk_hs = p->dk_head_stride;
+  a->dv_bs = p->dv_batch_stride;
+  a->dv_rs = p->dv_row_stride;
+  a->dv_hs = p->dv_head_stride;
+  a->cu_q = varlen ? p->cu_seqlens_q : nullptr;
+  a->cu_k = varlen ? p->cu_seqlens_k : nullptr;
+  a->batch = p->batch;
+  a->seqlen_q = max_q;
+  a->seqlen_k = max_k;
+  a->hq = p->num_heads_q;
+  a->hkv = p->num_heads_kv;
+  a->group = group;
+  a->total_q = varlen ? p->total_q : 0;
+  a->scale = p->softmax_scale;
+  a->scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  normalise_window(p->causal, p->window_left, p->window_right, &a->wl, &a->wr);
+  return MI_ATTN_OK;
+}
+
+size_t bwd_workspace_for(const mi_attn::BwdArgs& a) {
+  const int64_t n = mi_attn::bwd_dpsum_elems(a);
+  return n > 0 ? round_up((size_t)n * sizeof(float)) : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mi_attn_bwd_workspace_bytes(const mi_attn_bwd_params* p) {
+  mi_attn::BwdArgs a;
+  if (check_bwd(p, &a) != MI_ATTN_OK) return 0;
+  ok();
+  return bwd_workspace_for(a);
+}
+
+int mi_attn_bwd(const mi_attn_bwd_params* p, void* stream) {
+  mi_attn::BwdArgs a;
+  const int st = check_bwd(p, &a);
+  if (st != MI_ATTN_OK) return st;
+  if (p->batch == 0) return ok();
+  // no query rows: no workspace, and dk, dv are written as zeros
+  const size_t need = bwd_workspace_for(a);
+  if (!p->q || !p->k || !p->v || !p->out || !p->dout || !p->dq || !p->dk || !p->dv ||
+      (need > 0 && !p->lse))
+    return fail(MI_ATTN_EINVAL, "q, k, v, out, dout, lse, dq, dk and dv must be non-NULL");
+  const void* ptrs[] = {p->q, p->k, p->v, p->out, p->dout, p->dq, p->dk, p->dv};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return fail(MI_ATTN_EINVAL, "tensors must be 16-byte aligned");
+  if (need > 0 && (p->workspace == nullptr || p->workspace_bytes < need))
+    return fail(MI_ATTN_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                p->workspace == nullptr ? (size_t)0 : p->workspace_bytes);
+  if (need > 0 && !aligned16(p->workspace))
+    return fail(MI_ATTN_EINVAL, "workspace must be 16-byte aligned");
+  a.dpsum = need > 0 ? static_cast<float*>(p->workspace) : nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = p->head_dim == 64 ? mi_attn::launch_bwd<64>(a, s) : mi_attn::launch_bwd<128>(a, s);
   if (e != hipSuccess) return fail(MI_ATTN_EHIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

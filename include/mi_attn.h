@@ -251,6 +251,65 @@ int mi_attn_combine(const float *o_partial, const float *lse_partial, void *out,
                     int64_t out_row_stride, float *lse, int32_t rows, int32_t num_splits,
                     int32_t head_dim, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Backward pass of the prefill forward (Blackwell backward page
+ * flash_bwd_sm100.py and the interface page's `_flash_attn_bwd`): given the
+ * forward's inputs q, k, v, its output out and LSE, and the output gradient
+ * dout, writes dq, dk, dv for
+ *   P = exp(scale * q.k^T - LSE) over the visible keys,
+ *   dv = P^T dout,  dS = P * (dout v^T - rowsum(out * dout)),
+ *   dq = scale * dS k,  dk = scale * dS^T q,
+ * with dk / dv of a KV head summed over the query heads that read it (GQA).
+ *
+ * Layouts as mi_attn_fwd: q, out, dout, dq share the query layout (dense
+ * [batch, seqlen_q, heads, head_dim] or packed [total_q, heads, head_dim]
+ * with cu_seqlens_q), k, v, dk, dv the key layout, each with its own
+ * batch/row/head strides (elements; row and head strides non-negative
+ * multiples of 8, head_dim contiguous); every tensor bf16, 16-byte aligned.
+ * lse is the forward's float32 LSE in its layout ([batch, num_heads_q,
+ * seqlen_q] dense, [num_heads_q, total_q] packed); a row with LSE = -inf
+ * (no visible key) gets dq = 0 and contributes nothing to dk, dv. Masks
+ * (causal, window_left, window_right, bottom-right alignment) and
+ * softmax_scale mean what they mean for mi_attn_fwd; cu_seqlens_q and
+ * cu_seqlens_k are given together or not at all. Paged K/V and the
+ * learnable sink are not part of the backward.
+ *
+ * head_dim 64 or 128 (256 returns MI_ATTN_EUNSUPPORTED). The result is
+ * deterministic: nothing is accumulated with atomics. The caller owns every
+ * buffer, including the workspace (float32 row sums of out * dout, one per
+ * query row and head, size from mi_attn_bwd_workspace_bytes; a smaller one
+ * returns MI_ATTN_EWORKSPACE). Work is enqueued on `stream`; nothing is
+ * allocated and the stream is not synchronised.
+ * --------------------------------------------------------------------- */
+typedef struct {
+  const void *q, *k, *v, *out, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  int64_t q_batch_stride, q_row_stride, q_head_stride;
+  int64_t k_batch_stride, k_row_stride, k_head_stride;
+  int64_t v_batch_stride, v_row_stride, v_head_stride;
+  int64_t o_batch_stride, o_row_stride, o_head_stride;
+  int64_t do_batch_stride, do_row_stride, do_head_stride;
+  int64_t dq_batch_stride, dq_row_stride, dq_head_stride;
+  int64_t dk_batch_stride, dk_row_stride, dk_head_stride;
+  int64_t dv_batch_stride, dv_row_stride, dv_head_stride;
+  int32_t batch, seqlen_q, seqlen_k;
+  int32_t num_heads_q, num_heads_kv, head_dim;
+  const int32_t *cu_seqlens_q, *cu_seqlens_k; /* device, [batch+1], or NULL */
+  int32_t total_q;                            /* varlen: cu_seqlens_q[batch] */
+  int32_t max_seqlen_q, max_seqlen_k;         /* varlen: host upper bounds   */
+  float softmax_scale;
+  int32_t causal, window_left, window_right;
+  void *workspace;
+  size_t workspace_bytes;
+} mi_attn_bwd_params;
+
+/* Workspace bytes mi_attn_bwd needs for *p; 0 if *p is invalid
+ * (mi_attn_last_error() then says why) or needs none. */
+size_t mi_attn_bwd_workspace_bytes(const mi_attn_bwd_params *p);
+
+int mi_attn_bwd(const mi_attn_bwd_params *p, void *stream);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char *mi_attn_last_error(void);
 

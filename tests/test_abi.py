@@ -43,7 +43,8 @@ def test_exports_every_declared_symbol(lib):
 
 def test_struct_layout_matches_header():
     """Compiles a C program against the header and compares offsets with ctypes."""
-    structs = {"mi_attn_fwd_params": mi.FwdParams, "mi_attn_decode_params": mi.DecodeParams}
+    structs = {"mi_attn_fwd_params": mi.FwdParams, "mi_attn_decode_params": mi.DecodeParams,
+               "mi_attn_bwd_params": mi.BwdParams}
     lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void){"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
@@ -217,3 +218,58 @@ def test_combine_invalid_arguments(lib, args, code):
 
 def test_version(lib):
     assert "gfx950" in mi.mi_attn_version()
+
+
+def _bwd(**kw):
+    p = mi.BwdParams()
+    p.q = p.k = p.v = p.out = p.dout = p.lse = p.dq = p.dk = p.dv = FAKE
+    B, S, Hq, Hkv, D = 2, 1000, 8, 2, 128
+    for t, h in (("q", Hq), ("o", Hq), ("do", Hq), ("dq", Hq), ("k", Hkv), ("v", Hkv),
+                 ("dk", Hkv), ("dv", Hkv)):
+        setattr(p, f"{t}_batch_stride", S * h * D)
+        setattr(p, f"{t}_row_stride", h * D)
+        setattr(p, f"{t}_head_stride", D)
+    p.batch, p.seqlen_q, p.seqlen_k = B, S, S
+    p.num_heads_q, p.num_heads_kv, p.head_dim = Hq, Hkv, D
+    p.softmax_scale = 0.088
+    p.window_left = p.window_right = -1
+    p.workspace, p.workspace_bytes = FAKE, 1 << 30
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_bwd_workspace_size(lib):
+    # one float32 row sum per (batch, head, query), 256-byte rounded
+    assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(_bwd())) == -(-2 * 8 * 1000 * 4 // 256) * 256
+    p = _bwd(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, total_q=777, max_seqlen_q=500, max_seqlen_k=500)
+    assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(p)) == -(-8 * 777 * 4 // 256) * 256
+    assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(_bwd(head_dim=256))) == 0
+    assert "head_dim" in mi.mi_attn_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=256), mi.MI_ATTN_EUNSUPPORTED),
+    (dict(head_dim=96), mi.MI_ATTN_EUNSUPPORTED),
+    (dict(num_heads_q=7), mi.MI_ATTN_EINVAL),
+    (dict(dout=0), mi.MI_ATTN_EINVAL),
+    (dict(dk=FAKE + 4), mi.MI_ATTN_EINVAL),
+    (dict(do_row_stride=100), mi.MI_ATTN_EINVAL),
+    (dict(dq_head_stride=-8), mi.MI_ATTN_EINVAL),
+    (dict(dv_row_stride=64), mi.MI_ATTN_EINVAL),           # rows would overlap (< head_dim)
+    (dict(cu_seqlens_k=FAKE), mi.MI_ATTN_EINVAL),          # cu_seqlens go together
+    (dict(softmax_scale=float("inf")), mi.MI_ATTN_EUNSUPPORTED),
+    (dict(seqlen_k=-1), mi.MI_ATTN_EINVAL),
+    (dict(workspace=0), mi.MI_ATTN_EWORKSPACE),
+    (dict(workspace_bytes=100), mi.MI_ATTN_EWORKSPACE),
+    (dict(batch=70000), mi.MI_ATTN_EINVAL),
+])
+def test_bwd_invalid_arguments(lib, kw, code):
+    rc = lib.mi_attn_bwd(ctypes.byref(_bwd(**kw)), None)
+    assert rc == code, (rc, mi.mi_attn_last_error())
+    assert mi.mi_attn_last_error()
+
+
+def test_bwd_null_and_empty(lib):
+    assert lib.mi_attn_bwd(None, None) == mi.MI_ATTN_EINVAL
+    assert lib.mi_attn_bwd(ctypes.byref(_bwd(batch=0)), None) == mi.MI_ATTN_OK

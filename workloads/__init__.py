@@ -125,6 +125,13 @@ def dense_case(seed: int, batch: int, seqlen_q: int, seqlen_k: int, hq: int, hkv
                     seqlen_k=seqlen_k, max_seqlen_q=seqlen_q, max_seqlen_k=seqlen_k, seed=seed)
 
 
+def grad_output(seed: int, shape) -> np.ndarray:
+    """Output gradient dO for a backward workload: bf16 N(0, 1) bit patterns of
+    the given shape (the forward output's), from its own generator seeded with
+    seed + 7919 so the forward inputs of the same seed are unchanged."""
+    return _normal_bf16(np.random.default_rng(seed + 7919), shape)
+
+
 def _cu(lengths) -> np.ndarray:
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
