@@ -481,9 +481,13 @@ int check_bwd(const mi_attn_bwd_params* p, mi_attn::BwdArgs* a) {
   return MI_ATTN_OK;
 }
 
-size_t bwd_workspace_for(const mi_attn::BwdArgs& a) {
+// Workspace: dPsum (float32 per query row and head), then the dK/dV split
+// partials when the walk is split.
+size_t bwd_workspace_for(const mi_attn::BwdArgs& a, int head_dim) {
   const int64_t n = mi_attn::bwd_dpsum_elems(a);
-  return n > 0 ? round_up((size_t)n * sizeof(float)) : 0;
+  if (n <= 0) return 0;
+  const int64_t parts = mi_attn::bwd_part_elems(a, mi_attn::bwd_splits(a), head_dim);
+  return round_up((size_t)n * sizeof(float)) + round_up((size_t)parts * sizeof(float));
 }
 
 }  // namespace
@@ -494,7 +498,7 @@ size_t mi_attn_bwd_workspace_bytes(const mi_attn_bwd_params* p) {
   mi_attn::BwdArgs a;
   if (check_bwd(p, &a) != MI_ATTN_OK) return 0;
   ok();
-  return bwd_workspace_for(a);
+  return bwd_workspace_for(a, p->head_dim);
 }
 
 int mi_attn_bwd(const mi_attn_bwd_params* p, void* stream) {
@@ -503,7 +507,7 @@ int mi_attn_bwd(const mi_attn_bwd_params* p, void* stream) {
   if (st != MI_ATTN_OK) return st;
   if (p->batch == 0) return ok();
   // no query rows: no workspace, and dk, dv are written as zeros
-  const size_t need = bwd_workspace_for(a);
+  const size_t need = bwd_workspace_for(a, p->head_dim);
   if (!p->q || !p->k || !p->v || !p->out || !p->dout || !p->dq || !p->dk || !p->dv ||
       (need > 0 && !p->lse))
     return fail(MI_ATTN_EINVAL, "q, k, v, out, dout, lse, dq, dk and dv must be non-NULL");
@@ -516,6 +520,11 @@ int mi_attn_bwd(const mi_attn_bwd_params* p, void* stream) {
   if (need > 0 && !aligned16(p->workspace))
     return fail(MI_ATTN_EINVAL, "workspace must be 16-byte aligned");
   a.dpsum = need > 0 ? static_cast<float*>(p->workspace) : nullptr;
+  a.splits = need > 0 ? mi_attn::bwd_splits(a) : 1;
+  a.dkv_part = a.splits > 1 ? reinterpret_cast<float*>(
+                                  static_cast<char*>(p->workspace) +
+                                  round_up((size_t)mi_attn::bwd_dpsum_elems(a) * sizeof(float)))
+                            : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = p->head_dim == 64 ? mi_attn::launch_bwd<64>(a, s) : mi_attn::launch_bwd<128>(a, s);
   if (e != hipSuccess) return fail(MI_ATTN_EHIP, "launch failed: %s", hipGetErrorString(e));

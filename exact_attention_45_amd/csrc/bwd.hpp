@@ -21,6 +21,10 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dpsum;  // workspace: row sums of O * dO
+  // workspace when splits > 1: float32 dK / dV partials of each split,
+  // [splits][batch][seqlen_k][hkv][2][head_dim] (seqlen_k: the maximum)
+  float* dkv_part;
+  int32_t splits;  // workgroups sharing one key block's walk over the queries
   int64_t q_bs, q_rs, q_hs;
   int64_t k_bs, k_rs, k_hs;
   int64_t v_bs, v_rs, v_hs;
@@ -40,7 +44,7 @@ struct BwdArgs {
 };
 
 constexpr int kBwdBlockM = 128;   // dQ kernel: packed query rows per workgroup
-constexpr int kBwdBlockN = 128;   // dK/dV kernel: keys per workgroup
+constexpr int kBwdBlockN = 128;   // dK/dV kernel: keys per workgroup (32 per wave)
 constexpr int kBwdTileM = 64;     // dK/dV kernel: queries per step
 constexpr int kBwdTileN = 64;     // dQ kernel: keys per step
 
@@ -48,6 +52,21 @@ constexpr int kBwdTileN = 64;     // dQ kernel: keys per step
 inline int64_t bwd_dpsum_elems(const BwdArgs& a) {
   return a.cu_q != nullptr ? (int64_t)a.hq * a.total_q
                            : (int64_t)a.batch * a.hq * a.seqlen_q;
+}
+
+// Splits of the dK/dV walk: enough workgroups for about two per compute
+// unit of a 256-unit device, at most four (each split adds a float32 partial
+// of dK and dV to write and reduce).
+inline int bwd_splits(const BwdArgs& a) {
+  const int64_t nblocks = ((int64_t)a.seqlen_k + kBwdBlockN - 1) / kBwdBlockN;
+  const int64_t wg = nblocks * a.hkv * a.batch;
+  if (wg <= 0 || a.batch > 16383) return 1;
+  const int64_t s = (512 + wg - 1) / wg;
+  return (int)(s < 1 ? 1 : (s > 4 ? 4 : s));
+}
+
+inline int64_t bwd_part_elems(const BwdArgs& a, int splits, int head_dim) {
+  return splits > 1 ? (int64_t)splits * a.batch * a.seqlen_k * a.hkv * 2 * head_dim : 0;
 }
 
 template <int D>

@@ -7,17 +7,20 @@
 // O * dO, and its postprocess scales and, with GQA, sums dK/dV over the
 // query heads of a KV head).
 //
-// Three launches, no atomics, deterministic:
+// Three or four launches, no atomics, deterministic:
 //   bwd_pre_kernel   dPsum[row] = sum_d O[row, d] dO[row, d]  (float32 workspace)
 //   bwd_dq_kernel    one workgroup per 128 packed query rows (as the forward
 //                    packs GQA heads): walks the visible 64-key tiles, per
 //                    tile S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - dPsum),
 //                    dQ^T += K^T dS^T; dQ is written once, scaled
-//   bwd_dkdv_kernel  one workgroup per 128 keys of a KV head: walks every
-//                    query head of the group and its visible 64-query tiles,
-//                    per tile S = Q K^T, dP = dO V^T, dS = P (dP - dPsum),
-//                    dV^T += dO^T P, dK^T += Q^T dS; dK (scaled) and dV are
-//                    written once, already summed over the group
+//   bwd_dkdv_kernel  one workgroup per 128 keys of a KV head (32 per wave)
+//                    and split: walks its part of (query head of the group,
+//                    visible 64-query tile), per tile S = Q K^T, dP = dO V^T,
+//                    dS = P (dP - dPsum), dV^T += dO^T P, dK^T += Q^T dS;
+//                    with one split dK (scaled) and dV are written once,
+//                    already summed over the group; with several, float32
+//                    partials go to the workspace and
+//   bwd_dkv_reduce_kernel  sums them in split order (deterministic)
 // S and dP are recomputed in both kernels (seven tile products per score
 // tile instead of five) in exchange for no dQ accumulation buffer and no
 // atomic traffic.
@@ -247,14 +250,30 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdArgs a) {
       s[kb] = zero_f32x16();
       dp[kb] = zero_f32x16();
     }
+    {
+      // MFMA i: contraction step i / 4, key block (i / 2) % 2; even i: S^T
+      // from K rows, odd i: dP^T from V rows
+      constexpr int N = 4 * (D / 16), LEAD = 6;
+      auto rdf = [&](int i) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>((i & 1 ? vt : kt) + ((i >> 1) & 1) * 32 * ROW_B +
+                                                rd[i >> 2]);
+      };
+      bf16x8 ring[LEAD];
 #pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc)
+      for (int i = 0; i < LEAD; ++i) ring[i] = rdf(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int ro = kb * 32 * ROW_B + rd[cc];
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kt + ro), qf[cc], s[kb]);
-        dp[kb] = mfma32(*reinterpret_cast<const bf16x8*>(vt + ro), gf[cc], dp[kb]);
+      for (int i = 0; i < N; ++i) {
+        const bf16x8 f = ring[i % LEAD];
+        if (i + LEAD < N) ring[i % LEAD] = rdf(i + LEAD);
+        const int kb = (i >> 1) & 1;
+        if (i & 1)
+          dp[kb] = mfma32(f, gf[i >> 2], dp[kb]);
+        else
+          s[kb] = mfma32(f, qf[i >> 2], s[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
     // element (kb, v) holds key n0 + 4*half + 32*kb + 8*(v>>2) + (v&3)
     const uint64_t vis = vis64(lo - n0 - 4 * half, hi - n0 - 4 * half);
 #pragma unroll
@@ -269,11 +288,21 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdArgs a) {
     }
     bf16x8 dsf[4];
     acc_to_frags(s, dsf);
+    {
+      // MFMA i: 16-key step i / NDB, d-block i % NDB
+      constexpr int NDB = D / 32, N = 4 * NDB, LEAD = 4;
+      bf16x8 ring[LEAD];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int i = 0; i < LEAD; ++i) ring[i] = tr_frag<ROW_B>(kt, tr, i / NDB, i % NDB);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        dqa[db] = mfma32(tr_frag<ROW_B>(kt, tr, t, db), dsf[t], dqa[db]);
+      for (int i = 0; i < N; ++i) {
+        const bf16x8 f = ring[i % LEAD];
+        if (i + LEAD < N) ring[i % LEAD] = tr_frag<ROW_B>(kt, tr, (i + LEAD) / NDB, (i + LEAD) % NDB);
+        dqa[i % NDB] = mfma32(f, dsf[i / NDB], dqa[i % NDB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
 
   if (n_end > n_begin) {
@@ -305,19 +334,27 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------- dK dV ----
 
+// One workgroup per 128 keys of a KV head (32 per wave) and split: the walk
+// over (query head of the group, 64-query tile) is cut into `splits`
+// contiguous parts, one per workgroup; every wave reads the whole staged
+// tile. With one split dK (scaled) and dV are written as bf16; otherwise
+// each split writes float32 partials that bwd_dkv_reduce_kernel sums in
+// split order.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_dkdv_kernel(const BwdArgs a) {
-  using T = BwdTile<D>;
-  constexpr int ROW_B = T::ROW_B, CPR = T::CPR, TILE_B = T::TILE_B, NL = T::NL;
+  constexpr int ROW_B = D * 2, CPR = D / 8;
   constexpr int BNK = kBwdBlockN, BM = kBwdTileM;
-  static_assert(BM == T::ROWS, "one staged tile per query step");
+  static_assert(BNK == 128 && BM == 64, "four 32-key waves, 64-query tiles");
+  constexpr int TILE_B = BM * ROW_B;
+  constexpr int NL = BM * CPR / 256;  // 16-byte chunks per thread per tile
   // Q tile, dO tile, then LSE*log2e and dPsum of the tile's 64 queries
   __shared__ __attribute__((aligned(16))) char smem[2 * TILE_B + 2 * BM * 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, half = lane >> 5;
-  const int nb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int S = a.splits;
+  const int nb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z / S, sp = blockIdx.z - b * S;
 
   int sq = a.seqlen_q, sk = a.seqlen_k, q_tok0 = 0;
   int64_t q_base, do_base, k_base, v_base, dk_base, dv_base;
@@ -354,15 +391,16 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int r = a.group;
   const int off = sk - sq;
   // queries that see key j: j - off - wr <= i <= j - off + wl, 0 <= i < sq
-  int qlo = a.wr >= 0 ? max(0, kk - off - a.wr) : 0;
-  int qhi = a.wl >= 0 ? min(sq - 1, kk - off + a.wl) : sq - 1;
-  if (!kvalid) qhi = qlo - 1;
+  const int qlo = a.wr >= 0 ? max(0, kk - off - a.wr) : 0;
+  const int qhi = kvalid ? (a.wl >= 0 ? min(sq - 1, kk - off + a.wl) : sq - 1) : qlo - 1;
   const int j1 = min(sk, j0 + BNK) - 1;
   const int i_lo = uniform(a.wr >= 0 ? max(0, j0 - off - a.wr) : 0);
   const int i_hi = uniform(a.wl >= 0 ? min(sq - 1, j1 - off + a.wl) : sq - 1);
   const int m_begin = i_lo / BM;
   const int nm = i_hi >= i_lo ? i_hi / BM - m_begin + 1 : 0;
-  const int n_it = uniform(nm * r);
+  const int n_all = nm * r;
+  const int it_begin = uniform((int)((int64_t)n_all * sp / S));
+  const int it_end = uniform((int)((int64_t)n_all * (sp + 1) / S));
 
   // this lane's key: K^T and V^T fragments (B operands)
   const __bf16* kp = static_cast<const __bf16*>(a.k) + k_base + (int64_t)kk * a.k_rs +
@@ -412,17 +450,17 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       qreg[i] = buf_ld16(qr, gq[i]);
       dreg[i] = buf_ld16(gr, gd[i]);
     }
-    if (tid < 2 * BM) {
-      const int qi = m0 + (tid & (BM - 1));
-      const int64_t li = a.cu_q != nullptr ? (int64_t)h * a.total_q + q_tok0 + qi
-                                           : ((int64_t)b * a.hq + h) * sq + qi;
-      if (tid < BM) {
-        const float l = qi < sq ? a.lse[li] : kNegInf;
-        sreg = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
-      } else {
-        sreg = qi < sq ? a.dpsum[li] : 0.0f;
-      }
-    }
+    // branch-free (a load under a divergent branch makes the compiler wait
+    // for every outstanding load, the tile prefetch included): every thread
+    // reads both arrays at a clamped row and keeps one value
+    const int qi = m0 + (tid & (BM - 1));
+    const int qc = min(qi, sq - 1);
+    const int64_t li = a.cu_q != nullptr ? (int64_t)h * a.total_q + q_tok0 + qc
+                                         : ((int64_t)b * a.hq + h) * sq + qc;
+    const float l = a.lse[li];
+    const float dps = a.dpsum[li];
+    const float l2 = (qi >= sq || l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
+    sreg = (tid & BM) == 0 ? l2 : (qi < sq ? dps : 0.0f);
   };
   auto store = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -450,14 +488,30 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       s[qb] = zero_f32x16();
       dp[qb] = zero_f32x16();
     }
+    {
+      // MFMA i: contraction step i / 4, query block (i / 2) % 2; even i: S
+      // from Q rows, odd i: dP from dO rows
+      constexpr int N = 4 * (D / 16), LEAD = 6;
+      auto rdf = [&](int i) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>((i & 1 ? gt : qt) + ((i >> 1) & 1) * 32 * ROW_B +
+                                                rd[i >> 2]);
+      };
+      bf16x8 ring[LEAD];
 #pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc)
+      for (int i = 0; i < LEAD; ++i) ring[i] = rdf(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int ro = qb * 32 * ROW_B + rd[cc];
-        s[qb] = mfma32(*reinterpret_cast<const bf16x8*>(qt + ro), kf[cc], s[qb]);
-        dp[qb] = mfma32(*reinterpret_cast<const bf16x8*>(gt + ro), vf[cc], dp[qb]);
+      for (int i = 0; i < N; ++i) {
+        const bf16x8 f = ring[i % LEAD];
+        if (i + LEAD < N) ring[i % LEAD] = rdf(i + LEAD);
+        const int qb = (i >> 1) & 1;
+        if (i & 1)
+          dp[qb] = mfma32(f, vf[i >> 2], dp[qb]);
+        else
+          s[qb] = mfma32(f, kf[i >> 2], s[qb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
     // element (qb, v) holds query m0 + 4*half + 32*qb + 8*(v>>2) + (v&3), key `key`
     const uint64_t vis = vis64(qlo - m0 - 4 * half, qhi - m0 - 4 * half);
 #pragma unroll
@@ -481,28 +535,45 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     bf16x8 pf[4], dsf[4];
     acc_to_frags(s, pf);
     acc_to_frags(dp, dsf);
+    {
+      // MFMA i: (t, db) = (i / (2 NDB), (i / 2) % NDB); even i: dV from
+      // dO^T, odd i: dK from Q^T
+      constexpr int NDB = D / 32, N = 8 * NDB, LEAD = 4;
+      auto rdf = [&](int i) __attribute__((always_inline)) {
+        return tr_frag<ROW_B>(i & 1 ? qt : gt, tr, i / (2 * NDB), (i >> 1) % NDB);
+      };
+      bf16x8 ring[LEAD];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int i = 0; i < LEAD; ++i) ring[i] = rdf(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        dva[db] = mfma32(tr_frag<ROW_B>(gt, tr, t, db), pf[t], dva[db]);
-        dka[db] = mfma32(tr_frag<ROW_B>(qt, tr, t, db), dsf[t], dka[db]);
+      for (int i = 0; i < N; ++i) {
+        const bf16x8 f = ring[i % LEAD];
+        if (i + LEAD < N) ring[i % LEAD] = rdf(i + LEAD);
+        const int t = i / (2 * NDB), db = (i >> 1) % NDB;
+        if (i & 1)
+          dka[db] = mfma32(f, dsf[t], dka[db]);
+        else
+          dva[db] = mfma32(f, pf[t], dva[db]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
   };
 
-  if (n_it > 0) {
-    load(0);
-    for (int it = 0; it < n_it; ++it) {
+  if (it_end > it_begin) {
+    load(it_begin);
+    for (int it = it_begin; it < it_end; ++it) {
       __syncthreads();  // every wave is done with the previous tile
       store();
       __syncthreads();
       const int m0 = uniform((m_begin + it % nm) * BM);
-      if (it + 1 < n_it) load(it + 1);
+      if (it + 1 < it_end) load(it + 1);
       compute(m0);
     }
   }
 
-  if (kvalid) {
+  if (!kvalid) return;
+  if (S == 1) {
     __bf16* dkp = static_cast<__bf16*>(a.dk) + dk_base + (int64_t)key * a.dk_rs +
                   (int64_t)hk * a.dk_hs;
     __bf16* dvp = static_cast<__bf16*>(a.dv) + dv_base + (int64_t)key * a.dv_rs +
@@ -519,7 +590,59 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         *reinterpret_cast<bf16x4*>(dvp + d0) =
             cvt4(dva[db][4 * i], dva[db][4 * i + 1], dva[db][4 * i + 2], dva[db][4 * i + 3]);
       }
+  } else {
+    // partial row (split, sequence, key, KV head): dK then dV, D floats each
+    float* pp = a.dkv_part +
+                ((((int64_t)sp * a.batch + b) * a.seqlen_k + key) * a.hkv + hk) * (2 * D);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * half;
+        *reinterpret_cast<f32x4*>(pp + d0) =
+            f32x4{dka[db][4 * i], dka[db][4 * i + 1], dka[db][4 * i + 2], dka[db][4 * i + 3]};
+        *reinterpret_cast<f32x4*>(pp + D + d0) =
+            f32x4{dva[db][4 * i], dva[db][4 * i + 1], dva[db][4 * i + 2], dva[db][4 * i + 3]};
+      }
   }
+}
+
+// Sums the splits' float32 partials in split order (deterministic), scales
+// dK, and writes dK and dV as bf16. One thread per 4 floats of a partial row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(const BwdArgs a) {
+  constexpr int CH = D / 2;  // float4 chunks per partial row (dK then dV)
+  const int64_t rows = (int64_t)a.batch * a.seqlen_k * a.hkv;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= rows * CH) return;
+  const int64_t row = e / CH;
+  const int cidx = (int)(e - row * CH);
+  const int hk = (int)(row % a.hkv);
+  const int64_t bk = row / a.hkv;
+  const int key = (int)(bk % a.seqlen_k);
+  const int b = (int)(bk / a.seqlen_k);
+  int sk = a.seqlen_k;
+  int64_t kb;
+  const bool is_v = cidx >= CH / 2;
+  const int d0 = 4 * (cidx - (is_v ? CH / 2 : 0));
+  if (a.cu_k != nullptr) {
+    sk = a.cu_k[b + 1] - a.cu_k[b];
+    kb = (int64_t)(a.cu_k[b] + key) * (is_v ? a.dv_rs : a.dk_rs);
+  } else {
+    kb = (int64_t)b * (is_v ? a.dv_bs : a.dk_bs) + (int64_t)key * (is_v ? a.dv_rs : a.dk_rs);
+  }
+  if (key >= sk) return;
+  const int64_t stride = (int64_t)a.batch * a.seqlen_k * a.hkv * (2 * D);
+  const float* src = a.dkv_part + row * (2 * D) + (is_v ? D : 0) + d0;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+  for (int s = 1; s < a.splits; ++s) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(src + s * stride);
+    acc += x;
+  }
+  const float sc = is_v ? 1.0f : a.scale;
+  __bf16* dst = static_cast<__bf16*>(is_v ? a.dv : a.dk) + kb +
+                (int64_t)hk * (is_v ? a.dv_hs : a.dk_hs) + d0;
+  *reinterpret_cast<bf16x4*>(dst) = cvt4(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc);
 }
 
 template <int D>
@@ -536,9 +659,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)mblocks, a.hkv, a.batch), dim3(256), 0,
                        s, a);
   const int64_t nblocks = ((int64_t)a.seqlen_k + kBwdBlockN - 1) / kBwdBlockN;
-  if (nblocks > 0 && a.batch > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)nblocks, a.hkv, a.batch), dim3(256),
-                       0, s, a);
+  if (nblocks > 0 && a.batch > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)nblocks, a.hkv, a.batch * a.splits),
+                       dim3(256), 0, s, a);
+    if (a.splits > 1) {
+      const int64_t chunks = (int64_t)a.batch * a.seqlen_k * a.hkv * (D / 2);
+      hipLaunchKernelGGL((bwd_dkv_reduce_kernel<D>), dim3((unsigned)((chunks + 255) / 256)),
+                         dim3(256), 0, s, a);
+    }
+  }
   return hipGetLastError();
 }
 

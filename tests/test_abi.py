@@ -239,11 +239,25 @@ def _bwd(**kw):
     return p
 
 
+def _bwd_ws(batch, hq, hkv, d, rows_q, max_k):
+    """One float32 row sum per (query row, head), then float32 dK and dV
+    partials of each split of the dK/dV walk (splits: about 512 workgroups of
+    128 keys, at most 4), each part 256-byte rounded."""
+    rnd = lambda x: -(-x // 256) * 256
+    wg = -(-max_k // 128) * hkv * batch
+    splits = max(1, min(4, -(-512 // wg)))
+    parts = splits * batch * max_k * hkv * 2 * d if splits > 1 else 0
+    return rnd(rows_q * hq * 4) + rnd(parts * 4)
+
+
 def test_bwd_workspace_size(lib):
-    # one float32 row sum per (batch, head, query), 256-byte rounded
-    assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(_bwd())) == -(-2 * 8 * 1000 * 4 // 256) * 256
+    assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(_bwd())) == _bwd_ws(2, 8, 2, 128, 2000, 1000)
     p = _bwd(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, total_q=777, max_seqlen_q=500, max_seqlen_k=500)
-    assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(p)) == -(-8 * 777 * 4 // 256) * 256
+    assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(p)) == _bwd_ws(2, 8, 2, 128, 777, 500)
+    # enough key blocks: one split, no partials
+    p = _bwd(batch=64, seqlen_q=1024, seqlen_k=1024)
+    assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(p)) == _bwd_ws(64, 8, 2, 128, 64 * 1024, 1024)
+    assert _bwd_ws(64, 8, 2, 128, 64 * 1024, 1024) == 64 * 1024 * 8 * 4
     assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(_bwd(head_dim=256))) == 0
     assert "head_dim" in mi.mi_attn_last_error()
 

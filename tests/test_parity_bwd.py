@@ -69,6 +69,9 @@ DENSE = [
     ("mqa8_d128_causal", 1, 190, 190, 8, 1, 128, True, None, None),
     ("local_window_causal_d64", 1, 400, 400, 2, 1, 64, True, 64, None),
     ("tiny_one_key", 1, 5, 1, 2, 1, 128, False, None, None),
+    # 8 key blocks x 16 KV heads x 4 sequences = 512 workgroups: one split
+    # (dK, dV written directly); the cases above take the split path
+    ("no_split_mha16_b4_s1024_d64", 4, 1024, 1024, 16, 16, 64, True, None, None),
 ]
 
 
