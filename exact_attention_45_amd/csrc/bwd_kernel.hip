@@ -433,7 +433,10 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     sl[i] = (uint32_t)(row * ROW_B + ((ch ^ swz_key(row)) * 16));
   }
   uint4 qreg[NL], dreg[NL];
-  float sreg = 0.0f;  // threads 0..63: LSE*log2e of query m0+tid; 64..127: dPsum of m0+tid-64
+  // LSE and dPsum of query m0 + (tid & 63) (clamped to the last row) and
+  // whether that query exists; threads 0..63 stage LSE*log2e, 64..127 dPsum
+  float lreg = 0.0f, dreg1 = 0.0f;
+  bool qreal = false;
   // iteration it: query head hk*r + it / nm, query tile m_begin + it % nm
   auto load = [&](int it) __attribute__((always_inline)) {
     const int h = uniform(hk * r + it / nm);
@@ -450,17 +453,17 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       qreg[i] = buf_ld16(qr, gq[i]);
       dreg[i] = buf_ld16(gr, gd[i]);
     }
-    // branch-free (a load under a divergent branch makes the compiler wait
-    // for every outstanding load, the tile prefetch included): every thread
-    // reads both arrays at a clamped row and keeps one value
+    // Every thread reads both arrays at a clamped row, unconditionally; the
+    // choice of value waits for the store. (A load under a divergent branch,
+    // or one the compiler can move into one, makes it wait for every
+    // outstanding load, the tile prefetch included.)
     const int qi = m0 + (tid & (BM - 1));
     const int qc = min(qi, sq - 1);
     const int64_t li = a.cu_q != nullptr ? (int64_t)h * a.total_q + q_tok0 + qc
                                          : ((int64_t)b * a.hq + h) * sq + qc;
-    const float l = a.lse[li];
-    const float dps = a.dpsum[li];
-    const float l2 = (qi >= sq || l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
-    sreg = (tid & BM) == 0 ? l2 : (qi < sq ? dps : 0.0f);
+    lreg = a.lse[li];
+    dreg1 = a.dpsum[li];
+    qreal = qi < sq;
   };
   auto store = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -468,7 +471,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       *reinterpret_cast<uint4*>(smem + sl[i]) = qreg[i];
       *reinterpret_cast<uint4*>(smem + TILE_B + sl[i]) = dreg[i];
     }
-    if (tid < 2 * BM) reinterpret_cast<float*>(smem + 2 * TILE_B)[tid] = sreg;
+    const float l2 = (!qreal || lreg == kNegInf) ? __builtin_huge_valf() : lreg * kLog2e;
+    const float sv = (tid & BM) == 0 ? l2 : (qreal ? dreg1 : 0.0f);
+    if (tid < 2 * BM) reinterpret_cast<float*>(smem + 2 * TILE_B)[tid] = sv;
   };
 
   int rd[D / 16];
