@@ -126,12 +126,14 @@ __device__ __forceinline__ void acc_to_frags(const f32x16 x[2], bf16x8 f[4]) {
 // ------------------------------------------------------------------- dQ ----
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_kernel(const BwdArgs a) {
   using T = BwdTile<D>;
-  constexpr int ROW_B = T::ROW_B, CPR = T::CPR, TILE_B = T::TILE_B, NL = T::NL;
+  constexpr int ROW_B = T::ROW_B, CPR = T::CPR, TILE_B = T::TILE_B;
   constexpr int BM = kBwdBlockM, BN = kBwdTileN;
   static_assert(BN == T::ROWS, "one staged tile per key step");
-  __shared__ __attribute__((aligned(16))) char smem[2 * TILE_B];  // K tile, V tile
+  constexpr int BUF_B = 2 * TILE_B;  // K tile, V tile
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUF_B];  // two buffers
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, half = lane >> 5;
@@ -205,34 +207,32 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dqa[i] = zero_f32x16();
 
-  // staging: thread chunk e = tid + 256 i -> tile row e / CPR, chunk e % CPR
+  // K/V tiles go global -> LDS directly (dma16), double-buffered: for each
+  // tensor, instruction i of wave w fills tile rows RPI*(NI*w + i) ..
+  // +RPI-1; lane j lands at row offset j / CPR, physical chunk j % CPR, so it
+  // loads logical chunk (j % CPR) ^ swz_key(row) of that row.
   const __bf16* kp = static_cast<const __bf16*>(a.k) + k_base + (int64_t)hk * a.k_hs;
   const __bf16* vp = static_cast<const __bf16*>(a.v) + v_base + (int64_t)hk * a.v_hs;
-  uint32_t gk[NL], gv[NL], sl[NL];
+  constexpr int RPI = 1024 / ROW_B;  // rows per instruction
+  constexpr int NI = BN / RPI / 4;   // instructions per wave per tensor
+  static_assert(NI * RPI * 4 == BN, "a tile splits evenly over four waves");
+  uint32_t kdo[NI], vdo[NI];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int e = tid + 256 * i, row = e / CPR, ch = e % CPR;
-    gk[i] = (uint32_t)(row * a.k_rs * 2 + ch * 16);
-    gv[i] = (uint32_t)(row * a.v_rs * 2 + ch * 16);
-    sl[i] = (uint32_t)(row * ROW_B + ((ch ^ swz_key(row)) * 16));
+  for (int i = 0; i < NI; ++i) {
+    const int row = RPI * (NI * wave + i) + lane / CPR;
+    kdo[i] = (uint32_t)(row * a.k_rs * 2 + ((lane % CPR) ^ swz_key(row)) * 16);
+    vdo[i] = (uint32_t)(row * a.v_rs * 2 + ((lane % CPR) ^ swz_key(row)) * 16);
   }
-  uint4 kreg[NL], vreg[NL];
-  auto load = [&](int n0) __attribute__((always_inline)) {
-    const int nrows = min(sk - n0, BN);  // >= 1
+  const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
+  auto issue = [&](int n0, int buf) __attribute__((always_inline)) {
+    const int nrows = min(sk - n0, BN);  // >= 1; rows past it read as zero
     const auto kr = make_rsrc(kp + (int64_t)n0 * a.k_rs, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
     const auto vr = make_rsrc(vp + (int64_t)n0 * a.v_rs, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      kreg[i] = buf_ld16(kr, gk[i]);
-      vreg[i] = buf_ld16(vr, gv[i]);
-    }
-  };
-  auto store = [&]() __attribute__((always_inline)) {
+    for (int i = 0; i < NI; ++i) dma16(kr, kdo[i], lds_w + (uint32_t)(buf * BUF_B + i * 1024));
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      *reinterpret_cast<uint4*>(smem + sl[i]) = kreg[i];
-      *reinterpret_cast<uint4*>(smem + TILE_B + sl[i]) = vreg[i];
-    }
+    for (int i = 0; i < NI; ++i)
+      dma16(vr, vdo[i], lds_w + (uint32_t)(buf * BUF_B + TILE_B + i * 1024));
   };
 
   int rd[D / 16];
@@ -241,9 +241,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdArgs a) {
   int tr[2];
   tr_offsets(lane, ROW_B, tr);
 
-  auto compute = [&](int n0) __attribute__((always_inline)) {
-    const char* kt = smem;
-    const char* vt = smem + TILE_B;
+  auto compute = [&](int n0, const char* kt) __attribute__((always_inline)) {
+    const char* vt = kt + TILE_B;
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -306,13 +305,16 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdArgs a) {
   };
 
   if (n_end > n_begin) {
-    load(n_begin * BN);
+    issue(n_begin * BN, 0);
+    vmcnt_wait<0>();
+    lds_barrier();
     for (int n = n_begin; n < n_end; ++n) {
-      __syncthreads();  // every wave is done with the previous tile
-      store();
-      __syncthreads();
-      if (n + 1 < n_end) load((n + 1) * BN);
-      compute(n * BN);
+      const int cur = (n - n_begin) & 1;
+      // the other buffer's last readers finished before the previous barrier
+      if (n + 1 < n_end) issue((n + 1) * BN, cur ^ 1);
+      compute(n * BN, smem + cur * BUF_B);
+      vmcnt_wait<0>();  // this wave's share of tile n+1 has landed
+      lds_barrier();    // and every other wave's
     }
   }
 
