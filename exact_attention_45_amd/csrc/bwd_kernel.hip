@@ -78,9 +78,18 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs a) {
 
 // ----------------------------------------------------------- shared bits ----
 
-// Logical chunk ch of tile row `row` sits at chunk position ch ^ swz_key(row)
-// (attn_common.hpp). Row fragments: lane (c32, half) reads chunk
+// Logical chunk ch of tile row `row` sits at chunk position ch ^ tswz<D>(row).
+// tswz extends swz_key (attn_common.hpp) for D = 128 by key bit 3 into
+// chunk bit 3, as the forward does for its K tiles: the 16 lanes an LDS
+// cycle serves, reading one logical chunk of 16 consecutive rows, then hit
+// 16 different chunk positions (row fragments conflict-free), while each
+// transposing read (8 rows with the same bit 3) sees swz_key alone, shifted
+// by a whole 128-byte half. Row fragments: lane (c32, half) reads chunk
 // 2*cc + half of row c32 (+32 per 32-row block; same swizzle).
+template <int D>
+__device__ __forceinline__ int tswz(int row) {
+  return D == 128 ? (swz_key(row) | (((row >> 3) & 1) << 3)) : swz_key(row);
+}
 template <int D>
 struct BwdTile {
   static constexpr int ROW_B = D * 2;
@@ -104,11 +113,15 @@ __device__ __forceinline__ void tr_offsets(int lane, int row_b, int tr[2]) {
   for (int i = 0; i < 2; ++i) tr[i] = row * row_b + (((4 * i + c) ^ f) * 16) + (j & 1) * 8;
 }
 
+// The second read covers rows with bit 3 set: under tswz<128> its 128-byte
+// half is the other one.
 template <int ROW_B>
 __device__ __forceinline__ bf16x8 tr_frag(const char* tile, const int tr[2], int t, int db) {
-  const char* p = tile + (16 * t) * ROW_B + (db >> 1) * 128 + tr[db & 1];
-  const bf16x4 v0 = ds_read_tr16(reinterpret_cast<const __bf16*>(p));
-  const bf16x4 v1 = ds_read_tr16(reinterpret_cast<const __bf16*>(p + 8 * ROW_B));
+  constexpr int FLIP = ROW_B == 256 ? 1 : 0;
+  const char* p = tile + (16 * t) * ROW_B + tr[db & 1];
+  const bf16x4 v0 = ds_read_tr16(reinterpret_cast<const __bf16*>(p + (db >> 1) * 128));
+  const bf16x4 v1 = ds_read_tr16(
+      reinterpret_cast<const __bf16*>(p + 8 * ROW_B + ((db >> 1) ^ FLIP) * 128));
   return cat(v0, v1);
 }
 
@@ -210,7 +223,7 @@ void bwd_dq_kernel(const BwdArgs a) {
   // K/V tiles go global -> LDS directly (dma16), double-buffered: for each
   // tensor, instruction i of wave w fills tile rows RPI*(NI*w + i) ..
   // +RPI-1; lane j lands at row offset j / CPR, physical chunk j % CPR, so it
-  // loads logical chunk (j % CPR) ^ swz_key(row) of that row.
+  // loads logical chunk (j % CPR) ^ tswz(row) of that row.
   const __bf16* kp = static_cast<const __bf16*>(a.k) + k_base + (int64_t)hk * a.k_hs;
   const __bf16* vp = static_cast<const __bf16*>(a.v) + v_base + (int64_t)hk * a.v_hs;
   constexpr int RPI = 1024 / ROW_B;  // rows per instruction
@@ -220,8 +233,8 @@ void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int row = RPI * (NI * wave + i) + lane / CPR;
-    kdo[i] = (uint32_t)(row * a.k_rs * 2 + ((lane % CPR) ^ swz_key(row)) * 16);
-    vdo[i] = (uint32_t)(row * a.v_rs * 2 + ((lane % CPR) ^ swz_key(row)) * 16);
+    kdo[i] = (uint32_t)(row * a.k_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
+    vdo[i] = (uint32_t)(row * a.v_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
   }
   const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
   auto issue = [&](int n0, int buf) __attribute__((always_inline)) {
@@ -237,7 +250,7 @@ void bwd_dq_kernel(const BwdArgs a) {
 
   int rd[D / 16];
 #pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ swz_key(c32)) * 16);
+  for (int cc = 0; cc < D / 16; ++cc) rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ tswz<D>(c32)) * 16);
   int tr[2];
   tr_offsets(lane, ROW_B, tr);
 
@@ -432,7 +445,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     const int e = tid + 256 * i, row = e / CPR, ch = e % CPR;
     gq[i] = (uint32_t)(row * a.q_rs * 2 + ch * 16);
     gd[i] = (uint32_t)(row * a.do_rs * 2 + ch * 16);
-    sl[i] = (uint32_t)(row * ROW_B + ((ch ^ swz_key(row)) * 16));
+    sl[i] = (uint32_t)(row * ROW_B + ((ch ^ tswz<D>(row)) * 16));
   }
   uint4 qreg[NL], dreg[NL];
   // LSE and dPsum of query m0 + (tid & 63) (clamped to the last row) and
@@ -480,10 +493,18 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 
   int rd[D / 16];
 #pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ swz_key(c32)) * 16);
+  for (int cc = 0; cc < D / 16; ++cc) rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ tswz<D>(c32)) * 16);
   int tr[2];
   tr_offsets(lane, ROW_B, tr);
 
+  // One step, software-pipelined over the two 32-query blocks qb of the
+  // tile so that each block's exponentials run between matrix instructions
+  // of the other block (a wave's VALU work proceeds while its earlier MFMAs
+  // execute):
+  //   part 1: S, dP of block 0 (MFMAs 0..NS-1), then S, dP of block 1, one
+  //           block-0 softmax slice after each of those MFMAs
+  //   part 2: dV, dK of block 0, one block-1 softmax slice after each of
+  //           the first NP MFMAs; then dV, dK of block 1
   auto compute = [&](int m0) __attribute__((always_inline)) {
     const char* qt = smem;
     const char* gt = smem + TILE_B;
@@ -495,73 +516,93 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       s[qb] = zero_f32x16();
       dp[qb] = zero_f32x16();
     }
-    {
-      // MFMA i: contraction step i / 4, query block (i / 2) % 2; even i: S
-      // from Q rows, odd i: dP from dO rows
-      constexpr int N = 4 * (D / 16), LEAD = 6;
-      auto rdf = [&](int i) __attribute__((always_inline)) {
-        return *reinterpret_cast<const bf16x8*>((i & 1 ? gt : qt) + ((i >> 1) & 1) * 32 * ROW_B +
-                                                rd[i >> 2]);
-      };
-      bf16x8 ring[LEAD];
-#pragma unroll
-      for (int i = 0; i < LEAD; ++i) ring[i] = rdf(i);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const bf16x8 f = ring[i % LEAD];
-        if (i + LEAD < N) ring[i % LEAD] = rdf(i + LEAD);
-        const int qb = (i >> 1) & 1;
-        if (i & 1)
-          dp[qb] = mfma32(f, vf[i >> 2], dp[qb]);
-        else
-          s[qb] = mfma32(f, kf[i >> 2], s[qb]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
     // element (qb, v) holds query m0 + 4*half + 32*qb + 8*(v>>2) + (v&3), key `key`
     const uint64_t vis = vis64(qlo - m0 - 4 * half, qhi - m0 - 4 * half);
+    f32x4 l4[2][4], d4[2][4];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const uint32_t w = (uint32_t)(vis >> (32 * qb));
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int qo = 32 * qb + 8 * i + 4 * half;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + qo);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dss + qo);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int v = 4 * i + j;
-          const float x = mask_by_bit(s[qb][v], w, 8 * i + j);
-          const float p = fast_exp2(fmaf(x, c, -l4[j]));
-          s[qb][v] = p;
-          dp[qb][v] = p * (dp[qb][v] - d4[j]);  // dS
-        }
+        l4[qb][i] = *reinterpret_cast<const f32x4*>(l2s + qo);
+        d4[qb][i] = *reinterpret_cast<const f32x4*>(dss + qo);
       }
-    }
-    bf16x8 pf[4], dsf[4];
-    acc_to_frags(s, pf);
-    acc_to_frags(dp, dsf);
+    // softmax elements [e0, e1) of block qb: P, then dS in place of dP
+    auto sm = [&](int qb, int e0, int e1) __attribute__((always_inline)) {
+      const uint32_t w = (uint32_t)(vis >> (32 * qb));
+#pragma unroll
+      for (int v = e0; v < e1; ++v) {
+        const float x = mask_by_bit(s[qb][v], w, 8 * (v >> 2) + (v & 3));
+        const float p = fast_exp2(fmaf(x, c, -l4[qb][v >> 2][v & 3]));
+        s[qb][v] = p;
+        dp[qb][v] = p * (dp[qb][v] - d4[qb][v >> 2][v & 3]);
+      }
+    };
     {
-      // MFMA i: (t, db) = (i / (2 NDB), (i / 2) % NDB); even i: dV from
-      // dO^T, odd i: dK from Q^T
-      constexpr int NDB = D / 32, N = 8 * NDB, LEAD = 4;
-      auto rdf = [&](int i) __attribute__((always_inline)) {
-        return tr_frag<ROW_B>(i & 1 ? qt : gt, tr, i / (2 * NDB), (i >> 1) % NDB);
+      // MFMA g: block g / NS, i = g % NS: contraction step i / 2; even i: S
+      // from Q rows, odd i: dP from dO rows
+      constexpr int NS = 2 * (D / 16), N = 2 * NS, LEAD = 6;
+      auto rdf = [&](int g) __attribute__((always_inline)) {
+        const int qb = g / NS, i = g % NS;
+        return *reinterpret_cast<const bf16x8*>((i & 1 ? gt : qt) + qb * 32 * ROW_B + rd[i >> 1]);
       };
       bf16x8 ring[LEAD];
 #pragma unroll
-      for (int i = 0; i < LEAD; ++i) ring[i] = rdf(i);
+      for (int g = 0; g < LEAD; ++g) ring[g] = rdf(g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const bf16x8 f = ring[i % LEAD];
-        if (i + LEAD < N) ring[i % LEAD] = rdf(i + LEAD);
-        const int t = i / (2 * NDB), db = (i >> 1) % NDB;
+      for (int g = 0; g < N; ++g) {
+        const bf16x8 f = ring[g % LEAD];
+        if (g + LEAD < N) ring[g % LEAD] = rdf(g + LEAD);
+        const int qb = g / NS, i = g % NS;
         if (i & 1)
+          dp[qb] = mfma32(f, vf[i >> 1], dp[qb]);
+        else
+          s[qb] = mfma32(f, kf[i >> 1], s[qb]);
+        if (qb == 1) sm(0, 16 * i / NS, 16 * (i + 1) / NS);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    bf16x8 pf[4], dsf[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int i0 = 8 * t;
+      pf[t] = cat(cvt4(s[0][i0], s[0][i0 + 1], s[0][i0 + 2], s[0][i0 + 3]),
+                  cvt4(s[0][i0 + 4], s[0][i0 + 5], s[0][i0 + 6], s[0][i0 + 7]));
+      dsf[t] = cat(cvt4(dp[0][i0], dp[0][i0 + 1], dp[0][i0 + 2], dp[0][i0 + 3]),
+                   cvt4(dp[0][i0 + 4], dp[0][i0 + 5], dp[0][i0 + 6], dp[0][i0 + 7]));
+    }
+    {
+      // MFMA g: fragment t = g / (2 NDB) (t < 2: block 0, else block 1),
+      // d-block (g / 2) % NDB; even g: dV from dO^T, odd g: dK from Q^T
+      constexpr int NDB = D / 32, NP = 4 * NDB, N = 2 * NP, LEAD = 4;
+      auto rdf = [&](int g) __attribute__((always_inline)) {
+        return tr_frag<ROW_B>(g & 1 ? qt : gt, tr, g / (2 * NDB), (g >> 1) % NDB);
+      };
+      bf16x8 ring[LEAD];
+#pragma unroll
+      for (int g = 0; g < LEAD; ++g) ring[g] = rdf(g);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < N; ++g) {
+        if (g == NP) {
+#pragma unroll
+          for (int t = 2; t < 4; ++t) {
+            const int i0 = 8 * (t - 2);
+            pf[t] = cat(cvt4(s[1][i0], s[1][i0 + 1], s[1][i0 + 2], s[1][i0 + 3]),
+                        cvt4(s[1][i0 + 4], s[1][i0 + 5], s[1][i0 + 6], s[1][i0 + 7]));
+            dsf[t] = cat(cvt4(dp[1][i0], dp[1][i0 + 1], dp[1][i0 + 2], dp[1][i0 + 3]),
+                         cvt4(dp[1][i0 + 4], dp[1][i0 + 5], dp[1][i0 + 6], dp[1][i0 + 7]));
+          }
+        }
+        const bf16x8 f = ring[g % LEAD];
+        if (g + LEAD < N) ring[g % LEAD] = rdf(g + LEAD);
+        const int t = g / (2 * NDB), db = (g >> 1) % NDB;
+        if (g & 1)
           dka[db] = mfma32(f, dsf[t], dka[db]);
         else
           dva[db] = mfma32(f, pf[t], dva[db]);
+        if (g < NP) sm(1, 16 * g / NP, 16 * (g + 1) / NP);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
