@@ -125,6 +125,23 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* tile, const int tr[2], int
   return cat(v0, v1);
 }
 
+// Direct global-to-LDS load of one dword per lane (buffer_load_dword ... lds):
+// lane i's 4 bytes at buffer offset voff land at LDS address lds_base + 4 i;
+// offsets past the descriptor's bound load zero, dword by dword. Same
+// conventions as dma16 (attn_common.hpp): lds_base is wave-uniform and goes
+// through M0, the caller waits for the load (vmcnt) and then barriers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(lds_base)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // B-operand fragments (contraction over the 64 rows of a tile) from two
 // 32x32 accumulators, in the order the transposing reads deliver.
 __device__ __forceinline__ void acc_to_frags(const f32x16 x[2], bf16x8 f[4]) {
@@ -362,9 +379,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int BNK = kBwdBlockN, BM = kBwdTileM;
   static_assert(BNK == 128 && BM == 64, "four 32-key waves, 64-query tiles");
   constexpr int TILE_B = BM * ROW_B;
-  constexpr int NL = BM * CPR / 256;  // 16-byte chunks per thread per tile
-  // Q tile, dO tile, then LSE*log2e and dPsum of the tile's 64 queries
-  __shared__ __attribute__((aligned(16))) char smem[2 * TILE_B + 2 * BM * 4];
+  // per buffer: Q tile, dO tile, then the tile's 64 LSE and 64 dPsum values
+  constexpr int BUF_B = 2 * TILE_B + 2 * 256;
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUF_B];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, half = lane >> 5;
@@ -439,24 +456,29 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     dva[i] = zero_f32x16();
   }
 
-  uint32_t gq[NL], gd[NL], sl[NL];
+  // Q / dO tiles (and the tile's LSE and dPsum) go global -> LDS directly
+  // (dma16), double-buffered. For each tensor, instruction i of wave w fills
+  // tile rows RPI*(NI*w + i) .. +RPI-1; lane j lands at row offset j / CPR,
+  // physical chunk j % CPR, so it loads logical chunk (j % CPR) ^ tswz(row).
+  // Wave 0 loads the 64 LSE values, wave 1 the 64 dPsum values (one dword
+  // per lane; rows past the sequence load zero).
+  constexpr int RPI = 1024 / ROW_B;  // rows per instruction
+  constexpr int NI = BM / RPI / 4;   // instructions per wave per tensor
+  static_assert(NI * RPI * 4 == BM, "a tile splits evenly over four waves");
+  uint32_t qdo[NI], gdo[NI];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int e = tid + 256 * i, row = e / CPR, ch = e % CPR;
-    gq[i] = (uint32_t)(row * a.q_rs * 2 + ch * 16);
-    gd[i] = (uint32_t)(row * a.do_rs * 2 + ch * 16);
-    sl[i] = (uint32_t)(row * ROW_B + ((ch ^ tswz<D>(row)) * 16));
+  for (int i = 0; i < NI; ++i) {
+    const int row = RPI * (NI * wave + i) + lane / CPR;
+    qdo[i] = (uint32_t)(row * a.q_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
+    gdo[i] = (uint32_t)(row * a.do_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
   }
-  uint4 qreg[NL], dreg[NL];
-  // LSE and dPsum of query m0 + (tid & 63) (clamped to the last row) and
-  // whether that query exists; threads 0..63 stage LSE*log2e, 64..127 dPsum
-  float lreg = 0.0f, dreg1 = 0.0f;
-  bool qreal = false;
+  const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
+  const uint32_t lds_s = (uint32_t)uniform((int)(lds_addr(smem) + 2 * TILE_B + (wave & 1) * 256));
   // iteration it: query head hk*r + it / nm, query tile m_begin + it % nm
-  auto load = [&](int it) __attribute__((always_inline)) {
+  auto issue = [&](int it, int buf) __attribute__((always_inline)) {
     const int h = uniform(hk * r + it / nm);
     const int m0 = uniform((m_begin + it % nm) * BM);
-    const int nrows = min(sq - m0, BM);  // >= 1
+    const int nrows = min(sq - m0, BM);  // >= 1; rows past it read as zero
     const __bf16* q0 = static_cast<const __bf16*>(a.q) + q_base + (int64_t)m0 * a.q_rs +
                        (int64_t)h * a.q_hs;
     const __bf16* g0 = static_cast<const __bf16*>(a.dout) + do_base + (int64_t)m0 * a.do_rs +
@@ -464,31 +486,16 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     const auto qr = make_rsrc(q0, (uint32_t)((nrows - 1) * a.q_rs * 2 + ROW_B));
     const auto gr = make_rsrc(g0, (uint32_t)((nrows - 1) * a.do_rs * 2 + ROW_B));
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      qreg[i] = buf_ld16(qr, gq[i]);
-      dreg[i] = buf_ld16(gr, gd[i]);
-    }
-    // Every thread reads both arrays at a clamped row, unconditionally; the
-    // choice of value waits for the store. (A load under a divergent branch,
-    // or one the compiler can move into one, makes it wait for every
-    // outstanding load, the tile prefetch included.)
-    const int qi = m0 + (tid & (BM - 1));
-    const int qc = min(qi, sq - 1);
-    const int64_t li = a.cu_q != nullptr ? (int64_t)h * a.total_q + q_tok0 + qc
-                                         : ((int64_t)b * a.hq + h) * sq + qc;
-    lreg = a.lse[li];
-    dreg1 = a.dpsum[li];
-    qreal = qi < sq;
-  };
-  auto store = [&]() __attribute__((always_inline)) {
+    for (int i = 0; i < NI; ++i) dma16(qr, qdo[i], lds_w + (uint32_t)(buf * BUF_B + i * 1024));
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      *reinterpret_cast<uint4*>(smem + sl[i]) = qreg[i];
-      *reinterpret_cast<uint4*>(smem + TILE_B + sl[i]) = dreg[i];
+    for (int i = 0; i < NI; ++i)
+      dma16(gr, gdo[i], lds_w + (uint32_t)(buf * BUF_B + TILE_B + i * 1024));
+    if (wave < 2) {  // wave-uniform
+      const int64_t li = a.cu_q != nullptr ? (int64_t)h * a.total_q + q_tok0 + m0
+                                           : ((int64_t)b * a.hq + h) * sq + m0;
+      const auto sr = make_rsrc(wave == 0 ? a.lse + li : a.dpsum + li, (uint32_t)(nrows * 4));
+      dma4(sr, (uint32_t)(4 * lane), lds_s + (uint32_t)(buf * BUF_B));
     }
-    const float l2 = (!qreal || lreg == kNegInf) ? __builtin_huge_valf() : lreg * kLog2e;
-    const float sv = (tid & BM) == 0 ? l2 : (qreal ? dreg1 : 0.0f);
-    if (tid < 2 * BM) reinterpret_cast<float*>(smem + 2 * TILE_B)[tid] = sv;
   };
 
   int rd[D / 16];
@@ -505,10 +512,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   //           block-0 softmax slice after each of those MFMAs
   //   part 2: dV, dK of block 0, one block-1 softmax slice after each of
   //           the first NP MFMAs; then dV, dK of block 1
-  auto compute = [&](int m0) __attribute__((always_inline)) {
-    const char* qt = smem;
-    const char* gt = smem + TILE_B;
-    const float* l2s = reinterpret_cast<const float*>(smem + 2 * TILE_B);
+  auto compute = [&](int m0, const char* qt) __attribute__((always_inline)) {
+    const char* gt = qt + TILE_B;
+    const float* l2s = reinterpret_cast<const float*>(qt + 2 * TILE_B);  // raw LSE
     const float* dss = l2s + BM;
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -524,8 +530,13 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int qo = 32 * qb + 8 * i + 4 * half;
-        l4[qb][i] = *reinterpret_cast<const f32x4*>(l2s + qo);
+        const f32x4 l = *reinterpret_cast<const f32x4*>(l2s + qo);
         d4[qb][i] = *reinterpret_cast<const f32x4*>(dss + qo);
+        // LSE*log2e; a row with no visible key (LSE = -inf) gets +inf, so
+        // P = 0 (rows past the sequence read 0 and are masked)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          l4[qb][i][j] = l[j] == kNegInf ? __builtin_huge_valf() : l[j] * kLog2e;
       }
     // softmax elements [e0, e1) of block qb: P, then dS in place of dP
     auto sm = [&](int qb, int e0, int e1) __attribute__((always_inline)) {
@@ -609,14 +620,17 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   };
 
   if (it_end > it_begin) {
-    load(it_begin);
+    issue(it_begin, 0);
+    vmcnt_wait<0>();
+    lds_barrier();
     for (int it = it_begin; it < it_end; ++it) {
-      __syncthreads();  // every wave is done with the previous tile
-      store();
-      __syncthreads();
+      const int cur = (it - it_begin) & 1;
       const int m0 = uniform((m_begin + it % nm) * BM);
-      if (it + 1 < it_end) load(it + 1);
-      compute(m0);
+      // the other buffer's last readers finished before the previous barrier
+      if (it + 1 < it_end) issue(it + 1, cur ^ 1);
+      compute(m0, smem + cur * BUF_B);
+      vmcnt_wait<0>();  // this wave's share of the next tile has landed
+      lds_barrier();    // and every other wave's
     }
   }
 
