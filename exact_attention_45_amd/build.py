@@ -23,8 +23,11 @@ SOURCES = ["api.hip", "fwd_kernel.hip", "fwd_pp_kernel.hip", "fwd_sp_kernel.hip"
 # 256 registers; by default the compiler then places every MFMA accumulator in
 # accumulation registers, and the vector instructions that rescale O force
 # copies of all of O at every loop iteration. The VGPR form keeps O and S in
-# vector registers (other values still use accumulation registers).
-SOURCE_FLAGS = {"fwd_sp_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# vector registers (other values still use accumulation registers). The
+# backward's dK/dV kernel is in the same situation (its score accumulators
+# feed the softmax arithmetic).
+SOURCE_FLAGS = {"fwd_sp_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "bwd_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code; scalar/float2 math
