@@ -96,11 +96,23 @@ def softmax_lse_rows(s: np.ndarray, vis: np.ndarray, sink: Optional[float] = Non
     return p, lse
 
 
+def softcap_scores(s: np.ndarray, softcap: Optional[float]) -> np.ndarray:
+    """Logit soft-capping of the scaled scores (interface page, `softcap`
+    argument of `_flash_attn_fwd`, turned into a score modifier whose body the
+    pages do not show; 0 or None means none). Reading: cap * tanh(s / cap),
+    which keeps every score in (-cap, cap) and equals s to first order."""
+    if softcap is None or softcap == 0.0:
+        return s
+    return softcap * np.tanh(s / softcap)
+
+
 def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                   vis: np.ndarray, sink: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+                   vis: np.ndarray, sink: Optional[float] = None,
+                   softcap: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Single head. q (Sq, D), k (Sk, D), v (Sk, Dv), vis (Sq, Sk) -> O (Sq, Dv), LSE (Sq,).
-    sink: this head's learnable-sink logit or None (softmax_lse_rows)."""
-    s = scale * (q @ k.T)
+    sink: this head's learnable-sink logit or None (softmax_lse_rows); softcap:
+    the soft-capping constant or None (softcap_scores)."""
+    s = softcap_scores(scale * (q @ k.T), softcap)
     p, lse = softmax_lse_rows(s, vis, sink)
     return p @ v, lse
 
@@ -112,7 +124,7 @@ def _sink_of(sink, h):
 # ------------------------------------------------------- dense / varlen ----
 
 def attention_dense(q, k, v, scale, causal=False, window_left=None, window_right=None,
-                    sink=None):
+                    sink=None, softcap=None):
     """q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D) float64 -> O (B, Sq, Hq, Dv), LSE (B, Hq, Sq).
     sink: per-query-head learnable-sink logits (Hq,) or None."""
     B, Sq, Hq, _ = q.shape
@@ -126,12 +138,12 @@ def attention_dense(q, k, v, scale, causal=False, window_left=None, window_right
         for h in range(Hq):
             g = h // r
             out[b, :, h], lse[b, h] = attention_head(q[b, :, h], k[b, :, g], v[b, :, g], scale, vis,
-                                                     _sink_of(sink, h))
+                                                     _sink_of(sink, h), softcap)
     return out, lse
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
-                     window_left=None, window_right=None, sink=None):
+                     window_left=None, window_right=None, sink=None, softcap=None):
     """Packed sequences. q (Tq, Hq, D), k/v (Tk, Hkv, D) -> O (Tq, Hq, Dv), LSE (Hq, Tq).
 
     The LSE layout (num_heads, total_q) is the interface page's varlen layout.
@@ -150,7 +162,7 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
             g = h // r
             out[q0:q1, h], lse[h, q0:q1] = attention_head(q[q0:q1, h], k[k0:k1, g],
                                                           v[k0:k1, g], scale, vis,
-                                                          _sink_of(sink, h))
+                                                          _sink_of(sink, h), softcap)
     return out, lse
 
 
@@ -227,7 +239,7 @@ def attention_varlen_backward(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, scale, 
 
 def attention_rows(q_rows: np.ndarray, row_index: np.ndarray, k: np.ndarray, v: np.ndarray,
                    scale: float, seqlen_q: int, causal=False, window_left=None,
-                   window_right=None):
+                   window_right=None, softcap=None):
     """Selected query rows of one (sequence, head) problem, for sampling huge inputs.
 
     q_rows (n, D) are the queries at positions row_index (n,) of a length-seqlen_q
@@ -235,7 +247,7 @@ def attention_rows(q_rows: np.ndarray, row_index: np.ndarray, k: np.ndarray, v: 
     Returns O (n, Dv), LSE (n,), computed from the same definition row by row.
     """
     vis = visible_mask(seqlen_q, k.shape[0], causal, window_left, window_right, rows=row_index)
-    return attention_head(q_rows, k, v, scale, vis)
+    return attention_head(q_rows, k, v, scale, vis, softcap=softcap)
 
 
 # ------------------------------------------------------------- split-KV ----
@@ -250,7 +262,7 @@ def split_bounds(seqlen_k: int, num_splits: int) -> List[Tuple[int, int]]:
     return [(min(seqlen_k, s * c), min(seqlen_k, (s + 1) * c)) for s in range(num_splits)]
 
 
-def attention_partials(q, k, v, scale, vis, bounds: Sequence[Tuple[int, int]]):
+def attention_partials(q, k, v, scale, vis, bounds: Sequence[Tuple[int, int]], softcap=None):
     """Per-split (O_s, LSE_s) for one head: attention restricted to each key range.
 
     q (n, D), k/v (Sk, D), vis (n, Sk). Returns O (S, n, Dv), LSE (S, n). An
@@ -262,7 +274,8 @@ def attention_partials(q, k, v, scale, vis, bounds: Sequence[Tuple[int, int]]):
     for s, (a, b) in enumerate(bounds):
         if b <= a:
             continue
-        o_parts[s], lse_parts[s] = attention_head(q, k[a:b], v[a:b], scale, vis[:, a:b])
+        o_parts[s], lse_parts[s] = attention_head(q, k[a:b], v[a:b], scale, vis[:, a:b],
+                                                  softcap=softcap)
     return o_parts, lse_parts
 
 
@@ -358,7 +371,7 @@ def with_sink(out, lse, sink):
 
 def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1,
                  causal=False, window_left=None, window_right=None, heads=None,
-                 k_descale=None, v_descale=None, sink=None):
+                 k_descale=None, v_descale=None, sink=None, softcap=None):
     """One query per sequence over a paged cache.
 
     q (B, Hq, D) float64. Returns O (B, Hq, Dv), LSE (B, Hq), and the split
@@ -371,7 +384,7 @@ def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1
     caches are then the decoded values (e4m3_decode or e5m2_decode of the
     stored codes).
     sink: per-query-head learnable-sink logits (Hq,), merged after the split
-    combine (with_sink).
+    combine (with_sink). softcap: as attention_head.
     """
     B, Hq, _ = q.shape
     Hkv = k_cache.shape[2]
@@ -391,7 +404,8 @@ def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1
         bounds = split_bounds(sk, num_splits)
         for h in heads:
             g = h // r
-            o, l = attention_partials(q[b, h][None, :], kb[:, g], vb[:, g], scale, vis, bounds)
+            o, l = attention_partials(q[b, h][None, :], kb[:, g], vb[:, g], scale, vis, bounds,
+                                      softcap)
             o_parts[:, b, h] = o[:, 0]
             lse_parts[:, b, h] = l[:, 0]
     out, lse = combine(o_parts, lse_parts)
@@ -401,7 +415,8 @@ def paged_decode(q, k_cache, v_cache, page_table, seqused_k, scale, num_splits=1
 
 
 def paged_prefill(q, k_cache, v_cache, page_table, seqused_k, scale, causal=False,
-                  window_left=None, window_right=None, cu_seqlens_q=None, sink=None):
+                  window_left=None, window_right=None, cu_seqlens_q=None, sink=None,
+                  softcap=None):
     """Queries against a paged K/V cache (interface page, the page_table branch
     of `_flash_attn_fwd`: caches (num_pages, page_size, Hkv, D), a
     (B, max_pages) page table, per-sequence key counts seqused_k).
@@ -433,7 +448,8 @@ def paged_prefill(q, k_cache, v_cache, page_table, seqused_k, scale, causal=Fals
         vis = visible_mask(qb.shape[0], sk, causal, window_left, window_right)
         for h in range(Hq):
             g = h // r
-            o, l = attention_head(qb[:, h], kb[:, g], vb[:, g], scale, vis, _sink_of(sink, h))
+            o, l = attention_head(qb[:, h], kb[:, g], vb[:, g], scale, vis, _sink_of(sink, h),
+                                  softcap)
             if packed:
                 out[q0:q1, h], lse[h, q0:q1] = o, l
             else:

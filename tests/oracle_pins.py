@@ -33,6 +33,9 @@ What each pin rests on:
   paged_prefill  queries (dense and packed) against a paged cache equal the
                  scalar loops run on contiguous copies built token by token,
                  with ragged seqused_k, Sq < Sk, empty sequences and masks
+  softcap_limits a large soft cap leaves the scores unchanged (to 1/cap**2),
+                 small scores pass through to first order, and every
+                 probability ratio in a row stays within exp(2 cap)
   bwd_fd         backward gradients equal central finite differences of the
                  scalar-loop forward (loss sum(O * G)), GQA, Sq != Sk, masks,
                  rows with no visible key
@@ -532,6 +535,53 @@ def pin_torch_sdpa():
     return True, "ok"
 
 
+def pin_softcap_limits():
+    rng = _rng(41)
+    B, Sq, Sk, Hq, Hkv, D = 2, 6, 9, 4, 2, 5
+    q = rng.standard_normal((B, Sq, Hq, D))
+    k = rng.standard_normal((B, Sk, Hkv, D))
+    v = rng.standard_normal((B, Sk, Hkv, D))
+    for mk in (MASKS[0], MASKS[1], MASKS[2]):
+        o0, l0 = A.attention_dense(q, k, v, 0.5, **mk)
+        # cap 1e4: |s - cap tanh(s / cap)| <= |s|**3 / (3 cap**2) ~ 1e-7
+        o1, l1 = A.attention_dense(q, k, v, 0.5, softcap=1e4, **mk)
+        ok1, d1 = _close(o1, o0, 1e-6)
+        ok2, d2 = _close(l1, l0, 1e-6)
+        if not (ok1 and ok2):
+            return False, f"large cap {mk}: O {d1} LSE {d2}"
+        # tiny scores (scale 1e-4, |s| < 1e-3) against cap 0.5: the cubic
+        # term |s|**3 / (3 cap**2) stays under 2e-9
+        o2, l2 = A.attention_dense(q, k, v, 1e-4, **mk)
+        o3, l3 = A.attention_dense(q, k, v, 1e-4, softcap=0.5, **mk)
+        ok1, d1 = _close(o3, o2, 1e-8)
+        ok2, d2 = _close(l3, l2, 1e-8)
+        if not (ok1 and ok2):
+            return False, f"small scores {mk}: O {d1} LSE {d2}"
+    # saturation: huge scores, cap 1 -> probabilities within a factor e**2
+    qs, ks = q[:1, :, :1] * 50.0, k[:1, :, :1] * 50.0
+    s_full = np.ones((Sq, Sk), dtype=bool)
+    o, lse = A.attention_head(qs[0, :, 0], ks[0, :, 0], v[0, :, 0], 1.0, s_full, softcap=1.0)
+    for i in range(Sq):
+        # P_ij = exp(t_ij - LSE_i) with t in (-1, 1): LSE_i - ln Sk in (-1, 1)
+        if not (-1.0 < lse[i] - math.log(Sk) < 1.0):
+            return False, f"row {i}: LSE {lse[i]} not within 1 of ln {Sk}"
+    # the capping is strictly increasing: keys with distinct scores keep
+    # distinct, equally ordered capped scores (a one-key row's LSE is its
+    # capped score), also past the cap (|s| / cap up to ~8)
+    q3, k3 = q[0, :, 0], k[0, :, 0]
+    s = q3 @ k3.T
+    one = np.ones((1, 1), dtype=bool)
+    for i in range(Sq):
+        t = np.array([A.attention_head(q3[i:i + 1], k3[j:j + 1], v[0, j:j + 1, 0], 1.0, one,
+                                       softcap=1.0)[1][0] for j in range(Sk)])
+        order = np.argsort(s[i], kind="stable")
+        if not np.all(np.diff(t[order]) > 0):
+            return False, f"row {i}: capped scores not strictly increasing with the scores"
+        if not np.all(np.abs(t) < 1.0):
+            return False, f"row {i}: a capped score reaches the cap"
+    return True, "ok"
+
+
 def _fd_grads(loss, arrays, h=1e-6):
     """Central differences of loss(*arrays) with respect to every element."""
     out = []
@@ -688,6 +738,7 @@ ALL_PINS = {
     "sink_as_key": pin_sink_as_key,
     "sink_merge": pin_sink_merge,
     "descale": pin_descale,
+    "softcap_limits": pin_softcap_limits,
     "bwd_fd": pin_bwd_fd,
     "bwd_varlen": pin_bwd_varlen,
     "bwd_closed": pin_bwd_closed,

@@ -24,7 +24,8 @@ MUTANTS = [
      "lse[nonempty] = np.log(lsum[nonempty])", "LSE drops the max term"),
     ("softmax_lse_rows", "lse[nonempty] = m[nonempty] + np.log(lsum[nonempty])",
      "lse[nonempty] = m[nonempty] + np.log2(lsum[nonempty])", "LSE in base 2"),
-    ("attention_head", "s = scale * (q @ k.T)", "s = (q @ k.T)", "scale dropped"),
+    ("attention_head", "softcap_scores(scale * (q @ k.T), softcap)",
+     "softcap_scores((q @ k.T), softcap)", "scale dropped"),
     ("attention_head", "return p @ v, lse", "return p @ v[::-1], lse", "values reversed"),
     ("attention_dense", "g = h // r", "g = h % Hkv", "interleaved GQA grouping"),
     ("attention_varlen", "g = h // r", "g = h % Hkv", "interleaved GQA grouping (varlen)"),
@@ -57,6 +58,12 @@ MUTANTS = [
      "kb = kb * np.asarray(v_descale, dtype=np.float64)[b][None, :, None]", "K scaled by the V descale"),
     ("paged_decode", "vb = vb * np.asarray(v_descale, dtype=np.float64)[b][None, :, None]",
      "vb = vb * np.asarray(v_descale, dtype=np.float64)[0][None, :, None]", "V descale of sequence 0 for all"),
+    ("softcap_scores", "return softcap * np.tanh(s / softcap)", "return softcap * np.tanh(s)",
+     "soft cap without the 1/cap inside"),
+    ("softcap_scores", "return softcap * np.tanh(s / softcap)", "return np.tanh(s / softcap)",
+     "soft cap without the outer cap"),
+    ("softcap_scores", "return softcap * np.tanh(s / softcap)", "return np.clip(s, -softcap, softcap)",
+     "hard clip instead of tanh"),
     ("attention_head_backward", "ds = p * (dp - dpsum[:, None])", "ds = p * dp",
      "backward drops the dPsum term"),
     ("attention_head_backward", "dq = scale * (ds @ k)", "dq = ds @ k", "dQ without the scale"),
