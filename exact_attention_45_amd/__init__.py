@@ -80,6 +80,7 @@ class FwdParams(ctypes.Structure):
         ("seqused_k", _vp),
         ("page_size", _i32), ("num_pages", _i32), ("max_pages_per_seq", _i32),
         ("learnable_sink", _vp),
+        ("softcap", ctypes.c_float),
     ]
 
 
@@ -115,6 +116,7 @@ class DecodeParams(ctypes.Structure):
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("kv_dtype", _i32), ("k_descale", _vp), ("v_descale", _vp),
         ("learnable_sink", _vp),
+        ("softcap", ctypes.c_float),
     ]
 
 
@@ -206,7 +208,8 @@ def mi_attn_fwd(q, k, v, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=Non
                 softmax_scale: Optional[float] = None, causal: bool = False,
                 window_left: Optional[int] = None, window_right: Optional[int] = None,
                 return_lse: bool = True, page_table=None, seqused_k=None,
-                check_bounds: bool = False, learnable_sink=None) -> Tuple:
+                check_bounds: bool = False, learnable_sink=None,
+                softcap: float = 0.0) -> Tuple:
     """Exact attention forward (interface page, `_flash_attn_fwd` contract).
 
     Dense: q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D); lse (B, Hq, Sq).
@@ -218,6 +221,7 @@ def mi_attn_fwd(q, k, v, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=Non
     by cu_seqlens_q (cu_seqlens_k must be None). check_bounds validates the
     page ids and seqused_k on the host first (one device-to-host copy).
     learnable_sink: bf16 (Hq,) per-head sink logits (see include/mi_attn.h).
+    softcap: > 0 caps every scaled score x to softcap * tanh(x / softcap); 0 is none.
     """
     import torch
     lib = load()
@@ -327,6 +331,7 @@ def mi_attn_fwd(q, k, v, out=None, lse=None, cu_seqlens_q=None, cu_seqlens_k=Non
     p.softmax_scale = scale
     p.causal, p.window_left, p.window_right = int(bool(causal)), _win(window_left), _win(window_right)
     p.learnable_sink = _req_sink(learnable_sink, hq, dev)
+    p.softcap = float(softcap)
     _check(lib.mi_attn_fwd(ctypes.byref(p), _stream_ptr(dev)))
     return out, lse
 
@@ -544,13 +549,14 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
                            softmax_scale: Optional[float] = None, num_splits: int = 0,
                            window_left: Optional[int] = None, workspace=None,
                            return_lse: bool = True, check_bounds: bool = False,
-                           k_descale=None, v_descale=None, learnable_sink=None):
+                           k_descale=None, v_descale=None, learnable_sink=None,
+                           softcap: float = 0.0):
     """One query token per sequence against a paged cache, split along keys.
 
     q (B, Hq, D); k/v cache (num_pages, page_size, Hkv, D) contiguous, bf16 or
     fp8 (float8_e4m3fn, raw uint8 e4m3 bytes, or float8_e5m2; then k_descale / v_descale are
     float32 (B, Hkv) or None for 1); page_table int32 (B, max_pages);
-    seqused_k int32 (B,) or None.
+    seqused_k int32 (B,) or None. softcap as for mi_attn_fwd (on the descaled scores).
     Returns out (B, Hq, D) bf16 and lse (B, Hq) float32.
     """
     import torch
@@ -593,6 +599,7 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
             raise MiAttnError(MI_ATTN_EINVAL, f"{n} must be contiguous float32 {(B, k_cache.shape[2])}")
     p.k_descale, p.v_descale = _ptr(k_descale), _ptr(v_descale)
     p.learnable_sink = _req_sink(learnable_sink, hq, dev)
+    p.softcap = float(softcap)
     _check(lib.mi_attn_decode_splitkv(ctypes.byref(p), _stream_ptr(dev)))
     return out, lse
 

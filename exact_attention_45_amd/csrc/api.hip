@@ -95,6 +95,8 @@ int check_decode(const mi_attn_decode_params* p) {
       p->kv_dtype != MI_ATTN_KV_FP8_E5M2)
     return fail(MI_ATTN_EUNSUPPORTED, "kv_dtype %d not supported (bf16, fp8 e4m3, fp8 e5m2)",
                 p->kv_dtype);
+  if (!isfinite(p->softcap) || p->softcap < 0.0f)
+    return fail(MI_ATTN_EUNSUPPORTED, "softcap must be finite and >= 0 (0: none)");
   if (p->kv_dtype != MI_ATTN_KV_BF16 && !mi_attn::decode_streams(p->head_dim, p->page_size))
     return fail(MI_ATTN_EUNSUPPORTED, "fp8 K/V needs head_dim 64/128 and page_size a multiple "
                 "of 32 (got %d, %d)", p->head_dim, p->page_size);
@@ -169,6 +171,8 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
     return fail(MI_ATTN_EUNSUPPORTED, "head_dim %d not supported (64, 128, 256)", p->head_dim);
   if (!isfinite(p->softmax_scale) || p->softmax_scale < 0.0f)
     return fail(MI_ATTN_EUNSUPPORTED, "softmax_scale must be finite and >= 0");
+  if (!isfinite(p->softcap) || p->softcap < 0.0f)
+    return fail(MI_ATTN_EUNSUPPORTED, "softcap must be finite and >= 0 (0: none)");
   int max_q, max_k;
   if (varlen) {
     if (p->max_seqlen_q < 0 || (!paged && p->max_seqlen_k < 0) || p->total_q < 0)
@@ -241,6 +245,12 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
   a.num_pages = paged ? p->num_pages : 0;
   a.max_pages = paged ? p->max_pages_per_seq : 0;
   a.sink = static_cast<const __bf16*>(p->learnable_sink);
+  // soft-capping; with a zero scale every score is 0 and stays 0
+  a.softcap = p->softmax_scale > 0.0f ? p->softcap : 0.0f;
+  if (a.softcap > 0.0f) {
+    a.sc_k1x = 2.0f * 1.4426950408889634f * p->softmax_scale / a.softcap;
+    a.sc_k2 = a.softcap / p->softmax_scale;
+  }
   a.hq = p->num_heads_q;
   a.hkv = p->num_heads_kv;
   a.group = group;
@@ -315,6 +325,7 @@ int mi_attn_decode_splitkv(const mi_attn_decode_params* p, void* stream) {
   a.kv_fp8 = p->kv_dtype == MI_ATTN_KV_FP8_E4M3 ? 1 : p->kv_dtype == MI_ATTN_KV_FP8_E5M2 ? 2 : 0;
   a.k_descale = a.kv_fp8 ? p->k_descale : nullptr;
   a.v_descale = a.kv_fp8 ? p->v_descale : nullptr;
+  a.softcap = p->softmax_scale > 0.0f ? p->softcap : 0.0f;
   if ((int64_t)a.batch * a.hkv * a.row_blocks * splits > INT32_MAX)
     return fail(MI_ATTN_EINVAL, "launch grid too large");
 

@@ -149,6 +149,17 @@ __device__ __forceinline__ float merge_sink(float lse_keys, float sink, float* w
   return lse;
 }
 
+// Logit soft-capping in raw score units. With the scaled score x = scale * s
+// capped to cap * tanh(x / cap), the raw score becomes
+// k2 * tanh(k1 * s), k1 = scale / cap, k2 = cap / scale, so the exp2-domain
+// softmax after it is unchanged. Here k1x = 2 k1 log2(e) and
+// tanh(y) = 1 - 2 / (exp(2y) + 1), whose limits are exact: exp2 overflows to
+// +inf (rcp gives 0, tanh 1) or underflows to 0 (tanh -1).
+__device__ __forceinline__ float softcap_raw(float s, float k1x, float k2) {
+  const float e = fast_exp2(s * k1x);
+  return k2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
+}
+
 // Workgroup barrier that waits only for this wave's LDS operations
 // (lgkmcnt = 0), not for outstanding global loads: register prefetches for
 // later tiles stay in flight across it. (__syncthreads also waits vmcnt = 0.)

@@ -171,6 +171,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   const int tr_c = (tr_g & 1) * 2 + ((tr_j & 3) >> 1);
   const int tr_e = (tr_j & 1) * 4;
   const float c = a.scale_log2;
+  // soft-capping (this path reads bf16 caches only: no descale)
+  const float sc_k1x = a.softcap > 0.0f ? 2.0f * kLog2e * a.scale / a.softcap : 0.0f;
+  const float sc_k2 = a.softcap > 0.0f ? a.softcap / a.scale : 0.0f;
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, NSET == 2 ? 1 : 0>;
@@ -216,6 +219,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
       for (int cc = 0; cc < D / 16; ++cc)
         s = mfma32(*reinterpret_cast<const bf16x8*>(krow + dswz<D>(key, 2 * cc + half) * 8),
                    qf[cc], s);
+    }
+    if (a.softcap > 0.0f) {  // uniform
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = softcap_raw(s[v], sc_k1x, sc_k2);
     }
     if (n0 + BN > k_end) {
 #pragma unroll

@@ -115,7 +115,7 @@ __device__ __forceinline__ void stream_slices(int n_w, Issue& issue, Stage& stag
 }
 
 // KV: 0 = bf16 cache, 1 = fp8 e4m3, 2 = fp8 e5m2
-template <int D, int KV>
+template <int D, int KV, bool SC>
 __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) {
   constexpr bool FP8 = KV != 0;
   using C = StreamCfg<D, KV>;
@@ -182,6 +182,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   }
   const float c = a.scale_log2 * kds;
   const float rescale_raw = C::RESCALE_LOG2 / fmaxf(c, 1e-30f);
+  // soft-capping of scale * kds * s (a zero effective scale leaves all scores 0)
+  const float sc_eff = a.scale * kds;
+  const float sc_k1x = SC && sc_eff != 0.0f ? 2.0f * kLog2e * sc_eff / a.softcap : 0.0f;
+  const float sc_k2 = SC && sc_eff != 0.0f ? a.softcap / sc_eff : 0.0f;
 
   // ---- slice addressing
   const int64_t ts2 = (int64_t)a.hkv * GROW_B;  // bytes between consecutive tokens
@@ -285,6 +289,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
 #pragma unroll
     for (int cc = 0; cc < D / 16; ++cc)
       s = mfma32(*reinterpret_cast<const bf16x8*>(kslot + k_rd[cc]), qf[cc], s);
+    if constexpr (SC) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = softcap_raw(s[v], sc_k1x, sc_k2);
+    }
     // keys outside [kv_lo, sk) (first and last slices, and padding)
     const int key0 = 32 * (m_lo + i);
     if (i >= n_w || key0 < kv_lo || key0 + 32 > sk) [[unlikely]] {
@@ -385,7 +393,11 @@ template <int D, int KV>
 hipError_t launch_stream(const DecodeArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.batch * ((a.hkv + 3) / 4) * a.row_blocks * a.num_splits;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_stream_kernel<D, KV>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  if (a.softcap > 0.0f)
+    hipLaunchKernelGGL((decode_stream_kernel<D, KV, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<D, KV, false>), dim3((unsigned)grid), dim3(256), 0, s,
+                       a);
   return hipGetLastError();
 }
 

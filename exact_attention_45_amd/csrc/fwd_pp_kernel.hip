@@ -43,7 +43,7 @@ struct PPCfg {
   static_assert(BN == 64 && (CPR == 8 || CPR == 16), "staging assumes 64-key tiles, D 64/128");
 };
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool SC>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_pp_kernel(const FwdArgs a) {
   using C = PPCfg<D>;
@@ -264,6 +264,12 @@ void fwd_pp_kernel(const FwdArgs a) {
   auto sm_item = [&](int k) {
     const int n0 = (n_begin + k) * BN;
     const bool full = (n0 + BN <= sk) && (n0 + BN - 1 <= full_hi) && (n0 >= full_lo);
+    if constexpr (SC) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb][v] = softcap_raw(s[kb][v], a.sc_k1x, a.sc_k2);
+    }
     if (!full) {
       // element (kb, v) holds key n0 + 4*half + l, l = 32*kb + 8*(v>>2) + (v&3)
       const uint64_t vis = vis64(lo - n0 - 4 * half, hi - n0 - 4 * half);
@@ -410,10 +416,18 @@ hipError_t launch_fwd_pp(const FwdArgs& args, hipStream_t s) {
   a.num_m_blocks = (int)(((int64_t)a.max_rows + kFwdPPBlockM - 1) / kFwdPPBlockM);
   const int64_t grid = fwd_blocks_per_head(a, kFwdPPBlockM) * a.hkv;
   if (grid <= 0) return hipSuccess;
-  if (a.page_table != nullptr)
-    hipLaunchKernelGGL((fwd_pp_kernel<D, true>), dim3((unsigned)grid), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd_pp_kernel<D, false>), dim3((unsigned)grid), dim3(512), 0, s, a);
+  const bool sc = a.softcap > 0.0f;
+  if (a.page_table != nullptr) {
+    if (sc)
+      hipLaunchKernelGGL((fwd_pp_kernel<D, true, true>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_pp_kernel<D, true, false>), dim3((unsigned)grid), dim3(512), 0, s, a);
+  } else {
+    if (sc)
+      hipLaunchKernelGGL((fwd_pp_kernel<D, false, true>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_pp_kernel<D, false, false>), dim3((unsigned)grid), dim3(512), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -73,7 +73,7 @@ struct SPCfg {
 // multiple of 256 bytes, so those reads hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int kswz16(int key) { return swz_key(key) | (((key >> 3) & 1) << 3); }
 
-template <int D, int QB, bool PAGED>
+template <int D, int QB, bool PAGED, bool SC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_sp_kernel(const FwdArgs a) {
   using C = SPCfg<D, QB>;
@@ -266,6 +266,15 @@ void fwd_sp_kernel(const FwdArgs a) {
   auto sm_max = [&](STile& s, int j) {
     const int n0 = (n_begin + j) * BN;
     const bool full = (n0 + BN <= sk) && (n0 + BN - 1 <= full_hi) && (n0 >= full_lo);
+    if constexpr (SC) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            s[kb][qb][v] = softcap_raw(s[kb][qb][v], a.sc_k1x, a.sc_k2);
+    }
     if (!full) {
       // element (kb, v) holds key n0 + 4*half + l, l = 32*kb + 8*(v>>2) + (v&3)
 #pragma unroll
@@ -513,10 +522,19 @@ hipError_t launch_fwd_sp(const FwdArgs& args, hipStream_t s) {
   a.num_m_blocks = (int)(((int64_t)a.max_rows + BM - 1) / BM);
   const int64_t grid = fwd_blocks_per_head(a, BM) * a.hkv;
   if (grid <= 0) return hipSuccess;
-  if (a.page_table != nullptr)
-    hipLaunchKernelGGL((fwd_sp_kernel<D, QB, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd_sp_kernel<D, QB, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  const bool sc = a.softcap > 0.0f;
+  if (a.page_table != nullptr) {
+    if (sc)
+      hipLaunchKernelGGL((fwd_sp_kernel<D, QB, true, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_sp_kernel<D, QB, true, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  } else {
+    if (sc)
+      hipLaunchKernelGGL((fwd_sp_kernel<D, QB, false, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_sp_kernel<D, QB, false, false>), dim3((unsigned)grid), dim3(256), 0,
+                         s, a);
+  }
   return hipGetLastError();
 }
 

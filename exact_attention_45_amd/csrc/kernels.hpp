@@ -35,6 +35,10 @@ struct FwdArgs {
   const int32_t* seqused_k;
   int32_t page_size, num_pages, max_pages;
   const __bf16* sink;  // learnable-sink logits [hq], or NULL
+  // Logit soft-capping (softcap > 0): raw scores s become
+  // softcap_raw(s, sc_k1x, sc_k2), i.e. scale * s -> cap * tanh(scale * s / cap)
+  float softcap;
+  float sc_k1x, sc_k2;
 };
 
 // Query blocks (of BM packed rows) a prefill launch covers per KV head.
@@ -174,6 +178,7 @@ struct DecodeArgs {
   int32_t kv_fp8;
   const float* k_descale;    // [batch][hkv] or NULL
   const float* v_descale;
+  float softcap;  // > 0: logit soft-capping of scale * s (per-head descale included)
 };
 
 struct CombineArgs {

@@ -126,6 +126,12 @@ typedef enum {
  * value, so LSE = log(exp(s_h) + sum_j exp(scale * q.k_j)) and
  * O = sum_j exp(scale * q.k_j - LSE) v_j; a row with no visible key gets
  * O = 0 and LSE = s_h; s_h = -inf is no sink.
+ *
+ * softcap (interface page, `softcap` of `_flash_attn_fwd`; 0 means none):
+ * every scaled score x = scale * q.k_j is replaced by softcap * tanh(x /
+ * softcap) before the softmax (and before any sink is merged), so scores
+ * stay inside (-softcap, softcap); the LSE is over the capped scores. Must
+ * be finite and >= 0 (otherwise MI_ATTN_EUNSUPPORTED).
  * --------------------------------------------------------------------- */
 typedef struct {
   const void *q, *k, *v;
@@ -148,6 +154,7 @@ typedef struct {
   const int32_t *seqused_k;                   /* device [batch], paged only  */
   int32_t page_size, num_pages, max_pages_per_seq; /* paged only           */
   const void *learnable_sink;                 /* device bf16 [num_heads_q], or NULL */
+  float softcap;                              /* 0: none; > 0: logit soft-capping */
 } mi_attn_fwd_params;
 
 int mi_attn_fwd(const mi_attn_fwd_params *p, void *stream);
@@ -219,6 +226,8 @@ typedef struct {
   const float *k_descale, *v_descale;   /* fp8 only: [batch, num_heads_kv] or NULL */
   const void *learnable_sink;           /* device bf16 [num_heads_q], or NULL; as for
                                            mi_attn_fwd, merged in the combine step */
+  float softcap;                        /* 0: none; > 0: logit soft-capping, as for
+                                           mi_attn_fwd (on the descaled scores) */
 } mi_attn_decode_params;
 
 /* The split count mi_attn_decode_splitkv will use for *p (resolves

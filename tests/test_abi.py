@@ -121,6 +121,8 @@ def _call_fwd(lib, p):
     (dict(softmax_scale=float("nan")), mi.MI_ATTN_EUNSUPPORTED),
     (dict(softmax_scale=-1.0), mi.MI_ATTN_EUNSUPPORTED),
     (dict(seqlen_q=-1), mi.MI_ATTN_EINVAL),
+    (dict(softcap=-1.0), mi.MI_ATTN_EUNSUPPORTED),
+    (dict(softcap=float("inf")), mi.MI_ATTN_EUNSUPPORTED),
 ])
 def test_fwd_invalid_arguments(lib, kw, code):
     rc = _call_fwd(lib, _fwd(**kw))
@@ -172,6 +174,7 @@ def test_decode_workspace_size(lib):
     (dict(k_cache=FAKE + 4), mi.MI_ATTN_EINVAL),
     (dict(max_pages_per_seq=1 << 24, page_size=1 << 10), mi.MI_ATTN_EBOUNDS),
     (dict(kv_dtype=3), mi.MI_ATTN_EUNSUPPORTED),                      # no such cache type
+    (dict(softcap=float("nan")), mi.MI_ATTN_EUNSUPPORTED),
     (dict(kv_dtype=mi.MI_ATTN_KV_FP8_E4M3, head_dim=256), mi.MI_ATTN_EUNSUPPORTED),
     (dict(kv_dtype=mi.MI_ATTN_KV_FP8_E4M3, page_size=48), mi.MI_ATTN_EUNSUPPORTED),
 ])
