@@ -157,12 +157,12 @@ def decode_bytes(w) -> int:
 
 
 class Prefill:
-    def __init__(self, mi, w, torch):
+    def __init__(self, mi, w, torch, softcap: float = 0.0):
         from tests.gpu_util import dev_bf16, dev_i32
         self.mi, self.w = mi, w
         self.q, self.k, self.v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
         self.kw = dict(softmax_scale=w.softmax_scale, causal=w.causal,
-                       window_left=w.window_left, window_right=w.window_right)
+                       window_left=w.window_left, window_right=w.window_right, softcap=softcap)
         if w.kind == "varlen":
             self.kw.update(cu_seqlens_q=dev_i32(w.cu_seqlens_q), cu_seqlens_k=dev_i32(w.cu_seqlens_k),
                            max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k)
@@ -365,6 +365,19 @@ def main():
             log(f"[bench] {wi.name}: {med * 1e3:.1f} us, {extra[wi.name]['tflops']:.1f} TFLOP/s")
             del p
             torch.cuda.empty_cache()
+        # the causal GQA S4096 D128 workload with logit soft-capping (cap 30)
+        wc = W.standard_config(2)
+        pc = Prefill(mi, wc, torch, softcap=30.0)
+        warm_up(torch, pc)
+        ms = sorted(time_launches(torch, pc, max(5, args.steps // 2)))
+        med = ms[len(ms) // 2]
+        f = prefill_flops(wc)
+        name = "softcap30_" + wc.name
+        extra[name] = {"median_us": med * 1e3, "tflops": f / (med * 1e-3) / 1e12,
+                       "frac": f / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        log(f"[bench] {name}: {med * 1e3:.1f} us, {extra[name]['tflops']:.1f} TFLOP/s")
+        del pc
+        torch.cuda.empty_cache()
         # backward of the causal GQA S4096 D128 workload; algorithmic flops
         # 2.5x the forward's (five tile products per score tile against two)
         wb = W.standard_config(2)
