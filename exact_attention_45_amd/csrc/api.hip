@@ -32,6 +32,9 @@ int ok() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool stride_ok(int64_t s) { return s >= 0 && (s % 8) == 0; }
 bool dim_supported(int d) { return d == 64 || d == 128 || d == 256; }
+// The prefill forward also takes head dims 96 and 192 (in the LDS layouts of
+// 128 and 256).
+bool fwd_dim_supported(int d) { return dim_supported(d) || d == 96 || d == 192; }
 
 // Mask normalisation (interface page, `_flash_attn_fwd`): causal forces a
 // right window of 0; negative sizes are unbounded.
@@ -127,6 +130,17 @@ size_t workspace_for(const mi_attn_decode_params* p, int splits) {
 }
 
 template <class F>
+hipError_t by_fwd_dim(int d, F&& f) {
+  switch (d) {
+    case 64: return f(std::integral_constant<int, 64>{});
+    case 96: return f(std::integral_constant<int, 96>{});
+    case 128: return f(std::integral_constant<int, 128>{});
+    case 192: return f(std::integral_constant<int, 192>{});
+    default: return f(std::integral_constant<int, 256>{});
+  }
+}
+
+template <class F>
 hipError_t by_dim(int d, F&& f) {
   switch (d) {
     case 64: return f(std::integral_constant<int, 64>{});
@@ -167,8 +181,9 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
   if (p->num_heads_q % p->num_heads_kv != 0)
     return fail(MI_ATTN_EINVAL, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
                 p->num_heads_q, p->num_heads_kv);
-  if (!dim_supported(p->head_dim))
-    return fail(MI_ATTN_EUNSUPPORTED, "head_dim %d not supported (64, 128, 256)", p->head_dim);
+  if (!fwd_dim_supported(p->head_dim))
+    return fail(MI_ATTN_EUNSUPPORTED, "head_dim %d not supported (64, 96, 128, 192, 256)",
+                p->head_dim);
   if (!isfinite(p->softmax_scale) || p->softmax_scale < 0.0f)
     return fail(MI_ATTN_EUNSUPPORTED, "softmax_scale must be finite and >= 0");
   if (!isfinite(p->softcap) || p->softcap < 0.0f)
@@ -264,7 +279,7 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
     return fail(MI_ATTN_EINVAL, "launch grid too large");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = by_dim(p->head_dim, [&](auto dc) {
+  hipError_t e = by_fwd_dim(p->head_dim, [&](auto dc) {
     return mi_attn::launch_fwd<decltype(dc)::value>(a, s);
   });
   if (e != hipSuccess) return fail(MI_ATTN_EHIP, "launch failed: %s", hipGetErrorString(e));

@@ -52,7 +52,9 @@ hipError_t launch_fwd(const FwdArgs& args, hipStream_t s) {
 }
 
 template hipError_t launch_fwd<64>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd<96>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd<128>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd<192>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd<256>(const FwdArgs&, hipStream_t);
 
 }  // namespace mi_attn

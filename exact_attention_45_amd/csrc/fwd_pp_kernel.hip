@@ -31,13 +31,18 @@
 
 namespace mi_attn {
 
+// Head dim 96 uses the head-dim-128 LDS layout (rows of 256 bytes): tiles
+// load whole 256-byte row slots (the last 64 bytes of a row slot hold the
+// next row's first values, or zeros past the end of the tensor) and every
+// product reads only the first 96 columns.
 template <int D>
 struct PPCfg {
+  static constexpr int DL = D == 96 ? 128 : D;  // layout head dim
   static constexpr int BM = kFwdPPBlockM;      // 256 packed rows
   static constexpr int BN = kFwdBlockN;        // 64 keys
   static constexpr int NT = 512;               // 8 waves
-  static constexpr int CPR = D / 8;            // 16-byte chunks per row
-  static constexpr int TILE_B = BN * D * 2;    // bytes per K (or V) tile
+  static constexpr int CPR = DL / 8;           // 16-byte chunks per LDS row
+  static constexpr int TILE_B = BN * DL * 2;   // bytes per K (or V) tile
   static constexpr int NBUF = 4;
   static constexpr float RESCALE_LOG2 = 8.0f;
   static_assert(BN == 64 && (CPR == 8 || CPR == 16), "staging assumes 64-key tiles, D 64/128");
@@ -49,7 +54,7 @@ void fwd_pp_kernel(const FwdArgs a) {
   using C = PPCfg<D>;
   constexpr int BM = C::BM, BN = C::BN, CPR = C::CPR;
   constexpr int TILE_B = C::TILE_B;
-  constexpr int ROW_B = D * 2;
+  constexpr int ROW_B = C::DL * 2;  // LDS row bytes
   constexpr int BUF_B = 2 * TILE_B;  // K then V
   __shared__ __attribute__((aligned(16))) char smem[C::NBUF * BUF_B];
 
@@ -150,7 +155,7 @@ void fwd_pp_kernel(const FwdArgs a) {
   const __bf16* kp = static_cast<const __bf16*>(a.k) + k_base + (int64_t)hk * a.k_hs;
   const __bf16* vp = static_cast<const __bf16*>(a.v) + v_base + (int64_t)hk * a.v_hs;
   auto kswz = [](int key) {
-    return D == 128 ? (swz_key(key) | (((key >> 3) & 1) << 3)) : ((key >> 1) & 7);
+    return C::DL == 128 ? (swz_key(key) | (((key >> 3) & 1) << 3)) : ((key >> 1) & 7);
   };
   uint32_t kdo[NI], vdo[NI];
 #pragma unroll
@@ -168,8 +173,8 @@ void fwd_pp_kernel(const FwdArgs a) {
   // buffer buf: K parts i = 0..NI-1, then V parts.
   auto issue_tile = [&](int n0, int buf, int64_t ko, int64_t vo) {
     const int nrows = min(sk - n0, BN);  // >= 1
-    const auto kr = make_rsrc(kp + ko, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
-    const auto vr = make_rsrc(vp + vo, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
+    const auto kr = make_rsrc(kp + ko, (uint32_t)((nrows - 1) * a.k_rs * 2 + D * 2));
+    const auto vr = make_rsrc(vp + vo, (uint32_t)((nrows - 1) * a.v_rs * 2 + D * 2));
 #pragma unroll
     for (int i = 0; i < NI; ++i) dma16(kr, kdo[i], lds_w + (uint32_t)(buf * BUF_B + i * 1024));
 #pragma unroll
@@ -432,6 +437,7 @@ hipError_t launch_fwd_pp(const FwdArgs& args, hipStream_t s) {
 }
 
 template hipError_t launch_fwd_pp<64>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd_pp<96>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd_pp<128>(const FwdArgs&, hipStream_t);
 
 }  // namespace mi_attn

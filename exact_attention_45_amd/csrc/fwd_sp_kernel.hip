@@ -53,18 +53,23 @@
 
 namespace mi_attn {
 
+// Head dim 192 uses the head-dim-256 LDS layout (rows of 512 bytes): tiles
+// load whole 512-byte row slots (the last 128 bytes of a row slot hold the
+// next row's first values, or zeros past the end of the tensor) and every
+// product reads only the first 192 columns.
 template <int D, int QB>
 struct SPCfg {
+  static constexpr int DL = D == 192 ? 256 : D;  // layout head dim
   static constexpr int BM = 128 * QB;          // packed rows per workgroup
   static constexpr int BN = kFwdBlockN;        // 64 keys per tile
-  static constexpr int ROW_B = D * 2;          // bytes per K/V row
-  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int ROW_B = DL * 2;         // bytes per K/V LDS row
+  static constexpr int CPR = DL / 8;           // 16-byte chunks per LDS row
   static constexpr int TILE_B = BN * ROW_B;    // bytes per K (or V) tile
   static constexpr int RPI = 1024 / ROW_B;     // rows per direct-to-LDS wave instruction
   static constexpr int NI = BN / RPI / 4;      // such instructions per wave per tensor
   static constexpr float RESCALE_LOG2 = 8.0f;  // lazy-rescale threshold
   static_assert(NI * RPI * 4 == BN, "a tile splits evenly over four waves");
-  static_assert(D == 128 || D == 256, "16-byte-chunk swizzles assume 256- or 512-byte rows");
+  static_assert(DL == 128 || DL == 256, "16-byte-chunk swizzles assume 256- or 512-byte rows");
 };
 
 // K tile swizzle: chunk c of key row `key` sits at chunk c ^ kswz16(key). The
@@ -202,7 +207,7 @@ void fwd_sp_kernel(const FwdArgs a) {
     constexpr int buf = decltype(buf_c)::value;
     const int n0 = (n_begin + j) * BN;
     const int nrows = min(sk - n0, BN);  // >= 1
-    const auto rs = make_rsrc(kp + ko, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
+    const auto rs = make_rsrc(kp + ko, (uint32_t)((nrows - 1) * a.k_rs * 2 + D * 2));
 #pragma unroll
     for (int i = 0; i < NI; ++i) dma16(rs, kdo[i], lds_w + (uint32_t)(buf * TILE_B + i * 1024));
   };
@@ -210,7 +215,7 @@ void fwd_sp_kernel(const FwdArgs a) {
     constexpr int buf = decltype(buf_c)::value;
     const int n0 = (n_begin + j) * BN;
     const int nrows = min(sk - n0, BN);
-    const auto rs = make_rsrc(vp + vo, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
+    const auto rs = make_rsrc(vp + vo, (uint32_t)((nrows - 1) * a.v_rs * 2 + D * 2));
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       dma16(rs, vdo[i], lds_w + (uint32_t)((2 + buf) * TILE_B + i * 1024));
@@ -355,13 +360,14 @@ void fwd_sp_kernel(const FwdArgs a) {
   // Q^T fused with the exponentials of S(cur). MFMA i (contraction step
   // i / 2, key block i % 2) is issued with the K fragment read LEAD1 MFMAs
   // ahead and with the exponentials, row-sum adds and bf16 packing of
-  // 32 / N_MF score elements of the current tile, in that source order, held
+  // 32 / N score elements of the current tile (elements 32 i / N .. 32 (i + 1)
+  // / N - 1 with MFMA i), in that source order, held
   // by scheduling barriers between the groups.
   auto phase1 = [&](auto buf_c, STile& cur, STile& nxt) __attribute__((always_inline)) {
     static_assert(QB == 1, "fused phase 1 handles one query block per wave");
     constexpr int buf = decltype(buf_c)::value;
     constexpr int N = 2 * NKC;   // MFMAs and K fragment reads
-    constexpr int EPM = 32 / N;  // score elements per MFMA
+    static_assert(N <= 32, "at least one score element per MFMA");
     constexpr int L1 = FWD_SP_LEAD1;
     auto kread = [&](int i) __attribute__((always_inline)) {
       const int cc = i >> 1, kb = i & 1;
@@ -380,8 +386,8 @@ void fwd_sp_kernel(const FwdArgs a) {
       if (i + L1 < N) ring[i % L1] = kread(i + L1);
       nxt[kb][0] = mfma32(kf, qf[0][cc], cc == 0 ? zero_f32x16() : nxt[kb][0]);
 #pragma unroll
-      for (int e = 0; e < EPM; ++e) {
-        const int j = i * EPM + e;  // element: key block j / 16, register j % 16
+      for (int j = 32 * i / N; j < 32 * (i + 1) / N; ++j) {
+        // element j: key block j / 16, register j % 16
         const int jb = j >> 4, jv = j & 15;
         const float x = fast_exp2(fmaf(cur[jb][0][jv], c, -ms[0]));
         cur[jb][0][jv] = x;
@@ -538,6 +544,7 @@ hipError_t launch_fwd_sp(const FwdArgs& args, hipStream_t s) {
   return hipGetLastError();
 }
 
+template hipError_t launch_fwd_sp<192, 1>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd_sp<256, 1>(const FwdArgs&, hipStream_t);
 
 }  // namespace mi_attn

@@ -100,7 +100,8 @@ def _call_fwd(lib, p):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(head_dim=96), mi.MI_ATTN_EUNSUPPORTED),
+    (dict(head_dim=80), mi.MI_ATTN_EUNSUPPORTED),
+    (dict(head_dim=160), mi.MI_ATTN_EUNSUPPORTED),
     (dict(head_dim=512), mi.MI_ATTN_EUNSUPPORTED),
     (dict(num_heads_q=5), mi.MI_ATTN_EINVAL),
     (dict(num_heads_kv=0), mi.MI_ATTN_EINVAL),
