@@ -352,7 +352,11 @@ def main():
         # with K/V in a cache of 256-token pages behind a permuted page table
         paged = W.paged_prefill_case(1002, 1, 32, 4, 128, 256, 16, None, seqlen_q=4096,
                                      causal=True, name="paged256_causal_gqa32x4_s4096_d128")
-        for i in (1, 3, 4, paged):
+        d96 = W.dense_case(1006, 1, 4096, 4096, 32, 4, 96, causal=True,
+                           name="causal_gqa32x4_s4096_d96")
+        d192 = W.dense_case(1007, 1, 8192, 8192, 16, 2, 192, causal=True,
+                            name="causal_gqa16x2_s8192_d192")
+        for i in (1, 3, 4, paged, d96, d192):
             wi = W.standard_config(i) if isinstance(i, int) else i
             p = Prefill(mi, wi, torch)
             warm_up(torch, p)
