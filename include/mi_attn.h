@@ -42,8 +42,10 @@
  *     contiguous; base pointers and strides must keep 16-byte alignment of
  *     each row (head_dim % 8 == 0, strides % 8 == 0, pointers 16-byte
  *     aligned).
- *   - Supported head_dim: 64, 128, 256 (the interface page allows <= 256 in
- *     multiples of 8; other sizes return MI_ATTN_EUNSUPPORTED).
+ *   - Supported head_dim: 64, 96, 128, 192, 256 for mi_attn_fwd; 64, 128,
+ *     256 for the decode and the combine; 64, 128 for the backward (the
+ *     interface page allows <= 256 in multiples of 8; other sizes return
+ *     MI_ATTN_EUNSUPPORTED).
  *   - Return value: MI_ATTN_OK, or a negative mi_attn_status; on error
  *     nothing is enqueued and mi_attn_last_error() describes the problem.
  *   - The contents of device index arrays (cu_seqlens, seqused_k,
