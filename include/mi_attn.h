@@ -68,7 +68,7 @@ extern "C" {
 typedef enum {
   MI_ATTN_OK = 0,
   MI_ATTN_EINVAL = -1,        /* bad pointer, shape, stride or alignment      */
-  MI_ATTN_EUNSUPPORTED = -2,  /* valid request this build does not implement  */
+  MI_ATTN_EUNSUPPORTED = -2,  /* valid request the library does not implement */
   MI_ATTN_EBOUNDS = -3,       /* host-visible lengths exceed a table capacity */
   MI_ATTN_EWORKSPACE = -4,    /* workspace missing or too small               */
   MI_ATTN_EHIP = -5           /* the HIP runtime reported an error at launch  */

@@ -22,7 +22,7 @@ def _gpu_present():
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The HIP library on a GPU machine. Fails (never skips) if the library is missing."""
+    """The HIP library, where a GPU is visible. Fails (never skips) if the library is missing."""
     if not _gpu_present():
         pytest.skip("no GPU visible to torch")
     import exact_attention_45_amd as mi
