@@ -72,3 +72,22 @@ def test_dims_unsupported_elsewhere(gpu_lib):
     with pytest.raises(gpu_lib.MiAttnError) as e:
         gpu_lib.mi_attn_bwd(q, k, v, out, out, lse)
     assert e.value.code == gpu_lib.MI_ATTN_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("d,hq,hkv,s", [(96, 32, 4, 4096), (192, 16, 2, 8192)])
+def test_dims_full_size_sampled(gpu_lib, d, hq, hkv, s):
+    """The bench's D96 (GQA 32/4, S4096) and D192 (GQA 16/2, S8192) causal prefills:
+    sampled query rows of three heads against the oracle row by row."""
+    print(f"[case] dims {d} full size", flush=True)
+    w = W.dense_case(1006 if d == 96 else 1007, 1, s, s, hq, hkv, d, causal=True)
+    out, lse = gpu_lib.mi_attn_fwd(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), causal=True)
+    torch.cuda.synchronize()
+    pos = np.array([0, 1, 63, 64, 127, 128, 1000, s // 2, s - 2, s - 1])
+    q, k, v = f64(w.q[0]), f64(w.k[0]), f64(w.v[0])
+    o_gpu = host_f64(out[0][torch.as_tensor(pos)])
+    l_gpu = host_f64(lse[0][:, torch.as_tensor(pos)])
+    r = hq // hkv
+    for h in (0, hq // 2 + 1, hq - 1):
+        g = h // r
+        o_ref, l_ref = OA.attention_rows(q[pos, h], pos, k[:, g], v[:, g], w.softmax_scale, s, True)
+        check(o_gpu[:, h], o_ref, l_gpu[h], l_ref, what=f"d{d} full size head {h}")

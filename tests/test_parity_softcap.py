@@ -117,3 +117,24 @@ def test_softcap_zero_is_off_and_huge_cap_is_identity(gpu_lib):
     torch.cuda.synchronize()
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
     check(host_f64(o2), host_f64(o0), host_f64(l2), host_f64(l0), what="cap 1e4")
+
+
+def test_softcap_full_size_sampled(gpu_lib):
+    """The causal GQA S4096 D128 workload with softcap 30 (the bench's soft-capped line):
+    sampled query rows of heads 0, 13, 31 against the oracle row by row."""
+    print("[case] softcap full size", flush=True)
+    w = W.standard_config(2)
+    out, lse = gpu_lib.mi_attn_fwd(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
+                                   softmax_scale=w.softmax_scale, causal=True, softcap=30.0)
+    torch.cuda.synchronize()
+    S = w.seqlen_q
+    pos = np.array([0, 1, 63, 64, 255, 1000, 2047, 2048, 3333, S - 1])
+    q, k, v = f64(w.q[0]), f64(w.k[0]), f64(w.v[0])
+    o_gpu = host_f64(out[0][torch.as_tensor(pos)])
+    l_gpu = host_f64(lse[0][:, torch.as_tensor(pos)])
+    r = w.num_heads_q // w.num_heads_kv
+    for h in (0, 13, 31):
+        g = h // r
+        o_ref, l_ref = OA.attention_rows(q[pos, h], pos, k[:, g], v[:, g], w.softmax_scale, S,
+                                         True, softcap=30.0)
+        check(o_gpu[:, h], o_ref, l_gpu[h], l_ref, what=f"softcap full size head {h}")
