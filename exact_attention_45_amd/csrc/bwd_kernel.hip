@@ -386,7 +386,21 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, half = lane >> 5;
   const int S = a.splits;
-  const int nb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z / S, sp = blockIdx.z - b * S;
+  // XCD-aware work order: consecutive workgroups go to the eight XCDs in
+  // turn, so workgroup L runs on XCD L % 8. Work items are numbered key
+  // block fastest, then (KV head, sequence, split), and XCD x takes the
+  // contiguous range x * W / 8 .. : the workgroups that share one query
+  // head group's Q and dO rows then share one L2. (When W is not a
+  // multiple of 8 the plain order is kept.)
+  const int NB = gridDim.x;
+  const int W = NB * gridDim.y * gridDim.z;
+  const int L = blockIdx.x + NB * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int w_item = (W & 7) == 0 ? (L & 7) * (W >> 3) + (L >> 3) : L;
+  const int nb = w_item % NB;
+  const int combo = w_item / NB;  // hk + hkv * (b * S + sp)
+  const int hk = combo % gridDim.y;
+  const int bs = combo / gridDim.y;
+  const int b = bs / S, sp = bs - b * S;
 
   int sq = a.seqlen_q, sk = a.seqlen_k, q_tok0 = 0;
   int64_t q_base, do_base, k_base, v_base, dk_base, dv_base;
