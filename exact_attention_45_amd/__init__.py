@@ -405,9 +405,10 @@ def mi_attn_bwd_workspace_bytes(q, k, v, out, dout, lse, cu_seqlens_q=None, cu_s
     p = _bwd_params(q, k, v, out, dout, lse, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                     max_seqlen_k, None, causal, None, None)
     n = lib.mi_attn_bwd_workspace_bytes(ctypes.byref(p))
-    err = mi_attn_last_error()
-    if n == 0 and err:
-        raise MiAttnError(MI_ATTN_EINVAL if "supported" not in err else MI_ATTN_EUNSUPPORTED, err)
+    if n == 0 and mi_attn_last_error():
+        # invalid parameters: mi_attn_bwd runs the same checks first and
+        # returns their status without launching anything
+        _check(lib.mi_attn_bwd(ctypes.byref(p), None))
     return int(n)
 
 
