@@ -392,14 +392,14 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   // contiguous range x * W / 8 .. : the workgroups that share one query
   // head group's Q and dO rows then share one L2. (When W is not a
   // multiple of 8 the plain order is kept.)
-  const int NB = gridDim.x;
-  const int W = NB * gridDim.y * gridDim.z;
-  const int L = blockIdx.x + NB * (blockIdx.y + gridDim.y * blockIdx.z);
-  const int w_item = (W & 7) == 0 ? (L & 7) * (W >> 3) + (L >> 3) : L;
-  const int nb = w_item % NB;
-  const int combo = w_item / NB;  // hk + hkv * (b * S + sp)
-  const int hk = combo % gridDim.y;
-  const int bs = combo / gridDim.y;
+  const int64_t NB = gridDim.x;
+  const int64_t W = NB * gridDim.y * gridDim.z;
+  const int64_t L = blockIdx.x + NB * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t w_item = (W & 7) == 0 ? (L & 7) * (W >> 3) + (L >> 3) : L;
+  const int nb = (int)(w_item % NB);
+  const int64_t combo = w_item / NB;  // hk + hkv * (b * S + sp)
+  const int hk = (int)(combo % gridDim.y);
+  const int bs = (int)(combo / gridDim.y);
   const int b = bs / S, sp = bs - b * S;
 
   int sq = a.seqlen_q, sk = a.seqlen_k, q_tok0 = 0;
