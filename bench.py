@@ -1,25 +1,34 @@
 #!/usr/bin/env python3
 """Benchmark of the exact-attention hot path on one MI355X.
 
-One step = one prefill forward on the causal GQA workload (B1, Hq32/Hkv4,
-S4096, D128) plus one paged split-KV decode (B16, Hq32/Hkv4, D128, Sk32768,
-256-token pages in a random page table, 16 splits, then the LSE combine).
-Inputs are resident in HBM before timing starts.
+One step runs the five benchmark workloads once each, every input resident in
+HBM before timing starts:
+  C1 tiny non-causal MHA (B1, Hq=Hkv=2, S256, D64),
+  C2 causal GQA prefill (B1, Hq32/Hkv4, S4096, D128),
+  C3 long causal GQA prefill (B1, Hq16/Hkv2, S16384, D256),
+  C4 varlen causal sliding-window prefill (8 packed sequences, Hq32/Hkv8, D128,
+     window 1024 left / 0 right),
+  C5 paged split-KV decode (B16, Hq32/Hkv4, D128, Sk32768, 256-token pages in
+     a random page table, 16 splits, then the LSE combine).
 
-Prints ONE JSON line on stdout. `value` is the prefill forward's algorithmic
-throughput: 4*D*(visible query-key pairs)*Hq flops per launch (causal pairs
-only) over the launch's duration measured with HIP events on the launch
-stream. The decode half is reported under "decode" as K/V bytes read per
-second (plus Q, O, LSE and page-table bytes). Progress goes to stderr.
+Prints ONE JSON line on stdout. `value` is C3's (the largest prefill that fits
+one GPU) algorithmic throughput: 4*D*(visible query-key pairs)*Hq flops per
+launch (causal pairs only) over the launch's duration, measured with HIP events
+recorded on the launch stream around every launch of the timed steps. Every
+workload has its own entry under "workloads" (average launch time, throughput,
+roofline fraction, HBM counter traffic); the decode's K/V bytes per second is
+also under "decode". Progress goes to stderr.
 
 Flags: --gpus N (only 1 is supported: the path is single-GPU), --steps K,
---warmup W, --no-cpu-baseline, --cpu-seconds S (oracle sample budget),
---all-configs (also time the other benchmark workloads; stderr only).
+--warmup W, --warmup-gpu-ms T, --no-cpu-baseline, --cpu-seconds S (oracle
+sample budget), --all-configs (also time further workloads: head dims 96/192,
+paged prefill, softcap, backward, fp8 decode).
 
-The default warmup is 200 steps (~70 ms of GPU work): on MI355X the core
-clock climbs for the first few tens of milliseconds of sustained matrix-core
-load, and a handful of warmup steps times the prefill ~20% slower than it
-runs in steady state.
+Warm-up: W untimed steps, then more untimed steps until at least T ms (default
+1000) of GPU time has passed since the first. The core clock climbs only under
+sustained matrix-core load; a step-count warm-up of a few steps times the
+prefill kernels ~20% slower than they run in steady state. The line states
+both (`warmup`, `warmup_gpu_ms`).
 """
 from __future__ import annotations
 
@@ -39,15 +48,15 @@ PEAK_HBM_GBS = 8000.0
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "exact_attention_45_amd", "csrc")
+PROFILES = os.path.join(HERE, "profiles")
 # sources whose compiled code the counted kernels consist of
 KERNEL_SOURCES = {
+    "fwd_pp_kernel<64>": ["fwd_pp_kernel.hip", "attn_common.hpp", "kernels.hpp"],
     "fwd_pp_kernel<128>": ["fwd_pp_kernel.hip", "attn_common.hpp", "kernels.hpp"],
+    "fwd_sp_kernel<256,1>": ["fwd_sp_kernel.hip", "attn_common.hpp", "kernels.hpp"],
     "decode_stream_kernel<128>": ["decode_stream_kernel.hip", "attn_common.hpp", "kernels.hpp"],
     "combine_kernel<128>": ["decode_kernel.hip", "attn_common.hpp", "kernels.hpp"],
-    "fwd_sp_kernel<256,1>": ["fwd_sp_kernel.hip", "attn_common.hpp", "kernels.hpp"],
 }
-COUNTER_SUMMARY = os.path.join(
-    HERE, "profiles", "hbm_counters_prefill_s4096_d128_and_paged_decode_sk32768.md")
 
 
 def source_digest(kernel: str) -> str:
@@ -59,23 +68,33 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(*kernels: str):
-    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch, summed over `kernels`,
-    read from the committed counter summary; None when the summary has no
-    line for one of them or its sources changed since the counters were taken."""
-    try:
-        with open(COUNTER_SUMMARY) as fh:
-            lines = fh.read().splitlines()
-    except OSError:
-        return None
+def _traffic_lines():
+    """`traffic:` lines of the committed counter summaries under profiles/."""
     found = {}
-    for ln in lines:
-        if ln.startswith("traffic: "):
-            kv = dict(t.split("=", 1) for t in ln[len("traffic: "):].split())
-            found[kv.get("kernel")] = kv
+    try:
+        names = sorted(os.listdir(PROFILES))
+    except OSError:
+        return found
+    for n in names:
+        if not n.endswith(".md"):
+            continue
+        with open(os.path.join(PROFILES, n)) as fh:
+            for ln in fh.read().splitlines():
+                if ln.startswith("traffic: "):
+                    kv = dict(t.split("=", 1) for t in ln[len("traffic: "):].split())
+                    found[(kv.get("kernel"), kv.get("workload"))] = kv
+    return found
+
+
+def counter_traffic(workload: str, *kernels: str):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch of `workload`, summed
+    over `kernels`, read from the committed counter summaries; None when a
+    summary has no line for one of them or the kernel's sources changed since
+    the counters were taken."""
+    found = _traffic_lines()
     total = 0
     for k in kernels:
-        kv = found.get(k)
+        kv = found.get((k, workload))
         if kv is None or kv.get("source_sha256") != source_digest(k):
             return None
         total += int(kv["fetch_bytes"]) + int(kv["write_bytes"])
@@ -89,8 +108,9 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-gpu-ms", type=float, default=1000.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--all-configs", action="store_true")
@@ -255,9 +275,12 @@ def warm_up(torch, fn, gpu_ms: float = 40.0):
 
 
 def cpu_baseline(w, budget_s: float):
-    """The float64 oracle (full score matrices) on a bounded sample of the
-    prefill workload: whole query heads, one after another, until the budget
-    is spent. Throughput uses the same causal-adjusted flop count."""
+    """The float64 oracle on a bounded sample of a dense causal prefill
+    workload: blocks of 512 query rows (full fp64 score rows against every
+    key, masked as the definition says), taken from the last rows backwards,
+    query head 0 first, then head 1, ..., until the budget is spent.
+    Throughput uses the same causal-adjusted flop count (visible pairs of the
+    sampled rows)."""
     import numpy as np
     import oracle.attention as OA
     import workloads as W
@@ -266,28 +289,112 @@ def cpu_baseline(w, budget_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    q = W.bf16_bits_to_f64(w.q[0])
-    k = W.bf16_bits_to_f64(w.k[0])
-    v = W.bf16_bits_to_f64(w.v[0])
-    r = w.num_heads_q // w.num_heads_kv
-    vis = OA.visible_mask(w.seqlen_q, w.seqlen_k, w.causal, w.window_left, w.window_right)
-    pairs = int(vis.sum())
+    S, r = w.seqlen_q, w.num_heads_q // w.num_heads_kv
+    blk = 512
     t0 = time.perf_counter()
-    heads = 0
-    while heads < w.num_heads_q:
-        g = heads // r
-        OA.attention_head(q[:, heads], k[:, g], v[:, g], w.softmax_scale, vis)
-        heads += 1
-        if time.perf_counter() - t0 >= budget_s:
+    pairs = rows = 0
+    heads = set()
+    done = False
+    for h in range(w.num_heads_q):
+        g = h // r
+        k = W.bf16_bits_to_f64(w.k[0, :, g])
+        v = W.bf16_bits_to_f64(w.v[0, :, g])
+        for hi in range(S, 0, -blk):
+            pos = np.arange(max(0, hi - blk), hi)
+            q = W.bf16_bits_to_f64(w.q[0, pos, h])
+            OA.attention_rows(q, pos, k, v, w.softmax_scale, S, w.causal, w.window_left,
+                              w.window_right)
+            pairs += int(OA.visible_mask(S, w.seqlen_k, w.causal, w.window_left,
+                                         w.window_right, rows=pos).sum())
+            rows += len(pos)
+            heads.add(h)
+            if time.perf_counter() - t0 >= budget_s:
+                done = True
+                break
+        if done:
             break
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.head_dim * pairs * heads
-    del np
+    flops = 4.0 * w.head_dim * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{heads} of {w.num_heads_q} query heads of the causal GQA S{w.seqlen_q} "
-                      f"D{w.head_dim} prefill workload, full fp64 score matrices, "
-                      f"{dt:.1f} s wall"}
+            "sample": f"{rows} query rows ({pairs} visible pairs) of {len(heads)} of "
+                      f"{w.num_heads_q} query heads of the {w.name} workload, full fp64 "
+                      f"score rows, {dt:.1f} s wall"}
+
+
+# (workload id, label, kernel(s) the counters and the roofline refer to)
+STEP = (
+    (1, "C1 tiny non-causal MHA B1 Hq2 Hkv2 S256 D64", ("fwd_pp_kernel<64>",)),
+    (2, "C2 causal GQA prefill B1 Hq32 Hkv4 S4096 D128", ("fwd_pp_kernel<128>",)),
+    (3, "C3 long causal GQA prefill B1 Hq16 Hkv2 S16384 D256", ("fwd_sp_kernel<256,1>",)),
+    (4, "C4 varlen causal window prefill 8 seqs Hq32 Hkv8 D128 wl1024 wr0",
+     ("fwd_pp_kernel<128>",)),
+    (5, "C5 paged split-KV decode B16 Hq32 Hkv4 D128 Sk32768 page256 16 splits",
+     ("decode_stream_kernel<128>", "combine_kernel<128>")),
+)
+HEADLINE = 3
+
+
+def timed_extra(torch, fn, n):
+    """Median per-launch duration (ms) of fn after a 40 ms GPU-time warm-up."""
+    warm_up(torch, fn)
+    ms = sorted(time_launches(torch, fn, n))
+    return ms[len(ms) // 2]
+
+
+def extra_workloads(mi, W, torch, args, extra):
+    """--all-configs: head dims 96/192, paged prefill, softcap, backward and
+    fp8 decode (median of event-timed launches, stderr and "other_workloads")."""
+    n = max(5, args.steps)
+    paged = W.paged_prefill_case(1002, 1, 32, 4, 128, 256, 16, None, seqlen_q=4096,
+                                 causal=True, name="paged256_causal_gqa32x4_s4096_d128")
+    d96 = W.dense_case(1006, 1, 4096, 4096, 32, 4, 96, causal=True,
+                       name="causal_gqa32x4_s4096_d96")
+    d192 = W.dense_case(1007, 1, 8192, 8192, 16, 2, 192, causal=True,
+                        name="causal_gqa16x2_s8192_d192")
+    for wi in (paged, d96, d192):
+        p = Prefill(mi, wi, torch)
+        med = timed_extra(torch, p, n)
+        f = prefill_flops(wi)
+        extra[wi.name] = {"median_us": med * 1e3, "tflops": f / (med * 1e-3) / 1e12,
+                          "frac": f / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        log(f"[bench] {wi.name}: {med * 1e3:.1f} us, {extra[wi.name]['tflops']:.1f} TFLOP/s")
+        del p
+        torch.cuda.empty_cache()
+    wc = W.standard_config(2)
+    pc = Prefill(mi, wc, torch, softcap=30.0)
+    med = timed_extra(torch, pc, n)
+    f = prefill_flops(wc)
+    name = "softcap30_" + wc.name
+    extra[name] = {"median_us": med * 1e3, "tflops": f / (med * 1e-3) / 1e12,
+                   "frac": f / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    log(f"[bench] {name}: {med * 1e3:.1f} us, {extra[name]['tflops']:.1f} TFLOP/s")
+    del pc
+    torch.cuda.empty_cache()
+    # backward; algorithmic flops 2.5x the forward's (five tile products per
+    # score tile against two)
+    for wb in (W.standard_config(2),):
+        bw = Backward(mi, wb, torch)
+        med = timed_extra(torch, bw, n)
+        f = 2.5 * prefill_flops(wb)
+        name = "backward_" + wb.name
+        extra[name] = {"median_us": med * 1e3, "tflops": f / (med * 1e-3) / 1e12,
+                       "frac": f / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        log(f"[bench] {name}: {med * 1e3:.1f} us, {extra[name]['tflops']:.1f} TFLOP/s")
+        del bw
+        torch.cuda.empty_cache()
+    for fmt, wname in (("e4m3", "paged_decode_fp8_b16_sk32768"),
+                       ("e5m2", "paged_decode_fp8_e5m2_b16_sk32768")):
+        w8 = W.paged_decode_fp8_case(1005, 16, 32, 4, 128, 256, 128, num_splits=16,
+                                     name=wname, fmt=fmt)
+        d8 = Decode(mi, w8, torch)
+        med = timed_extra(torch, d8, n)
+        gb = decode_bytes(w8) / (med * 1e-3) / 1e9
+        extra[w8.name] = {"median_us": med * 1e3, "gbs": gb, "frac": gb / PEAK_HBM_GBS,
+                          "bytes_per_launch": decode_bytes(w8)}
+        log(f"[bench] {w8.name}: {med * 1e3:.1f} us, {gb:.0f} GB/s")
+        del d8, w8
+        torch.cuda.empty_cache()
 
 
 def main():
@@ -309,125 +416,95 @@ def main():
     mi.load()  # raises if the HIP library is missing
     torch.cuda.init()
     log("[bench] generating inputs")
-    w2 = W.standard_config(2)
-    w5 = W.standard_config(5)
-    pre = Prefill(mi, w2, torch)
-    dec = Decode(mi, w5, torch)
-    flops = prefill_flops(w2)
-    dbytes = decode_bytes(w5)
+    ws, runs, work = {}, {}, {}
+    for i, label, _ in STEP:
+        ws[i] = W.standard_config(i)
+        if ws[i].kind == "paged":
+            runs[i] = Decode(mi, ws[i], torch)
+            work[i] = decode_bytes(ws[i])
+        else:
+            runs[i] = Prefill(mi, ws[i], torch)
+            work[i] = prefill_flops(ws[i])
+        if i not in (HEADLINE,):
+            ws[i].q = ws[i].k = ws[i].v = None  # host copies no longer needed
     torch.cuda.synchronize()
 
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        pre()
-        dec()
+    def step():
+        for i, _, _ in STEP:
+            runs[i]()
+
+    stream = torch.cuda.current_stream()
+    log(f"[bench] warmup: {args.warmup} steps, then until {args.warmup_gpu_ms:.0f} ms of GPU time")
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    t0 = time.perf_counter()
+    nw = 0
+    while nw < args.warmup or (time.perf_counter() - t0) * 1e3 < args.warmup_gpu_ms:
+        step()
+        nw += 1
+        if nw % 8 == 0:
+            torch.cuda.synchronize()
+    w1.record(stream)
     torch.cuda.synchronize()
+    warm_gpu_ms = w0.elapsed_time(w1)
 
     log(f"[bench] timing {args.steps} steps")
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in STEP] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in ev:
-        e[0].record(stream)
-        pre()
-        e[1].record(stream)
-        e[2].record(stream)
-        dec()
-        e[3].record(stream)
+        for (i, _, _), (a, b) in zip(STEP, e):
+            a.record(stream)
+            runs[i]()
+            b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    dec_ms = [e[2].elapsed_time(e[3]) for e in ev]
-    pre_avg = sum(pre_ms) / len(pre_ms)
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    tflops = flops / (pre_avg * 1e-3) / 1e12
-    gbs = dbytes / (dec_avg * 1e-3) / 1e9
-    log(f"[bench] prefill {pre_avg * 1e3:.1f} us ({tflops:.1f} TFLOP/s), "
-        f"decode {dec_avg * 1e3:.1f} us ({gbs:.0f} GB/s)")
+
+    per = {}
+    for j, (i, label, kernels) in enumerate(STEP):
+        ms = [e[j][0].elapsed_time(e[j][1]) for e in ev]
+        avg = sum(ms) / len(ms)
+        rec = {"label": label, "kernel": " + ".join(kernels), "avg_launch_us": round(avg * 1e3, 2),
+               "min_launch_us": round(min(ms) * 1e3, 2)}
+        if ws[i].kind == "paged":
+            gbs = work[i] / (avg * 1e-3) / 1e9
+            rec.update({"bound": "hbm", "achieved": round(gbs, 1), "unit": "GB/s",
+                        "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "bytes_per_launch": work[i]})
+            log(f"[bench] {label}: {avg * 1e3:.1f} us, {gbs:.0f} GB/s")
+        else:
+            tf = work[i] / (avg * 1e-3) / 1e12
+            rec.update({"bound": "mfma", "achieved": round(tf, 2), "unit": "TFLOP/s",
+                        "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "flops_per_launch": work[i]})
+            log(f"[bench] {label}: {avg * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+        rec["traffic"] = counter_traffic(ws[i].name, *kernels)
+        per[ws[i].name] = rec
 
     extra = {}
     if args.all_configs:
-        # the three other prefill workloads, then the causal GQA S4096 D128 one
-        # with K/V in a cache of 256-token pages behind a permuted page table
-        paged = W.paged_prefill_case(1002, 1, 32, 4, 128, 256, 16, None, seqlen_q=4096,
-                                     causal=True, name="paged256_causal_gqa32x4_s4096_d128")
-        d96 = W.dense_case(1006, 1, 4096, 4096, 32, 4, 96, causal=True,
-                           name="causal_gqa32x4_s4096_d96")
-        d192 = W.dense_case(1007, 1, 8192, 8192, 16, 2, 192, causal=True,
-                            name="causal_gqa16x2_s8192_d192")
-        for i in (1, 3, 4, paged, d96, d192):
-            wi = W.standard_config(i) if isinstance(i, int) else i
-            p = Prefill(mi, wi, torch)
-            warm_up(torch, p)
-            ms = time_launches(torch, p, max(5, args.steps // 2))
-            ms.sort()
-            med = ms[len(ms) // 2]
-            f = prefill_flops(wi)
-            extra[wi.name] = {"median_us": med * 1e3, "tflops": f / (med * 1e-3) / 1e12,
-                              "frac": f / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-            log(f"[bench] {wi.name}: {med * 1e3:.1f} us, {extra[wi.name]['tflops']:.1f} TFLOP/s")
-            del p
-            torch.cuda.empty_cache()
-        # the causal GQA S4096 D128 workload with logit soft-capping (cap 30)
-        wc = W.standard_config(2)
-        pc = Prefill(mi, wc, torch, softcap=30.0)
-        warm_up(torch, pc)
-        ms = sorted(time_launches(torch, pc, max(5, args.steps // 2)))
-        med = ms[len(ms) // 2]
-        f = prefill_flops(wc)
-        name = "softcap30_" + wc.name
-        extra[name] = {"median_us": med * 1e3, "tflops": f / (med * 1e-3) / 1e12,
-                       "frac": f / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-        log(f"[bench] {name}: {med * 1e3:.1f} us, {extra[name]['tflops']:.1f} TFLOP/s")
-        del pc
+        del runs
         torch.cuda.empty_cache()
-        # backward of the causal GQA S4096 D128 workload; algorithmic flops
-        # 2.5x the forward's (five tile products per score tile against two)
-        wb = W.standard_config(2)
-        bw = Backward(mi, wb, torch)
-        warm_up(torch, bw)
-        ms = sorted(time_launches(torch, bw, max(5, args.steps // 2)))
-        med = ms[len(ms) // 2]
-        f = 2.5 * prefill_flops(wb)
-        name = "backward_" + wb.name
-        extra[name] = {"median_us": med * 1e3, "tflops": f / (med * 1e-3) / 1e12,
-                       "frac": f / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-        log(f"[bench] {name}: {med * 1e3:.1f} us, {extra[name]['tflops']:.1f} TFLOP/s")
-        del bw
-        torch.cuda.empty_cache()
-        # the paged decode workload with an fp8 cache, e4m3 then e5m2
-        # (per-(batch, KV head) descales): half the K/V bytes
-        del dec
-        torch.cuda.empty_cache()
-        for fmt, wname in (("e4m3", "paged_decode_fp8_b16_sk32768"),
-                           ("e5m2", "paged_decode_fp8_e5m2_b16_sk32768")):
-            w8 = W.paged_decode_fp8_case(1005, 16, 32, 4, 128, 256, 128, num_splits=16,
-                                         name=wname, fmt=fmt)
-            d8 = Decode(mi, w8, torch)
-            warm_up(torch, d8)
-            ms = sorted(time_launches(torch, d8, max(5, args.steps)))
-            med = ms[len(ms) // 2]
-            gb = decode_bytes(w8) / (med * 1e-3) / 1e9
-            extra[w8.name] = {"median_us": med * 1e3, "gbs": gb, "frac": gb / PEAK_HBM_GBS,
-                              "bytes_per_launch": decode_bytes(w8)}
-            log(f"[bench] {w8.name}: {med * 1e3:.1f} us, {gb:.0f} GB/s")
-            del d8, w8
-            torch.cuda.empty_cache()
+        extra_workloads(mi, W, torch, args, extra)
 
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(w2, args.cpu_seconds)
+        cpu = cpu_baseline(ws[HEADLINE], args.cpu_seconds)
         log(f"[bench] oracle {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
 
+    head = per[ws[HEADLINE].name]
+    dec = per[ws[5].name]
     rec = {
         "metric": METRIC,
-        "value": round(tflops, 2),
+        "value": head["achieved"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": nw,
+        "warmup_gpu_ms": round(warm_gpu_ms, 1),
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -435,25 +512,25 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "causal GQA prefill B1 Hq32 Hkv4 S4096 D128 (value) + paged split-KV "
-                        "decode B16 Hq32 Hkv4 D128 Sk32768 page256 16 splits (decode)",
-            "prefill_flops_per_launch": flops,
-            "decode_bytes_per_launch": dbytes,
+            "workload": "long causal GQA prefill B1 Hq16 Hkv2 S16384 D256 (value); every step "
+                        "also runs the tiny MHA, causal GQA S4096 D128, varlen window and paged "
+                        "split-KV decode workloads (each under workloads)",
+            "prefill_flops_per_launch": work[HEADLINE],
+            "decode_bytes_per_launch": work[5],
         },
         "roofline": {
-            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": counter_traffic("fwd_pp_kernel<128>"),
-            "kernel": "fwd_pp_kernel<128>", "avg_launch_us": round(pre_avg * 1e3, 2),
+            "bound": "mfma", "achieved": head["achieved"], "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": head["frac"], "traffic": head["traffic"],
+            "kernel": head["kernel"], "avg_launch_us": head["avg_launch_us"],
         },
         "cpu_baseline": cpu,
         "decode": {
-            "value": round(gbs, 1), "unit": "GB/s", "avg_launch_us": round(dec_avg * 1e3, 2),
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": counter_traffic("decode_stream_kernel<128>", "combine_kernel<128>"),
-                         "kernel": "decode_stream_kernel<128> + combine_kernel<128>"},
+            "value": dec["achieved"], "unit": "GB/s", "avg_launch_us": dec["avg_launch_us"],
+            "roofline": {"bound": "hbm", "achieved": dec["achieved"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": dec["frac"], "traffic": dec["traffic"],
+                         "kernel": dec["kernel"]},
         },
+        "workloads": per,
     }
     if extra:
         rec["other_workloads"] = extra

@@ -583,8 +583,15 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
         out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=dev)
     else:
         _req_bf16("out", out, dev)
+        if tuple(out.shape) != (B, hq, d):
+            raise MiAttnError(MI_ATTN_EINVAL, f"out must have shape {(B, hq, d)}")
     if lse is None and return_lse:
         lse = torch.empty(B, hq, dtype=torch.float32, device=dev)
+    elif lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, hq) \
+                or not lse.is_cuda or lse.device != dev:
+            raise MiAttnError(MI_ATTN_EINVAL, f"lse must be a contiguous float32 {(B, hq)} "
+                                              f"tensor on {dev}")
     if workspace is None:
         nbytes = mi_attn_decode_workspace_bytes(q, k_cache, v_cache, page_table, num_splits)
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)

@@ -44,6 +44,18 @@ void normalise_window(int causal, int wl_in, int wr_in, int* wl, int* wr) {
   if (causal) *wr = 0;
 }
 
+// softmax_scale * log2(e), the factor the kernels apply to raw scores inside
+// exp2. A zero scale (every score 0: uniform weights over the visible keys)
+// is raised to a tiny positive value: masked scores are -inf, and -inf * 0
+// would be NaN where -inf * 1e-30 is -inf (weight 0); visible raw scores
+// times 1e-30 round to exactly 0 against the running max, so the weights
+// stay exactly uniform. The LSE uses softmax_scale itself.
+constexpr float kMinExp2Scale = 1e-30f;
+float exp2_scale(float scale) {
+  const float c = scale * 1.4426950408889634f;
+  return c > kMinExp2Scale ? c : kMinExp2Scale;
+}
+
 constexpr size_t kAlign = 256;
 constexpr int64_t kFwdRowsPerTile = mi_attn::kFwdBlockN;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -55,18 +67,17 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // row block, split) and aims at one wave per SIMD (four per compute unit);
 // the tile kernel runs one workgroup per (sequence, KV head, row block,
 // split) and aims at two workgroups per compute unit.
+// The compute-unit count is that of the gfx950 parts this library is built
+// for (MI350X / MI355X: 256), a constant rather than a device query, so the
+// split count and the workspace size are pure functions of the parameters
+// and sizing makes no HIP call. A partitioned device with fewer units only
+// gets more splits than it needs, never a wrong result.
+constexpr int kComputeUnits = 256;
 int split_heuristic(const mi_attn_decode_params* p) {
   const int cap = p->max_pages_per_seq * p->page_size;
   const int n_blocks = (cap + mi_attn::kDecBlockN - 1) / mi_attn::kDecBlockN;
   if (n_blocks <= 4) return 1;
-  int cus = 256;
-  int dev = 0;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        v > 0)
-      cus = v;
-  }
+  const int cus = kComputeUnits;
   const int group = p->num_heads_q / p->num_heads_kv;
   const long work = (long)p->batch * p->num_heads_kv * ((group + 31) / 32);
   const long per_cu = mi_attn::decode_streams(p->head_dim, p->page_size) ? 4L : 2L;
@@ -272,7 +283,7 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
   a.total_q = p->total_q;
   a.max_rows = max_q * group;
   a.scale = p->softmax_scale;
-  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.scale_log2 = exp2_scale(p->softmax_scale);
   normalise_window(p->causal, p->window_left, p->window_right, &a.wl, &a.wr);
   if (((int64_t)a.max_rows + mi_attn::kFwdBlockM - 1) / mi_attn::kFwdBlockM * a.hkv * a.batch >
       INT32_MAX)
@@ -333,7 +344,7 @@ int mi_attn_decode_splitkv(const mi_attn_decode_params* p, void* stream) {
   a.num_splits = splits;
   a.row_blocks = (group + 31) / 32;
   a.scale = p->softmax_scale;
-  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.scale_log2 = exp2_scale(p->softmax_scale);
   int wl, wr;
   normalise_window(p->causal, p->window_left, p->window_right, &wl, &wr);
   a.wl = wl;
@@ -502,7 +513,7 @@ int check_bwd(const mi_attn_bwd_params* p, mi_attn::BwdArgs* a) {
   a->group = group;
   a->total_q = varlen ? p->total_q : 0;
   a->scale = p->softmax_scale;
-  a->scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a->scale_log2 = exp2_scale(p->softmax_scale);
   normalise_window(p->causal, p->window_left, p->window_right, &a->wl, &a->wr);
   return MI_ATTN_OK;
 }

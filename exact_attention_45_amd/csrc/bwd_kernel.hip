@@ -666,8 +666,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         *reinterpret_cast<bf16x4*>(dvp + d0) =
             cvt4(dva[db][4 * i], dva[db][4 * i + 1], dva[db][4 * i + 2], dva[db][4 * i + 3]);
       }
-  } else {
-    // partial row (split, sequence, key, KV head): dK then dV, D floats each
+  } else if (key < a.seqlen_k) {
+    // partial row (split, sequence, key, KV head): dK then dV, D floats each.
+    // The partial buffer holds seqlen_k (the caller's max_seqlen_k) keys per
+    // sequence; keys of a longer sequence (an understated maximum) are not
+    // written anywhere.
     float* pp = a.dkv_part +
                 ((((int64_t)sp * a.batch + b) * a.seqlen_k + key) * a.hkv + hk) * (2 * D);
 #pragma unroll

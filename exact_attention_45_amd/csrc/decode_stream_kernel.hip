@@ -180,8 +180,12 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
     if (a.k_descale != nullptr) kds = a.k_descale[(int64_t)b * a.hkv + hk];
     if (a.v_descale != nullptr) vds = a.v_descale[(int64_t)b * a.hkv + hk];
   }
-  const float c = a.scale_log2 * kds;
-  const float rescale_raw = C::RESCALE_LOG2 / fmaxf(c, 1e-30f);
+  // a zero key descale makes every score 0 (uniform weights; the constant is
+  // kept positive so masked -inf scores still give weight 0); a negative or
+  // NaN one has no meaning for a cache scale: this wave's rows get NaN
+  bad |= !(kds >= 0.0f);
+  const float c = fmaxf(a.scale_log2 * kds, 1e-30f);
+  const float rescale_raw = C::RESCALE_LOG2 / c;
   // soft-capping of scale * kds * s (a zero effective scale leaves all scores 0)
   const float sc_eff = a.scale * kds;
   const float sc_k1x = SC && sc_eff != 0.0f ? 2.0f * kLog2e * sc_eff / a.softcap : 0.0f;

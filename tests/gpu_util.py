@@ -10,6 +10,9 @@ correctly rounded oracle value, and the test reports how many did.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -73,3 +76,16 @@ def check(o_gpu, o_ref, lse_gpu=None, lse_ref=None, what=""):
         stats["lse_max_abs"] = float(d.max(initial=0.0))
         assert stats["lse_max_abs"] <= LSE_ABS, f"{what}: LSE max abs {stats['lse_max_abs']:.3e}"
     return stats
+
+
+def run_parallel(jobs, workers: int = 0):
+    """Runs the callables in `jobs` on a thread pool and returns their results
+    in order. numpy releases the interpreter lock inside its array kernels, so
+    independent per-head oracle evaluations overlap; BLAS is limited to two
+    threads per call to avoid oversubscribing the host."""
+    from threadpoolctl import threadpool_limits
+    if workers <= 0:
+        workers = max(1, min(8, len(os.sched_getaffinity(0)) // 2))
+    with threadpool_limits(limits=2):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(lambda f: f(), jobs))

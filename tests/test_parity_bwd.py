@@ -186,6 +186,20 @@ def test_bwd_full_size_sampled(gpu_lib):
         check_grad(dv[0, j, gk], dv_w[n], f"dv key {j}")
 
 
+def test_bwd_zero_scale(gpu_lib):
+    """softmax_scale = 0: P is uniform over each row's visible keys, dQ = dK =
+    0, dV = P^T dO; masked keys (causal, rows with no key) must not give NaN."""
+    print("[case] bwd zero scale", flush=True)
+    for B, Sq, Sk, D in ((1, 130, 130, 128), (1, 90, 40, 64)):
+        w = W.dense_case(93 + Sq, B, Sq, Sk, 4, 2, D, causal=True, softmax_scale=0.0)
+        g = W.grad_output(93 + Sq, (B, Sq, 4, D))
+        dq, dk, dv = run_dense(gpu_lib, w, g)
+        ref = OA.attention_dense_backward(f64(w.q), f64(w.k), f64(w.v), f64(g), 0.0,
+                                          causal=True)
+        for nm, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            print("scale0", nm, check_grad(host_f64(got), r, f"scale0 {nm}"))
+
+
 def test_bwd_rejects_head_dim_256(gpu_lib):
     w = W.dense_case(3, 1, 64, 64, 2, 1, 256)
     q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)

@@ -131,3 +131,36 @@ def test_combine_kernel(gpu_lib, rows, splits, d):
     assert np.array_equal(np.isneginf(l), ~fin)
     assert np.abs(l[fin] - l_ref[fin]).max() <= 1e-5
     assert np.all(o[0] == 0) and np.isneginf(l[0])
+
+
+def test_decode_zero_scale(gpu_lib):
+    """softmax_scale = 0: uniform weights over each sequence's keys; ragged
+    lengths leave masked key slots in the last slice, which must get weight
+    0 (not NaN), and an empty sequence gets O = 0, LSE = -inf."""
+    print("[case] decode zero scale", flush=True)
+    w = W.paged_decode_case(91, 3, 16, 2, 128, 64, 5, seqused_k=[1, 250, 0], num_splits=3,
+                            softmax_scale=0.0)
+    out, lse = run_decode(gpu_lib, w)
+    o_ref, l_ref = oracle_decode(w)
+    print("decode scale0", check(host_f64(out), o_ref, host_f64(lse), l_ref, what="scale0"))
+
+
+def test_decode_rejects_bad_out_and_lse(gpu_lib):
+    """Caller-supplied out must be (B, Hq, D) bf16 and lse a contiguous
+    float32 (B, Hq) tensor on the same device; the binding refuses anything
+    the combine would write past."""
+    w = W.paged_decode_case(92, 2, 8, 2, 128, 64, 2, num_splits=2)
+    q, kc, vc = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    pt = dev_i32(w.page_table)
+    bad = [
+        dict(out=torch.empty(2, 4, 128, dtype=torch.bfloat16, device="cuda")),
+        dict(out=torch.empty(2, 8, 128, dtype=torch.float16, device="cuda")),
+        dict(lse=torch.empty(2, 8, dtype=torch.bfloat16, device="cuda")),
+        dict(lse=torch.empty(2, 4, dtype=torch.float32, device="cuda")),
+        dict(lse=torch.empty(8, 2, dtype=torch.float32, device="cuda").t()),
+        dict(lse=torch.empty(2, 8, dtype=torch.float32)),
+    ]
+    for kw in bad:
+        with pytest.raises(gpu_lib.MiAttnError) as e:
+            gpu_lib.mi_attn_decode_splitkv(q, kc, vc, pt, num_splits=2, **kw)
+        assert e.value.code == gpu_lib.MI_ATTN_EINVAL, kw

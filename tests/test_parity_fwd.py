@@ -9,7 +9,7 @@ import torch
 
 import oracle.attention as OA
 import workloads as W
-from tests.gpu_util import check, dev_bf16, dev_i32, f64, host_f64
+from tests.gpu_util import check, dev_bf16, dev_i32, f64, host_f64, run_parallel
 
 pytestmark = pytest.mark.gpu
 
@@ -108,61 +108,75 @@ def _sample_rows(rng, n_rows, count, must=()):
     return np.array(sorted(idx))
 
 
-def _check_sampled_dense(w, out, lse, n_pos, heads, seed):
-    rng = np.random.default_rng(seed)
-    S = w.seqlen_q
-    pos = _sample_rows(rng, S, n_pos, must=(0, 1, 63, 64, 127, 128, S - 1))
-    q = f64(w.q[0])  # (S, Hq, D)
-    k = f64(w.k[0])
-    v = f64(w.v[0])
-    r = w.num_heads_q // w.num_heads_kv
-    o_gpu = host_f64(out[0][torch.as_tensor(pos)])   # (n, Hq, D)
-    l_gpu = host_f64(lse[0][:, torch.as_tensor(pos)])  # (Hq, n)
-    worst = {}
-    for h in heads:
-        g = h // r
-        o_ref, l_ref = OA.attention_rows(q[pos, h], pos, k[:, g], v[:, g], w.softmax_scale, S,
-                                         w.causal, w.window_left, w.window_right)
-        st = check(o_gpu[:, h], o_ref, l_gpu[h], l_ref, what=f"{w.name} head {h}")
-        for k_, v_ in st.items():
-            worst[k_] = max(worst.get(k_, 0), v_)
-    return worst
-
-
-@pytest.mark.parametrize("cfg", [2, 3])
-def test_full_size_dense_sampled(gpu_lib, cfg):
-    print(f"[case] full-size workload {cfg}", flush=True)
-    w = W.standard_config(cfg)
+def test_full_size_causal_gqa_s4096_d128_every_element(gpu_lib):
+    """The causal GQA S4096 D128 workload: every output element and every LSE
+    against the oracle (32 full fp64 score matrices)."""
+    print("[case] full-size causal GQA S4096 D128, all outputs", flush=True)
+    w = W.standard_config(2)
     out, lse = run_dense(gpu_lib, w)
-    heads = sorted({0, 1, w.num_heads_q // 2, w.num_heads_q - 1})
-    print(w.name, _check_sampled_dense(w, out, lse, 48, heads, seed=cfg))
+    o_gpu, l_gpu = host_f64(out[0]), host_f64(lse[0])
+    S, r = w.seqlen_q, w.num_heads_q // w.num_heads_kv
+    vis = OA.visible_mask(S, S, w.causal, w.window_left, w.window_right)
+    q, k, v = f64(w.q[0]), f64(w.k[0]), f64(w.v[0])
+
+    def head(h):
+        return lambda: OA.attention_head(q[:, h], k[:, h // r], v[:, h // r], w.softmax_scale, vis)
+    res = run_parallel([head(h) for h in range(w.num_heads_q)])
+    o_ref = np.stack([o for o, _ in res], axis=1)  # (S, Hq, D)
+    l_ref = np.stack([l for _, l in res], axis=0)  # (Hq, S)
+    print(w.name, check(o_gpu, o_ref, l_gpu, l_ref, what=w.name))
 
 
-def test_full_size_varlen_sampled(gpu_lib):
-    print("[case] full-size varlen window workload", flush=True)
+def test_full_size_long_causal_gqa_s16384_d256_all_heads(gpu_lib):
+    """The long causal GQA S16384 D256 workload: all 16 query heads on every
+    row next to a 64-key tile boundary (positions 64t - 1 and 64t), the last
+    64 rows and 64 random rows (about 640 rows per head)."""
+    print("[case] full-size long causal GQA S16384 D256, all heads", flush=True)
+    w = W.standard_config(3)
+    out, lse = run_dense(gpu_lib, w)
+    S, r = w.seqlen_q, w.num_heads_q // w.num_heads_kv
+    rng = np.random.default_rng(3)
+    edges = [p for t in range(S // 64) for p in (64 * t - 1, 64 * t)]
+    pos = _sample_rows(rng, S, 64, must=edges + list(range(S - 64, S)))
+    o_gpu = host_f64(out[0][torch.as_tensor(pos)])    # (n, Hq, D)
+    l_gpu = host_f64(lse[0][:, torch.as_tensor(pos)])  # (Hq, n)
+    k_all, v_all = f64(w.k[0]), f64(w.v[0])
+
+    def head(h):
+        q = f64(w.q[0, pos, h])
+        return lambda: OA.attention_rows(q, pos, k_all[:, h // r], v_all[:, h // r],
+                                         w.softmax_scale, S, w.causal, w.window_left,
+                                         w.window_right)
+    res = run_parallel([head(h) for h in range(w.num_heads_q)], workers=4)
+    o_ref = np.stack([o for o, _ in res], axis=1)
+    l_ref = np.stack([l for _, l in res], axis=0)
+    print(w.name, len(pos), "rows per head", check(o_gpu, o_ref, l_gpu, l_ref, what=w.name))
+
+
+def test_full_size_varlen_window_every_element(gpu_lib):
+    """The varlen sliding-window workload (8 packed sequences, window 1024):
+    every output element and every LSE against the oracle."""
+    print("[case] full-size varlen window workload, all outputs", flush=True)
     w = W.standard_config(4)
     out, lse = run_varlen(gpu_lib, w)
-    rng = np.random.default_rng(44)
+    o_gpu, l_gpu = host_f64(out), host_f64(lse)
     cu = w.cu_seqlens_q
     r = w.num_heads_q // w.num_heads_kv
-    worst = {}
-    o_all = host_f64(out)
-    l_all = host_f64(lse)
+    q, k, v = f64(w.q), f64(w.k), f64(w.v)
+    jobs, keys = [], []
     for b in range(len(cu) - 1):
-        L = int(cu[b + 1] - cu[b])
-        pos = _sample_rows(rng, L, 12, must=(0, 1, 1023, 1024, 1025, L - 1))
-        q = f64(w.q[cu[b]:cu[b + 1]])
-        k = f64(w.k[cu[b]:cu[b + 1]])
-        v = f64(w.v[cu[b]:cu[b + 1]])
-        for h in (0, 5, 31):
-            g = h // r
-            o_ref, l_ref = OA.attention_rows(q[pos, h], pos, k[:, g], v[:, g], w.softmax_scale, L,
-                                             w.causal, w.window_left, w.window_right)
-            st = check(o_all[cu[b] + pos, h], o_ref, l_all[h, cu[b] + pos], l_ref,
-                       what=f"seq {b} head {h}")
-            for k_, v_ in st.items():
-                worst[k_] = max(worst.get(k_, 0), v_)
-    print(w.name, worst)
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        vis = OA.visible_mask(t1 - t0, t1 - t0, w.causal, w.window_left, w.window_right)
+        for h in range(w.num_heads_q):
+            jobs.append(lambda t0=t0, t1=t1, h=h, vis=vis: OA.attention_head(
+                q[t0:t1, h], k[t0:t1, h // r], v[t0:t1, h // r], w.softmax_scale, vis))
+            keys.append((t0, t1, h))
+    o_ref = np.zeros_like(o_gpu)
+    l_ref = np.zeros_like(l_gpu)
+    for (t0, t1, h), (o, l) in zip(keys, run_parallel(jobs)):
+        o_ref[t0:t1, h] = o
+        l_ref[h, t0:t1] = l
+    print(w.name, check(o_gpu, o_ref, l_gpu, l_ref, what=w.name))
 
 
 def test_deterministic(gpu_lib):
@@ -218,3 +232,32 @@ def test_fully_masked_rows_give_zero_and_neg_inf(gpu_lib):
     assert np.all(np.isneginf(l[0, :, :60]))
     o_ref, l_ref = oracle_dense(w)
     check(o, o_ref, l, l_ref, what="masked rows")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_zero_scale_uniform_weights(gpu_lib, d):
+    """softmax_scale = 0: every score is 0, so each row averages the values of
+    its visible keys (LSE = ln |visible keys|); masked keys (causal, ragged
+    tails, fully masked rows) must still get weight 0, not NaN."""
+    print(f"[case] zero scale D{d}", flush=True)
+    w = W.dense_case(77 + d, 2, 150, 203, 4, 2, d, causal=True, softmax_scale=0.0)
+    out, lse = run_dense(gpu_lib, w)
+    o_ref, l_ref = oracle_dense(w)
+    print("zero scale", check(host_f64(out), o_ref, host_f64(lse), l_ref, what=f"scale0 D{d}"))
+    # Sq > Sk: the first rows see no key
+    w = W.dense_case(78 + d, 1, 100, 40, 2, 1, d, causal=True, softmax_scale=0.0)
+    out, lse = run_dense(gpu_lib, w)
+    o_ref, l_ref = oracle_dense(w)
+    check(host_f64(out), o_ref, host_f64(lse), l_ref, what=f"scale0 empty rows D{d}")
+
+
+def test_zero_scale_varlen_window(gpu_lib):
+    print("[case] zero scale varlen window", flush=True)
+    lq = [70, 1, 0, 129, 300]
+    w = W.varlen_case(79, lq, lq, 8, 2, 128, causal=True, window_left=50, window_right=0,
+                      softmax_scale=0.0)
+    out, lse = run_varlen(gpu_lib, w)
+    o_ref, l_ref = OA.attention_varlen(f64(w.q), f64(w.k), f64(w.v), w.cu_seqlens_q,
+                                       w.cu_seqlens_k, 0.0, True, 50, 0)
+    print("zero scale varlen", check(host_f64(out), o_ref, host_f64(lse), l_ref,
+                                     what="scale0 varlen"))
