@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
   mi_attn_fwd(q, k, v, ...)              -> (out, lse)
   mi_attn_bwd(q, k, v, out, dout, lse, ...) -> (dq, dk, dv)
   mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, ...) -> (out, lse)
+  mi_attn_decode_splitkv_noalloc(...)    the same decode with no workspace
+                                         (static per-GPU scratch in the library)
   mi_attn_combine(o_partial, lse_partial, ...) -> (out, lse)
   mi_attn_decode_workspace_bytes(...), mi_attn_decode_num_splits(...)
 """
@@ -24,7 +26,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "MiAttnError", "load", "lib_path", "mi_attn_fwd", "mi_attn_bwd", "mi_attn_bwd_workspace_bytes",
-    "BwdParams", "mi_attn_decode_splitkv",
+    "BwdParams", "mi_attn_decode_splitkv", "mi_attn_decode_splitkv_noalloc",
     "mi_attn_combine", "mi_attn_decode_workspace_bytes", "mi_attn_decode_num_splits",
     "mi_attn_last_error", "mi_attn_version", "FwdParams", "DecodeParams",
     "MI_ATTN_OK", "MI_ATTN_EINVAL", "MI_ATTN_EUNSUPPORTED", "MI_ATTN_EBOUNDS",
@@ -138,6 +140,8 @@ def load(path: Optional[str] = None):
     lib.mi_attn_fwd.restype = ctypes.c_int
     lib.mi_attn_decode_splitkv.argtypes = [ctypes.POINTER(DecodeParams), _vp]
     lib.mi_attn_decode_splitkv.restype = ctypes.c_int
+    lib.mi_attn_decode_splitkv_noalloc.argtypes = [ctypes.POINTER(DecodeParams), _vp]
+    lib.mi_attn_decode_splitkv_noalloc.restype = ctypes.c_int
     lib.mi_attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeParams)]
     lib.mi_attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.mi_attn_decode_num_splits.argtypes = [ctypes.POINTER(DecodeParams)]
@@ -560,6 +564,30 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
     seqused_k int32 (B,) or None. softcap as for mi_attn_fwd (on the descaled scores).
     Returns out (B, Hq, D) bf16 and lse (B, Hq) float32.
     """
+    return _decode(False, q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
+                   num_splits, window_left, workspace, return_lse, check_bounds, k_descale,
+                   v_descale, learnable_sink, softcap)
+
+
+def mi_attn_decode_splitkv_noalloc(q, k_cache, v_cache, page_table, seqused_k=None, out=None,
+                                   lse=None, softmax_scale: Optional[float] = None,
+                                   num_splits: int = 0, window_left: Optional[int] = None,
+                                   return_lse: bool = True, check_bounds: bool = False,
+                                   k_descale=None, v_descale=None, learnable_sink=None,
+                                   softcap: float = 0.0):
+    """mi_attn_decode_splitkv through the C entry point that allocates
+    nothing: the split partials go to the library's static per-GPU scratch
+    (64 MiB; larger requests raise EWORKSPACE) instead of a workspace. Calls
+    that may overlap on one GPU race on that scratch. Pass out (and lse) to
+    keep this call free of allocations on the Python side as well."""
+    return _decode(True, q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
+                   num_splits, window_left, None, return_lse, check_bounds, k_descale,
+                   v_descale, learnable_sink, softcap)
+
+
+def _decode(noalloc, q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
+            num_splits, window_left, workspace, return_lse, check_bounds, k_descale, v_descale,
+            learnable_sink, softcap):
     import torch
     lib = load()
     dev = q.device
@@ -592,7 +620,7 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
                 or not lse.is_cuda or lse.device != dev:
             raise MiAttnError(MI_ATTN_EINVAL, f"lse must be a contiguous float32 {(B, hq)} "
                                               f"tensor on {dev}")
-    if workspace is None:
+    if workspace is None and not noalloc:
         nbytes = mi_attn_decode_workspace_bytes(q, k_cache, v_cache, page_table, num_splits)
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     p = _decode_params(q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
@@ -608,7 +636,8 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
     p.k_descale, p.v_descale = _ptr(k_descale), _ptr(v_descale)
     p.learnable_sink = _req_sink(learnable_sink, hq, dev)
     p.softcap = float(softcap)
-    _check(lib.mi_attn_decode_splitkv(ctypes.byref(p), _stream_ptr(dev)))
+    entry = lib.mi_attn_decode_splitkv_noalloc if noalloc else lib.mi_attn_decode_splitkv
+    _check(entry(ctypes.byref(p), _stream_ptr(dev)))
     return out, lse
 
 

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "bwd.hpp"
 #include "kernels.hpp"
@@ -308,19 +309,22 @@ size_t mi_attn_decode_workspace_bytes(const mi_attn_decode_params* p) {
   return workspace_for(p, resolved_splits(p));
 }
 
-int mi_attn_decode_splitkv(const mi_attn_decode_params* p, void* stream) {
-  int rc = check_decode(p);
-  if (rc == MI_ATTN_OK) rc = check_decode_pointers(p);
-  if (rc != MI_ATTN_OK) return rc;
-  if (p->batch == 0) return ok();
-  const int splits = resolved_splits(p);
-  const size_t need = workspace_for(p, splits);
-  if (p->workspace == nullptr || p->workspace_bytes < need)
-    return fail(MI_ATTN_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need,
-                p->workspace == nullptr ? (size_t)0 : p->workspace_bytes);
-  if ((reinterpret_cast<uintptr_t>(p->workspace) & (kAlign - 1)) != 0)
-    return fail(MI_ATTN_EWORKSPACE, "workspace must be 256-byte aligned");
+}  // extern "C"
 
+// Scratch for mi_attn_decode_splitkv_noalloc: the decode partials live in
+// this file-scope device array (one copy per GPU, held until the process
+// ends) instead of a caller workspace. Host code never passes `scratch`
+// itself (its host-side name is a stand-in, not a device address): the
+// device address comes from hipGetSymbolAddress, once per device
+// (scratch_address below).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// The decode after validation: partials in `ws` (device memory of at least
+// workspace_for(p, splits) bytes, 256-byte aligned), then the combine.
+int decode_launch(const mi_attn_decode_params* p, int splits, void* ws, void* stream) {
   const int group = p->num_heads_q / p->num_heads_kv;
   const size_t rows = (size_t)p->batch * p->num_heads_q;
   mi_attn::DecodeArgs a{};
@@ -329,8 +333,8 @@ int mi_attn_decode_splitkv(const mi_attn_decode_params* p, void* stream) {
   a.v_cache = p->v_cache;
   a.page_table = p->page_table;
   a.seqused_k = p->seqused_k;
-  a.o_part = static_cast<float*>(p->workspace);
-  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(p->workspace) +
+  a.o_part = static_cast<float*>(ws);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                         round_up(rows * splits * p->head_dim * sizeof(float)));
   a.q_bs = p->q_batch_stride;
   a.q_hs = p->q_head_stride;
@@ -377,6 +381,71 @@ int mi_attn_decode_splitkv(const mi_attn_decode_params* p, void* stream) {
   });
   if (e != hipSuccess) return fail(MI_ATTN_EHIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch` (looked up on the first call on each
+// device, with that device current), or NULL with the error set.
+void* scratch_address(int* rc) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *rc = fail(MI_ATTN_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *rc = fail(MI_ATTN_EUNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *rc = fail(MI_ATTN_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int mi_attn_decode_splitkv(const mi_attn_decode_params* p, void* stream) {
+  int rc = check_decode(p);
+  if (rc == MI_ATTN_OK) rc = check_decode_pointers(p);
+  if (rc != MI_ATTN_OK) return rc;
+  if (p->batch == 0) return ok();
+  const int splits = resolved_splits(p);
+  const size_t need = workspace_for(p, splits);
+  if (p->workspace == nullptr || p->workspace_bytes < need)
+    return fail(MI_ATTN_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                p->workspace == nullptr ? (size_t)0 : p->workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(p->workspace) & (kAlign - 1)) != 0)
+    return fail(MI_ATTN_EWORKSPACE, "workspace must be 256-byte aligned");
+  return decode_launch(p, splits, p->workspace, stream);
+}
+
+int mi_attn_decode_splitkv_noalloc(const mi_attn_decode_params* p, void* stream) {
+  int rc = check_decode(p);
+  if (rc == MI_ATTN_OK) rc = check_decode_pointers(p);
+  if (rc != MI_ATTN_OK) return rc;
+  if (p->batch == 0) return ok();
+  const int splits = resolved_splits(p);
+  const size_t need = workspace_for(p, splits);
+  if (need > kScratchBytes)
+    return fail(MI_ATTN_EWORKSPACE, "partials need %zu bytes, beyond the %zu-byte static "
+                "scratch of the no-allocation decode (use mi_attn_decode_splitkv with a "
+                "workspace, or fewer splits)", need, kScratchBytes);
+  void* ws = scratch_address(&rc);
+  if (ws == nullptr) return rc;
+  return decode_launch(p, splits, ws, stream);
 }
 
 int mi_attn_combine(const float* o_partial, const float* lse_partial, void* out,

@@ -244,6 +244,23 @@ size_t mi_attn_decode_workspace_bytes(const mi_attn_decode_params *p);
 
 int mi_attn_decode_splitkv(const mi_attn_decode_params *p, void *stream);
 
+/* The same decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * identical arguments, kernels and results as mi_attn_decode_splitkv, except
+ * that p->workspace and p->workspace_bytes are ignored. The float32 partials
+ * go to a static scratch array of 64 MiB inside the library, one per GPU,
+ * created when the library's code is loaded on that GPU and held until the
+ * process ends; nothing is allocated or freed by this call. A request whose
+ * partials (mi_attn_decode_workspace_bytes(p)) exceed 64 MiB returns
+ * MI_ATTN_EWORKSPACE. The first call on each device looks the array's device
+ * address up (hipGetSymbolAddress) with that device current; a failed
+ * lookup returns MI_ATTN_EHIP.
+ * Every call on one GPU uses that GPU's one array and leaves the last call's
+ * partials in it: calls that can overlap on one GPU (different streams, or
+ * different host threads without ordering) race and must be serialised by
+ * the caller; calls in order on one stream are safe. */
+int mi_attn_decode_splitkv_noalloc(const mi_attn_decode_params *p, void *stream);
+
 /* ------------------------------------------------------------------------
  * LSE-weighted combine of split partials (interface page,
  * `flash_attn_combine` / `_flash_attn_fwd_combine`; split-K page,
