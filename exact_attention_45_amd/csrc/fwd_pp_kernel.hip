@@ -19,10 +19,11 @@
 // from global memory (direct-to-LDS buffer loads, nothing staged in
 // registers). Tile k is read in half-steps 2k..2k+3; tile k+2 is requested
 // during iteration k into the buffer tile k-2 vacated (each group issues its
-// share at the start of its softmax half-step), and an explicit load-count
-// wait plus a barrier at the end of iteration k make tile k+1 visible. Every
-// request is issued unconditionally (tiles past the end re-read the last
-// tile), which keeps the wait counts static.
+// share spread over the S MFMAs of its matrix phase), and an explicit
+// load-count wait plus a barrier at the end of iteration k make tile k+1
+// visible. Every request is issued unconditionally (tiles past the end get
+// zero-length descriptors and load nothing), which keeps the wait counts
+// static.
 #include <climits>
 #include <type_traits>
 
@@ -169,17 +170,32 @@ void fwd_pp_kernel(const FwdArgs a) {
   // One buffer descriptor per tensor per tile, ending at the last row before
   // seqlen_k (rows past it read as zero); its base is the tile's first row,
   // ko / vo elements from the sequence's K / V base (contiguous, or in the
-  // page that holds it). This wave's loads of the tile at key n0 into LDS
-  // buffer buf: K parts i = 0..NI-1, then V parts.
-  auto issue_tile = [&](int n0, int buf, int64_t ko, int64_t vo) {
+  // page that holds it). Tile j >= T (the loop requests two tiles ahead)
+  // gets zero-length descriptors: its loads touch no memory and only write
+  // zeros into a buffer nothing reads again, so every iteration issues the
+  // same number of loads and the load-count waits stay static.
+  struct TileDesc {
+    __amdgpu_buffer_rsrc_t k, v;
+    int buf;
+  };
+  auto tile_desc = [&](int j) __attribute__((always_inline)) {
+    const int jj = min(j, T - 1);
+    const int n0 = (n_begin + jj) * BN;
+    int64_t ko, vo;
+    fwd_tile_rows<PAGED>(a, b, n0, ko, vo);
     const int nrows = min(sk - n0, BN);  // >= 1
-    const auto kr = make_rsrc(kp + ko, (uint32_t)((nrows - 1) * a.k_rs * 2 + D * 2));
-    const auto vr = make_rsrc(vp + vo, (uint32_t)((nrows - 1) * a.v_rs * 2 + D * 2));
-#pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(kr, kdo[i], lds_w + (uint32_t)(buf * BUF_B + i * 1024));
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      dma16(vr, vdo[i], lds_w + (uint32_t)(buf * BUF_B + TILE_B + i * 1024));
+    TileDesc t;
+    t.k = make_rsrc(kp + ko, j < T ? (uint32_t)((nrows - 1) * a.k_rs * 2 + D * 2) : 0u);
+    t.v = make_rsrc(vp + vo, j < T ? (uint32_t)((nrows - 1) * a.v_rs * 2 + D * 2) : 0u);
+    t.buf = j & 3;
+    return t;
+  };
+  // this wave's load p of a tile: K parts p = 0..NI-1, then V parts
+  auto dma_part = [&](const TileDesc& t, int p) __attribute__((always_inline)) {
+    if (p < NI)
+      dma16(t.k, kdo[p], lds_w + (uint32_t)(t.buf * BUF_B + p * 1024));
+    else
+      dma16(t.v, vdo[p - NI], lds_w + (uint32_t)(t.buf * BUF_B + TILE_B + (p - NI) * 1024));
   };
 
   // ---- fragment read offsets. K: lane (c32, half) reads logical chunk
@@ -213,8 +229,12 @@ void fwd_pp_kernel(const FwdArgs a) {
   // accumulators, and scheduling barriers between the {read i + LEAD,
   // MFMA i} groups so the compiler keeps that order.
   constexpr int LEAD = 8;
-  // S(k) = K(k) Q^T into s[]; MFMA i: contraction step i / 2, key block i % 2
-  auto s_part = [&](int k) __attribute__((always_inline)) {
+  // S(k) = K(k) Q^T into s[]; MFMA i: contraction step i / 2, key block i % 2.
+  // This wave's 2 * NI loads of the tile two ahead (descriptor nx) go out
+  // spread over the MFMAs: issued in one burst by the four waves of a group,
+  // 16 direct-to-LDS loads of 1 KB queue in the CU's load path for several
+  // hundred cycles, and the issuing waves stall with them.
+  auto s_part = [&](int k, const TileDesc& nx) __attribute__((always_inline)) {
     const char* kb0 = smem + (k & 3) * BUF_B;
     constexpr int N = 2 * (D / 16);  // i -> cc = i / 2, kb = i % 2
     auto rd = [&](int i) __attribute__((always_inline)) {
@@ -226,11 +246,14 @@ void fwd_pp_kernel(const FwdArgs a) {
     s[0] = zero_f32x16();
     s[1] = zero_f32x16();
     __builtin_amdgcn_sched_barrier(0);
+    constexpr int NP = 2 * NI;  // loads per wave per tile
+    static_assert(N % NP == 0, "loads spread evenly over the MFMAs");
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const bf16x8 kf = ring[i % LEAD];
       if (i + LEAD < N) ring[i % LEAD] = rd(i + LEAD);
       s[i & 1] = mfma32(kf, qf[i >> 1], s[i & 1]);
+      if (i % (N / NP) == 1 % (N / NP)) dma_part(nx, i / (N / NP));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -260,9 +283,10 @@ void fwd_pp_kernel(const FwdArgs a) {
   };
 
   // MFMA item k: O += P(k-1) V(k-1) (k >= 1), then S(k) = K(k) Q^T (k < T)
+  // with the loads of tile k + 2
   auto mfma_item = [&](int k) {
     if (k >= 1) pv_part(k - 1);
-    if (k < T) s_part(k);
+    if (k < T) s_part(k, tile_desc(k + 2));
   };
 
   // softmax of S(k) into P(k): mask edge tiles, lazy running max, exp2
@@ -329,27 +353,24 @@ void fwd_pp_kernel(const FwdArgs a) {
   };
 
   if (T > 0) {
-    // prologue: tiles 0 and 1 (or a re-read of tile 0) in flight; wait for
-    // tile 0 (this wave's part), then the barrier makes all parts visible
-    int64_t ko, vo;
-    fwd_tile_rows<PAGED>(a, b, n_begin * BN, ko, vo);
-    issue_tile(n_begin * BN, 0, ko, vo);
-    fwd_tile_rows<PAGED>(a, b, min(n_begin + 1, n_end - 1) * BN, ko, vo);
-    issue_tile(min(n_begin + 1, n_end - 1) * BN, 1, ko, vo);
+    // prologue: tiles 0 and 1 requested (tile 1 loads nothing when T == 1);
+    // wait for tile 0 (this wave's part), then the barrier makes all parts
+    // visible
+    {
+      const TileDesc t0 = tile_desc(0), t1 = tile_desc(1);
+#pragma unroll
+      for (int p = 0; p < 2 * NI; ++p) dma_part(t0, p);
+#pragma unroll
+      for (int p = 0; p < 2 * NI; ++p) dma_part(t1, p);
+    }
     vmcnt_wait<2 * NI>();
     lds_barrier();
     for (int k = 0; k < T; ++k) {
-      // tile k+2 goes into the buffer tile k-2 left (its last reader finished
-      // before the previous barrier). Each group issues its loads at the
-      // start of its softmax half-step (B: 2k, A: 2k+1): loads issued by all
-      // eight waves at the same instant queue behind each other in the CU's
-      // load path.
-      const int dn0 = min(n_begin + k + 2, n_end - 1) * BN;
-      const int dbuf = (k + 2) & 3;
-      int64_t dko, dvo;
-      fwd_tile_rows<PAGED>(a, b, dn0, dko, dvo);
+      // Tile k+2 goes into the buffer tile k-2 left (its last reader finished
+      // before the previous barrier); each group requests its share during
+      // its own matrix phase (A: half-step 2k, B: 2k+1), spread over the S
+      // MFMAs.
       // half-step 2k: A matrix work, B softmax
-      if (grp == 1) issue_tile(dn0, dbuf, dko, dvo);
       if (grp == 0) {
         __builtin_amdgcn_s_setprio(1);
         mfma_item(k);
@@ -360,7 +381,6 @@ void fwd_pp_kernel(const FwdArgs a) {
       lds_barrier();
       // half-step 2k+1: A softmax, B matrix work; then tile k+1 must have
       // landed (only tile k+2's loads may still be in flight)
-      if (grp == 0) issue_tile(dn0, dbuf, dko, dvo);
       if (grp == 0) {
         sm_item(k);
       } else {
@@ -379,8 +399,8 @@ void fwd_pp_kernel(const FwdArgs a) {
     }
     lds_barrier();
     if (grp == 1) mfma_item(T);
-    // the last re-read tiles may still be landing; none may outlive the
-    // workgroup's LDS
+    // the last (zero-length) requests must land before the workgroup's LDS
+    // is released
     vmcnt_wait<0>();
   }
 

@@ -14,19 +14,22 @@
 // 512-entry register file; wave w owns 32*QB consecutive packed rows (QB query
 // blocks of 32 MFMA columns), so every K or V fragment read from LDS feeds QB
 // MFMAs. Iteration k of the key-tile loop:
-//   top     : wait until K(k+1) and V(k) have landed, barrier; request
-//             K(k+2) and V(k+1) straight into LDS (direct-to-LDS buffer loads)
+//   top     : wait until K(k+1) has landed, barrier
 //   softmax : mask S(k) on edge tiles, running max, lazy rescale of O
 //   phase 1 : S(k+1) = K(k+1) Q^T on the matrix cores, each MFMA issued
 //             together with exponentials, row-sum adds and bf16 packing of
-//             P(k), K fragment reads a few MFMAs ahead
+//             P(k), K fragment reads a few MFMAs ahead; V(k+1) requested
+//             straight into LDS (direct-to-LDS buffer loads), one load every
+//             few MFMAs
+//   mid     : wait until V(k) has landed, barrier
 //   phase 2 : O += P(k) V(k), the transposing V reads issued several MFMAs
-//             ahead
+//             ahead; K(k+3) requested the same way
 // Both phases are written in the intended issue order and held there by
-// scheduling barriers.
-// K runs one tile ahead of V; each has two LDS buffers (tile j in buffer
-// j & 1). The loop is unrolled by two so buffer offsets and the two score
-// register sets are fixed at compile time.
+// scheduling barriers. Each tile is requested about one and a half
+// iterations before its use, and no wave ever issues its loads in a burst.
+// K and V each have two LDS buffers (tile j in buffer j & 1). The loop is
+// unrolled by two so buffer offsets and the two score register sets are
+// fixed at compile time.
 //
 // With one wave per SIMD nothing hides LDS latency but the wave's own
 // read-ahead: with each read issued just before its MFMA (the compiler's
@@ -43,13 +46,6 @@
 
 #include "attn_common.hpp"
 #include "kernels.hpp"
-
-#ifndef FWD_SP_LEAD1
-#define FWD_SP_LEAD1 4
-#endif
-#ifndef FWD_SP_LEAD2
-#define FWD_SP_LEAD2 6
-#endif
 
 namespace mi_attn {
 
@@ -199,26 +195,34 @@ void fwd_sp_kernel(const FwdArgs a) {
     vdo[i] = (uint32_t)(row * a.v_rs * 2 + ((lane % CPR) ^ swz_key(row)) * 16);
   }
   const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
-  // one buffer descriptor per tensor per tile, based at the tile's first row
-  // (ko / vo elements from the sequence's K / V base: contiguous, or in the
-  // page that holds it) and ending at the last row before seqlen_k (rows past
-  // it read as zero)
-  auto issue_k = [&](int j, auto buf_c, int64_t ko) {
-    constexpr int buf = decltype(buf_c)::value;
-    const int n0 = (n_begin + j) * BN;
-    const int nrows = min(sk - n0, BN);  // >= 1
-    const auto rs = make_rsrc(kp + ko, (uint32_t)((nrows - 1) * a.k_rs * 2 + D * 2));
-#pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(rs, kdo[i], lds_w + (uint32_t)(buf * TILE_B + i * 1024));
+  // Buffer descriptor of K (V) tile j: based at the tile's first row (ko / vo
+  // elements from the sequence's K / V base: contiguous, or in the page that
+  // holds it), ending at the last row before seqlen_k (rows past it read as
+  // zero). A tile j >= T gets a zero-length descriptor: its loads touch no
+  // memory (they only write zeros into a buffer nothing reads again), so
+  // every iteration issues the same number of loads and the load-count waits
+  // stay static.
+  auto k_rsrc = [&](int j) __attribute__((always_inline)) {
+    const int jj = min(j, T - 1);
+    int64_t ko, vo;
+    fwd_tile_rows<PAGED>(a, b, (n_begin + jj) * BN, ko, vo);
+    const int nrows = min(sk - (n_begin + jj) * BN, BN);  // >= 1
+    return make_rsrc(kp + ko, j < T ? (uint32_t)((nrows - 1) * a.k_rs * 2 + D * 2) : 0u);
   };
-  auto issue_v = [&](int j, auto buf_c, int64_t vo) {
-    constexpr int buf = decltype(buf_c)::value;
-    const int n0 = (n_begin + j) * BN;
-    const int nrows = min(sk - n0, BN);
-    const auto rs = make_rsrc(vp + vo, (uint32_t)((nrows - 1) * a.v_rs * 2 + D * 2));
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      dma16(rs, vdo[i], lds_w + (uint32_t)((2 + buf) * TILE_B + i * 1024));
+  auto v_rsrc = [&](int j) __attribute__((always_inline)) {
+    const int jj = min(j, T - 1);
+    int64_t ko, vo;
+    fwd_tile_rows<PAGED>(a, b, (n_begin + jj) * BN, ko, vo);
+    const int nrows = min(sk - (n_begin + jj) * BN, BN);
+    return make_rsrc(vp + vo, j < T ? (uint32_t)((nrows - 1) * a.v_rs * 2 + D * 2) : 0u);
+  };
+  // this wave's part i (of NI) of a K tile into K buffer kbuf, of a V tile
+  // into V buffer vbuf
+  auto dma_k = [&](__amdgpu_buffer_rsrc_t r, int kbuf, int i) __attribute__((always_inline)) {
+    dma16(r, kdo[i], lds_w + (uint32_t)(kbuf * TILE_B + i * 1024));
+  };
+  auto dma_v = [&](__amdgpu_buffer_rsrc_t r, int vbuf, int i) __attribute__((always_inline)) {
+    dma16(r, vdo[i], lds_w + (uint32_t)((2 + vbuf) * TILE_B + i * 1024));
   };
 
   // ---- fragment read offsets. K: lane (c32, half) reads logical chunk
@@ -363,12 +367,18 @@ void fwd_sp_kernel(const FwdArgs a) {
   // 32 / N score elements of the current tile (elements 32 i / N .. 32 (i + 1)
   // / N - 1 with MFMA i), in that source order, held
   // by scheduling barriers between the groups.
-  auto phase1 = [&](auto buf_c, STile& cur, STile& nxt) __attribute__((always_inline)) {
+  // This wave's NI loads of the next V tile (descriptor vr, V buffer vbuf)
+  // go out spread over the MFMAs, one every N / NI: issued in one burst by all
+  // four waves, 64 direct-to-LDS loads of 1 KB queue in the CU's load path
+  // for about a thousand cycles, and the issuing waves stall with them.
+  auto phase1 = [&](auto buf_c, STile& cur, STile& nxt, __amdgpu_buffer_rsrc_t vr, int vbuf)
+      __attribute__((always_inline)) {
     static_assert(QB == 1, "fused phase 1 handles one query block per wave");
     constexpr int buf = decltype(buf_c)::value;
     constexpr int N = 2 * NKC;   // MFMAs and K fragment reads
     static_assert(N <= 32, "at least one score element per MFMA");
-    constexpr int L1 = FWD_SP_LEAD1;
+    static_assert(N % NI == 0, "loads spread evenly over the MFMAs");
+    constexpr int L1 = 4;
     auto kread = [&](int i) __attribute__((always_inline)) {
       const int cc = i >> 1, kb = i & 1;
       return *reinterpret_cast<const bf16x8*>(smem + k_rd[cc & 7] +
@@ -385,6 +395,7 @@ void fwd_sp_kernel(const FwdArgs a) {
       const bf16x8 kf = ring[i % L1];
       if (i + L1 < N) ring[i % L1] = kread(i + L1);
       nxt[kb][0] = mfma32(kf, qf[0][cc], cc == 0 ? zero_f32x16() : nxt[kb][0]);
+      if (i % (N / NI) == 0) dma_v(vr, vbuf, i / (N / NI));
 #pragma unroll
       for (int j = 32 * i / N; j < 32 * (i + 1) / N; ++j) {
         // element j: key block j / 16, register j % 16
@@ -412,10 +423,13 @@ void fwd_sp_kernel(const FwdArgs a) {
   // barriers (nothing may cross them) between the {read i + LEAD2, MFMA i}
   // groups keep that order: left free, the scheduler issues each read right
   // before its MFMA, which then waits out the whole LDS latency.
-  auto pv_tile = [&](auto buf_c) __attribute__((always_inline)) {
+  // The NI loads of a K tile (descriptor kr, K buffer kbuf) go out spread
+  // over the MFMAs as in phase 1.
+  auto pv_tile = [&](auto buf_c, __amdgpu_buffer_rsrc_t kr, int kbuf) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value;
     constexpr int N = 4 * NDB;
-    constexpr int LEAD2 = FWD_SP_LEAD2;
+    static_assert(N % NI == 0, "loads spread evenly over the MFMAs");
+    constexpr int LEAD2 = 6;
     auto read = [&](int i) __attribute__((always_inline)) {
       const int t = i / NDB, db = i % NDB;
       const char* p = smem + v_rd[db & 1] + (buf * TILE_B + (16 * t) * ROW_B + (db >> 1) * 128);
@@ -434,6 +448,7 @@ void fwd_sp_kernel(const FwdArgs a) {
       if (i + LEAD2 < N) ring[i % LEAD2] = read(i + LEAD2);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma32(vf, pf[qb][t], o[db][qb]);
+      if (i % (N / NI) == 0) dma_k(kr, kbuf, i / (N / NI));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -443,47 +458,65 @@ void fwd_sp_kernel(const FwdArgs a) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  // iteration k: cur holds S(k); nxt receives S(k+1). par = k & 1.
-  // row offsets of tile j (clamped to the last tile) from the sequence's K/V
-  auto rows_of = [&](int j, int64_t& ko, int64_t& vo) __attribute__((always_inline)) {
-    fwd_tile_rows<PAGED>(a, b, (n_begin + min(j, T - 1)) * BN, ko, vo);
-  };
-
+  // Iteration k (cur holds S(k); nxt receives S(k+1); par = k & 1). Tile j
+  // of K lives in K buffer j & 1, tile j of V in V buffer j & 1. Per wave the
+  // loads go out in the order ..., V(k) in phase 1 of iteration k-1, K(k+2)
+  // in its P V phase, V(k+1) in phase 1 of iteration k, K(k+3) in its P V
+  // phase, ...:
+  //   top: K(k+1) has landed once at most 2*NI loads (V(k), K(k+2)) are
+  //        outstanding; the barrier also ends every wave's reads of V(k-1),
+  //        whose buffer phase 1 refills with V(k+1)
+  //   mid: V(k) has landed once at most 2*NI loads (K(k+2), V(k+1)) are
+  //        outstanding; the barrier also ends every wave's reads of K(k+1),
+  //        whose buffer the P V phase refills with K(k+3)
+  // so each tile is requested about one and a half iterations before use.
   auto step = [&](int k, auto par_c, STile& cur, STile& nxt) {
     constexpr int par = decltype(par_c)::value;
     using PN = std::integral_constant<int, par ^ 1>;
-    vmcnt_wait<0>();  // K(k+1), V(k) (this wave's parts)
-    lds_barrier();    // everyone's parts landed; K(k), V(k-1) no longer read
-    int64_t k_nx, v_nx, unused;
-    rows_of(k + 2, k_nx, unused);
-    rows_of(k + 1, unused, v_nx);
-    if (k + 2 < T) issue_k(k + 2, par_c, k_nx);  // into the buffer K(k) left
-    if (k + 1 < T) issue_v(k + 1, PN{}, v_nx);   // into the buffer V(k-1) left
+    vmcnt_wait<2 * NI>();
+    lds_barrier();
+    const auto vr = v_rsrc(k + 1);
     sm_max(cur, k);
     if (k + 1 < T) {
-      phase1(PN{}, cur, nxt);
+      phase1(PN{}, cur, nxt, vr, par ^ 1);
     } else {
       sm_exp(cur);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma_v(vr, par ^ 1, i);  // zero-length: keeps the count
     }
-    pv_tile(par_c);
+    vmcnt_wait<2 * NI>();
+    lds_barrier();
+    pv_tile(par_c, k_rsrc(k + 3), par ^ 1);
   };
 
   if (T > 0) {
-    // prologue: K(0), V(0), K(1) requested (K(0) re-read when T == 1); wait
-    // for K(0), compute S(0)
-    int64_t ko, vo;
-    rows_of(0, ko, vo);
-    issue_k(0, I0{}, ko);
-    issue_v(0, I0{}, vo);
-    rows_of(1, ko, vo);
-    issue_k(min(1, T - 1), I1{}, ko);
+    // prologue: K(0), K(1), V(0) requested (tiles past the last one load
+    // nothing); wait for K(0), compute S(0); once every wave has read K(0),
+    // K(2) goes into its buffer (the loop's waits assume K(2) after V(0))
+    {
+      const auto k0 = k_rsrc(0), k1 = k_rsrc(1), v0 = v_rsrc(0);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma_k(k0, 0, i);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma_k(k1, 1, i);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma_v(v0, 0, i);
+    }
     vmcnt_wait<2 * NI>();
     lds_barrier();
     s_tile(I0{}, sA);
+    lds_barrier();
+    {
+      const auto k2 = k_rsrc(2);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma_k(k2, 0, i);
+    }
     for (int k = 0; k < T; k += 2) {
       step(k, I0{}, sA, sB);
       if (k + 1 < T) step(k + 1, I1{}, sB, sA);
     }
+    // the last requests (zero-length) must land before the workgroup's LDS
+    // is released
     vmcnt_wait<0>();
   }
 
