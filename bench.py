@@ -225,6 +225,38 @@ class Decode:
                                        k_descale=self.kd, v_descale=self.vd)
 
 
+class VarlenDecode:
+    """mi_attn_decode_splitkv with several query tokens per sequence (packed
+    by cu_seqlens_q, causal), split heuristic."""
+
+    def __init__(self, mi, w, torch):
+        from tests.gpu_util import dev_bf16, dev_i32
+        self.mi, self.w = mi, w
+        self.q, self.kc, self.vc = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+        self.pt, self.su = dev_i32(w.page_table), dev_i32(w.seqused_k)
+        self.cu = dev_i32(w.cu_seqlens_q)
+        self.kw = dict(seqused_k=self.su, cu_seqlens_q=self.cu, max_seqlen_q=w.max_seqlen_q,
+                       causal=True, softmax_scale=w.softmax_scale, num_splits=0)
+        nb = mi.mi_attn_decode_workspace_bytes(self.q, self.kc, self.vc, self.pt, 0, self.cu,
+                                               w.max_seqlen_q)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        self.out, self.lse = mi.mi_attn_decode_splitkv(self.q, self.kc, self.vc, self.pt,
+                                                       workspace=self.ws, **self.kw)
+
+    def __call__(self):
+        self.mi.mi_attn_decode_splitkv(self.q, self.kc, self.vc, self.pt, out=self.out,
+                                       lse=self.lse, workspace=self.ws, **self.kw)
+
+
+def varlen_decode_bytes(w) -> int:
+    kv = 2 * int(w.seqused_k.sum()) * w.num_heads_kv * w.head_dim * 2
+    tq = int(w.cu_seqlens_q[-1])
+    qo = 2 * tq * w.num_heads_q * w.head_dim * 2
+    lse = tq * w.num_heads_q * 4
+    table = sum(-(-int(s) // w.page_size) for s in w.seqused_k) * 4
+    return kv + qo + lse + table + 4 * (len(w.seqused_k) + 1)
+
+
 class Backward:
     """mi_attn_bwd on a dense workload: the forward's out and LSE are made
     once, outside the timed calls; each call runs the three backward
@@ -383,6 +415,18 @@ def extra_workloads(mi, W, torch, args, extra):
         log(f"[bench] {name}: {med * 1e3:.1f} us, {extra[name]['tflops']:.1f} TFLOP/s")
         del bw
         torch.cuda.empty_cache()
+    # speculative decoding step: the paged decode workload's cache with 4
+    # causal query tokens per sequence
+    wv = W.paged_prefill_case(1005, 16, 32, 4, 128, 256, 128, [32768] * 16, seqlens_q=[4] * 16,
+                              causal=True, name="paged_decode_4tok_b16_gqa32x4_sk32768_d128")
+    vd = VarlenDecode(mi, wv, torch)
+    med = timed_extra(torch, vd, n)
+    gb = varlen_decode_bytes(wv) / (med * 1e-3) / 1e9
+    extra[wv.name] = {"median_us": med * 1e3, "gbs": gb, "frac": gb / PEAK_HBM_GBS,
+                      "bytes_per_launch": varlen_decode_bytes(wv)}
+    log(f"[bench] {wv.name}: {med * 1e3:.1f} us, {gb:.0f} GB/s")
+    del vd, wv
+    torch.cuda.empty_cache()
     for fmt, wname in (("e4m3", "paged_decode_fp8_b16_sk32768"),
                        ("e5m2", "paged_decode_fp8_e5m2_b16_sk32768")):
         w8 = W.paged_decode_fp8_case(1005, 16, 32, 4, 128, 256, 128, num_splits=16,

@@ -119,6 +119,7 @@ class DecodeParams(ctypes.Structure):
         ("kv_dtype", _i32), ("k_descale", _vp), ("v_descale", _vp),
         ("learnable_sink", _vp),
         ("softcap", ctypes.c_float),
+        ("cu_seqlens_q", _vp), ("max_seqlen_q", _i32), ("total_q", _i32),
     ]
 
 
@@ -451,23 +452,30 @@ def mi_attn_bwd(q, k, v, out, dout, lse, cu_seqlens_q=None, cu_seqlens_k=None,
 
 
 def _decode_params(q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
-                   num_splits, window_left, workspace) -> DecodeParams:
+                   num_splits, window_left, workspace, cu_seqlens_q=None, max_seqlen_q=None,
+                   causal=False, window_right=None) -> DecodeParams:
+    """q (B, Hq, D), or (total_q, Hq, D) packed by cu_seqlens_q; B is the
+    page table's row count."""
     p = DecodeParams()
     p.q, p.k_cache, p.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
     p.page_table, p.seqused_k, p.out, p.lse = _ptr(page_table), _ptr(seqused_k), _ptr(out), _ptr(lse)
     p.q_batch_stride, p.q_head_stride = q.stride(0), q.stride(1)
     if out is not None:
         p.o_batch_stride, p.o_head_stride = out.stride(0), out.stride(1)
-    p.batch, p.num_heads_q, p.head_dim = q.shape[0], q.shape[1], q.shape[2]
+    p.batch, p.num_heads_q, p.head_dim = page_table.shape[0], q.shape[1], q.shape[2]
     p.num_pages, p.page_size, p.num_heads_kv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
     p.max_pages_per_seq = page_table.shape[1]
     p.softmax_scale = (1.0 / math.sqrt(q.shape[2]) if softmax_scale is None
                        else float(softmax_scale))
-    p.causal, p.window_left, p.window_right = 0, _win(window_left), -1
+    p.causal, p.window_left, p.window_right = int(bool(causal)), _win(window_left), _win(window_right)
     p.num_splits = int(num_splits)
     if workspace is not None:
         p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     p.kv_dtype = _kv_dtype(k_cache)
+    if cu_seqlens_q is not None:
+        p.cu_seqlens_q = cu_seqlens_q.data_ptr()
+        p.total_q = q.shape[0]
+        p.max_seqlen_q = q.shape[0] if max_seqlen_q is None else int(max_seqlen_q)
     return p
 
 
@@ -507,12 +515,13 @@ def _req_kv(name, t, device, fp8: bool):
         raise MiAttnError(MI_ATTN_EINVAL, f"{name} must be a device tensor on {device}")
 
 
-def mi_attn_decode_workspace_bytes(q, k_cache, v_cache, page_table, num_splits: int = 0) -> int:
+def mi_attn_decode_workspace_bytes(q, k_cache, v_cache, page_table, num_splits: int = 0,
+                                   cu_seqlens_q=None, max_seqlen_q: Optional[int] = None) -> int:
     lib = load()
     p = _decode_params(q, k_cache, v_cache, page_table, None, None, None, None, num_splits, None,
-                       None)
+                       None, cu_seqlens_q, max_seqlen_q)
     n = lib.mi_attn_decode_workspace_bytes(ctypes.byref(p))
-    if n == 0:
+    if n == 0 and mi_attn_last_error():
         # the size query only says "invalid"; the split-count query returns
         # the status itself for the same validation
         rc = lib.mi_attn_decode_num_splits(ctypes.byref(p))
@@ -520,10 +529,11 @@ def mi_attn_decode_workspace_bytes(q, k_cache, v_cache, page_table, num_splits: 
     return n
 
 
-def mi_attn_decode_num_splits(q, k_cache, v_cache, page_table, num_splits: int = 0) -> int:
+def mi_attn_decode_num_splits(q, k_cache, v_cache, page_table, num_splits: int = 0,
+                              cu_seqlens_q=None, max_seqlen_q: Optional[int] = None) -> int:
     lib = load()
     p = _decode_params(q, k_cache, v_cache, page_table, None, None, None, None, num_splits, None,
-                       None)
+                       None, cu_seqlens_q, max_seqlen_q)
     n = lib.mi_attn_decode_num_splits(ctypes.byref(p))
     _check(min(n, 0))
     return n
@@ -555,18 +565,26 @@ def mi_attn_decode_splitkv(q, k_cache, v_cache, page_table, seqused_k=None, out=
                            window_left: Optional[int] = None, workspace=None,
                            return_lse: bool = True, check_bounds: bool = False,
                            k_descale=None, v_descale=None, learnable_sink=None,
-                           softcap: float = 0.0):
-    """One query token per sequence against a paged cache, split along keys.
+                           softcap: float = 0.0, cu_seqlens_q=None,
+                           max_seqlen_q: Optional[int] = None, causal: bool = False,
+                           window_right: Optional[int] = None):
+    """Query tokens against a paged cache, split along keys, then combined.
 
-    q (B, Hq, D); k/v cache (num_pages, page_size, Hkv, D) contiguous, bf16 or
-    fp8 (float8_e4m3fn, raw uint8 e4m3 bytes, or float8_e5m2; then k_descale / v_descale are
-    float32 (B, Hkv) or None for 1); page_table int32 (B, max_pages);
-    seqused_k int32 (B,) or None. softcap as for mi_attn_fwd (on the descaled scores).
-    Returns out (B, Hq, D) bf16 and lse (B, Hq) float32.
+    q (B, Hq, D): one token per sequence; or (total_q, Hq, D) with cu_seqlens_q
+    int32 (B+1,) packing a few tokens per sequence (aligned bottom-right to
+    its keys; causal / window_right then apply), max_seqlen_q their maximum
+    (None: total_q, which is safe but sizes the launch for it).
+    k/v cache (num_pages, page_size, Hkv, D) contiguous, bf16 or fp8
+    (float8_e4m3fn, raw uint8 e4m3 bytes, or float8_e5m2; then k_descale /
+    v_descale are float32 (B, Hkv) or None for 1); page_table int32
+    (B, max_pages); seqused_k int32 (B,) or None. softcap as for mi_attn_fwd
+    (on the descaled scores). Returns out shaped like q (bf16) and lse
+    (q.shape[0], Hq) float32.
     """
     return _decode(False, q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
                    num_splits, window_left, workspace, return_lse, check_bounds, k_descale,
-                   v_descale, learnable_sink, softcap)
+                   v_descale, learnable_sink, softcap, cu_seqlens_q, max_seqlen_q, causal,
+                   window_right)
 
 
 def mi_attn_decode_splitkv_noalloc(q, k_cache, v_cache, page_table, seqused_k=None, out=None,
@@ -574,7 +592,9 @@ def mi_attn_decode_splitkv_noalloc(q, k_cache, v_cache, page_table, seqused_k=No
                                    num_splits: int = 0, window_left: Optional[int] = None,
                                    return_lse: bool = True, check_bounds: bool = False,
                                    k_descale=None, v_descale=None, learnable_sink=None,
-                                   softcap: float = 0.0):
+                                   softcap: float = 0.0, cu_seqlens_q=None,
+                                   max_seqlen_q: Optional[int] = None, causal: bool = False,
+                                   window_right: Optional[int] = None):
     """mi_attn_decode_splitkv through the C entry point that allocates
     nothing: the split partials go to the library's static per-GPU scratch
     (64 MiB; larger requests raise EWORKSPACE) instead of a workspace. Calls
@@ -582,12 +602,14 @@ def mi_attn_decode_splitkv_noalloc(q, k_cache, v_cache, page_table, seqused_k=No
     keep this call free of allocations on the Python side as well."""
     return _decode(True, q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
                    num_splits, window_left, None, return_lse, check_bounds, k_descale,
-                   v_descale, learnable_sink, softcap)
+                   v_descale, learnable_sink, softcap, cu_seqlens_q, max_seqlen_q, causal,
+                   window_right)
 
 
 def _decode(noalloc, q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
             num_splits, window_left, workspace, return_lse, check_bounds, k_descale, v_descale,
-            learnable_sink, softcap):
+            learnable_sink, softcap, cu_seqlens_q=None, max_seqlen_q=None, causal=False,
+            window_right=None):
     import torch
     lib = load()
     dev = q.device
@@ -601,30 +623,38 @@ def _decode(noalloc, q, k_cache, v_cache, page_table, seqused_k, out, lse, softm
         raise MiAttnError(MI_ATTN_EINVAL, "q must be (B, Hq, D) and caches (pages, page_size, Hkv, D)")
     if not k_cache.is_contiguous() or not v_cache.is_contiguous():
         raise MiAttnError(MI_ATTN_EINVAL, "k_cache and v_cache must be contiguous")
-    B, hq, d = q.shape
+    T, hq, d = q.shape  # T: query tokens (one per sequence, or packed)
+    B = page_table.shape[0]
+    if cu_seqlens_q is None:
+        if T != B:
+            raise MiAttnError(MI_ATTN_EINVAL, f"q has {T} rows but page_table {B} sequences")
+    else:
+        _req_i32("cu_seqlens_q", cu_seqlens_q, (B + 1,), dev)
     _req_i32("page_table", page_table, (B, page_table.shape[1]), dev)
     if seqused_k is not None:
         _req_i32("seqused_k", seqused_k, (B,), dev)
     if check_bounds:
         check_paged_bounds(page_table, seqused_k, k_cache.shape[0], k_cache.shape[1])
     if out is None:
-        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=dev)
+        out = torch.empty(T, hq, d, dtype=torch.bfloat16, device=dev)
     else:
         _req_bf16("out", out, dev)
-        if tuple(out.shape) != (B, hq, d):
-            raise MiAttnError(MI_ATTN_EINVAL, f"out must have shape {(B, hq, d)}")
+        if tuple(out.shape) != (T, hq, d):
+            raise MiAttnError(MI_ATTN_EINVAL, f"out must have shape {(T, hq, d)}")
     if lse is None and return_lse:
-        lse = torch.empty(B, hq, dtype=torch.float32, device=dev)
+        lse = torch.empty(T, hq, dtype=torch.float32, device=dev)
     elif lse is not None:
-        if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, hq) \
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (T, hq) \
                 or not lse.is_cuda or lse.device != dev:
-            raise MiAttnError(MI_ATTN_EINVAL, f"lse must be a contiguous float32 {(B, hq)} "
+            raise MiAttnError(MI_ATTN_EINVAL, f"lse must be a contiguous float32 {(T, hq)} "
                                               f"tensor on {dev}")
     if workspace is None and not noalloc:
-        nbytes = mi_attn_decode_workspace_bytes(q, k_cache, v_cache, page_table, num_splits)
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        nbytes = mi_attn_decode_workspace_bytes(q, k_cache, v_cache, page_table, num_splits,
+                                                cu_seqlens_q, max_seqlen_q)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     p = _decode_params(q, k_cache, v_cache, page_table, seqused_k, out, lse, softmax_scale,
-                       num_splits, window_left, workspace)
+                       num_splits, window_left, workspace, cu_seqlens_q, max_seqlen_q, causal,
+                       window_right)
     for n, t in (("k_descale", k_descale), ("v_descale", v_descale)):
         if t is None:
             continue

@@ -74,13 +74,26 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // and sizing makes no HIP call. A partitioned device with fewer units only
 // gets more splits than it needs, never a wrong result.
 constexpr int kComputeUnits = 256;
+// Query tokens per sequence (the maximum), query rows of the launch, and
+// 32-row blocks per (sequence, KV head): one token per sequence unless
+// cu_seqlens_q packs several.
+int decode_max_q(const mi_attn_decode_params* p) {
+  return p->cu_seqlens_q != nullptr ? p->max_seqlen_q : 1;
+}
+size_t decode_rows(const mi_attn_decode_params* p) {
+  return (p->cu_seqlens_q != nullptr ? (size_t)p->total_q : (size_t)p->batch) * p->num_heads_q;
+}
+int decode_row_blocks(const mi_attn_decode_params* p) {
+  const int64_t group = p->num_heads_q / p->num_heads_kv;
+  return (int)(((int64_t)decode_max_q(p) * group + 31) / 32);
+}
+
 int split_heuristic(const mi_attn_decode_params* p) {
   const int cap = p->max_pages_per_seq * p->page_size;
   const int n_blocks = (cap + mi_attn::kDecBlockN - 1) / mi_attn::kDecBlockN;
   if (n_blocks <= 4) return 1;
   const int cus = kComputeUnits;
-  const int group = p->num_heads_q / p->num_heads_kv;
-  const long work = (long)p->batch * p->num_heads_kv * ((group + 31) / 32);
+  const long work = (long)p->batch * p->num_heads_kv * decode_row_blocks(p);
   const long per_cu = mi_attn::decode_streams(p->head_dim, p->page_size) ? 4L : 2L;
   const long want = std::max(1L, (per_cu * cus) / std::max(1L, work));
   return (int)std::max(1L, std::min<long>({want, 128L, (long)n_blocks}));
@@ -115,12 +128,19 @@ int check_decode(const mi_attn_decode_params* p) {
   if (p->kv_dtype != MI_ATTN_KV_BF16 && !mi_attn::decode_streams(p->head_dim, p->page_size))
     return fail(MI_ATTN_EUNSUPPORTED, "fp8 K/V needs head_dim 64/128 and page_size a multiple "
                 "of 32 (got %d, %d)", p->head_dim, p->page_size);
+  if (p->cu_seqlens_q != nullptr) {
+    if (p->max_seqlen_q < 0 || p->total_q < 0)
+      return fail(MI_ATTN_EINVAL, "max_seqlen_q and total_q must be >= 0 with cu_seqlens_q");
+    if ((int64_t)p->max_seqlen_q * (p->num_heads_q / p->num_heads_kv) > INT32_MAX - 32 ||
+        (int64_t)p->total_q * p->num_heads_q > INT32_MAX)
+      return fail(MI_ATTN_EINVAL, "query tokens * heads overflow int32");
+  }
   return MI_ATTN_OK;
 }
 
 // Pointer, alignment and stride checks, needed only to launch.
 int check_decode_pointers(const mi_attn_decode_params* p) {
-  if (p->batch == 0) return MI_ATTN_OK;
+  if (decode_rows(p) == 0) return MI_ATTN_OK;
   if (!p->q || !p->k_cache || !p->v_cache || !p->page_table || !p->out)
     return fail(MI_ATTN_EINVAL, "q, k_cache, v_cache, page_table and out must be non-NULL");
   if (!aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->v_cache) || !aligned16(p->out))
@@ -136,7 +156,7 @@ int resolved_splits(const mi_attn_decode_params* p) {
 }
 
 size_t workspace_for(const mi_attn_decode_params* p, int splits) {
-  const size_t rows = (size_t)p->batch * p->num_heads_q;
+  const size_t rows = decode_rows(p);
   return round_up(rows * splits * p->head_dim * sizeof(float)) +
          round_up(rows * splits * sizeof(float));
 }
@@ -306,6 +326,7 @@ int mi_attn_decode_num_splits(const mi_attn_decode_params* p) {
 
 size_t mi_attn_decode_workspace_bytes(const mi_attn_decode_params* p) {
   if (check_decode(p) != MI_ATTN_OK) return 0;
+  ok();
   return workspace_for(p, resolved_splits(p));
 }
 
@@ -326,7 +347,7 @@ namespace {
 // workspace_for(p, splits) bytes, 256-byte aligned), then the combine.
 int decode_launch(const mi_attn_decode_params* p, int splits, void* ws, void* stream) {
   const int group = p->num_heads_q / p->num_heads_kv;
-  const size_t rows = (size_t)p->batch * p->num_heads_q;
+  const size_t rows = decode_rows(p);
   mi_attn::DecodeArgs a{};
   a.q = p->q;
   a.k_cache = p->k_cache;
@@ -346,12 +367,14 @@ int decode_launch(const mi_attn_decode_params* p, int splits, void* ws, void* st
   a.num_pages = p->num_pages;
   a.max_pages = p->max_pages_per_seq;
   a.num_splits = splits;
-  a.row_blocks = (group + 31) / 32;
+  a.row_blocks = decode_row_blocks(p);
+  a.cu_q = p->cu_seqlens_q;
   a.scale = p->softmax_scale;
   a.scale_log2 = exp2_scale(p->softmax_scale);
   int wl, wr;
   normalise_window(p->causal, p->window_left, p->window_right, &wl, &wr);
   a.wl = wl;
+  a.wr = wr;
   a.kv_fp8 = p->kv_dtype == MI_ATTN_KV_FP8_E4M3 ? 1 : p->kv_dtype == MI_ATTN_KV_FP8_E5M2 ? 2 : 0;
   a.k_descale = a.kv_fp8 ? p->k_descale : nullptr;
   a.v_descale = a.kv_fp8 ? p->v_descale : nullptr;
@@ -421,7 +444,7 @@ int mi_attn_decode_splitkv(const mi_attn_decode_params* p, void* stream) {
   int rc = check_decode(p);
   if (rc == MI_ATTN_OK) rc = check_decode_pointers(p);
   if (rc != MI_ATTN_OK) return rc;
-  if (p->batch == 0) return ok();
+  if (decode_rows(p) == 0 || decode_max_q(p) == 0) return ok();
   const int splits = resolved_splits(p);
   const size_t need = workspace_for(p, splits);
   if (p->workspace == nullptr || p->workspace_bytes < need)
@@ -436,7 +459,7 @@ int mi_attn_decode_splitkv_noalloc(const mi_attn_decode_params* p, void* stream)
   int rc = check_decode(p);
   if (rc == MI_ATTN_OK) rc = check_decode_pointers(p);
   if (rc != MI_ATTN_OK) return rc;
-  if (p->batch == 0) return ok();
+  if (decode_rows(p) == 0 || decode_max_q(p) == 0) return ok();
   const int splits = resolved_splits(p);
   const size_t need = workspace_for(p, splits);
   if (need > kScratchBytes)

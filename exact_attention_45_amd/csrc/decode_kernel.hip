@@ -75,21 +75,30 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   int sk = a.seqused_k != nullptr ? a.seqused_k[b] : cap;
   // a length outside [0, capacity] would index past the page-table row
   bool bad_page = sk < 0 || sk > cap;
-  sk = min(max(sk, 0), cap);
-  // the query sits at position sk - 1; a left window keeps the last wl+1 keys
-  const int kv_lo = a.wl >= 0 ? max(0, sk - 1 - a.wl) : 0;
-  const int span = max(0, sk - kv_lo);
+  sk = __builtin_amdgcn_readfirstlane(min(max(sk, 0), cap));
+  int t0, n;
+  dec_tokens(a, b, t0, n);
+  const int rows = n * a.group;
+  if (rb * 32 >= rows) return;  // no (token, head) row in this block (uniform)
+  // this lane's row, and the block's first and last rows: their visible keys
+  // bound the block's key range and the tiles every row sees in full
+  const DecRow row = dec_row(a, t0, n, sk, hk, rb, c32);
+  const DecRow r_first = dec_row(a, t0, n, sk, hk, rb, 0);
+  const DecRow r_last = dec_row(a, t0, n, sk, hk, rb, min(31, rows - 1 - rb * 32));
+  const int kv_lo = __builtin_amdgcn_readfirstlane(r_first.lo);
+  const int kv_hi = __builtin_amdgcn_readfirstlane(max(r_last.hi + 1, kv_lo));  // exclusive
+  const int full_lo = __builtin_amdgcn_readfirstlane(r_last.lo);
+  const int full_hi = __builtin_amdgcn_readfirstlane(r_first.hi);
+  const int span = max(0, kv_hi - kv_lo);
   int chunk = (span + a.num_splits - 1) / a.num_splits;
   chunk = (chunk + BN - 1) / BN * BN;
-  const int k_begin = min(sk, kv_lo + split * chunk);
-  const int k_end = min(sk, k_begin + chunk);
+  const int k_begin = min(kv_hi, kv_lo + split * chunk);
+  const int k_end = min(kv_hi, k_begin + chunk);
   const int n_tiles = (k_end - k_begin + BN - 1) / BN;
 
-  // ---- this lane's query head
-  const int col = rb * 32 + c32;
-  const bool valid = col < a.group;
-  const int hq = hk * a.group + (valid ? col : 0);
-  const __bf16* qp = static_cast<const __bf16*>(a.q) + (int64_t)b * a.q_bs + (int64_t)hq * a.q_hs;
+  // ---- this lane's query row
+  const bool valid = row.valid;
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + row.token * a.q_bs + (int64_t)row.hq * a.q_hs;
   // branch-free: invalid lanes read head 0's row and zero it afterwards (a
   // load under a divergent branch makes every later wait drain all loads)
   bf16x8 qf[D / 16];
@@ -224,11 +233,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = softcap_raw(s[v], sc_k1x, sc_k2);
     }
-    if (n0 + BN > k_end) {
+    // keys past the split's end or outside the row's [lo, hi]
+    if (n0 + BN > k_end || n0 < full_lo || n0 + BN - 1 > full_hi) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = n0 + wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (key >= k_end) s[v] = kNegInf;
+        if (key >= k_end || key < row.lo || key > row.hi) s[v] = kNegInf;
       }
     }
 
@@ -313,9 +323,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   const int qcol = tid & 31;
   const int dpart = tid >> 5;  // 0..7
   constexpr int DPT = D / 8;
-  const int hcol = rb * 32 + qcol;
-  if (hcol < a.group) {
-    const int hq2 = hk * a.group + hcol;
+  const DecRow mrow = dec_row(a, t0, n, sk, hk, rb, qcol);
+  if (mrow.valid) {
     float mw[4], m = kNegInf;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     }
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const float nan = __builtin_nanf("");
-    const int64_t prow = (int64_t)b * a.hq + hq2;
+    const int64_t prow = mrow.prow;
     float* op = a.o_part + (prow * a.num_splits + split) * D + dpart * DPT;
 #pragma unroll
     for (int j = 0; j < DPT; j += 4) {

@@ -146,22 +146,31 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   int sk = a.seqused_k != nullptr ? a.seqused_k[b] : cap;
   bool bad = sk < 0 || sk > cap;  // would index past the page-table row
   sk = uniform(min(max(sk, 0), cap));
-  // the query sits at position sk - 1; a left window keeps the last wl+1 keys
-  const int kv_lo = uniform(a.wl >= 0 ? max(0, sk - 1 - a.wl) : 0);
+  int t0, n;
+  dec_tokens(a, b, t0, n);
+  const int rows = n * a.group;
+  if (rb * 32 >= rows) return;  // no (token, head) row in this block
+  // this lane's row, and the block's first and last rows: their visible keys
+  // bound the block's key range and the slices every row sees in full
+  const DecRow row = dec_row(a, t0, n, sk, hk, rb, c32);
+  const DecRow r_first = dec_row(a, t0, n, sk, hk, rb, 0);
+  const DecRow r_last = dec_row(a, t0, n, sk, hk, rb, min(31, rows - 1 - rb * 32));
+  const int kv_lo = uniform(r_first.lo);
+  const int kv_hi = uniform(max(r_last.hi + 1, kv_lo));  // exclusive
+  const int full_lo = uniform(r_last.lo);
+  const int full_hi = uniform(r_first.hi);
   // this split's slices [m_lo, m_hi) of the visible ones
   const int m_first = kv_lo / 32;
-  const int n_sl = sk > kv_lo ? (sk - 1) / 32 - m_first + 1 : 0;
+  const int n_sl = kv_hi > kv_lo ? (kv_hi - 1) / 32 - m_first + 1 : 0;
   const int per = (n_sl + a.num_splits - 1) / a.num_splits;
   const int m_lo = uniform(m_first + min(n_sl, split * per));
   const int m_hi = uniform(m_first + min(n_sl, (split + 1) * per));
   // this wave's slices m_lo + i, i < n_w (all of the split, for its head)
   const int n_w = uniform(m_hi - m_lo);
 
-  // ---- this lane's query head (MFMA B operand)
-  const int col = rb * 32 + c32;
-  const bool valid = col < a.group;
-  const int hq = hk * a.group + (valid ? col : 0);
-  const __bf16* qp = static_cast<const __bf16*>(a.q) + (int64_t)b * a.q_bs + (int64_t)hq * a.q_hs;
+  // ---- this lane's query row (MFMA B operand)
+  const bool valid = row.valid;
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + row.token * a.q_bs + (int64_t)row.hq * a.q_hs;
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int cc = 0; cc < D / 16; ++cc) {
@@ -297,10 +306,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = softcap_raw(s[v], sc_k1x, sc_k2);
     }
-    // keys outside [kv_lo, sk) (first and last slices, and padding)
+    // keys outside the row's [lo, hi] (first and last slices, and padding)
     const int key0 = 32 * (m_lo + i);
-    if (i >= n_w || key0 < kv_lo || key0 + 32 > sk) [[unlikely]] {
-      const uint32_t w = (uint32_t)vis64(kv_lo - key0 - 4 * half, sk - 1 - key0 - 4 * half);
+    if (i >= n_w || key0 < full_lo || key0 + 31 > full_hi) [[unlikely]] {
+      const uint32_t w = (uint32_t)vis64(row.lo - key0 - 4 * half, row.hi - key0 - 4 * half);
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = mask_by_bit(s[v], i < n_w ? w : 0u, 8 * (v >> 2) + (v & 3));
     }
@@ -374,7 +383,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   if (valid) {
     const float inv = l_tot > 0.0f ? vds / l_tot : 0.0f;
     const float nan = __builtin_nanf("");
-    const int64_t prow = (int64_t)b * a.hq + hq;
+    const int64_t prow = row.prow;
     float* op = a.o_part + (prow * a.num_splits + split) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)

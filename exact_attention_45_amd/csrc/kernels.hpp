@@ -163,16 +163,20 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* page_table;
   const int32_t* seqused_k;  // may be NULL
-  float* o_part;             // [batch*hq][splits][d]
-  float* lse_part;           // [batch*hq][splits]
-  int64_t q_bs, q_hs;
+  float* o_part;             // [rows][splits][d], rows = query tokens * hq
+  float* lse_part;           // [rows][splits]
+  int64_t q_bs, q_hs;        // q_bs: between sequences, or between tokens with cu_q
   int32_t batch, hq, hkv, group;
   int32_t page_size, num_pages, max_pages;
   int32_t num_splits;
-  int32_t row_blocks;        // ceil(group / 32)
+  int32_t row_blocks;        // ceil(max query tokens * group / 32)
   float scale;
   float scale_log2;
-  int32_t wl;                // < 0 unbounded
+  int32_t wl, wr;            // < 0 unbounded (causal folded into wr = 0)
+  // Packed query tokens (cu_q non-NULL): sequence b owns tokens
+  // [cu_q[b], cu_q[b+1]) of q, aligned bottom-right to its keys; NULL: one
+  // query token per sequence.
+  const int32_t* cu_q;
   // fp8 cache (1 = OCP e4m3, 2 = OCP e5m2; 0 = bf16): one byte per element,
   // real value = descale[b][kv head] * decoded byte; descales NULL = 1
   int32_t kv_fp8;
@@ -180,6 +184,48 @@ struct DecodeArgs {
   const float* v_descale;
   float softcap;  // > 0: logit soft-capping of scale * s (per-head descale included)
 };
+
+// The decode row of one lane: query column `col` (0..31) of row block rb of
+// (sequence b, KV head hk). Rows fold the query tokens of the sequence and
+// the group query heads of the KV head (row = token * group + head offset,
+// as the prefill packs GQA rows). The row's query sits at key position
+// sk - n + t (t its token within the sequence, n the sequence's tokens:
+// bottom-right alignment) and sees keys [lo, hi]; hi < lo means none.
+struct DecRow {
+  bool valid;     // a real (token, head) row
+  int hq;         // query head
+  int64_t token;  // query token (sequence index b when one token per sequence)
+  int64_t prow;   // partial / output row: token * hq_total + hq
+  int lo, hi;     // visible keys
+};
+
+// Query tokens of sequence b ([t0, t0 + n)): packed by cu_q, or one token b.
+__device__ __forceinline__ void dec_tokens(const DecodeArgs& a, int b, int& t0, int& n) {
+  if (a.cu_q != nullptr) {
+    t0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]);
+    n = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]) - t0;
+  } else {
+    t0 = b;
+    n = 1;
+  }
+}
+
+__device__ __forceinline__ DecRow dec_row(const DecodeArgs& a, int t0, int n, int sk, int hk,
+                                          int rb, int col) {
+  DecRow r;
+  const int rows = n * a.group;
+  const int rho0 = rb * 32 + col;
+  r.valid = rho0 < rows;
+  const int rho = r.valid ? rho0 : max(rows - 1, 0);  // invalid lanes: the last row's values
+  const int t = rho / a.group;
+  r.hq = hk * a.group + (rho - t * a.group);
+  r.token = (int64_t)t0 + t;
+  r.prow = r.token * a.hq + r.hq;
+  const int p = sk - n + t;
+  r.lo = a.wl >= 0 ? max(0, p - a.wl) : 0;
+  r.hi = a.wr >= 0 ? min(p + a.wr, sk - 1) : sk - 1;
+  return r;
+}
 
 struct CombineArgs {
   const float* o_part;

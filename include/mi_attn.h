@@ -184,6 +184,22 @@ int mi_attn_fwd(const mi_attn_fwd_params *p, void *stream);
  * causal and window_right change nothing; window_left >= 0 restricts keys to
  * the last window_left + 1.
  *
+ * Several query tokens per sequence (cu_seqlens_q non-NULL; interface page,
+ * `flash_attn_varlen_func` with a page table and splits, e.g. a speculative
+ * decoding step): sequence b owns query tokens [cu_seqlens_q[b],
+ * cu_seqlens_q[b+1]) of
+ *   q    [total_q, num_heads_q, head_dim]  (q_batch_stride is the stride
+ *        between tokens, q_head_stride between heads)
+ *   out  [total_q, num_heads_q, head_dim]  (o_batch_stride between tokens)
+ *   lse  [total_q, num_heads_q] float32, or NULL
+ * with cu_seqlens_q a device int32 [batch + 1] array, total_q =
+ * cu_seqlens_q[batch] and max_seqlen_q >= every sequence's token count (host
+ * ints; max_seqlen_q sizes the launch, total_q the workspace). The n tokens
+ * of sequence b sit bottom-right at key positions seqused_k[b] - n ..
+ * seqused_k[b] - 1, so causal / window_right now matter: with causal, token
+ * i sees keys <= seqused_k[b] - n + i. With cu_seqlens_q NULL (one token per
+ * sequence) the three fields are ignored.
+ *
  * Keys are split into num_splits contiguous ranges (num_splits == 0 picks a
  * count from the occupancy heuristic; 1..256 are taken as given). Each split
  * writes float32 partials (O_s, LSE_s) into the workspace; the combine step
@@ -230,6 +246,9 @@ typedef struct {
                                            mi_attn_fwd, merged in the combine step */
   float softcap;                        /* 0: none; > 0: logit soft-capping, as for
                                            mi_attn_fwd (on the descaled scores) */
+  const int32_t *cu_seqlens_q;          /* device [batch+1] packed query tokens, or NULL
+                                           for one token per sequence */
+  int32_t max_seqlen_q, total_q;        /* with cu_seqlens_q: host bounds (see above) */
 } mi_attn_decode_params;
 
 /* The split count mi_attn_decode_splitkv will use for *p (resolves
@@ -237,9 +256,11 @@ typedef struct {
 int mi_attn_decode_num_splits(const mi_attn_decode_params *p);
 
 /* Workspace bytes mi_attn_decode_splitkv needs for *p; 0 if *p is invalid
- * (mi_attn_last_error() then says why). Layout: float32 O partials
- * [batch * num_heads_q][splits][head_dim], then float32 LSE partials
- * [batch * num_heads_q][splits], each 256-byte aligned. */
+ * (mi_attn_last_error() then says why; with no query row at all a valid
+ * request also needs 0 bytes, and the error string is then empty). Layout:
+ * float32 O partials [rows][splits][head_dim], then float32 LSE partials
+ * [rows][splits], each 256-byte aligned, rows = batch * num_heads_q (one
+ * token per sequence) or total_q * num_heads_q. */
 size_t mi_attn_decode_workspace_bytes(const mi_attn_decode_params *p);
 
 int mi_attn_decode_splitkv(const mi_attn_decode_params *p, void *stream);

@@ -164,3 +164,91 @@ def test_decode_rejects_bad_out_and_lse(gpu_lib):
         with pytest.raises(gpu_lib.MiAttnError) as e:
             gpu_lib.mi_attn_decode_splitkv(q, kc, vc, pt, num_splits=2, **kw)
         assert e.value.code == gpu_lib.MI_ATTN_EINVAL, kw
+
+
+# Several query tokens per sequence (packed by cu_seqlens_q) against the paged
+# cache, split along the keys and combined: the queries sit bottom-right at
+# the end of each sequence's keys. Reference: the oracle's paged prefill
+# (the same definition, no split).
+VARLEN_CASES = [
+    # (name, B, Hq, Hkv, D, page_size, pages_per_seq, seqused, q_lens, splits, causal, wl)
+    ("spec4_causal_gqa8_page256", 3, 16, 2, 128, 256, 5, [700, 1280, 5], [4, 1, 3], 4, True, None),
+    ("mixed_noncausal_d64_page16", 4, 8, 2, 64, 16, 20, [320, 33, 0, 100], [2, 8, 0, 5], 0,
+     False, None),
+    ("window_causal_mha", 2, 4, 4, 128, 64, 6, [384, 200], [8, 6], 3, True, 50),
+    ("gqa32_rows_span_blocks", 2, 32, 1, 128, 64, 4, [256, 77], [8, 3], 2, True, None),
+    ("more_tokens_than_keys", 1, 8, 2, 128, 64, 2, [3], [6], 2, True, None),
+    ("d256_tile_path", 2, 8, 2, 256, 32, 9, [288, 100], [3, 2], 5, True, None),
+    ("page48_tile_path", 2, 8, 2, 128, 48, 8, [380, 47], [5, 1], 3, True, 100),
+]
+
+
+def run_varlen_decode(mi, w, q_lens, splits, causal, wl, noalloc=False):
+    q, kc, vc = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    fn = mi.mi_attn_decode_splitkv_noalloc if noalloc else mi.mi_attn_decode_splitkv
+    out, lse = fn(q, kc, vc, dev_i32(w.page_table), seqused_k=dev_i32(w.seqused_k),
+                  cu_seqlens_q=dev_i32(w.cu_seqlens_q), max_seqlen_q=max(q_lens),
+                  softmax_scale=w.softmax_scale, num_splits=splits, causal=causal,
+                  window_left=wl, check_bounds=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=[c[0] for c in VARLEN_CASES])
+def test_varlen_decode_elementwise(gpu_lib, case):
+    name, B, Hq, Hkv, D, ps, pps, used, q_lens, splits, causal, wl = case
+    print(f"[case] varlen decode {name}", flush=True)
+    w = W.paged_prefill_case(len(name) * 13 + B, B, Hq, Hkv, D, ps, pps, used, seqlens_q=q_lens)
+    out, lse = run_varlen_decode(gpu_lib, w, q_lens, splits, causal, wl)
+    o_ref, l_ref = OA.paged_prefill(f64(w.q), f64(w.k), f64(w.v), w.page_table, w.seqused_k,
+                                    w.softmax_scale, causal=causal, window_left=wl,
+                                    cu_seqlens_q=w.cu_seqlens_q)
+    print(name, check(host_f64(out), o_ref, host_f64(lse).T, l_ref, what=name))
+
+
+def test_varlen_decode_one_token_equals_decode(gpu_lib):
+    """cu_seqlens_q with one token per sequence is the plain decode, bit for bit."""
+    print("[case] varlen decode with one token per sequence", flush=True)
+    w = W.paged_decode_case(95, 3, 16, 2, 128, 64, 6, seqused_k=[384, 200, 1], num_splits=4)
+    q, kc, vc = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    pt, su = dev_i32(w.page_table), dev_i32(w.seqused_k)
+    o1, l1 = gpu_lib.mi_attn_decode_splitkv(q, kc, vc, pt, seqused_k=su, num_splits=4)
+    cu = dev_i32(np.arange(4, dtype=np.int32))
+    o2, l2 = gpu_lib.mi_attn_decode_splitkv(q, kc, vc, pt, seqused_k=su, num_splits=4,
+                                            cu_seqlens_q=cu, max_seqlen_q=1, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_varlen_decode_full_size_speculative(gpu_lib):
+    """The paged decode workload's cache (B16, GQA 32/4, D128, Sk 32768,
+    permuted 256-token pages) with 4 causal query tokens per sequence (a
+    speculative decoding step), split heuristic: sampled heads, every token."""
+    print("[case] varlen decode full size, 4 tokens per sequence", flush=True)
+    w = W.paged_prefill_case(1005, 16, 32, 4, 128, 256, 128, [32768] * 16, seqlens_q=[4] * 16)
+    out, lse = run_varlen_decode(gpu_lib, w, [4] * 16, 0, True, None)
+    o_gpu, l_gpu = host_f64(out), host_f64(lse)
+    heads = [0, 7, 8, 31]
+    r = 8
+    for b in (0, 5, 15):
+        kb = OA.paged_gather(f64(w.k), w.page_table[b], 32768)
+        vb = OA.paged_gather(f64(w.v), w.page_table[b], 32768)
+        t0 = int(w.cu_seqlens_q[b])
+        vis = OA.visible_mask(4, 32768, True)
+        for h in heads:
+            o, l = OA.attention_head(f64(w.q[t0:t0 + 4, h]), kb[:, h // r], vb[:, h // r],
+                                     w.softmax_scale, vis)
+            check(o_gpu[t0:t0 + 4, h], o, l_gpu[t0:t0 + 4, h], l, what=f"seq {b} head {h}")
+
+
+def test_varlen_decode_noalloc_matches(gpu_lib):
+    print("[case] varlen decode through the no-allocation entry point", flush=True)
+    case = VARLEN_CASES[0]
+    name, B, Hq, Hkv, D, ps, pps, used, q_lens, splits, causal, wl = case
+    w = W.paged_prefill_case(len(name) * 13 + B, B, Hq, Hkv, D, ps, pps, used, seqlens_q=q_lens)
+    o1, l1 = run_varlen_decode(gpu_lib, w, q_lens, splits, causal, wl)
+    o2, l2 = run_varlen_decode(gpu_lib, w, q_lens, splits, causal, wl, noalloc=True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.isneginf(), l2.isneginf()) and torch.equal(l1[~l1.isneginf()],
+                                                                   l2[~l2.isneginf()])

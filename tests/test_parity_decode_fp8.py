@@ -165,3 +165,34 @@ def test_fp8_unsupported_shapes_rejected(gpu_lib):
     with pytest.raises(gpu_lib.MiAttnError) as e:
         run_fp8(gpu_lib, w)
     assert e.value.code == gpu_lib.MI_ATTN_EUNSUPPORTED
+
+
+def test_fp8_varlen_decode(gpu_lib):
+    """fp8 e4m3 cache with descales and three causal query tokens per
+    sequence (packed by cu_seqlens_q): against the oracle's paged prefill over
+    the decoded, descaled cache values."""
+    print("[case] fp8 varlen decode", flush=True)
+    w = W.paged_decode_fp8_case(97, 3, 16, 2, 128, 64, 6, num_pages=20,
+                                seqused_k=[384, 130, 2], num_splits=3)
+    q_lens = [3, 1, 3]
+    rng = np.random.default_rng(98)
+    qp = W.round_to_bf16_bits(rng.standard_normal((sum(q_lens), 16, 128), dtype=np.float32))
+    cu = np.zeros(4, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    out, lse = gpu_lib.mi_attn_decode_splitkv(
+        dev_bf16(qp), dev_u8(w.k), dev_u8(w.v), dev_i32(w.page_table),
+        seqused_k=dev_i32(w.seqused_k), cu_seqlens_q=dev_i32(cu), max_seqlen_q=3, causal=True,
+        softmax_scale=w.softmax_scale, num_splits=3, k_descale=dev_f32(w.k_descale),
+        v_descale=dev_f32(w.v_descale), check_bounds=True)
+    torch.cuda.synchronize()
+    # cached values: each page's codes times the descale of the sequence owning it
+    kd = np.full((w.k.shape[0], 2), np.nan)
+    vd = np.full((w.v.shape[0], 2), np.nan)
+    for b in range(3):
+        kd[w.page_table[b]] = w.k_descale[b]
+        vd[w.page_table[b]] = w.v_descale[b]
+    kval = OA.e4m3_decode(w.k) * kd[:, None, :, None]
+    vval = OA.e4m3_decode(w.v) * vd[:, None, :, None]
+    o_ref, l_ref = OA.paged_prefill(f64(qp), kval, vval, w.page_table, w.seqused_k,
+                                    w.softmax_scale, causal=True, cu_seqlens_q=cu)
+    print("fp8 varlen", check(host_f64(out), o_ref, host_f64(lse).T, l_ref, what="fp8 varlen"))
