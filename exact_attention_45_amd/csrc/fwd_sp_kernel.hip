@@ -15,7 +15,7 @@
 // blocks of 32 MFMA columns), so every K or V fragment read from LDS feeds QB
 // MFMAs. Iteration k of the key-tile loop:
 //   top     : wait until K(k+1) has landed, barrier
-//   softmax : mask S(k) on edge tiles, running max, lazy rescale of O
+//   softmax : lazy rescale of O (the row max of S(k) is already known)
 //   phase 1 : S(k+1) = K(k+1) Q^T on the matrix cores, each MFMA issued
 //             together with exponentials, row-sum adds and bf16 packing of
 //             P(k), K fragment reads a few MFMAs ahead; V(k+1) requested
@@ -23,7 +23,8 @@
 //             few MFMAs
 //   mid     : wait until V(k) has landed, barrier
 //   phase 2 : O += P(k) V(k), the transposing V reads issued several MFMAs
-//             ahead; K(k+3) requested the same way
+//             ahead; K(k+3) requested the same way; the edge mask and the
+//             row max of S(k+1) computed between the first MFMAs
 // Both phases are written in the intended issue order and held there by
 // scheduling barriers. Each tile is requested about one and a half
 // iterations before its use, and no wave ever issues its loads in a burst.
@@ -271,8 +272,15 @@ void fwd_sp_kernel(const FwdArgs a) {
     }
   };
 
-  // mask (edge tiles), running max, lazy rescale of O and l
-  auto sm_max = [&](STile& s, int j) {
+  // Softmax statistics of a score tile are taken in two steps: sm_edge
+  // (soft-capping, the edge-tile mask) and the tile's row max with the
+  // rescale decision, normally interleaved with the P V MFMAs of the previous
+  // tile (pv_tile) so the matrix cores keep working; then sm_apply at the top
+  // of the tile's own iteration, once O holds the previous tile's products:
+  // the (rare) lazy rescale of O and l, and the exp2 offset.
+  float mt_n[QB];   // row max of the next tile's scores (raw units)
+  bool grow_n[QB];  // whether it moves the running max
+  auto sm_edge = [&](STile& s, int j) __attribute__((always_inline)) {
     const int n0 = (n_begin + j) * BN;
     const bool full = (n0 + BN <= sk) && (n0 + BN - 1 <= full_hi) && (n0 >= full_lo);
     if constexpr (SC) {
@@ -298,9 +306,14 @@ void fwd_sp_kernel(const FwdArgs a) {
         }
       }
     }
-    bool grow[QB];
-    float mt[QB];
-    bool any = false;
+  };
+  // row max of a tile (two independent chains, then the lane pair) and the
+  // rescale decision against the running max
+  auto max_grow = [&](float m0, float m1, int qb) __attribute__((always_inline)) {
+    mt_n[qb] = pair_max(vmax(m0, m1));
+    grow_n[qb] = (m_run[qb] == kNegInf) ? (mt_n[qb] != kNegInf) : (mt_n[qb] - m_run[qb] > rescale_raw);
+  };
+  auto sm_max = [&](STile& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float m0 = kNegInf, m1 = kNegInf;
@@ -309,15 +322,18 @@ void fwd_sp_kernel(const FwdArgs a) {
         m0 = vmax3(m0, s[0][qb][v], s[0][qb][v + 1]);
         m1 = vmax3(m1, s[1][qb][v], s[1][qb][v + 1]);
       }
-      mt[qb] = pair_max(vmax(m0, m1));
-      grow[qb] = (m_run[qb] == kNegInf) ? (mt[qb] != kNegInf) : (mt[qb] - m_run[qb] > rescale_raw);
-      any = any || grow[qb];
+      max_grow(m0, m1, qb);
     }
+  };
+  auto sm_apply = [&]() __attribute__((always_inline)) {
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) any = any || grow_n[qb];
     if (__builtin_amdgcn_ballot_w64(any) != 0) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float m_new = grow[qb] ? mt[qb] : m_run[qb];
-        const float alpha = grow[qb]
+        const float m_new = grow_n[qb] ? mt_n[qb] : m_run[qb];
+        const float alpha = grow_n[qb]
                                 ? ((m_run[qb] == kNegInf) ? 0.0f : fast_exp2((m_run[qb] - m_new) * c))
                                 : 1.0f;
         m_run[qb] = m_new;
@@ -424,10 +440,16 @@ void fwd_sp_kernel(const FwdArgs a) {
   // groups keep that order: left free, the scheduler issues each read right
   // before its MFMA, which then waits out the whole LDS latency.
   // The NI loads of a K tile (descriptor kr, K buffer kbuf) go out spread
-  // over the MFMAs as in phase 1.
-  auto pv_tile = [&](auto buf_c, __amdgpu_buffer_rsrc_t kr, int kbuf) __attribute__((always_inline)) {
+  // over the MFMAs as in phase 1. With WM, the next tile's scores nx (tile
+  // j) get their edge treatment before the MFMAs and their row max during the
+  // first nine MFMAs (the vector units are otherwise idle in this phase).
+  auto pv_tile = [&](auto buf_c, __amdgpu_buffer_rsrc_t kr, int kbuf, auto wm_c, STile& nx, int j)
+      __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value;
+    constexpr bool WM = decltype(wm_c)::value;
+    static_assert(!WM || QB == 1, "interleaved row max handles one query block per wave");
     constexpr int N = 4 * NDB;
+    static_assert(N >= 9, "row max spread over the first nine MFMAs");
     static_assert(N % NI == 0, "loads spread evenly over the MFMAs");
     constexpr int LEAD2 = 6;
     auto read = [&](int i) __attribute__((always_inline)) {
@@ -440,6 +462,8 @@ void fwd_sp_kernel(const FwdArgs a) {
     bf16x8 ring[LEAD2];
 #pragma unroll
     for (int i = 0; i < LEAD2; ++i) ring[i] = read(i);
+    if constexpr (WM) sm_edge(nx, j);
+    float m0 = kNegInf, m1 = kNegInf;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -449,6 +473,14 @@ void fwd_sp_kernel(const FwdArgs a) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma32(vf, pf[qb][t], o[db][qb]);
       if (i % (N / NI) == 0) dma_k(kr, kbuf, i / (N / NI));
+      if constexpr (WM) {
+        if (i < 8) {
+          m0 = vmax3(m0, nx[0][0][2 * i], nx[0][0][2 * i + 1]);
+          m1 = vmax3(m1, nx[1][0][2 * i], nx[1][0][2 * i + 1]);
+        } else if (i == 8) {
+          max_grow(m0, m1, 0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -470,13 +502,16 @@ void fwd_sp_kernel(const FwdArgs a) {
   //        outstanding; the barrier also ends every wave's reads of K(k+1),
   //        whose buffer the P V phase refills with K(k+3)
   // so each tile is requested about one and a half iterations before use.
+  // The statistics of S(k) (row max, rescale decision) were taken during the
+  // P V phase of iteration k-1 (for k = 0 in the prologue); sm_apply
+  // rescales O and l, which then hold the products of tiles < k.
   auto step = [&](int k, auto par_c, STile& cur, STile& nxt) {
     constexpr int par = decltype(par_c)::value;
     using PN = std::integral_constant<int, par ^ 1>;
     vmcnt_wait<2 * NI>();
     lds_barrier();
     const auto vr = v_rsrc(k + 1);
-    sm_max(cur, k);
+    sm_apply();
     if (k + 1 < T) {
       phase1(PN{}, cur, nxt, vr, par ^ 1);
     } else {
@@ -486,7 +521,10 @@ void fwd_sp_kernel(const FwdArgs a) {
     }
     vmcnt_wait<2 * NI>();
     lds_barrier();
-    pv_tile(par_c, k_rsrc(k + 3), par ^ 1);
+    // At the last tile nxt holds no scores; the statistics taken from it are
+    // never used. (A second instantiation without them, selected by a branch,
+    // makes the register allocator spill.)
+    pv_tile(par_c, k_rsrc(k + 3), par ^ 1, std::true_type{}, nxt, k + 1);
   };
 
   if (T > 0) {
@@ -505,6 +543,8 @@ void fwd_sp_kernel(const FwdArgs a) {
     vmcnt_wait<2 * NI>();
     lds_barrier();
     s_tile(I0{}, sA);
+    sm_edge(sA, 0);
+    sm_max(sA);
     lds_barrier();
     {
       const auto k2 = k_rsrc(2);
