@@ -22,7 +22,8 @@ also under "decode". Progress goes to stderr.
 Flags: --gpus N (only 1 is supported: the path is single-GPU), --steps K,
 --warmup W, --warmup-gpu-ms T, --no-cpu-baseline, --cpu-seconds S (oracle
 sample budget), --all-configs (also time further workloads: head dims 96/192,
-paged prefill, softcap, backward, fp8 decode).
+paged prefill, softcap, backward, fp8 decode), --zero-inputs (prefill workloads
+on all-zero inputs; a clock measurement, never the reported value's data).
 
 Warm-up: W untimed steps, then more untimed steps until at least T ms (default
 1000) of GPU time has passed since the first. The core clock climbs only under
@@ -114,6 +115,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--zero-inputs", action="store_true",
+                    help="prefill workloads on all-zero Q/K/V (the same kernels and cycle "
+                         "counts; the matrix cores then draw less power and the core clock "
+                         "runs higher): shows how much of a launch's duration is clock")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the "
                          "reference kernel for scaling HBM byte counters), then exit")
@@ -177,10 +182,13 @@ def decode_bytes(w) -> int:
 
 
 class Prefill:
-    def __init__(self, mi, w, torch, softcap: float = 0.0):
+    def __init__(self, mi, w, torch, softcap: float = 0.0, zero: bool = False):
         from tests.gpu_util import dev_bf16, dev_i32
         self.mi, self.w = mi, w
         self.q, self.k, self.v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+        if zero:
+            for t in (self.q, self.k, self.v):
+                t.zero_()
         self.kw = dict(softmax_scale=w.softmax_scale, causal=w.causal,
                        window_left=w.window_left, window_right=w.window_right, softcap=softcap)
         if w.kind == "varlen":
@@ -467,7 +475,7 @@ def main():
             runs[i] = Decode(mi, ws[i], torch)
             work[i] = decode_bytes(ws[i])
         else:
-            runs[i] = Prefill(mi, ws[i], torch)
+            runs[i] = Prefill(mi, ws[i], torch, zero=args.zero_inputs)
             work[i] = prefill_flops(ws[i])
         if i not in (HEADLINE,):
             ws[i].q = ws[i].k = ws[i].v = None  # host copies no longer needed
@@ -554,7 +562,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic, all-zero prefill inputs" if args.zero_inputs else "synthetic",
         "config": {
             "workload": "long causal GQA prefill B1 Hq16 Hkv2 S16384 D256 (value); every step "
                         "also runs the tiny MHA, causal GQA S4096 D128, varlen window and paged "
