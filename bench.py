@@ -413,7 +413,7 @@ def extra_workloads(mi, W, torch, args, extra):
     torch.cuda.empty_cache()
     # backward; algorithmic flops 2.5x the forward's (five tile products per
     # score tile against two)
-    for wb in (W.standard_config(2),):
+    for wb in (W.standard_config(2), W.standard_config(3)):
         bw = Backward(mi, wb, torch)
         med = timed_extra(torch, bw, n)
         f = 2.5 * prefill_flops(wb)

@@ -517,8 +517,8 @@ int check_bwd(const mi_attn_bwd_params* p, mi_attn::BwdArgs* a) {
   if (p->num_heads_q % p->num_heads_kv != 0)
     return fail(MI_ATTN_EINVAL, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
                 p->num_heads_q, p->num_heads_kv);
-  if (p->head_dim != 64 && p->head_dim != 128)
-    return fail(MI_ATTN_EUNSUPPORTED, "backward head_dim %d not supported (64, 128)",
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return fail(MI_ATTN_EUNSUPPORTED, "backward head_dim %d not supported (64, 128, 256)",
                 p->head_dim);
   if (!isfinite(p->softmax_scale) || p->softmax_scale < 0.0f)
     return fail(MI_ATTN_EUNSUPPORTED, "softmax_scale must be finite and >= 0");
@@ -615,7 +615,7 @@ int check_bwd(const mi_attn_bwd_params* p, mi_attn::BwdArgs* a) {
 size_t bwd_workspace_for(const mi_attn::BwdArgs& a, int head_dim) {
   const int64_t n = mi_attn::bwd_dpsum_elems(a);
   if (n <= 0) return 0;
-  const int64_t parts = mi_attn::bwd_part_elems(a, mi_attn::bwd_splits(a), head_dim);
+  const int64_t parts = mi_attn::bwd_part_elems(a, mi_attn::bwd_splits(a, head_dim), head_dim);
   return round_up((size_t)n * sizeof(float)) + round_up((size_t)parts * sizeof(float));
 }
 
@@ -649,13 +649,15 @@ int mi_attn_bwd(const mi_attn_bwd_params* p, void* stream) {
   if (need > 0 && !aligned16(p->workspace))
     return fail(MI_ATTN_EINVAL, "workspace must be 16-byte aligned");
   a.dpsum = need > 0 ? static_cast<float*>(p->workspace) : nullptr;
-  a.splits = need > 0 ? mi_attn::bwd_splits(a) : 1;
+  a.splits = need > 0 ? mi_attn::bwd_splits(a, p->head_dim) : 1;
   a.dkv_part = a.splits > 1 ? reinterpret_cast<float*>(
                                   static_cast<char*>(p->workspace) +
                                   round_up((size_t)mi_attn::bwd_dpsum_elems(a) * sizeof(float)))
                             : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = p->head_dim == 64 ? mi_attn::launch_bwd<64>(a, s) : mi_attn::launch_bwd<128>(a, s);
+  hipError_t e = p->head_dim == 64    ? mi_attn::launch_bwd<64>(a, s)
+                 : p->head_dim == 128 ? mi_attn::launch_bwd<128>(a, s)
+                                      : mi_attn::launch_bwd<256>(a, s);
   if (e != hipSuccess) return fail(MI_ATTN_EHIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -45,8 +45,14 @@ struct BwdArgs {
 
 constexpr int kBwdBlockM = 128;   // dQ kernel: packed query rows per workgroup
 constexpr int kBwdBlockN = 128;   // dK/dV kernel: keys per workgroup (32 per wave)
+constexpr int kBwdBlockNPair = 64;  // paired dK/dV kernel (head_dim 256): keys per workgroup
 constexpr int kBwdTileM = 64;     // dK/dV kernel: queries per step
 constexpr int kBwdTileN = 64;     // dQ kernel: keys per step
+
+// Keys per dK/dV workgroup at a head dimension: head_dim 256 runs the paired
+// kernel, whose two waves per 32 keys each hold one of the dK, dV
+// accumulators.
+inline int bwd_block_n(int head_dim) { return head_dim == 256 ? kBwdBlockNPair : kBwdBlockN; }
 
 // Elements of the dpsum workspace (float32) for a.
 inline int64_t bwd_dpsum_elems(const BwdArgs& a) {
@@ -57,8 +63,9 @@ inline int64_t bwd_dpsum_elems(const BwdArgs& a) {
 // Splits of the dK/dV walk: enough workgroups for about two per compute
 // unit of a 256-unit device, at most four (each split adds a float32 partial
 // of dK and dV to write and reduce).
-inline int bwd_splits(const BwdArgs& a) {
-  const int64_t nblocks = ((int64_t)a.seqlen_k + kBwdBlockN - 1) / kBwdBlockN;
+inline int bwd_splits(const BwdArgs& a, int head_dim) {
+  const int bn = bwd_block_n(head_dim);
+  const int64_t nblocks = ((int64_t)a.seqlen_k + bn - 1) / bn;
   const int64_t wg = nblocks * a.hkv * a.batch;
   if (wg <= 0 || a.batch > 16383) return 1;
   const int64_t s = (512 + wg - 1) / wg;

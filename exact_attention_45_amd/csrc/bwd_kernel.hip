@@ -1,4 +1,4 @@
-// Attention backward for head_dim 64/128: dQ, dK, dV of exact attention.
+// Attention backward for head_dim 64/128/256: dQ, dK, dV of exact attention.
 //
 // Method (Blackwell backward page flash_bwd_sm100.py: P is recomputed from
 // the scores and the forward LSE in the exp2 domain, dV = P^T dO,
@@ -21,6 +21,9 @@
 //                    already summed over the group; with several, float32
 //                    partials go to the workspace and
 //   bwd_dkv_reduce_kernel  sums them in split order (deterministic)
+// At head_dim 256 bwd_dkdv_pair_kernel takes the dK/dV walk: 64 keys per
+// workgroup, each 32-key column served by two waves, one computing P and
+// dV, the other dP, dS and dK (P passes between them through LDS).
 // S and dP are recomputed in both kernels (seven tile products per score
 // tile instead of five) in exchange for no dQ accumulation buffer and no
 // atomic traffic.
@@ -79,16 +82,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs a) {
 // ----------------------------------------------------------- shared bits ----
 
 // Logical chunk ch of tile row `row` sits at chunk position ch ^ tswz<D>(row).
-// tswz extends swz_key (attn_common.hpp) for D = 128 by key bit 3 into
+// tswz extends swz_key (attn_common.hpp) for D >= 128 by key bit 3 into
 // chunk bit 3, as the forward does for its K tiles: the 16 lanes an LDS
 // cycle serves, reading one logical chunk of 16 consecutive rows, then hit
 // 16 different chunk positions (row fragments conflict-free), while each
 // transposing read (8 rows with the same bit 3) sees swz_key alone, shifted
-// by a whole 128-byte half. Row fragments: lane (c32, half) reads chunk
-// 2*cc + half of row c32 (+32 per 32-row block; same swizzle).
+// by 128 bytes within its 256-byte quarter. Row fragments: lane (c32, half)
+// reads chunk 2*cc + half of row c32 (+32 per 32-row block; same swizzle).
 template <int D>
 __device__ __forceinline__ int tswz(int row) {
-  return D == 128 ? (swz_key(row) | (((row >> 3) & 1) << 3)) : swz_key(row);
+  return D >= 128 ? (swz_key(row) | (((row >> 3) & 1) << 3)) : swz_key(row);
 }
 template <int D>
 struct BwdTile {
@@ -113,11 +116,11 @@ __device__ __forceinline__ void tr_offsets(int lane, int row_b, int tr[2]) {
   for (int i = 0; i < 2; ++i) tr[i] = row * row_b + (((4 * i + c) ^ f) * 16) + (j & 1) * 8;
 }
 
-// The second read covers rows with bit 3 set: under tswz<128> its 128-byte
-// half is the other one.
+// The second read covers rows with bit 3 set: under tswz<D> (D >= 128) its
+// 128-byte segment is the other one of the 256-byte pair.
 template <int ROW_B>
 __device__ __forceinline__ bf16x8 tr_frag(const char* tile, const int tr[2], int t, int db) {
-  constexpr int FLIP = ROW_B == 256 ? 1 : 0;
+  constexpr int FLIP = ROW_B >= 256 ? 1 : 0;
   const char* p = tile + (16 * t) * ROW_B + tr[db & 1];
   const bf16x4 v0 = ds_read_tr16(reinterpret_cast<const __bf16*>(p + (db >> 1) * 128));
   const bf16x4 v1 = ds_read_tr16(
@@ -155,8 +158,10 @@ __device__ __forceinline__ void acc_to_frags(const f32x16 x[2], bf16x8 f[4]) {
 
 // ------------------------------------------------------------------- dQ ----
 
+// At head_dim 256 the row's Q^T, dO^T fragments and the dQ accumulators
+// alone take 256 registers: one wave per SIMD.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 void bwd_dq_kernel(const BwdArgs a) {
   using T = BwdTile<D>;
   constexpr int ROW_B = T::ROW_B, CPR = T::CPR, TILE_B = T::TILE_B;
@@ -366,6 +371,32 @@ void bwd_dq_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------- dK dV ----
 
+// XCD-aware work order of the dK/dV grids. Consecutive workgroups go to the
+// eight XCDs in turn, so workgroup L runs on XCD g = L % 8 as its slot
+// s = L / 8 there. W items, numbered key block fastest (NB blocks), then
+// (KV head, sequence, split): each XCD should hold whole (KV head,
+// sequence) walks, whose workgroups read the same Q and dO rows and so
+// share its L2, and an even share of the work. With P = W / 8 items per
+// XCD:
+//   - NB <= P: XCD g takes the contiguous items g*P .. g*P + P-1 (whole
+//     walks of P / NB combinations);
+//   - NB = q P with q dividing 8: the q XCDs g = c q .. c q + q-1 share
+//     combination c, XCD c q + ph taking key blocks ph, ph + q, ...:
+//     under a causal mask the walk length falls with the key block, and a
+//     contiguous range of blocks per XCD would give the first XCD up to
+//     seven times the work of another;
+//   - otherwise (W not a multiple of 8, or no such q) the plain order.
+__device__ __forceinline__ int64_t dkdv_item(int64_t L, int64_t W, int64_t NB) {
+  if ((W & 7) != 0) return L;
+  const int64_t P = W >> 3, g = L & 7, s = L >> 3;
+  if (NB > P && NB % P == 0 && 8 % (NB / P) == 0) {
+    const int64_t q = NB / P;
+    return (g / q) * NB + s * q + (g % q);
+  }
+  if (NB > P) return L;
+  return g * P + s;
+}
+
 // One workgroup per 128 keys of a KV head (32 per wave) and split: the walk
 // over (query head of the group, 64-query tile) is cut into `splits`
 // contiguous parts, one per workgroup; every wave reads the whole staged
@@ -386,16 +417,10 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, half = lane >> 5;
   const int S = a.splits;
-  // XCD-aware work order: consecutive workgroups go to the eight XCDs in
-  // turn, so workgroup L runs on XCD L % 8. Work items are numbered key
-  // block fastest, then (KV head, sequence, split), and XCD x takes the
-  // contiguous range x * W / 8 .. : the workgroups that share one query
-  // head group's Q and dO rows then share one L2. (When W is not a
-  // multiple of 8 the plain order is kept.)
   const int64_t NB = gridDim.x;
   const int64_t W = NB * gridDim.y * gridDim.z;
   const int64_t L = blockIdx.x + NB * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
-  const int64_t w_item = (W & 7) == 0 ? (L & 7) * (W >> 3) + (L >> 3) : L;
+  const int64_t w_item = dkdv_item(L, W, NB);
   const int nb = (int)(w_item % NB);
   const int64_t combo = w_item / NB;  // hk + hkv * (b * S + sp)
   const int hk = (int)(combo % gridDim.y);
@@ -686,6 +711,323 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   }
 }
 
+// ----------------------------------------------------- dK dV, paired waves ----
+
+// The dK/dV walk for head_dim 256. Holding the lane's K and V fragments and
+// both 32 x 256 accumulators (dK^T, dV^T) takes ~540 registers, past the
+// 512 a wave can have, so each 32-key column is served by a pair of waves
+// that split the four products without repeating any:
+//   wave A (even): S = Q K^T, P = exp2(S c - LSE log2e), dV^T += dO^T P
+//   wave B (odd):  dP = dO V^T, dS = P (dP - dPsum), dK^T += Q^T dS
+// A hands P (float32) to B through LDS between the two phases of a step.
+// Each wave holds one key fragment set (K or V, 64 registers) and one
+// accumulator (128). One workgroup = two pairs = 64 keys; the Q / dO tile
+// staging, the split of the walk and the XCD-aware order are those of
+// bwd_dkdv_kernel.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+void bwd_dkdv_pair_kernel(const BwdArgs a) {
+  constexpr int ROW_B = D * 2, CPR = D / 8;
+  constexpr int BNK = kBwdBlockNPair, BM = kBwdTileM;
+  static_assert(BNK == 64 && BM == 64, "two 32-key wave pairs, 64-query tiles");
+  constexpr int TILE_B = BM * ROW_B;
+  // per buffer: Q tile, dO tile, then the tile's 64 LSE and 64 dPsum values
+  constexpr int BUF_B = 2 * TILE_B + 2 * 256;
+  constexpr int PX_B = 64 * 32 * 4;  // one pair's P: 32 floats per lane
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUF_B + 2 * PX_B];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c32 = lane & 31, half = lane >> 5;
+  const int role = wave & 1, pair = wave >> 1;  // role 0: A, 1: B
+  const int S = a.splits;
+  const int64_t NB = gridDim.x;
+  const int64_t W = NB * gridDim.y * gridDim.z;
+  const int64_t L = blockIdx.x + NB * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t w_item = dkdv_item(L, W, NB);
+  const int nb = (int)(w_item % NB);
+  const int64_t combo = w_item / NB;  // hk + hkv * (b * S + sp)
+  const int hk = (int)(combo % gridDim.y);
+  const int bs = (int)(combo / gridDim.y);
+  const int b = bs / S, sp = bs - b * S;
+
+  int sq = a.seqlen_q, sk = a.seqlen_k, q_tok0 = 0;
+  int64_t q_base, do_base, k_base, v_base, dk_base, dv_base;
+  if (a.cu_q != nullptr) {
+    q_tok0 = a.cu_q[b];
+    sq = a.cu_q[b + 1] - q_tok0;
+    q_base = (int64_t)q_tok0 * a.q_rs;
+    do_base = (int64_t)q_tok0 * a.do_rs;
+  } else {
+    q_base = (int64_t)b * a.q_bs;
+    do_base = (int64_t)b * a.do_bs;
+  }
+  if (a.cu_k != nullptr) {
+    const int k0 = a.cu_k[b];
+    sk = a.cu_k[b + 1] - k0;
+    k_base = (int64_t)k0 * a.k_rs;
+    v_base = (int64_t)k0 * a.v_rs;
+    dk_base = (int64_t)k0 * a.dk_rs;
+    dv_base = (int64_t)k0 * a.dv_rs;
+  } else {
+    k_base = (int64_t)b * a.k_bs;
+    v_base = (int64_t)b * a.v_bs;
+    dk_base = (int64_t)b * a.dk_bs;
+    dv_base = (int64_t)b * a.dv_bs;
+  }
+  sq = uniform(sq);
+  sk = uniform(sk);
+  const int j0 = nb * BNK;
+  if (j0 >= sk) return;  // uniform over the workgroup
+
+  const int key = j0 + pair * 32 + c32;
+  const bool kvalid = key < sk;
+  const int kk = kvalid ? key : 0;
+  const int r = a.group;
+  const int off = sk - sq;
+  // queries that see key j: j - off - wr <= i <= j - off + wl, 0 <= i < sq
+  const int qlo = a.wr >= 0 ? max(0, kk - off - a.wr) : 0;
+  const int qhi = kvalid ? (a.wl >= 0 ? min(sq - 1, kk - off + a.wl) : sq - 1) : qlo - 1;
+  const int j1 = min(sk, j0 + BNK) - 1;
+  const int i_lo = uniform(a.wr >= 0 ? max(0, j0 - off - a.wr) : 0);
+  const int i_hi = uniform(a.wl >= 0 ? min(sq - 1, j1 - off + a.wl) : sq - 1);
+  const int m_begin = i_lo / BM;
+  const int nm = i_hi >= i_lo ? i_hi / BM - m_begin + 1 : 0;
+  const int n_all = nm * r;
+  const int it_begin = uniform((int)((int64_t)n_all * sp / S));
+  const int it_end = uniform((int)((int64_t)n_all * (sp + 1) / S));
+
+  // this lane's key: K^T (wave A) or V^T (wave B) fragments, the B operands
+  // of S and dP
+  const __bf16* kvp =
+      role == 0 ? static_cast<const __bf16*>(a.k) + k_base + (int64_t)kk * a.k_rs +
+                      (int64_t)hk * a.k_hs
+                : static_cast<const __bf16*>(a.v) + v_base + (int64_t)kk * a.v_rs +
+                      (int64_t)hk * a.v_hs;
+  bf16x8 mf[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) {
+    const bf16x8 x = as_bf16x8(ld16(kvp + 16 * cc + 8 * half));
+    mf[cc] = kvalid ? x : zero_bf16x8();
+  }
+  const float c = a.scale_log2;
+
+  f32x16 acc[D / 32];  // A: dV^T, B: dK^T (unscaled)
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = zero_f32x16();
+
+  // Q / dO tile staging as in bwd_dkdv_kernel: instruction i of wave w
+  // fills tile rows RPI*(NI*w + i) .. +RPI-1; wave 0 loads the 64 LSE
+  // values, wave 1 the 64 dPsum values.
+  constexpr int RPI = 1024 / ROW_B;  // rows per instruction
+  constexpr int NI = BM / RPI / 4;   // instructions per wave per tensor
+  static_assert(NI * RPI * 4 == BM, "a tile splits evenly over four waves");
+  uint32_t qdo[NI], gdo[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = RPI * (NI * wave + i) + lane / CPR;
+    qdo[i] = (uint32_t)(row * a.q_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
+    gdo[i] = (uint32_t)(row * a.do_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
+  }
+  const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
+  const uint32_t lds_s = (uint32_t)uniform((int)(lds_addr(smem) + 2 * TILE_B + (wave & 1) * 256));
+  // iteration it: query head hk*r + it / nm, query tile m_begin + it % nm
+  auto issue = [&](int it, int buf) __attribute__((always_inline)) {
+    const int h = uniform(hk * r + it / nm);
+    const int m0 = uniform((m_begin + it % nm) * BM);
+    const int nrows = min(sq - m0, BM);  // >= 1; rows past it read as zero
+    const __bf16* q0 = static_cast<const __bf16*>(a.q) + q_base + (int64_t)m0 * a.q_rs +
+                       (int64_t)h * a.q_hs;
+    const __bf16* g0 = static_cast<const __bf16*>(a.dout) + do_base + (int64_t)m0 * a.do_rs +
+                       (int64_t)h * a.do_hs;
+    const auto qr = make_rsrc(q0, (uint32_t)((nrows - 1) * a.q_rs * 2 + ROW_B));
+    const auto gr = make_rsrc(g0, (uint32_t)((nrows - 1) * a.do_rs * 2 + ROW_B));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(qr, qdo[i], lds_w + (uint32_t)(buf * BUF_B + i * 1024));
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      dma16(gr, gdo[i], lds_w + (uint32_t)(buf * BUF_B + TILE_B + i * 1024));
+    if (wave < 2) {  // wave-uniform
+      const int64_t li = a.cu_q != nullptr ? (int64_t)h * a.total_q + q_tok0 + m0
+                                           : ((int64_t)b * a.hq + h) * sq + m0;
+      const auto sr = make_rsrc(wave == 0 ? a.lse + li : a.dpsum + li, (uint32_t)(nrows * 4));
+      dma4(sr, (uint32_t)(4 * lane), lds_s + (uint32_t)(buf * BUF_B));
+    }
+  };
+
+  int rd[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ tswz<D>(c32)) * 16);
+  int tr[2];
+  tr_offsets(lane, ROW_B, tr);
+  // this pair's P exchange: chunk i (4 floats) of lane l at 1024 i + 16 l
+  char* px = smem + 2 * BUF_B + pair * PX_B + 16 * lane;
+
+  // phase 1: the S (A) or dP (B) products of both 32-query blocks, reading
+  // Q (A) or dO (B) rows; MFMA g: block g / NK, contraction step g % NK
+  auto rows_products = [&](const char* t, f32x16 x[2], auto&& between)
+      __attribute__((always_inline)) {
+    constexpr int NK = D / 16, N = 2 * NK, LEAD = 6;
+    auto rdf = [&](int g) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(t + (g / NK) * 32 * ROW_B + rd[g % NK]);
+    };
+    bf16x8 ring[LEAD];
+#pragma unroll
+    for (int g = 0; g < LEAD; ++g) ring[g] = rdf(g);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < N; ++g) {
+      const bf16x8 f = ring[g % LEAD];
+      if (g + LEAD < N) ring[g % LEAD] = rdf(g + LEAD);
+      x[g / NK] = mfma32(f, mf[g % NK], x[g / NK]);
+      between(g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // phase 2: acc^T += T^T F over the 64 queries, T read by transposing
+  // reads; MFMA g: 16-query step g / NDB, d-block g % NDB
+  auto trans_products = [&](const char* t, bf16x8 fr[4], auto&& between)
+      __attribute__((always_inline)) {
+    constexpr int NDB = D / 32, N = 4 * NDB, LEAD = 4;
+    bf16x8 ring[LEAD];
+#pragma unroll
+    for (int g = 0; g < LEAD; ++g) ring[g] = tr_frag<ROW_B>(t, tr, g / NDB, g % NDB);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < N; ++g) {
+      between(g);
+      const bf16x8 f = ring[g % LEAD];
+      if (g + LEAD < N) ring[g % LEAD] = tr_frag<ROW_B>(t, tr, (g + LEAD) / NDB, (g + LEAD) % NDB);
+      acc[g % NDB] = mfma32(f, fr[g / NDB], acc[g % NDB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto to_frags = [&](const f32x16& x, bf16x8& f0, bf16x8& f1) __attribute__((always_inline)) {
+    f0 = cat(cvt4(x[0], x[1], x[2], x[3]), cvt4(x[4], x[5], x[6], x[7]));
+    f1 = cat(cvt4(x[8], x[9], x[10], x[11]), cvt4(x[12], x[13], x[14], x[15]));
+  };
+
+  // element (qb, v) of a score accumulator holds query
+  // m0 + 4*half + 32*qb + 8*(v>>2) + (v&3), key `key`
+  auto step = [&](int m0, const char* qt) __attribute__((always_inline)) {
+    const char* gt = qt + TILE_B;
+    const float* lses = reinterpret_cast<const float*>(qt + 2 * TILE_B);  // raw LSE
+    const float* dss = lses + BM;
+    f32x16 x[2];
+    x[0] = zero_f32x16();
+    x[1] = zero_f32x16();
+    bf16x8 fr[4];
+    if (role == 0) {
+      const uint64_t vis = vis64(qlo - m0 - 4 * half, qhi - m0 - 4 * half);
+      f32x4 l4[2][4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 l = *reinterpret_cast<const f32x4*>(lses + 32 * qb + 8 * i + 4 * half);
+          // LSE*log2e; a row with no visible key (LSE = -inf) gets +inf, so
+          // P = 0 (rows past the sequence read 0 and are masked)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            l4[qb][i][j] = l[j] == kNegInf ? __builtin_huge_valf() : l[j] * kLog2e;
+        }
+      // P of block qb, elements [e0, e1)
+      auto sm = [&](int qb, int e0, int e1) __attribute__((always_inline)) {
+        const uint32_t w = (uint32_t)(vis >> (32 * qb));
+#pragma unroll
+        for (int v = e0; v < e1; ++v) {
+          const float xm = mask_by_bit(x[qb][v], w, 8 * (v >> 2) + (v & 3));
+          x[qb][v] = fast_exp2(fmaf(xm, c, -l4[qb][v >> 2][v & 3]));
+        }
+      };
+      constexpr int NK = D / 16;
+      // block 0's P between block 1's MFMAs
+      rows_products(qt, x, [&](int g) __attribute__((always_inline)) {
+        if (g >= NK) sm(0, 16 * (g - NK) / NK, 16 * (g - NK + 1) / NK);
+      });
+      sm(1, 0, 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const f32x16& xs = x[i >> 2];
+        *reinterpret_cast<f32x4*>(px + 1024 * i) =
+            f32x4{xs[4 * (i & 3)], xs[4 * (i & 3) + 1], xs[4 * (i & 3) + 2], xs[4 * (i & 3) + 3]};
+      }
+      to_frags(x[0], fr[0], fr[1]);
+      to_frags(x[1], fr[2], fr[3]);
+    } else {
+      rows_products(gt, x, [](int) __attribute__((always_inline)) {});
+    }
+    lds_barrier();  // A's P is in LDS
+    if (role == 0) {
+      trans_products(gt, fr, [](int) __attribute__((always_inline)) {});  // dV^T += dO^T P
+    } else {
+      // dS = P (dP - dPsum) of block qb, into x[qb], then its fragments
+      auto ds = [&](int qb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 p = *reinterpret_cast<const f32x4*>(px + 1024 * (4 * qb + i));
+          const f32x4 d = *reinterpret_cast<const f32x4*>(dss + 32 * qb + 8 * i + 4 * half);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[qb][4 * i + j] = p[j] * (x[qb][4 * i + j] - d[j]);
+        }
+        to_frags(x[qb], fr[2 * qb], fr[2 * qb + 1]);
+      };
+      ds(0);
+      constexpr int NDB = D / 32;
+      // dK^T += Q^T dS; block 1's dS before its first MFMA
+      trans_products(qt, fr, [&](int g) __attribute__((always_inline)) {
+        if (g == 2 * NDB) ds(1);
+      });
+    }
+  };
+
+  if (it_end > it_begin) {
+    issue(it_begin, 0);
+    vmcnt_wait<0>();
+    lds_barrier();
+    for (int it = it_begin; it < it_end; ++it) {
+      const int cur = (it - it_begin) & 1;
+      const int m0 = uniform((m_begin + it % nm) * BM);
+      // the other buffer's last readers finished before the previous barrier
+      if (it + 1 < it_end) issue(it + 1, cur ^ 1);
+      step(m0, smem + cur * BUF_B);
+      vmcnt_wait<0>();  // this wave's share of the next tile has landed
+      lds_barrier();    // and every other wave's; B is done with this P
+    }
+  }
+
+  if (!kvalid) return;
+  if (S == 1) {
+    __bf16* dst = role == 0 ? static_cast<__bf16*>(a.dv) + dv_base + (int64_t)key * a.dv_rs +
+                                  (int64_t)hk * a.dv_hs
+                            : static_cast<__bf16*>(a.dk) + dk_base + (int64_t)key * a.dk_rs +
+                                  (int64_t)hk * a.dk_hs;
+    const float sc = role == 0 ? 1.0f : a.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * half;
+        *reinterpret_cast<bf16x4*>(dst + d0) =
+            cvt4(acc[db][4 * i] * sc, acc[db][4 * i + 1] * sc, acc[db][4 * i + 2] * sc,
+                 acc[db][4 * i + 3] * sc);
+      }
+  } else if (key < a.seqlen_k) {
+    // partial row (split, sequence, key, KV head): dK then dV, D floats each
+    // (keys past the caller's max_seqlen_k are not written anywhere)
+    float* pp = a.dkv_part +
+                ((((int64_t)sp * a.batch + b) * a.seqlen_k + key) * a.hkv + hk) * (2 * D) +
+                (role == 0 ? D : 0);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * half;
+        *reinterpret_cast<f32x4*>(pp + d0) =
+            f32x4{acc[db][4 * i], acc[db][4 * i + 1], acc[db][4 * i + 2], acc[db][4 * i + 3]};
+      }
+  }
+}
+
 // Sums the splits' float32 partials in split order (deterministic), scales
 // dK, and writes dK and dV as bf16. One thread per 4 floats of a partial row.
 template <int D>
@@ -737,10 +1079,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   if (mblocks > 0 && a.batch > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)mblocks, a.hkv, a.batch), dim3(256), 0,
                        s, a);
-  const int64_t nblocks = ((int64_t)a.seqlen_k + kBwdBlockN - 1) / kBwdBlockN;
+  constexpr int BN = D == 256 ? kBwdBlockNPair : kBwdBlockN;
+  const int64_t nblocks = ((int64_t)a.seqlen_k + BN - 1) / BN;
   if (nblocks > 0 && a.batch > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)nblocks, a.hkv, a.batch * a.splits),
-                       dim3(256), 0, s, a);
+    if constexpr (D == 256)
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D>),
+                         dim3((unsigned)nblocks, a.hkv, a.batch * a.splits), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)nblocks, a.hkv, a.batch * a.splits),
+                         dim3(256), 0, s, a);
     if (a.splits > 1) {
       const int64_t chunks = (int64_t)a.batch * a.seqlen_k * a.hkv * (D / 2);
       hipLaunchKernelGGL((bwd_dkv_reduce_kernel<D>), dim3((unsigned)((chunks + 255) / 256)),
@@ -752,5 +1099,6 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
 
 template hipError_t launch_bwd<64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd<128>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd<256>(const BwdArgs&, hipStream_t);
 
 }  // namespace mi_attn

@@ -72,6 +72,17 @@ DENSE = [
     # 8 key blocks x 16 KV heads x 4 sequences = 512 workgroups: one split
     # (dK, dV written directly); the cases above take the split path
     ("no_split_mha16_b4_s1024_d64", 4, 1024, 1024, 16, 16, 64, True, None, None),
+    # head_dim 256 (paired dK/dV waves, 64-key workgroups): split path,
+    # bottom-right window with Sq != Sk, MQA, and 16 key blocks x 16 KV
+    # heads x 2 sequences = 512 workgroups (one split)
+    ("gqa2_d256_causal_s300", 1, 300, 300, 4, 2, 256, True, None, None),
+    ("window_40_7_d256_sq_gt_sk", 2, 257, 200, 2, 1, 256, False, 40, 7),
+    ("mqa4_d256_causal_s129", 1, 129, 129, 4, 1, 256, True, None, None),
+    ("no_split_mha16_b2_s1024_d256", 2, 1024, 1024, 16, 16, 256, True, None, None),
+    # one KV head, four splits: 16 key blocks over 64 workgroups, so two XCDs
+    # share each walk with interleaved key blocks
+    ("interleaved_xcd_mqa4_d256_s1024", 1, 1024, 1024, 4, 1, 256, True, None, None),
+    ("interleaved_xcd_mqa4_d128_s2048", 1, 2048, 2048, 4, 1, 128, True, None, None),
 ]
 
 
@@ -89,13 +100,14 @@ def test_bwd_dense_elementwise(gpu_lib, case):
         print(name, nm, check_grad(host_f64(got), r, f"{name} {nm}"))
 
 
-def test_bwd_varlen_elementwise(gpu_lib):
+@pytest.mark.parametrize("D", [128, 256])
+def test_bwd_varlen_elementwise(gpu_lib, D):
     """Packed sequences with an empty query sequence, a one-token one and
     ragged tails; GQA 4:1, causal (bottom-right per sequence)."""
-    print("[case] bwd varlen", flush=True)
+    print(f"[case] bwd varlen D{D}", flush=True)
     lq, lk = [1, 130, 0, 77, 200], [1, 150, 40, 77, 129]
-    w = W.varlen_case(4242, lq, lk, 8, 2, 128, causal=True)
-    g = W.grad_output(4242, (sum(lq), 8, 128))
+    w = W.varlen_case(4242 + D, lq, lk, 8, 2, D, causal=True)
+    g = W.grad_output(4242 + D, (sum(lq), 8, D))
     q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
     cq, ck = dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k)
     kw = dict(cu_seqlens_q=cq, cu_seqlens_k=ck, max_seqlen_q=max(lq), max_seqlen_k=max(lk),
@@ -106,7 +118,7 @@ def test_bwd_varlen_elementwise(gpu_lib):
     ref = OA.attention_varlen_backward(f64(w.q), f64(w.k), f64(w.v), f64(g), w.cu_seqlens_q,
                                        w.cu_seqlens_k, w.softmax_scale, causal=True)
     for nm, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
-        print("varlen", nm, check_grad(host_f64(got), r, f"varlen {nm}"))
+        print("varlen", D, nm, check_grad(host_f64(got), r, f"varlen D{D} {nm}"))
     # keys of the sequence with no queries get exactly zero gradients
     k0, k1 = int(w.cu_seqlens_k[2]), int(w.cu_seqlens_k[3])
     assert not host_f64(dk)[k0:k1].any() and not host_f64(dv)[k0:k1].any()
@@ -186,11 +198,59 @@ def test_bwd_full_size_sampled(gpu_lib):
         check_grad(dv[0, j, gk], dv_w[n], f"dv key {j}")
 
 
+def test_bwd_full_size_sampled_d256(gpu_lib):
+    """The long causal GQA prefill workload's shape (B1, Hq16, Hkv2, S16384,
+    D256): dQ rows of sampled heads, and dK / dV rows of keys in the last 512
+    positions (every query that sees them is among the last 512 rows, whose
+    probabilities need the whole row of keys)."""
+    print("[case] bwd full size d256", flush=True)
+    w = W.standard_config(3)
+    B, Sq, Hq, D = w.q.shape
+    Hkv = w.k.shape[2]
+    g = W.grad_output(w.seed, w.q.shape)
+    dq, dk, dv = run_dense(gpu_lib, w, g)
+    dq, dk, dv = host_f64(dq), host_f64(dk), host_f64(dv)
+    q, k, v, go = f64(w.q), f64(w.k), f64(w.v), f64(g)
+    r = Hq // Hkv
+    scale = w.softmax_scale
+    for h in (0, 9, 15):
+        gk = h // r
+        for i in (0, 63, 64, 9001, 16383):
+            s = scale * (k[0, :i + 1, gk] @ q[0, i, h])
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o = p @ v[0, :i + 1, gk]
+            dp = v[0, :i + 1, gk] @ go[0, i, h]
+            ds = p * (dp - o @ go[0, i, h])
+            want = scale * (ds @ k[0, :i + 1, gk])
+            check_grad(dq[0, i, h], want, f"dq row {i} head {h}")
+    gk = 1
+    keys = (Sq - 512, Sq - 64, Sq - 1)  # a 64-key block start, the last block
+    i0 = keys[0]
+    dk_w = np.zeros((len(keys), D))
+    dv_w = np.zeros((len(keys), D))
+    rows = np.arange(i0, Sq)
+    for h in range(gk * r, gk * r + r):
+        s = scale * (q[0, i0:, h] @ k[0, :, gk].T)
+        s[np.arange(Sq)[None, :] > rows[:, None]] = -np.inf
+        pr = np.exp(s - s.max(axis=1, keepdims=True))
+        pr /= pr.sum(axis=1, keepdims=True)
+        dpsum = np.sum((pr @ v[0, :, gk]) * go[0, i0:, h], axis=1)
+        for n, j in enumerate(keys):
+            ds_j = pr[:, j] * (go[0, i0:, h] @ v[0, j, gk] - dpsum)
+            dv_w[n] += pr[:, j] @ go[0, i0:, h]
+            dk_w[n] += scale * (ds_j @ q[0, i0:, h])
+        del s, pr
+    for n, j in enumerate(keys):
+        check_grad(dk[0, j, gk], dk_w[n], f"dk key {j}")
+        check_grad(dv[0, j, gk], dv_w[n], f"dv key {j}")
+
+
 def test_bwd_zero_scale(gpu_lib):
     """softmax_scale = 0: P is uniform over each row's visible keys, dQ = dK =
     0, dV = P^T dO; masked keys (causal, rows with no key) must not give NaN."""
     print("[case] bwd zero scale", flush=True)
-    for B, Sq, Sk, D in ((1, 130, 130, 128), (1, 90, 40, 64)):
+    for B, Sq, Sk, D in ((1, 130, 130, 128), (1, 90, 40, 64), (1, 100, 100, 256)):
         w = W.dense_case(93 + Sq, B, Sq, Sk, 4, 2, D, causal=True, softmax_scale=0.0)
         g = W.grad_output(93 + Sq, (B, Sq, 4, D))
         dq, dk, dv = run_dense(gpu_lib, w, g)
@@ -200,8 +260,9 @@ def test_bwd_zero_scale(gpu_lib):
             print("scale0", nm, check_grad(host_f64(got), r, f"scale0 {nm}"))
 
 
-def test_bwd_rejects_head_dim_256(gpu_lib):
-    w = W.dense_case(3, 1, 64, 64, 2, 1, 256)
+def test_bwd_rejects_head_dim_192(gpu_lib):
+    """The forward serves head_dim 192; the backward does not."""
+    w = W.dense_case(3, 1, 64, 64, 2, 1, 192)
     q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
     out, lse = gpu_lib.mi_attn_fwd(q, k, v)
     with pytest.raises(gpu_lib.MiAttnError) as e:
