@@ -610,13 +610,13 @@ int check_bwd(const mi_attn_bwd_params* p, mi_attn::BwdArgs* a) {
   return MI_ATTN_OK;
 }
 
-// Workspace: dPsum (float32 per query row and head), then the dK/dV split
-// partials when the walk is split.
+// Workspace: dPsum, then LSE log2 e (float32 per query row and head each),
+// then the dK/dV split partials when the walk is split.
 size_t bwd_workspace_for(const mi_attn::BwdArgs& a, int head_dim) {
   const int64_t n = mi_attn::bwd_dpsum_elems(a);
   if (n <= 0) return 0;
   const int64_t parts = mi_attn::bwd_part_elems(a, mi_attn::bwd_splits(a, head_dim), head_dim);
-  return round_up((size_t)n * sizeof(float)) + round_up((size_t)parts * sizeof(float));
+  return 2 * round_up((size_t)n * sizeof(float)) + round_up((size_t)parts * sizeof(float));
 }
 
 }  // namespace
@@ -648,12 +648,14 @@ int mi_attn_bwd(const mi_attn_bwd_params* p, void* stream) {
                 p->workspace == nullptr ? (size_t)0 : p->workspace_bytes);
   if (need > 0 && !aligned16(p->workspace))
     return fail(MI_ATTN_EINVAL, "workspace must be 16-byte aligned");
+  const size_t rows_b = round_up((size_t)mi_attn::bwd_dpsum_elems(a) * sizeof(float));
   a.dpsum = need > 0 ? static_cast<float*>(p->workspace) : nullptr;
+  a.lse_log2 =
+      need > 0 ? reinterpret_cast<float*>(static_cast<char*>(p->workspace) + rows_b) : nullptr;
   a.splits = need > 0 ? mi_attn::bwd_splits(a, p->head_dim) : 1;
-  a.dkv_part = a.splits > 1 ? reinterpret_cast<float*>(
-                                  static_cast<char*>(p->workspace) +
-                                  round_up((size_t)mi_attn::bwd_dpsum_elems(a) * sizeof(float)))
-                            : nullptr;
+  a.dkv_part = a.splits > 1
+                   ? reinterpret_cast<float*>(static_cast<char*>(p->workspace) + 2 * rows_b)
+                   : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = p->head_dim == 64    ? mi_attn::launch_bwd<64>(a, s)
                  : p->head_dim == 128 ? mi_attn::launch_bwd<128>(a, s)

@@ -20,7 +20,8 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dpsum;  // workspace: row sums of O * dO
+  float* dpsum;     // workspace: row sums of O * dO
+  float* lse_log2;  // workspace: LSE * log2(e), +inf where LSE = -inf
   // workspace when splits > 1: float32 dK / dV partials of each split,
   // [splits][batch][seqlen_k][hkv][2][head_dim] (seqlen_k: the maximum)
   float* dkv_part;
@@ -54,7 +55,7 @@ constexpr int kBwdTileN = 64;     // dQ kernel: keys per step
 // accumulators.
 inline int bwd_block_n(int head_dim) { return head_dim == 256 ? kBwdBlockNPair : kBwdBlockN; }
 
-// Elements of the dpsum workspace (float32) for a.
+// Elements of the dpsum workspace (float32) for a; lse_log2 has as many.
 inline int64_t bwd_dpsum_elems(const BwdArgs& a) {
   return a.cu_q != nullptr ? (int64_t)a.hq * a.total_q
                            : (int64_t)a.batch * a.hq * a.seqlen_q;

@@ -8,7 +8,9 @@
 // query heads of a KV head).
 //
 // Three or four launches, no atomics, deterministic:
-//   bwd_pre_kernel   dPsum[row] = sum_d O[row, d] dO[row, d]  (float32 workspace)
+//   bwd_pre_kernel   dPsum[row] = sum_d O[row, d] dO[row, d] and LSE[row] log2 e
+//                    (float32 workspace; +inf for LSE = -inf, so that the
+//                    probabilities exp2(S c - LSE log2 e) of such a row are 0)
 //   bwd_dq_kernel    one workgroup per 128 packed query rows (as the forward
 //                    packs GQA heads): walks the visible 64-key tiles, per
 //                    tile S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - dPsum),
@@ -76,7 +78,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs a) {
   }
 #pragma unroll
   for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, CPR);
-  if (ok && c == 0) a.dpsum[out_idx] = acc;
+  if (ok && c == 0) {
+    a.dpsum[out_idx] = acc;
+    const float l = a.lse[out_idx];
+    a.lse_log2[out_idx] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+  }
 }
 
 // ----------------------------------------------------------- shared bits ----
@@ -232,10 +238,9 @@ void bwd_dq_kernel(const BwdArgs a) {
   }
   const int64_t li = a.cu_q != nullptr ? (int64_t)hq * a.total_q + q_tok0 + pos
                                        : ((int64_t)b * a.hq + hq) * sq + pos;
-  const float lse = valid ? a.lse[li] : kNegInf;
+  // a row with no visible key (LSE = -inf) has +inf here: P = exp2(x - inf) = 0
+  const float lse2 = valid ? a.lse_log2[li] : __builtin_huge_valf();
   const float dps = valid ? a.dpsum[li] : 0.0f;
-  // a row with no visible key (LSE = -inf) gets P = exp2(x - inf) = 0
-  const float lse2 = lse == kNegInf ? __builtin_huge_valf() : lse * kLog2e;
   const float c = a.scale_log2;
 
   f32x16 dqa[D / 32];
@@ -276,6 +281,12 @@ void bwd_dq_kernel(const BwdArgs a) {
   int tr[2];
   tr_offsets(lane, ROW_B, tr);
 
+  // One step, software-pipelined over the two 32-key blocks kb of the tile
+  // so that each block's dS arithmetic runs between matrix instructions:
+  //   part 1: S^T, dP^T of block 0, then of block 1 with one block-0 dS
+  //           slice after each MFMA
+  //   part 2: dQ^T over the 16-key steps of block 0 with one block-1 dS
+  //           slice after each MFMA, then over those of block 1
   auto compute = [&](int n0, const char* kt) __attribute__((always_inline)) {
     const char* vt = kt + TILE_B;
     f32x16 s[2], dp[2];
@@ -284,56 +295,71 @@ void bwd_dq_kernel(const BwdArgs a) {
       s[kb] = zero_f32x16();
       dp[kb] = zero_f32x16();
     }
+    // element (kb, v) holds key n0 + 4*half + 32*kb + 8*(v>>2) + (v&3)
+    const uint64_t vis = vis64(lo - n0 - 4 * half, hi - n0 - 4 * half);
+    // dS^T elements [e0, e1) of block kb, in place of S^T
+    auto ds = [&](int kb, int e0, int e1) __attribute__((always_inline)) {
+      const uint32_t w = (uint32_t)(vis >> (32 * kb));
+#pragma unroll
+      for (int v = e0; v < e1; ++v) {
+        const float x = mask_by_bit(s[kb][v], w, 8 * (v >> 2) + (v & 3));
+        const float p = fast_exp2(fmaf(x, c, -lse2));
+        s[kb][v] = p * (dp[kb][v] - dps);
+      }
+    };
     {
-      // MFMA i: contraction step i / 4, key block (i / 2) % 2; even i: S^T
-      // from K rows, odd i: dP^T from V rows
-      constexpr int N = 4 * (D / 16), LEAD = 6;
-      auto rdf = [&](int i) __attribute__((always_inline)) {
-        return *reinterpret_cast<const bf16x8*>((i & 1 ? vt : kt) + ((i >> 1) & 1) * 32 * ROW_B +
-                                                rd[i >> 2]);
+      // MFMA g: block g / NS, i = g % NS: contraction step i / 2; even i:
+      // S^T from K rows, odd i: dP^T from V rows
+      constexpr int NS = 2 * (D / 16), N = 2 * NS, LEAD = 6;
+      auto rdf = [&](int g) __attribute__((always_inline)) {
+        const int kb = g / NS, i = g % NS;
+        return *reinterpret_cast<const bf16x8*>((i & 1 ? vt : kt) + kb * 32 * ROW_B + rd[i >> 1]);
       };
       bf16x8 ring[LEAD];
 #pragma unroll
-      for (int i = 0; i < LEAD; ++i) ring[i] = rdf(i);
+      for (int g = 0; g < LEAD; ++g) ring[g] = rdf(g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const bf16x8 f = ring[i % LEAD];
-        if (i + LEAD < N) ring[i % LEAD] = rdf(i + LEAD);
-        const int kb = (i >> 1) & 1;
+      for (int g = 0; g < N; ++g) {
+        const bf16x8 f = ring[g % LEAD];
+        if (g + LEAD < N) ring[g % LEAD] = rdf(g + LEAD);
+        const int kb = g / NS, i = g % NS;
         if (i & 1)
-          dp[kb] = mfma32(f, gf[i >> 2], dp[kb]);
+          dp[kb] = mfma32(f, gf[i >> 1], dp[kb]);
         else
-          s[kb] = mfma32(f, qf[i >> 2], s[kb]);
+          s[kb] = mfma32(f, qf[i >> 1], s[kb]);
+        if (kb == 1) ds(0, 16 * i / NS, 16 * (i + 1) / NS);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // element (kb, v) holds key n0 + 4*half + 32*kb + 8*(v>>2) + (v&3)
-    const uint64_t vis = vis64(lo - n0 - 4 * half, hi - n0 - 4 * half);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t w = (uint32_t)(vis >> (32 * kb));
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float x = mask_by_bit(s[kb][v], w, 8 * (v >> 2) + (v & 3));
-        const float p = fast_exp2(fmaf(x, c, -lse2));
-        s[kb][v] = p * (dp[kb][v] - dps);  // dS^T
-      }
-    }
     bf16x8 dsf[4];
-    acc_to_frags(s, dsf);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int i0 = 8 * t;
+      dsf[t] = cat(cvt4(s[0][i0], s[0][i0 + 1], s[0][i0 + 2], s[0][i0 + 3]),
+                   cvt4(s[0][i0 + 4], s[0][i0 + 5], s[0][i0 + 6], s[0][i0 + 7]));
+    }
     {
-      // MFMA i: 16-key step i / NDB, d-block i % NDB
-      constexpr int NDB = D / 32, N = 4 * NDB, LEAD = 4;
+      // MFMA g: 16-key step g / NDB (steps 0, 1: block 0), d-block g % NDB
+      constexpr int NDB = D / 32, NP = 2 * NDB, N = 4 * NDB, LEAD = 4;
       bf16x8 ring[LEAD];
 #pragma unroll
-      for (int i = 0; i < LEAD; ++i) ring[i] = tr_frag<ROW_B>(kt, tr, i / NDB, i % NDB);
+      for (int g = 0; g < LEAD; ++g) ring[g] = tr_frag<ROW_B>(kt, tr, g / NDB, g % NDB);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const bf16x8 f = ring[i % LEAD];
-        if (i + LEAD < N) ring[i % LEAD] = tr_frag<ROW_B>(kt, tr, (i + LEAD) / NDB, (i + LEAD) % NDB);
-        dqa[i % NDB] = mfma32(f, dsf[i / NDB], dqa[i % NDB]);
+      for (int g = 0; g < N; ++g) {
+        if (g == NP) {
+#pragma unroll
+          for (int t = 2; t < 4; ++t) {
+            const int i0 = 8 * (t - 2);
+            dsf[t] = cat(cvt4(s[1][i0], s[1][i0 + 1], s[1][i0 + 2], s[1][i0 + 3]),
+                         cvt4(s[1][i0 + 4], s[1][i0 + 5], s[1][i0 + 6], s[1][i0 + 7]));
+          }
+        }
+        const bf16x8 f = ring[g % LEAD];
+        if (g + LEAD < N) ring[g % LEAD] = tr_frag<ROW_B>(kt, tr, (g + LEAD) / NDB, (g + LEAD) % NDB);
+        dqa[g % NDB] = mfma32(f, dsf[g / NDB], dqa[g % NDB]);
+        if (g < NP) ds(1, 16 * g / NP, 16 * (g + 1) / NP);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -410,7 +436,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int BNK = kBwdBlockN, BM = kBwdTileM;
   static_assert(BNK == 128 && BM == 64, "four 32-key waves, 64-query tiles");
   constexpr int TILE_B = BM * ROW_B;
-  // per buffer: Q tile, dO tile, then the tile's 64 LSE and 64 dPsum values
+  // per buffer: Q tile, dO tile, then the tile's 64 LSE log2 e and 64 dPsum values
   constexpr int BUF_B = 2 * TILE_B + 2 * 256;
   __shared__ __attribute__((aligned(16))) char smem[2 * BUF_B];
 
@@ -532,7 +558,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     if (wave < 2) {  // wave-uniform
       const int64_t li = a.cu_q != nullptr ? (int64_t)h * a.total_q + q_tok0 + m0
                                            : ((int64_t)b * a.hq + h) * sq + m0;
-      const auto sr = make_rsrc(wave == 0 ? a.lse + li : a.dpsum + li, (uint32_t)(nrows * 4));
+      const auto sr =
+          make_rsrc(wave == 0 ? a.lse_log2 + li : a.dpsum + li, (uint32_t)(nrows * 4));
       dma4(sr, (uint32_t)(4 * lane), lds_s + (uint32_t)(buf * BUF_B));
     }
   };
@@ -553,7 +580,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   //           the first NP MFMAs; then dV, dK of block 1
   auto compute = [&](int m0, const char* qt) __attribute__((always_inline)) {
     const char* gt = qt + TILE_B;
-    const float* l2s = reinterpret_cast<const float*>(qt + 2 * TILE_B);  // raw LSE
+    const float* l2s = reinterpret_cast<const float*>(qt + 2 * TILE_B);  // LSE log2 e
     const float* dss = l2s + BM;
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -569,13 +596,10 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int qo = 32 * qb + 8 * i + 4 * half;
-        const f32x4 l = *reinterpret_cast<const f32x4*>(l2s + qo);
+        // LSE log2 e (+inf for a row with no visible key, so P = 0; rows
+        // past the sequence read 0 and are masked)
+        l4[qb][i] = *reinterpret_cast<const f32x4*>(l2s + qo);
         d4[qb][i] = *reinterpret_cast<const f32x4*>(dss + qo);
-        // LSE*log2e; a row with no visible key (LSE = -inf) gets +inf, so
-        // P = 0 (rows past the sequence read 0 and are masked)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          l4[qb][i][j] = l[j] == kNegInf ? __builtin_huge_valf() : l[j] * kLog2e;
       }
     // softmax elements [e0, e1) of block qb: P, then dS in place of dP
     auto sm = [&](int qb, int e0, int e1) __attribute__((always_inline)) {
@@ -719,7 +743,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 // that split the four products without repeating any:
 //   wave A (even): S = Q K^T, P = exp2(S c - LSE log2e), dV^T += dO^T P
 //   wave B (odd):  dP = dO V^T, dS = P (dP - dPsum), dK^T += Q^T dS
-// A hands P (float32) to B through LDS between the two phases of a step.
+// A hands P of the first 32 queries and the raw scores of the other 32
+// (float32) to B through LDS; B recomputes P of the latter.
 // Each wave holds one key fragment set (K or V, 64 registers) and one
 // accumulator (128). One workgroup = two pairs = 64 keys; the Q / dO tile
 // staging, the split of the walk and the XCD-aware order are those of
@@ -731,7 +756,7 @@ void bwd_dkdv_pair_kernel(const BwdArgs a) {
   constexpr int BNK = kBwdBlockNPair, BM = kBwdTileM;
   static_assert(BNK == 64 && BM == 64, "two 32-key wave pairs, 64-query tiles");
   constexpr int TILE_B = BM * ROW_B;
-  // per buffer: Q tile, dO tile, then the tile's 64 LSE and 64 dPsum values
+  // per buffer: Q tile, dO tile, then the tile's 64 LSE log2 e and 64 dPsum values
   constexpr int BUF_B = 2 * TILE_B + 2 * 256;
   constexpr int PX_B = 64 * 32 * 4;  // one pair's P: 32 floats per lane
   __shared__ __attribute__((aligned(16))) char smem[2 * BUF_B + 2 * PX_B];
@@ -849,7 +874,8 @@ void bwd_dkdv_pair_kernel(const BwdArgs a) {
     if (wave < 2) {  // wave-uniform
       const int64_t li = a.cu_q != nullptr ? (int64_t)h * a.total_q + q_tok0 + m0
                                            : ((int64_t)b * a.hq + h) * sq + m0;
-      const auto sr = make_rsrc(wave == 0 ? a.lse + li : a.dpsum + li, (uint32_t)(nrows * 4));
+      const auto sr =
+          make_rsrc(wave == 0 ? a.lse_log2 + li : a.dpsum + li, (uint32_t)(nrows * 4));
       dma4(sr, (uint32_t)(4 * lane), lds_s + (uint32_t)(buf * BUF_B));
     }
   };
@@ -862,7 +888,7 @@ void bwd_dkdv_pair_kernel(const BwdArgs a) {
   // this pair's P exchange: chunk i (4 floats) of lane l at 1024 i + 16 l
   char* px = smem + 2 * BUF_B + pair * PX_B + 16 * lane;
 
-  // phase 1: the S (A) or dP (B) products of both 32-query blocks, reading
+  // the S (A) or dP (B) products of both 32-query blocks, reading
   // Q (A) or dO (B) rows; MFMA g: block g / NK, contraction step g % NK
   auto rows_products = [&](const char* t, f32x16 x[2], auto&& between)
       __attribute__((always_inline)) {
@@ -883,101 +909,142 @@ void bwd_dkdv_pair_kernel(const BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // phase 2: acc^T += T^T F over the 64 queries, T read by transposing
-  // reads; MFMA g: 16-query step g / NDB, d-block g % NDB
-  auto trans_products = [&](const char* t, bf16x8 fr[4], auto&& between)
+  // acc^T += T^T F over the 32 queries of block qb, T read by transposing
+  // reads; MFMA g: 16-query step 2 qb + g / NDB, d-block g % NDB
+  auto trans_products = [&](const char* t, int qb, const bf16x8 fr[2], auto&& between)
       __attribute__((always_inline)) {
-    constexpr int NDB = D / 32, N = 4 * NDB, LEAD = 4;
+    constexpr int NDB = D / 32, N = 2 * NDB, LEAD = 4;
     bf16x8 ring[LEAD];
 #pragma unroll
-    for (int g = 0; g < LEAD; ++g) ring[g] = tr_frag<ROW_B>(t, tr, g / NDB, g % NDB);
+    for (int g = 0; g < LEAD; ++g) ring[g] = tr_frag<ROW_B>(t, tr, 2 * qb + g / NDB, g % NDB);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < N; ++g) {
-      between(g);
       const bf16x8 f = ring[g % LEAD];
-      if (g + LEAD < N) ring[g % LEAD] = tr_frag<ROW_B>(t, tr, (g + LEAD) / NDB, (g + LEAD) % NDB);
+      if (g + LEAD < N)
+        ring[g % LEAD] = tr_frag<ROW_B>(t, tr, 2 * qb + (g + LEAD) / NDB, (g + LEAD) % NDB);
       acc[g % NDB] = mfma32(f, fr[g / NDB], acc[g % NDB]);
+      between(g);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto to_frags = [&](const f32x16& x, bf16x8& f0, bf16x8& f1) __attribute__((always_inline)) {
-    f0 = cat(cvt4(x[0], x[1], x[2], x[3]), cvt4(x[4], x[5], x[6], x[7]));
-    f1 = cat(cvt4(x[8], x[9], x[10], x[11]), cvt4(x[12], x[13], x[14], x[15]));
+  auto to_frags = [&](const f32x16& x, bf16x8 f[2]) __attribute__((always_inline)) {
+    f[0] = cat(cvt4(x[0], x[1], x[2], x[3]), cvt4(x[4], x[5], x[6], x[7]));
+    f[1] = cat(cvt4(x[8], x[9], x[10], x[11]), cvt4(x[12], x[13], x[14], x[15]));
   };
 
-  // element (qb, v) of a score accumulator holds query
-  // m0 + 4*half + 32*qb + 8*(v>>2) + (v&3), key `key`
+  // One step over a 64-query tile, in two parts around a workgroup barrier
+  // (the pairs run the same schedule):
+  //   A: S of blocks 0, 1, block 0's P between block 1's MFMAs; out: P of
+  //      block 0 and the raw scores of block 1
+  //   B: dP of blocks 0, 1
+  //   -- barrier
+  //   A: dV from block 0 with block 1's P between its MFMAs, dV from block 1
+  //   B: dS of block 0 (its second half between the first MFMAs), dK from
+  //      block 0 with block 1's P and dS between its MFMAs, dK from block 1
+  // B recomputing block 1's P keeps the exponentials off the part before
+  // the barrier, which the MFMAs of both waves then fill evenly.
+  // Element (qb, v) of a score accumulator holds query
+  // m0 + 4*half + 32*qb + 8*(v>>2) + (v&3), key `key`. A tile that every
+  // lane sees whole (most of a causal walk) skips the mask; both waves of a
+  // pair hold the same keys and so take the same branch.
   auto step = [&](int m0, const char* qt) __attribute__((always_inline)) {
     const char* gt = qt + TILE_B;
-    const float* lses = reinterpret_cast<const float*>(qt + 2 * TILE_B);  // raw LSE
+    const float* lses = reinterpret_cast<const float*>(qt + 2 * TILE_B);  // LSE log2 e
     const float* dss = lses + BM;
+    constexpr int NK = D / 16, NDB = D / 32;
     f32x16 x[2];
     x[0] = zero_f32x16();
     x[1] = zero_f32x16();
-    bf16x8 fr[4];
-    if (role == 0) {
-      const uint64_t vis = vis64(qlo - m0 - 4 * half, qhi - m0 - 4 * half);
-      f32x4 l4[2][4];
+    bf16x8 fr[2][2];
+    const uint64_t vis = vis64(qlo - m0 - 4 * half, qhi - m0 - 4 * half);
+    // +inf for a row with no visible key, so P = 0; rows past the sequence
+    // read 0 and are masked
+    auto lse4 = [&](int qb, int i) __attribute__((always_inline)) {
+      return *reinterpret_cast<const f32x4*>(lses + 32 * qb + 8 * i + 4 * half);
+    };
+    auto path = [&](auto wm) __attribute__((always_inline)) {
+      // P of score s, element v of block qb
+      auto prob = [&](float sv, int qb, int v, float l) __attribute__((always_inline)) {
+        if constexpr (decltype(wm)::value)
+          sv = mask_by_bit(sv, (uint32_t)(vis >> (32 * qb)), 8 * (v >> 2) + (v & 3));
+        return fast_exp2(fmaf(sv, c, -l));
+      };
+      if (role == 0) {
+        f32x4 l4[2][4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) l4[qb][i] = lse4(qb, i);
+        auto sm = [&](int qb, int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+          for (int v = e0; v < e1; ++v) x[qb][v] = prob(x[qb][v], qb, v, l4[qb][v >> 2][v & 3]);
+        };
+        rows_products(qt, x, [&](int g) __attribute__((always_inline)) {
+          if (g >= NK) sm(0, 16 * (g - NK) / NK, 16 * (g - NK + 1) / NK);
+        });
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const f32x16& xs = x[i >> 2];
+          *reinterpret_cast<f32x4*>(px + 1024 * i) =
+              f32x4{xs[4 * (i & 3)], xs[4 * (i & 3) + 1], xs[4 * (i & 3) + 2], xs[4 * (i & 3) + 3]};
+        }
+        to_frags(x[0], fr[0]);
+        lds_barrier();  // P0 and S1 are in LDS
+        trans_products(gt, 0, fr[0], [&](int g) __attribute__((always_inline)) {
+          sm(1, 16 * g / (2 * NDB), 16 * (g + 1) / (2 * NDB));
+        });
+        to_frags(x[1], fr[1]);
+        trans_products(gt, 1, fr[1], [](int) __attribute__((always_inline)) {});
+      } else {
+        f32x4 d4[2][4], l4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x4 l = *reinterpret_cast<const f32x4*>(lses + 32 * qb + 8 * i + 4 * half);
-          // LSE*log2e; a row with no visible key (LSE = -inf) gets +inf, so
-          // P = 0 (rows past the sequence read 0 and are masked)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            l4[qb][i][j] = l[j] == kNegInf ? __builtin_huge_valf() : l[j] * kLog2e;
+          d4[0][i] = *reinterpret_cast<const f32x4*>(dss + 8 * i + 4 * half);
+          d4[1][i] = *reinterpret_cast<const f32x4*>(dss + 32 + 8 * i + 4 * half);
+          l4[i] = lse4(1, i);
         }
-      // P of block qb, elements [e0, e1)
-      auto sm = [&](int qb, int e0, int e1) __attribute__((always_inline)) {
-        const uint32_t w = (uint32_t)(vis >> (32 * qb));
+        rows_products(gt, x, [](int) __attribute__((always_inline)) {});
+        lds_barrier();  // P0 and S1 are in LDS
+        f32x4 pv[4], sv[4];
 #pragma unroll
-        for (int v = e0; v < e1; ++v) {
-          const float xm = mask_by_bit(x[qb][v], w, 8 * (v >> 2) + (v & 3));
-          x[qb][v] = fast_exp2(fmaf(xm, c, -l4[qb][v >> 2][v & 3]));
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = *reinterpret_cast<const f32x4*>(px + 1024 * i);
+          sv[i] = *reinterpret_cast<const f32x4*>(px + 1024 * (4 + i));
         }
-      };
-      constexpr int NK = D / 16;
-      // block 0's P between block 1's MFMAs
-      rows_products(qt, x, [&](int g) __attribute__((always_inline)) {
-        if (g >= NK) sm(0, 16 * (g - NK) / NK, 16 * (g - NK + 1) / NK);
-      });
-      sm(1, 0, 16);
+        // dS = P (dP - dPsum), in place of dP
+        auto ds0 = [&](int e0, int e1) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const f32x16& xs = x[i >> 2];
-        *reinterpret_cast<f32x4*>(px + 1024 * i) =
-            f32x4{xs[4 * (i & 3)], xs[4 * (i & 3) + 1], xs[4 * (i & 3) + 2], xs[4 * (i & 3) + 3]};
+          for (int v = e0; v < e1; ++v)
+            x[0][v] = pv[v >> 2][v & 3] * (x[0][v] - d4[0][v >> 2][v & 3]);
+        };
+        auto ds1 = [&](int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+          for (int v = e0; v < e1; ++v)
+            x[1][v] = prob(sv[v >> 2][v & 3], 1, v, l4[v >> 2][v & 3]) *
+                      (x[1][v] - d4[1][v >> 2][v & 3]);
+        };
+        ds0(0, 8);
+        fr[0][0] = cat(cvt4(x[0][0], x[0][1], x[0][2], x[0][3]),
+                       cvt4(x[0][4], x[0][5], x[0][6], x[0][7]));
+        trans_products(qt, 0, fr[0], [&](int g) __attribute__((always_inline)) {
+          if (g < NDB) {
+            ds0(8 + 8 * g / NDB, 8 + 8 * (g + 1) / NDB);
+            if (g == NDB - 1)
+              fr[0][1] = cat(cvt4(x[0][8], x[0][9], x[0][10], x[0][11]),
+                             cvt4(x[0][12], x[0][13], x[0][14], x[0][15]));
+          } else {
+            ds1(16 * (g - NDB) / NDB, 16 * (g - NDB + 1) / NDB);
+          }
+        });
+        to_frags(x[1], fr[1]);
+        trans_products(qt, 1, fr[1], [](int) __attribute__((always_inline)) {});
       }
-      to_frags(x[0], fr[0], fr[1]);
-      to_frags(x[1], fr[2], fr[3]);
-    } else {
-      rows_products(gt, x, [](int) __attribute__((always_inline)) {});
-    }
-    lds_barrier();  // A's P is in LDS
-    if (role == 0) {
-      trans_products(gt, fr, [](int) __attribute__((always_inline)) {});  // dV^T += dO^T P
-    } else {
-      // dS = P (dP - dPsum) of block qb, into x[qb], then its fragments
-      auto ds = [&](int qb) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 p = *reinterpret_cast<const f32x4*>(px + 1024 * (4 * qb + i));
-          const f32x4 d = *reinterpret_cast<const f32x4*>(dss + 32 * qb + 8 * i + 4 * half);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) x[qb][4 * i + j] = p[j] * (x[qb][4 * i + j] - d[j]);
-        }
-        to_frags(x[qb], fr[2 * qb], fr[2 * qb + 1]);
-      };
-      ds(0);
-      constexpr int NDB = D / 32;
-      // dK^T += Q^T dS; block 1's dS before its first MFMA
-      trans_products(qt, fr, [&](int g) __attribute__((always_inline)) {
-        if (g == 2 * NDB) ds(1);
-      });
-    }
+    };
+    if (__builtin_amdgcn_ballot_w64(vis != ~0ull) != 0)
+      path(std::true_type{});
+    else
+      path(std::false_type{});
   };
 
   if (it_end > it_begin) {

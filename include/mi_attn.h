@@ -323,11 +323,12 @@ int mi_attn_combine(const float *o_partial, const float *lse_partial, void *out,
  * cu_seqlens_k are given together or not at all. Paged K/V and the
  * learnable sink are not part of the backward.
  *
- * head_dim 64 or 128 (256 returns MI_ATTN_EUNSUPPORTED). The result is
- * deterministic: nothing is accumulated with atomics. The caller owns every
- * buffer, including the workspace (size from mi_attn_bwd_workspace_bytes; a
- * smaller one returns MI_ATTN_EWORKSPACE): float32 row sums of out * dout,
- * one per query row and head, then, when few key blocks would leave the
+ * head_dim 64, 128 or 256 (others return MI_ATTN_EUNSUPPORTED). The result
+ * is deterministic: nothing is accumulated with atomics. The caller owns
+ * every buffer, including the workspace (size from
+ * mi_attn_bwd_workspace_bytes; a smaller one returns MI_ATTN_EWORKSPACE):
+ * float32 row sums of out * dout and the LSE in base 2 (LSE * log2 e), one
+ * each per query row and head, then, when few key blocks would leave the
  * device idle, float32 dk / dv partials of up to four parts of each key
  * block's walk over the queries, summed in a fixed order. Work is enqueued on `stream`; nothing is
  * allocated and the stream is not synchronised.

@@ -244,7 +244,7 @@ def _bwd(**kw):
 
 
 def _bwd_ws(batch, hq, hkv, d, rows_q, max_k):
-    """One float32 row sum per (query row, head), then float32 dK and dV
+    """One float32 row sum and one base-2 LSE per (query row, head), then float32 dK and dV
     partials of each split of the dK/dV walk (splits: about 512 workgroups of
     128 keys, 64 at head_dim 256, at most 4), each part 256-byte rounded."""
     rnd = lambda x: -(-x // 256) * 256
@@ -252,7 +252,7 @@ def _bwd_ws(batch, hq, hkv, d, rows_q, max_k):
     wg = -(-max_k // bn) * hkv * batch
     splits = max(1, min(4, -(-512 // wg)))
     parts = splits * batch * max_k * hkv * 2 * d if splits > 1 else 0
-    return rnd(rows_q * hq * 4) + rnd(parts * 4)
+    return 2 * rnd(rows_q * hq * 4) + rnd(parts * 4)
 
 
 def test_bwd_workspace_size(lib):
@@ -262,7 +262,7 @@ def test_bwd_workspace_size(lib):
     # enough key blocks: one split, no partials
     p = _bwd(batch=64, seqlen_q=1024, seqlen_k=1024)
     assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(p)) == _bwd_ws(64, 8, 2, 128, 64 * 1024, 1024)
-    assert _bwd_ws(64, 8, 2, 128, 64 * 1024, 1024) == 64 * 1024 * 8 * 4
+    assert _bwd_ws(64, 8, 2, 128, 64 * 1024, 1024) == 2 * 64 * 1024 * 8 * 4
     for kw in (dict(), dict(seqlen_q=4096, seqlen_k=4096)):  # split, then one split
         p = _bwd(head_dim=256, **kw)
         S = kw.get("seqlen_q", 1000)
