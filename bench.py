@@ -17,12 +17,15 @@ launch (causal pairs only) over the launch's duration, measured with HIP events
 recorded on the launch stream around every launch of the timed steps. Every
 workload has its own entry under "workloads" (average launch time, throughput,
 roofline fraction, HBM counter traffic); the decode's K/V bytes per second is
-also under "decode". Progress goes to stderr.
+also under "decode". Outside the step, "backward" holds the same figures for
+the backward of C2 and C3 (one mi_attn_bwd call: all its launches). Progress
+goes to stderr.
 
 Flags: --gpus N (only 1 is supported: the path is single-GPU), --steps K,
 --warmup W, --warmup-gpu-ms T, --no-cpu-baseline, --cpu-seconds S (oracle
-sample budget), --all-configs (also time further workloads: head dims 96/192,
-paged prefill, softcap, backward, fp8 decode), --zero-inputs (prefill workloads
+sample budget), --no-backward (skip the backward entries), --all-configs (also
+time further workloads: head dims 96/192, paged prefill, softcap, a multi-token
+decode step, fp8 decode), --zero-inputs (prefill workloads
 on all-zero inputs; a clock measurement, never the reported value's data).
 
 Warm-up: W untimed steps, then more untimed steps until at least T ms (default
@@ -58,6 +61,15 @@ KERNEL_SOURCES = {
     "decode_stream_kernel<128>": ["decode_stream_kernel.hip", "attn_common.hpp", "kernels.hpp"],
     "combine_kernel<128>": ["decode_kernel.hip", "attn_common.hpp", "kernels.hpp"],
 }
+for _d in (128, 256):
+    for _k in ("bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_dkdv_pair_kernel",
+               "bwd_dkv_reduce_kernel"):
+        KERNEL_SOURCES[f"{_k}<{_d}>"] = ["bwd_kernel.hip", "bwd.hpp", "attn_common.hpp"]
+# the backward's launches per call, by head dim (the reduce runs when the dK/dV
+# walk is split, which the two measured workloads' shapes decide)
+BWD_KERNELS = {128: ["bwd_pre_kernel<128>", "bwd_dq_kernel<128>", "bwd_dkdv_kernel<128>",
+                     "bwd_dkv_reduce_kernel<128>"],
+               256: ["bwd_pre_kernel<256>", "bwd_dq_kernel<256>", "bwd_dkdv_pair_kernel<256>"]}
 
 
 def source_digest(kernel: str) -> str:
@@ -115,6 +127,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--zero-inputs", action="store_true",
                     help="prefill workloads on all-zero Q/K/V (the same kernels and cycle "
                          "counts; the matrix cores then draw less power and the core clock "
@@ -267,18 +280,23 @@ def varlen_decode_bytes(w) -> int:
 
 class Backward:
     """mi_attn_bwd on a dense workload: the forward's out and LSE are made
-    once, outside the timed calls; each call runs the three backward
-    launches (row sums of O dO, dQ, dK/dV)."""
+    once, outside the timed calls; each call runs the backward's launches
+    (row sums of O dO and LSE log2 e, dQ, dK/dV, and the reduce of split dK/dV
+    partials). `dev` reuses the device q, k, v of a Prefill of the same
+    workload."""
 
-    def __init__(self, mi, w, torch):
+    def __init__(self, mi, w, torch, dev=None):
         import workloads as W
         from tests.gpu_util import dev_bf16
         self.mi, self.w = mi, w
-        self.q, self.k, self.v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+        if dev is not None:
+            self.q, self.k, self.v = dev.q, dev.k, dev.v
+        else:
+            self.q, self.k, self.v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
         self.kw = dict(softmax_scale=w.softmax_scale, causal=w.causal,
                        window_left=w.window_left, window_right=w.window_right)
         self.out, self.lse = mi.mi_attn_fwd(self.q, self.k, self.v, **self.kw)
-        self.g = dev_bf16(W.grad_output(w.seed, w.q.shape))
+        self.g = dev_bf16(W.grad_output(w.seed, tuple(self.q.shape)))
         self.dq, self.dk, self.dv = (torch.empty_like(self.q), torch.empty_like(self.k),
                                      torch.empty_like(self.v))
         nb = mi.mi_attn_bwd_workspace_bytes(self.q, self.k, self.v, self.out, self.g, self.lse)
@@ -382,9 +400,35 @@ def timed_extra(torch, fn, n):
     return ms[len(ms) // 2]
 
 
+def backward_workloads(mi, W, torch, args, runs, ws):
+    """The backward of the causal GQA S4096 D128 and S16384 D256 prefill
+    workloads (median of event-timed calls after a GPU-time warm-up). The
+    algorithmic flops are 2.5x the forward's: five tile products per score
+    tile (S, dP, dV, dK, dQ) against two."""
+    res = {}
+    n = max(5, args.steps // 2)
+    for i in (2, 3):
+        w = ws[i]
+        bw = Backward(mi, w, torch, dev=runs[i])
+        med = timed_extra(torch, bw, n)
+        f = 2.5 * prefill_flops(w)
+        tf = f / (med * 1e-3) / 1e12
+        d = w.head_dim
+        res[w.name] = {"label": f"backward of {w.name}", "kernel": " + ".join(BWD_KERNELS[d]),
+                       "avg_call_us": round(med * 1e3, 2), "bound": "mfma",
+                       "achieved": round(tf, 2), "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
+                       "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": f,
+                       "traffic": counter_traffic("backward_" + w.name, *BWD_KERNELS[d])}
+        log(f"[bench] backward {w.name}: {med * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+        del bw
+        torch.cuda.empty_cache()
+    return res
+
+
 def extra_workloads(mi, W, torch, args, extra):
-    """--all-configs: head dims 96/192, paged prefill, softcap, backward and
-    fp8 decode (median of event-timed launches, stderr and "other_workloads")."""
+    """--all-configs: head dims 96/192, paged prefill, softcap, the multi-token
+    decode step and fp8 decode (median of event-timed launches, stderr and
+    "other_workloads")."""
     n = max(5, args.steps)
     paged = W.paged_prefill_case(1002, 1, 32, 4, 128, 256, 16, None, seqlen_q=4096,
                                  causal=True, name="paged256_causal_gqa32x4_s4096_d128")
@@ -411,18 +455,6 @@ def extra_workloads(mi, W, torch, args, extra):
     log(f"[bench] {name}: {med * 1e3:.1f} us, {extra[name]['tflops']:.1f} TFLOP/s")
     del pc
     torch.cuda.empty_cache()
-    # backward; algorithmic flops 2.5x the forward's (five tile products per
-    # score tile against two)
-    for wb in (W.standard_config(2), W.standard_config(3)):
-        bw = Backward(mi, wb, torch)
-        med = timed_extra(torch, bw, n)
-        f = 2.5 * prefill_flops(wb)
-        name = "backward_" + wb.name
-        extra[name] = {"median_us": med * 1e3, "tflops": f / (med * 1e-3) / 1e12,
-                       "frac": f / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-        log(f"[bench] {name}: {med * 1e3:.1f} us, {extra[name]['tflops']:.1f} TFLOP/s")
-        del bw
-        torch.cuda.empty_cache()
     # speculative decoding step: the paged decode workload's cache with 4
     # causal query tokens per sequence
     wv = W.paged_prefill_case(1005, 16, 32, 4, 128, 256, 128, [32768] * 16, seqlens_q=[4] * 16,
@@ -534,6 +566,8 @@ def main():
         rec["traffic"] = counter_traffic(ws[i].name, *kernels)
         per[ws[i].name] = rec
 
+    bwd = None if args.no_backward else backward_workloads(mi, W, torch, args, runs, ws)
+
     extra = {}
     if args.all_configs:
         del runs
@@ -584,6 +618,8 @@ def main():
         },
         "workloads": per,
     }
+    if bwd is not None:
+        rec["backward"] = bwd
     if extra:
         rec["other_workloads"] = extra
     print(json.dumps(rec), flush=True)
