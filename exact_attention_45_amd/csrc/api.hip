@@ -32,10 +32,9 @@ int ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool stride_ok(int64_t s) { return s >= 0 && (s % 8) == 0; }
-bool dim_supported(int d) { return d == 64 || d == 128 || d == 256; }
-// The prefill forward also takes head dims 96 and 192 (in the LDS layouts of
-// 128 and 256).
-bool fwd_dim_supported(int d) { return dim_supported(d) || d == 96 || d == 192; }
+// Head dims of the forward, the decode and the combine (96 and 192 run in the
+// LDS layouts of 128 and 256).
+bool dim_supported(int d) { return d == 64 || d == 96 || d == 128 || d == 192 || d == 256; }
 
 // Mask normalisation (interface page, `_flash_attn_fwd`): causal forces a
 // right window of 0; negative sizes are unbounded.
@@ -108,7 +107,8 @@ int check_decode(const mi_attn_decode_params* p) {
     return fail(MI_ATTN_EINVAL, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
                 p->num_heads_q, p->num_heads_kv);
   if (!dim_supported(p->head_dim))
-    return fail(MI_ATTN_EUNSUPPORTED, "head_dim %d not supported (64, 128, 256)", p->head_dim);
+    return fail(MI_ATTN_EUNSUPPORTED, "head_dim %d not supported (64, 96, 128, 192, 256)",
+                p->head_dim);
   if (p->page_size <= 0 || p->num_pages <= 0 || p->max_pages_per_seq <= 0)
     return fail(MI_ATTN_EINVAL, "page_size, num_pages and max_pages_per_seq must be > 0");
   if ((int64_t)p->max_pages_per_seq * p->page_size > INT32_MAX)
@@ -162,7 +162,7 @@ size_t workspace_for(const mi_attn_decode_params* p, int splits) {
 }
 
 template <class F>
-hipError_t by_fwd_dim(int d, F&& f) {
+hipError_t by_dim(int d, F&& f) {
   switch (d) {
     case 64: return f(std::integral_constant<int, 64>{});
     case 96: return f(std::integral_constant<int, 96>{});
@@ -172,14 +172,6 @@ hipError_t by_fwd_dim(int d, F&& f) {
   }
 }
 
-template <class F>
-hipError_t by_dim(int d, F&& f) {
-  switch (d) {
-    case 64: return f(std::integral_constant<int, 64>{});
-    case 128: return f(std::integral_constant<int, 128>{});
-    default: return f(std::integral_constant<int, 256>{});
-  }
-}
 
 }  // namespace
 
@@ -213,7 +205,7 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
   if (p->num_heads_q % p->num_heads_kv != 0)
     return fail(MI_ATTN_EINVAL, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
                 p->num_heads_q, p->num_heads_kv);
-  if (!fwd_dim_supported(p->head_dim))
+  if (!dim_supported(p->head_dim))
     return fail(MI_ATTN_EUNSUPPORTED, "head_dim %d not supported (64, 96, 128, 192, 256)",
                 p->head_dim);
   if (!isfinite(p->softmax_scale) || p->softmax_scale < 0.0f)
@@ -311,7 +303,7 @@ int mi_attn_fwd(const mi_attn_fwd_params* p, void* stream) {
     return fail(MI_ATTN_EINVAL, "launch grid too large");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = by_fwd_dim(p->head_dim, [&](auto dc) {
+  hipError_t e = by_dim(p->head_dim, [&](auto dc) {
     return mi_attn::launch_fwd<decltype(dc)::value>(a, s);
   });
   if (e != hipSuccess) return fail(MI_ATTN_EHIP, "launch failed: %s", hipGetErrorString(e));
@@ -478,7 +470,8 @@ int mi_attn_combine(const float* o_partial, const float* lse_partial, void* out,
   if (num_splits < 1 || num_splits > 256)
     return fail(MI_ATTN_EINVAL, "num_splits must be in 1..256 (got %d)", num_splits);
   if (!dim_supported(head_dim))
-    return fail(MI_ATTN_EUNSUPPORTED, "head_dim %d not supported (64, 128, 256)", head_dim);
+    return fail(MI_ATTN_EUNSUPPORTED, "head_dim %d not supported (64, 96, 128, 192, 256)",
+                head_dim);
   if (rows == 0) return ok();
   if (!o_partial || !lse_partial || !out)
     return fail(MI_ATTN_EINVAL, "o_partial, lse_partial and out must be non-NULL");

@@ -48,9 +48,21 @@ __device__ __forceinline__ int dswz(int key, int c) {
   return D >= 128 ? (c ^ ((key & 7) << 1)) : (c ^ ((key & 3) << 1));
 }
 
+// Head dims 96 and 192 run at the next power-of-two width DP (128, 256):
+// the LDS tiles, fragments and accumulators have DP columns, the chunks
+// past D are zero (never loaded: their lanes re-read chunk 0 of the row,
+// a line the same instruction fetches anyway, and drop it), so the scores
+// and the first D output columns are those of width D; only those are
+// stored.
+template <int D>
+constexpr int dec_width() {
+  return D == 96 ? 128 : (D == 192 ? 256 : D);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
-  using C = DecCfg<D>;
+  constexpr int DP = dec_width<D>();
+  using C = DecCfg<DP>;
   constexpr int BN = C::BN, CPR = C::CPR, NCH = C::NCH, TILE = C::TILE;
   constexpr int NBUF = C::NBUF, NSET = C::NSET;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
@@ -101,16 +113,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   const __bf16* qp = static_cast<const __bf16*>(a.q) + row.token * a.q_bs + (int64_t)row.hq * a.q_hs;
   // branch-free: invalid lanes read head 0's row and zero it afterwards (a
   // load under a divergent branch makes every later wait drain all loads)
-  bf16x8 qf[D / 16];
+  bf16x8 qf[DP / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    const bf16x8 x = as_bf16x8(ld16(qp + 16 * c + 8 * half));
-    qf[c] = valid ? x : zero_bf16x8();
+  for (int c = 0; c < DP / 16; ++c) {
+    const int e0 = 16 * c + 8 * half;  // columns past D (padding) are zero
+    const bf16x8 x = as_bf16x8(ld16(qp + (e0 < D ? e0 : 0)));
+    qf[c] = valid && e0 < D ? x : zero_bf16x8();
   }
 
-  f32x16 o[D / 32];
+  f32x16 o[DP / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) o[i] = zero_f32x16();
+  for (int i = 0; i < DP / 32; ++i) o[i] = zero_f32x16();
   float m_run = kNegInf;
   float l_run = 0.0f;
 
@@ -120,6 +133,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
   const int ld_c = lane % CPR;
   const int ld_r = lane / CPR;
+  const bool ld_in = ld_c < D / 8;  // a chunk of the row (not padding)
+  const int ld_off = (ld_in ? ld_c : 0) * 8;
 
   // Register prefetch sets. Page ids of tile t+1 are requested before the
   // K/V loads of tile t: load counters retire in issue order, so a page id
@@ -155,9 +170,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
       bad_page |= !ok;
       const int page = ok ? pid[slot][u] : 0;
       const int64_t off =
-          ((int64_t)page * a.page_size + key % a.page_size) * tok_stride + ld_c * 8;
-      kreg[set][u] = ld16_nt(kc + off);  // the cache is read once per step
-      vreg[set][u] = ld16_nt(vc + off);
+          ((int64_t)page * a.page_size + key % a.page_size) * tok_stride + ld_off;
+      const uint4 kx = ld16_nt(kc + off);  // the cache is read once per step
+      const uint4 vx = ld16_nt(vc + off);
+      kreg[set][u] = ld_in ? kx : make_uint4(0u, 0u, 0u, 0u);
+      vreg[set][u] = ld_in ? vx : make_uint4(0u, 0u, 0u, 0u);
     }
   };
   auto store_tile = [&](auto set_c, int buf) {
@@ -167,7 +184,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int row = tile_row(u);
-      const int p = row * D + dswz<D>(row, ld_c) * 8;
+      const int p = row * DP + dswz<DP>(row, ld_c) * 8;
       *reinterpret_cast<uint4*>(&sK[p]) = kreg[set][u];
       *reinterpret_cast<uint4*>(&sV[p]) = vreg[set][u];
     }
@@ -223,10 +240,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     f32x16 s = zero_f32x16();
     {
       const int key = wave * 32 + c32;
-      const __bf16* krow = sK + key * D;
+      const __bf16* krow = sK + key * DP;
 #pragma unroll
-      for (int cc = 0; cc < D / 16; ++cc)
-        s = mfma32(*reinterpret_cast<const bf16x8*>(krow + dswz<D>(key, 2 * cc + half) * 8),
+      for (int cc = 0; cc < DP / 16; ++cc)
+        s = mfma32(*reinterpret_cast<const bf16x8*>(krow + dswz<DP>(key, 2 * cc + half) * 8),
                    qf[cc], s);
     }
     if (a.softcap > 0.0f) {  // uniform
@@ -260,7 +277,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     l_run = l_run * alpha + rs;
     m_run = m_new;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DP / 32; ++db)
 #pragma unroll
       for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
 
@@ -272,14 +289,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
                    cvt4(s[4 * i0 + 4], s[4 * i0 + 5], s[4 * i0 + 6], s[4 * i0 + 7]));
     }
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < DP / 32; ++db) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int k0 = wave * 32 + 16 * tt + 4 * half + tr_key;
         const int k1 = k0 + 8;
         const int cc = 4 * db + tr_c;
-        const bf16x4 v0 = ds_read_tr16(sV + k0 * D + dswz<D>(k0, cc) * 8 + tr_e);
-        const bf16x4 v1 = ds_read_tr16(sV + k1 * D + dswz<D>(k1, cc) * 8 + tr_e);
+        const bf16x4 v0 = ds_read_tr16(sV + k0 * DP + dswz<DP>(k0, cc) * 8 + tr_e);
+        const bf16x4 v1 = ds_read_tr16(sV + k1 * DP + dswz<DP>(k1, cc) * 8 + tr_e);
         o[db] = mfma32(cat(v0, v1), pf[tt], o[db]);
       }
     }
@@ -304,14 +321,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   const float l_wave = pair_sum(l_run);
   const int any_bad = __syncthreads_or(bad_page ? 1 : 0);
   float* sO = reinterpret_cast<float*>(smem);          // [wave][d][32]
-  float* sM = sO + 4 * D * 32;                          // [wave][32]
+  float* sM = sO + 4 * DP * 32;                         // [wave][32]
   float* sL = sM + 4 * 32;                              // [wave][32]
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < DP / 32; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int d = db * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-      sO[(wave * D + d) * 32 + c32] = o[db][v];
+      sO[(wave * DP + d) * 32 + c32] = o[db][v];
     }
   if (half == 0) {
     sM[wave * 32 + c32] = m_run;
@@ -347,10 +364,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const int d = dpart * DPT + j;
-        acc.x += wgt[w] * sO[(w * D + d + 0) * 32 + qcol];
-        acc.y += wgt[w] * sO[(w * D + d + 1) * 32 + qcol];
-        acc.z += wgt[w] * sO[(w * D + d + 2) * 32 + qcol];
-        acc.w += wgt[w] * sO[(w * D + d + 3) * 32 + qcol];
+        acc.x += wgt[w] * sO[(w * DP + d + 0) * 32 + qcol];
+        acc.y += wgt[w] * sO[(w * DP + d + 1) * 32 + qcol];
+        acc.z += wgt[w] * sO[(w * DP + d + 2) * 32 + qcol];
+        acc.w += wgt[w] * sO[(w * DP + d + 3) * 32 + qcol];
       }
       *reinterpret_cast<float4*>(op + j) =
           any_bad ? make_float4(nan, nan, nan, nan)
@@ -371,7 +388,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 // clamped loads of a ragged last chunk add nothing).
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(const CombineArgs a) {
-  constexpr int EPL = D / 64;  // head_dim elements per lane
+  // head_dim elements per lane: D / 64, or D / 48 for D = 96 and 192 (whole
+  // 8- or 16-byte vectors; the first 48 lanes carry the row, the others
+  // re-read lane 47's and store nothing)
+  constexpr int EPL = (D == 96 || D == 192) ? D / 48 : D / 64;
+  constexpr int LANES = D / EPL;
+  static_assert(LANES * EPL == D && (EPL == 1 || EPL == 2 || EPL == 4), "row split over lanes");
   constexpr int CH = 16;       // splits per chunk
   typedef float vecE __attribute__((ext_vector_type(EPL)));
   __shared__ float sw[256 + CH];
@@ -379,7 +401,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombineArgs a) {
   const int row = blockIdx.x;
   const int S = a.num_splits;
   const float* lp = a.lse_part + (int64_t)row * S;
-  const float* op = a.o_part + (int64_t)row * S * D + lane * EPL;
+  const float* op = a.o_part + (int64_t)row * S * D + min(lane, LANES - 1) * EPL;
   auto load_chunk = [&](int s0, vecE (&x)[CH]) {
 #pragma unroll
     for (int i = 0; i < CH; ++i)
@@ -447,14 +469,16 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombineArgs a) {
     acc = lse;
   }
   __bf16* dst = static_cast<__bf16*>(a.out) + (int64_t)row * a.out_row_stride + lane * EPL;
+  if (lane < LANES) {
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) dst[e] = (__bf16)acc[e];
+    for (int e = 0; e < EPL; ++e) dst[e] = (__bf16)acc[e];
+  }
   if (lane == 0 && a.lse != nullptr) a.lse[row] = lse;
 }
 
 template <int D>
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  if constexpr (D <= 128) {
+  if constexpr (D == 64 || D == 128) {
     if (decode_streams(D, a.page_size))
       return a.kv_fp8 ? launch_decode_stream_fp8<D>(a, s) : launch_decode_stream<D>(a, s);
   }
@@ -473,10 +497,14 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
 }
 
 template hipError_t launch_decode<64>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode<96>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode<128>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode<192>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode<256>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_combine<64>(const CombineArgs&, hipStream_t);
+template hipError_t launch_combine<96>(const CombineArgs&, hipStream_t);
 template hipError_t launch_combine<128>(const CombineArgs&, hipStream_t);
+template hipError_t launch_combine<192>(const CombineArgs&, hipStream_t);
 template hipError_t launch_combine<256>(const CombineArgs&, hipStream_t);
 
 }  // namespace mi_attn

@@ -42,9 +42,9 @@
  *     contiguous; base pointers and strides must keep 16-byte alignment of
  *     each row (head_dim % 8 == 0, strides % 8 == 0, pointers 16-byte
  *     aligned).
- *   - Supported head_dim: 64, 96, 128, 192, 256 for mi_attn_fwd; 64, 128,
- *     256 for the decode and the combine; 64, 128 for the backward (the
- *     interface page allows <= 256 in multiples of 8; other sizes return
+ *   - Supported head_dim: 64, 96, 128, 192, 256 for mi_attn_fwd, the decode
+ *     and the combine; 64, 128, 256 for the backward (the interface page
+ *     allows <= 256 in multiples of 8; other sizes return
  *     MI_ATTN_EUNSUPPORTED).
  *   - Return value: MI_ATTN_OK, or a negative mi_attn_status; on error
  *     nothing is enqueued and mi_attn_last_error() describes the problem.
@@ -291,7 +291,7 @@ int mi_attn_decode_splitkv_noalloc(const mi_attn_decode_params *p, void *stream)
  *   lse_partial [rows, num_splits] float32, contiguous
  *   out         bf16, row r at out + r * out_row_stride (head_dim contiguous)
  *   lse         [rows] float32, or NULL
- * num_splits in 1..256, head_dim in {64, 128, 256}. A row whose partial LSEs
+ * num_splits in 1..256, head_dim in {64, 96, 128, 192, 256}. A row whose partial LSEs
  * are all -inf gets O = 0 and LSE = -inf. This is the merge the decode path
  * runs; exported so a caller holding partials from elsewhere (for example
  * key shards on other devices) can merge them.

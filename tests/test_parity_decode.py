@@ -42,6 +42,11 @@ CASES = [
     ("more_splits_than_tiles", 1, 8, 1, 128, 64, 2, 0, [100], 64, None),
     ("window_left", 2, 16, 4, 128, 128, 6, 2, [700, 90], 4, 200),
     ("gqa3_nonpow2", 2, 6, 2, 128, 256, 2, 0, [400, 512], 2, None),
+    # head dims 96 and 192 (the tile kernel at the LDS width of 128 / 256)
+    ("d96_page16_gqa4", 2, 8, 2, 96, 16, 30, 2, [480, 37], 6, None),
+    ("d96_page256_mha", 1, 4, 4, 96, 256, 3, 0, [700], 4, None),
+    ("d192_page64_window", 2, 8, 1, 192, 64, 6, 1, [380, 64], 3, 150),
+    ("d192_page32_ragged", 3, 16, 2, 192, 32, 10, 0, [1, 320, 129], 5, None),
 ]
 
 
@@ -108,7 +113,7 @@ def test_host_bounds_check_rejects_bad_table(gpu_lib):
 
 
 @pytest.mark.parametrize("rows,splits,d", [(37, 1, 64), (100, 16, 128), (9, 256, 256),
-                                           (64, 5, 128)])
+                                           (64, 5, 128), (20, 7, 96), (33, 17, 192)])
 def test_combine_kernel(gpu_lib, rows, splits, d):
     rng = np.random.default_rng(rows * splits + d)
     o_part = rng.standard_normal((rows, splits, d)).astype(np.float32)
@@ -180,6 +185,8 @@ VARLEN_CASES = [
     ("more_tokens_than_keys", 1, 8, 2, 128, 64, 2, [3], [6], 2, True, None),
     ("d256_tile_path", 2, 8, 2, 256, 32, 9, [288, 100], [3, 2], 5, True, None),
     ("page48_tile_path", 2, 8, 2, 128, 48, 8, [380, 47], [5, 1], 3, True, 100),
+    ("d96_spec_causal", 2, 8, 2, 96, 64, 5, [300, 17], [4, 2], 3, True, None),
+    ("d192_spec_window", 2, 8, 2, 192, 32, 9, [288, 100], [3, 5], 4, True, 60),
 ]
 
 

@@ -65,7 +65,7 @@ def test_dims_varlen_paged_softcap_sink(gpu_lib, d):
 
 
 def test_dims_unsupported_elsewhere(gpu_lib):
-    """The decode and the backward keep head dims 64/128(/256)."""
+    """The backward keeps head dims 64/128/256."""
     w = W.dense_case(5, 1, 64, 64, 2, 1, 96)
     q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
     out, lse = gpu_lib.mi_attn_fwd(q, k, v)
