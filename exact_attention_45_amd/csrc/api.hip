@@ -125,9 +125,6 @@ int check_decode(const mi_attn_decode_params* p) {
                 p->kv_dtype);
   if (!isfinite(p->softcap) || p->softcap < 0.0f)
     return fail(MI_ATTN_EUNSUPPORTED, "softcap must be finite and >= 0 (0: none)");
-  if (p->kv_dtype != MI_ATTN_KV_BF16 && !mi_attn::decode_streams(p->head_dim, p->page_size))
-    return fail(MI_ATTN_EUNSUPPORTED, "fp8 K/V needs head_dim 64/128 and page_size a multiple "
-                "of 32 (got %d, %d)", p->head_dim, p->page_size);
   if (p->cu_seqlens_q != nullptr) {
     if (p->max_seqlen_q < 0 || p->total_q < 0)
       return fail(MI_ATTN_EINVAL, "max_seqlen_q and total_q must be >= 0 with cu_seqlens_q");

@@ -265,6 +265,11 @@ __device__ __forceinline__ void vmcnt_wait() {
 
 // 16-byte global load / store of raw bits.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint2 ld8_nt(const void* p) {
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v[0], v[1]);
+}
 __device__ __forceinline__ uint4 ld16_nt(const void* p) {
   typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -273,6 +278,24 @@ __device__ __forceinline__ uint4 ld16_nt(const void* p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   return __builtin_bit_cast(bf16x8, u);
+}
+
+// Four OCP fp8 bytes (little-endian in w; e4m3, or e5m2 when E5M2) -> four
+// bf16 values (exact): the hardware conversion gives fp32, and every e4m3 and
+// e5m2 value is a bf16 value.
+template <bool E5M2>
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  f32x2 lo, hi;
+  if constexpr (E5M2) {
+    lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+  } else {
+    lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  }
+  const bf16x4 r = cvt4(lo[0], lo[1], hi[0], hi[1]);
+  return __builtin_bit_cast(uint2, r);
 }
 
 }  // namespace mi_attn

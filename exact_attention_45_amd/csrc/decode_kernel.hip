@@ -21,6 +21,12 @@
 //     split writes exactly one normalised partial per query head.
 //   * Page ids are looked up per key row; an id outside [0, num_pages) is
 //     never dereferenced and turns the split's partial into NaN.
+//   * fp8 caches (KV = 1 e4m3, 2 e5m2; sm_120 PR page, fp8 KV-cache decode):
+//     each lane loads the 8 bytes of its 8-element chunk, and the register
+//     set is widened to bf16 (exactly) when it is stored to LDS, so tiles,
+//     fragments and MFMAs are the bf16 path's. k_descale joins the score
+//     scale (S = scale * ks * q.k8), v_descale the normalised partial
+//     (O = vs * sum p v8), as in the streaming kernel.
 #include <climits>
 #include <type_traits>
 
@@ -59,8 +65,10 @@ constexpr int dec_width() {
   return D == 96 ? 128 : (D == 192 ? 256 : D);
 }
 
-template <int D>
+template <int D, int KV>
 __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
+  constexpr bool FP8 = KV != 0;
+  using Raw = std::conditional_t<FP8, uint2, uint4>;  // one lane's chunk as loaded
   constexpr int DP = dec_width<D>();
   using C = DecCfg<DP>;
   constexpr int BN = C::BN, CPR = C::CPR, NCH = C::NCH, TILE = C::TILE;
@@ -127,8 +135,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   float m_run = kNegInf;
   float l_run = 0.0f;
 
-  const __bf16* kc = static_cast<const __bf16*>(a.k_cache) + (int64_t)hk * D;
-  const __bf16* vc = static_cast<const __bf16*>(a.v_cache) + (int64_t)hk * D;
+  // element offsets; an element is 2 bytes (bf16) or 1 (fp8)
+  constexpr int EB = FP8 ? 1 : 2;
+  const char* kc = static_cast<const char*>(a.k_cache) + (int64_t)hk * D * EB;
+  const char* vc = static_cast<const char*>(a.v_cache) + (int64_t)hk * D * EB;
   const int64_t tok_stride = (int64_t)a.hkv * D;
   const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
   const int ld_c = lane % CPR;
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   // Register prefetch sets. Page ids of tile t+1 are requested before the
   // K/V loads of tile t: load counters retire in issue order, so a page id
   // requested after a tile's loads could not be used until that tile landed.
-  uint4 kreg[NSET][NCH], vreg[NSET][NCH];
+  Raw kreg[NSET][NCH], vreg[NSET][NCH];
   int pid[2][NCH];  // by tile parity
 
   auto tile_row = [&](int u) { return (u * 4 + wave) * C::ROWS_PER_LD + ld_r; };
@@ -171,10 +181,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
       const int page = ok ? pid[slot][u] : 0;
       const int64_t off =
           ((int64_t)page * a.page_size + key % a.page_size) * tok_stride + ld_off;
-      const uint4 kx = ld16_nt(kc + off);  // the cache is read once per step
-      const uint4 vx = ld16_nt(vc + off);
-      kreg[set][u] = ld_in ? kx : make_uint4(0u, 0u, 0u, 0u);
-      vreg[set][u] = ld_in ? vx : make_uint4(0u, 0u, 0u, 0u);
+      // the cache is read once per step
+      if constexpr (FP8) {
+        const uint2 kx = ld8_nt(kc + off), vx = ld8_nt(vc + off);
+        kreg[set][u] = ld_in ? kx : make_uint2(0u, 0u);
+        vreg[set][u] = ld_in ? vx : make_uint2(0u, 0u);
+      } else {
+        const uint4 kx = ld16_nt(kc + 2 * off), vx = ld16_nt(vc + 2 * off);
+        kreg[set][u] = ld_in ? kx : make_uint4(0u, 0u, 0u, 0u);
+        vreg[set][u] = ld_in ? vx : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   };
   auto store_tile = [&](auto set_c, int buf) {
@@ -185,8 +201,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     for (int u = 0; u < NCH; ++u) {
       const int row = tile_row(u);
       const int p = row * DP + dswz<DP>(row, ld_c) * 8;
-      *reinterpret_cast<uint4*>(&sK[p]) = kreg[set][u];
-      *reinterpret_cast<uint4*>(&sV[p]) = vreg[set][u];
+      if constexpr (FP8) {
+        const uint2 k0 = fp8x4_to_bf16x4<KV == 2>(kreg[set][u].x);
+        const uint2 k1 = fp8x4_to_bf16x4<KV == 2>(kreg[set][u].y);
+        const uint2 v0 = fp8x4_to_bf16x4<KV == 2>(vreg[set][u].x);
+        const uint2 v1 = fp8x4_to_bf16x4<KV == 2>(vreg[set][u].y);
+        *reinterpret_cast<uint4*>(&sK[p]) = make_uint4(k0.x, k0.y, k1.x, k1.y);
+        *reinterpret_cast<uint4*>(&sV[p]) = make_uint4(v0.x, v0.y, v1.x, v1.y);
+      } else {
+        *reinterpret_cast<uint4*>(&sK[p]) = kreg[set][u];
+        *reinterpret_cast<uint4*>(&sV[p]) = vreg[set][u];
+      }
     }
   };
 
@@ -196,10 +221,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   const int tr_key = tr_j >> 2;
   const int tr_c = (tr_g & 1) * 2 + ((tr_j & 3) >> 1);
   const int tr_e = (tr_j & 1) * 4;
-  const float c = a.scale_log2;
-  // soft-capping (this path reads bf16 caches only: no descale)
-  const float sc_k1x = a.softcap > 0.0f ? 2.0f * kLog2e * a.scale / a.softcap : 0.0f;
-  const float sc_k2 = a.softcap > 0.0f ? a.softcap / a.scale : 0.0f;
+  // fp8: the key descale joins the score scale, the value descale the output;
+  // a zero key descale makes every score 0 (uniform weights), a negative or
+  // NaN one turns the split's partial into NaN
+  float kds = 1.0f, vds = 1.0f;
+  if constexpr (FP8) {
+    if (a.k_descale != nullptr) kds = a.k_descale[(int64_t)b * a.hkv + hk];
+    if (a.v_descale != nullptr) vds = a.v_descale[(int64_t)b * a.hkv + hk];
+    bad_page |= !(kds >= 0.0f);
+  }
+  const float c = FP8 ? fmaxf(a.scale_log2 * kds, 1e-30f) : a.scale_log2;
+  // soft-capping of scale * kds * s (a zero effective scale leaves all scores 0)
+  const float sc_eff = a.scale * kds;
+  const float sc_k1x = a.softcap > 0.0f && sc_eff != 0.0f ? 2.0f * kLog2e * sc_eff / a.softcap : 0.0f;
+  const float sc_k2 = a.softcap > 0.0f && sc_eff != 0.0f ? a.softcap / sc_eff : 0.0f;
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, NSET == 2 ? 1 : 0>;
@@ -354,7 +389,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
       wgt[w] = (m == kNegInf) ? 0.0f : fast_exp2((mw[w] - m) * c);
       l += wgt[w] * sL[w * 32 + qcol];
     }
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float inv = l > 0.0f ? vds / l : 0.0f;
     const float nan = __builtin_nanf("");
     const int64_t prow = mrow.prow;
     float* op = a.o_part + (prow * a.num_splits + split) * D + dpart * DPT;
@@ -374,7 +409,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
                   : make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
     if (dpart == 0) {
-      const float lse = l > 0.0f ? m * a.scale + __logf(l) : kNegInf;
+      const float lse = l > 0.0f ? m * sc_eff + __logf(l) : kNegInf;
       a.lse_part[prow * a.num_splits + split] = any_bad ? nan : lse;
     }
   }
@@ -482,10 +517,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     if (decode_streams(D, a.page_size))
       return a.kv_fp8 ? launch_decode_stream_fp8<D>(a, s) : launch_decode_stream<D>(a, s);
   }
-  if (a.kv_fp8) return hipErrorInvalidValue;  // the host rejects this combination first
   const int64_t grid = (int64_t)a.batch * a.hkv * a.row_blocks * a.num_splits;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_split_kernel<D>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  if (a.kv_fp8 == 2)
+    hipLaunchKernelGGL((decode_split_kernel<D, 2>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  else if (a.kv_fp8 == 1)
+    hipLaunchKernelGGL((decode_split_kernel<D, 1>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, 0>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

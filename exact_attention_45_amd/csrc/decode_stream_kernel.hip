@@ -71,24 +71,6 @@ struct StreamCfg {
   static constexpr int LDS_B = SLOT_B;
 };
 
-// Four OCP fp8 bytes (little-endian in w; e4m3, or e5m2 when E5M2) -> four
-// bf16 values (exact): the hardware conversion gives fp32, and every e4m3 and
-// e5m2 value is a bf16 value.
-template <bool E5M2>
-__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
-  typedef __attribute__((ext_vector_type(2))) float f32x2;
-  f32x2 lo, hi;
-  if constexpr (E5M2) {
-    lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
-    hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
-  } else {
-    lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-    hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  }
-  const bf16x4 r = cvt4(lo[0], lo[1], hi[0], hi[1]);
-  return __builtin_bit_cast(uint2, r);
-}
-
 // LDS chunk position of logical 16-byte chunk c of V row `key`. The XOR
 // spreads the eight keys of a transposing read over distinct bank groups; it
 // is an involution, so it also maps a physical position back to its chunk.

@@ -218,9 +218,9 @@ int mi_attn_fwd(const mi_attn_fwd_params *p, void *stream);
  * k_descale[b * num_heads_kv + g] * fp8(byte) (likewise V), with
  * k_descale / v_descale device float32 [batch, num_heads_kv], or NULL for 1.
  * The query stays bf16 and the arithmetic is the bf16 path's (each byte is
- * widened to bf16 exactly). Supported for head_dim 64/128 with page_size a
- * multiple of 32; other combinations return MI_ATTN_EUNSUPPORTED. With
- * kv_dtype == MI_ATTN_KV_BF16 the descale pointers are ignored.
+ * widened to bf16 exactly). Every head_dim and page_size of the bf16 cache
+ * is supported. With kv_dtype == MI_ATTN_KV_BF16 the descale pointers are
+ * ignored.
  * --------------------------------------------------------------------- */
 enum { MI_ATTN_KV_BF16 = 0, MI_ATTN_KV_FP8_E4M3 = 1, MI_ATTN_KV_FP8_E5M2 = 2 };
 

@@ -176,8 +176,6 @@ def test_decode_workspace_size(lib):
     (dict(max_pages_per_seq=1 << 24, page_size=1 << 10), mi.MI_ATTN_EBOUNDS),
     (dict(kv_dtype=3), mi.MI_ATTN_EUNSUPPORTED),                      # no such cache type
     (dict(softcap=float("nan")), mi.MI_ATTN_EUNSUPPORTED),
-    (dict(kv_dtype=mi.MI_ATTN_KV_FP8_E4M3, head_dim=256), mi.MI_ATTN_EUNSUPPORTED),
-    (dict(kv_dtype=mi.MI_ATTN_KV_FP8_E4M3, page_size=48), mi.MI_ATTN_EUNSUPPORTED),
 ])
 def test_decode_invalid_arguments(lib, kw, code):
     p = _dec(**kw)

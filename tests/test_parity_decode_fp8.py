@@ -58,6 +58,13 @@ CASES = [
     ("gqa32_heuristic_splits", 2, 32, 1, 128, 128, 8, 1, [1024, 333], 0, None, True),
     ("window_left", 2, 8, 2, 128, 256, 4, 0, [900, 300], 3, 150, True),
     ("empty_and_tiny", 4, 8, 2, 64, 64, 3, 0, [0, 1, 64, 65], 8, None, True),
+    # the tile kernel: head dims 96 / 192 / 256 and page sizes that are not
+    # multiples of 32
+    ("tile_d256_page32", 2, 8, 2, 256, 32, 9, 1, [288, 100], 5, None, True),
+    ("tile_page16_d128", 2, 16, 2, 128, 16, 30, 2, [470, 33], 6, None, True),
+    ("tile_d96_page48_window", 2, 8, 2, 96, 48, 8, 0, [380, 47], 3, 100, True),
+    ("tile_d192_page64_gqa8", 2, 16, 2, 192, 64, 6, 1, [350, 130], 4, None, True),
+    ("tile_page48_d64_empty", 3, 8, 4, 64, 48, 4, 0, [0, 150, 47], 2, None, False),
 ]
 
 
@@ -74,7 +81,8 @@ def test_fp8_decode_elementwise(gpu_lib, case):
 
 
 E5M2_CASES = [c for c in CASES if c[0] in ("gqa8_page256_ragged", "gqa4_page64_d64",
-                                            "window_left", "empty_and_tiny")]
+                                            "window_left", "empty_and_tiny",
+                                            "tile_d256_page32", "tile_d96_page48_window")]
 
 
 @pytest.mark.parametrize("case", E5M2_CASES, ids=[c[0] for c in E5M2_CASES])
@@ -89,10 +97,11 @@ def test_e5m2_decode_elementwise(gpu_lib, case):
     print(name, check(host_f64(out), o_ref, host_f64(lse), l_ref, what=name))
 
 
-def test_e5m2_every_finite_code_decodes_exactly(gpu_lib):
+@pytest.mark.parametrize("D,ps", [(128, 64), (256, 64), (96, 48)])  # stream, tile, tile
+def test_e5m2_every_finite_code_decodes_exactly(gpu_lib, D, ps):
     """As the e4m3 case below for e5m2: each of its 248 finite codes placed in
     V comes back exactly (every e5m2 value is a bf16 value)."""
-    B, Hq, Hkv, D, ps = 2, 4, 4, 128, 64
+    B, Hq, Hkv = 2, 4, 4
     w = W.paged_decode_fp8_case(78, B, Hq, Hkv, D, ps, 1, seqused_k=[1, 1], num_splits=1,
                                 descale=False, fmt="e5m2")
     finite = np.array([c for c in range(256) if (c & 0x7C) != 0x7C], dtype=np.uint8)
@@ -117,11 +126,12 @@ def test_fp8_mixed_formats_rejected(gpu_lib):
     assert e.value.code == gpu_lib.MI_ATTN_EINVAL
 
 
-def test_fp8_every_code_decodes_exactly(gpu_lib):
+@pytest.mark.parametrize("D,ps", [(128, 64), (256, 64), (192, 16)])  # stream, tile, tile
+def test_fp8_every_code_decodes_exactly(gpu_lib, D, ps):
     """One key per sequence: O is that key's V row times its descale, so every
     finite e4m3 code placed in V must come back exactly (vs = 1, the value is
     a bf16 value); the float8_e4m3fn tensor dtype is accepted as well."""
-    B, Hq, Hkv, D, ps = 2, 4, 4, 128, 64
+    B, Hq, Hkv = 2, 4, 4
     w = W.paged_decode_fp8_case(77, B, Hq, Hkv, D, ps, 1, seqused_k=[1, 1], num_splits=1,
                                 descale=False)
     finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
@@ -160,23 +170,35 @@ def test_fp8_full_size_decode_sampled(gpu_lib):
             check(o_all[b, h], o_ref[0, h], l_all[b, h], l_ref[0, h], what=f"seq {b} head {h}")
 
 
-def test_fp8_unsupported_shapes_rejected(gpu_lib):
-    w = W.paged_decode_fp8_case(9, 1, 4, 2, 128, 16, 4)  # page_size 16: not a multiple of 32
-    with pytest.raises(gpu_lib.MiAttnError) as e:
-        run_fp8(gpu_lib, w)
-    assert e.value.code == gpu_lib.MI_ATTN_EUNSUPPORTED
+@pytest.mark.parametrize("descale", [0.0, -1.0, float("nan")])
+def test_fp8_tile_path_key_descale_edges(gpu_lib, descale):
+    """The tile kernel (page size 48) with a key descale of 0 (every score 0:
+    uniform weights over the visible keys), or negative / NaN (no meaning for
+    a cache scale: that sequence's output and LSE are NaN, the others'
+    unaffected)."""
+    w = W.paged_decode_fp8_case(31, 2, 8, 2, 128, 48, 4, seqused_k=[150, 60], num_splits=2)
+    w.k_descale[0, :] = descale
+    out, lse = run_fp8(gpu_lib, w)
+    o, l = host_f64(out), host_f64(lse)
+    o_ref, l_ref = oracle_fp8(w)
+    if descale == 0.0:
+        check(o, o_ref, l, l_ref, what="zero key descale")
+    else:
+        assert np.isnan(o[0]).all() and np.isnan(l[0]).all()
+        check(o[1:], o_ref[1:], l[1:], l_ref[1:], what="other sequence")
 
 
-def test_fp8_varlen_decode(gpu_lib):
+@pytest.mark.parametrize("D,ps", [(128, 64), (256, 32)])  # stream kernel, tile kernel
+def test_fp8_varlen_decode(gpu_lib, D, ps):
     """fp8 e4m3 cache with descales and three causal query tokens per
     sequence (packed by cu_seqlens_q): against the oracle's paged prefill over
     the decoded, descaled cache values."""
-    print("[case] fp8 varlen decode", flush=True)
-    w = W.paged_decode_fp8_case(97, 3, 16, 2, 128, 64, 6, num_pages=20,
+    print(f"[case] fp8 varlen decode D{D} page {ps}", flush=True)
+    w = W.paged_decode_fp8_case(97, 3, 16, 2, D, ps, 384 // ps, num_pages=3 * (384 // ps) + 2,
                                 seqused_k=[384, 130, 2], num_splits=3)
     q_lens = [3, 1, 3]
     rng = np.random.default_rng(98)
-    qp = W.round_to_bf16_bits(rng.standard_normal((sum(q_lens), 16, 128), dtype=np.float32))
+    qp = W.round_to_bf16_bits(rng.standard_normal((sum(q_lens), 16, D), dtype=np.float32))
     cu = np.zeros(4, dtype=np.int32)
     cu[1:] = np.cumsum(q_lens)
     out, lse = gpu_lib.mi_attn_decode_splitkv(

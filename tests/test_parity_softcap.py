@@ -69,11 +69,13 @@ def test_softcap_prefill_varlen_and_paged(gpu_lib):
 
 
 DECODE = [
-    # (name, D, page_size, kv) -- stream kernel (bf16, fp8) and the tile kernel (page 48, D256)
+    # (name, D, page_size, kv) -- stream kernel (bf16, fp8) and the tile kernel (page 48,
+    # D256, fp8 at D256)
     ("stream_bf16_d128", 128, 64, "bf16"),
     ("stream_fp8_d128", 128, 256, "fp8_e4m3"),
     ("tile_page48_d128", 128, 48, "bf16"),
     ("tile_d256", 256, 64, "bf16"),
+    ("tile_fp8_d256", 256, 64, "fp8_e4m3"),
 ]
 
 
