@@ -18,13 +18,15 @@
 //   softmax : lazy rescale of O (the row max of S(k) is already known)
 //   phase 1 : S(k+1) = K(k+1) Q^T on the matrix cores, each MFMA issued
 //             together with exponentials, row-sum adds and bf16 packing of
-//             P(k), K fragment reads a few MFMAs ahead; V(k+1) requested
-//             straight into LDS (direct-to-LDS buffer loads), one load every
-//             few MFMAs
+//             key block 0 of P(k) (one element every other MFMA), K
+//             fragment reads a few MFMAs ahead; V(k+1) requested straight
+//             into LDS (direct-to-LDS buffer loads), one load every few MFMAs
 //   mid     : wait until V(k) has landed, barrier
 //   phase 2 : O += P(k) V(k), the transposing V reads issued several MFMAs
-//             ahead; K(k+3) requested the same way; the edge mask and the
-//             row max of S(k+1) computed between the first MFMAs
+//             ahead; K(k+3) requested the same way; the exponentials of key
+//             block 1 of P(k) between the MFMAs of key block 0 (which do not
+//             use them), the edge mask and the row max of S(k+1) between the
+//             later ones
 // Both phases are written in the intended issue order and held there by
 // scheduling barriers. Each tile is requested about one and a half
 // iterations before its use, and no wave ever issues its loads in a burst.
@@ -36,7 +38,8 @@
 // read-ahead: with each read issued just before its MFMA (the compiler's
 // choice when left alone) the long-context D256 workload ran 2.85 ms; with
 // six MFMAs of read-ahead in phase 2, 2.35 ms; with phase 1 also written out
-// group by group, 2.07 ms.
+// group by group, 2.07 ms. Moving half of each tile's exponentials from
+// phase 1 into phase 2 took another 2% (1.86 vs 1.90 ms on one box).
 //
 // Register classes: this source is compiled with MFMA results in vector
 // registers (the build's per-file flag), so O and S stay where the softmax
@@ -348,14 +351,15 @@ void fwd_sp_kernel(const FwdArgs a) {
     for (int qb = 0; qb < QB; ++qb) ms[qb] = (m_run[qb] == kNegInf) ? 0.0f : m_run[qb] * c;
   };
 
-  // P = exp2(S*c - m*c), row sums, P^T fragments in the key order of the V^T
-  // fragments (attn_common.hpp)
+  // P = exp2(S*c - m*c) of key block 0, row sums, P^T fragments 0 and 1 in
+  // the key order of the V^T fragments (attn_common.hpp): phase 1's share at
+  // the last tile (the P V phase does key block 1)
   auto sm_exp = [&](STile& s) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 1; ++kb) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = fast_exp2(fmaf(s[kb][qb][v], c, -ms[qb]));
@@ -365,7 +369,7 @@ void fwd_sp_kernel(const FwdArgs a) {
       }
       l_run[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 2; ++t) {
         const int kb = t >> 1;
         const int i0 = 2 * (t & 1);
         pf[qb][t] = cat(cvt4(s[kb][qb][4 * i0 + 0], s[kb][qb][4 * i0 + 1], s[kb][qb][4 * i0 + 2],
@@ -377,12 +381,12 @@ void fwd_sp_kernel(const FwdArgs a) {
   };
 
   // Phase 1 for one query block per wave: S(next) = K(tile in buffer buf)
-  // Q^T fused with the exponentials of S(cur). MFMA i (contraction step
-  // i / 2, key block i % 2) is issued with the K fragment read LEAD1 MFMAs
-  // ahead and with the exponentials, row-sum adds and bf16 packing of
-  // 32 / N score elements of the current tile (elements 32 i / N .. 32 (i + 1)
-  // / N - 1 with MFMA i), in that source order, held
-  // by scheduling barriers between the groups.
+  // Q^T fused with the exponentials of key block 0 of S(cur). MFMA i
+  // (contraction step i / 2, key block i % 2) is issued with the K fragment
+  // read LEAD1 MFMAs ahead and with the exponentials, row-sum adds and bf16
+  // packing of 16 / N score elements (elements 16 i / N .. 16 (i + 1) / N - 1
+  // with MFMA i), in that source order, held by scheduling barriers between
+  // the groups.
   // This wave's NI loads of the next V tile (descriptor vr, V buffer vbuf)
   // go out spread over the MFMAs, one every N / NI: issued in one burst by all
   // four waves, 64 direct-to-LDS loads of 1 KB queue in the CU's load path
@@ -413,9 +417,9 @@ void fwd_sp_kernel(const FwdArgs a) {
       nxt[kb][0] = mfma32(kf, qf[0][cc], cc == 0 ? zero_f32x16() : nxt[kb][0]);
       if (i % (N / NI) == 0) dma_v(vr, vbuf, i / (N / NI));
 #pragma unroll
-      for (int j = 32 * i / N; j < 32 * (i + 1) / N; ++j) {
-        // element j: key block j / 16, register j % 16
-        const int jb = j >> 4, jv = j & 15;
+      for (int j = 16 * i / N; j < 16 * (i + 1) / N; ++j) {
+        // element j of key block 0 (block 1's follow in the P V phase)
+        const int jb = 0, jv = j;
         const float x = fast_exp2(fmaf(cur[jb][0][jv], c, -ms[0]));
         cur[jb][0][jv] = x;
         rs[jv & 3] += x;
@@ -440,16 +444,18 @@ void fwd_sp_kernel(const FwdArgs a) {
   // groups keep that order: left free, the scheduler issues each read right
   // before its MFMA, which then waits out the whole LDS latency.
   // The NI loads of a K tile (descriptor kr, K buffer kbuf) go out spread
-  // over the MFMAs as in phase 1. With WM, the next tile's scores nx (tile
-  // j) get their edge treatment before the MFMAs and their row max during the
-  // first nine MFMAs (the vector units are otherwise idle in this phase).
-  auto pv_tile = [&](auto buf_c, __amdgpu_buffer_rsrc_t kr, int kbuf, auto wm_c, STile& nx, int j)
-      __attribute__((always_inline)) {
+  // over the MFMAs as in phase 1. The first 2 NDB MFMAs (key block 0, P^T
+  // fragments 0 and 1) carry the exponentials of key block 1 of the current
+  // tile's scores cu (fragments 2 and 3, first read by MFMA 2 NDB). With WM,
+  // the next tile's scores nx (tile j) get their edge treatment before the
+  // MFMAs and their row max during the nine MFMAs after those.
+  auto pv_tile = [&](auto buf_c, __amdgpu_buffer_rsrc_t kr, int kbuf, auto wm_c, STile& cu,
+                     STile& nx, int j) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value;
     constexpr bool WM = decltype(wm_c)::value;
     static_assert(!WM || QB == 1, "interleaved row max handles one query block per wave");
     constexpr int N = 4 * NDB;
-    static_assert(N >= 9, "row max spread over the first nine MFMAs");
+    static_assert(N >= 2 * NDB + 9, "row max spread over nine MFMAs of the second half");
     static_assert(N % NI == 0, "loads spread evenly over the MFMAs");
     constexpr int LEAD2 = 6;
     auto read = [&](int i) __attribute__((always_inline)) {
@@ -464,6 +470,8 @@ void fwd_sp_kernel(const FwdArgs a) {
     for (int i = 0; i < LEAD2; ++i) ring[i] = read(i);
     if constexpr (WM) sm_edge(nx, j);
     float m0 = kNegInf, m1 = kNegInf;
+    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int H = 2 * NDB;  // MFMAs of the first key block (P^T fragments 0, 1)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -473,16 +481,35 @@ void fwd_sp_kernel(const FwdArgs a) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma32(vf, pf[qb][t], o[db][qb]);
       if (i % (N / NI) == 0) dma_k(kr, kbuf, i / (N / NI));
+      if (i < H) {
+        // exponentials of key block 1 of the current tile (fragments 2, 3,
+        // first used by MFMA H)
+#pragma unroll
+        for (int e = 16 * i / H; e < 16 * (i + 1) / H; ++e) {
+          const float x = fast_exp2(fmaf(cu[1][0][e], c, -ms[0]));
+          cu[1][0][e] = x;
+          rs[e & 3] += x;
+          if ((e & 7) == 7) {
+            const int t0 = e - 7;
+            pf[0][2 + (e >> 3)] = cat(cvt4(cu[1][0][t0 + 0], cu[1][0][t0 + 1], cu[1][0][t0 + 2],
+                                           cu[1][0][t0 + 3]),
+                                      cvt4(cu[1][0][t0 + 4], cu[1][0][t0 + 5], cu[1][0][t0 + 6],
+                                           cu[1][0][t0 + 7]));
+          }
+        }
+      }
       if constexpr (WM) {
-        if (i < 8) {
-          m0 = vmax3(m0, nx[0][0][2 * i], nx[0][0][2 * i + 1]);
-          m1 = vmax3(m1, nx[1][0][2 * i], nx[1][0][2 * i + 1]);
-        } else if (i == 8) {
+        if (i >= H && i < H + 8) {
+          const int r = i - H;
+          m0 = vmax3(m0, nx[0][0][2 * r], nx[0][0][2 * r + 1]);
+          m1 = vmax3(m1, nx[1][0][2 * r], nx[1][0][2 * r + 1]);
+        } else if (i == H + 8) {
           max_grow(m0, m1, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    l_run[0] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
 
 
@@ -524,7 +551,7 @@ void fwd_sp_kernel(const FwdArgs a) {
     // At the last tile nxt holds no scores; the statistics taken from it are
     // never used. (A second instantiation without them, selected by a branch,
     // makes the register allocator spill.)
-    pv_tile(par_c, k_rsrc(k + 3), par ^ 1, std::true_type{}, nxt, k + 1);
+    pv_tile(par_c, k_rsrc(k + 3), par ^ 1, std::true_type{}, cur, nxt, k + 1);
   };
 
   if (T > 0) {
