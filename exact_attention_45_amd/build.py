@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmiattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "fwd_kernel.hip", "fwd_pp_kernel.hip", "fwd_sp_kernel.hip",
+SOURCES = ["api.hip", "fwd_pp_kernel.hip", "fwd_sp_kernel.hip",
            "decode_kernel.hip", "decode_stream_kernel.hip", "bwd_kernel.hip"]
 # Per-source extra flags. fwd_sp_kernel runs one wave per SIMD with more than
 # 256 registers; by default the compiler then places every MFMA accumulator in

@@ -1,6 +1,6 @@
 // Prefill forward for head_dim 64/128: eight waves in two ping-pong groups.
 //
-// Same method as in fwd_kernel.hip (mslk flash_attn interface.py page,
+// Same method as launch_fwd in kernels.hpp (mslk flash_attn interface.py page,
 // `_flash_attn_fwd`: exact attention with online softmax in the exp2 domain
 // and a natural-log LSE; lazily updated running max). What differs is the
 // schedule. A workgroup owns 256 packed query rows: group A = waves 0-3

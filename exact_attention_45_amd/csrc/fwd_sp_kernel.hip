@@ -3,7 +3,7 @@
 // runs the current tile's exponentials. Serves head_dim 256, whose O
 // accumulators alone take 128 registers per lane.
 //
-// Method as in fwd_kernel.hip (mslk flash_attn interface.py page,
+// Method as launch_fwd in kernels.hpp (mslk flash_attn interface.py page,
 // `_flash_attn_fwd`): exact attention, online softmax in the exp2 domain with
 // a lazily updated running max, natural-log LSE, empty rows O = 0 and
 // LSE = -inf. Same MFMA conventions (attn_common.hpp: both GEMMs transposed so
