@@ -25,7 +25,8 @@
 //   bwd_dkv_reduce_kernel  sums them in split order (deterministic)
 // At head_dim 256 bwd_dkdv_pair_kernel takes the dK/dV walk: 64 keys per
 // workgroup, each 32-key column served by two waves, one computing P and
-// dV, the other dP, dS and dK (P passes between them through LDS).
+// dV, the other dP, dS and dK (P of half the tile's queries and the raw
+// scores of the other half pass between them through LDS).
 // S and dP are recomputed in both kernels (seven tile products per score
 // tile instead of five) in exchange for no dQ accumulation buffer and no
 // atomic traffic.
@@ -223,7 +224,7 @@ void bwd_dq_kernel(const BwdArgs a) {
   const int n_begin = uniform(kv_lo / BN);
   const int n_end = uniform(kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : n_begin);
 
-  // this lane's row: Q^T and dO^T fragments (B operands), LSE, dPsum
+  // this lane's row: Q^T and dO^T fragments (B operands), LSE log2 e, dPsum
   const __bf16* qp = static_cast<const __bf16*>(a.q) + q_base + (int64_t)pos * a.q_rs +
                      (int64_t)hq * a.q_hs;
   const __bf16* gp = static_cast<const __bf16*>(a.dout) + do_base + (int64_t)pos * a.do_rs +
@@ -521,11 +522,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     dva[i] = zero_f32x16();
   }
 
-  // Q / dO tiles (and the tile's LSE and dPsum) go global -> LDS directly
+  // Q / dO tiles (and the tile's LSE log2 e and dPsum) go global -> LDS directly
   // (dma16), double-buffered. For each tensor, instruction i of wave w fills
   // tile rows RPI*(NI*w + i) .. +RPI-1; lane j lands at row offset j / CPR,
   // physical chunk j % CPR, so it loads logical chunk (j % CPR) ^ tswz(row).
-  // Wave 0 loads the 64 LSE values, wave 1 the 64 dPsum values (one dword
+  // Wave 0 loads the 64 LSE log2 e values, wave 1 the 64 dPsum values (one dword
   // per lane; rows past the sequence load zero).
   constexpr int RPI = 1024 / ROW_B;  // rows per instruction
   constexpr int NI = BM / RPI / 4;   // instructions per wave per tensor
@@ -841,7 +842,7 @@ void bwd_dkdv_pair_kernel(const BwdArgs a) {
   for (int i = 0; i < D / 32; ++i) acc[i] = zero_f32x16();
 
   // Q / dO tile staging as in bwd_dkdv_kernel: instruction i of wave w
-  // fills tile rows RPI*(NI*w + i) .. +RPI-1; wave 0 loads the 64 LSE
+  // fills tile rows RPI*(NI*w + i) .. +RPI-1; wave 0 loads the 64 LSE log2 e
   // values, wave 1 the 64 dPsum values.
   constexpr int RPI = 1024 / ROW_B;  // rows per instruction
   constexpr int NI = BM / RPI / 4;   // instructions per wave per tensor
