@@ -72,12 +72,24 @@ BWD_KERNELS = {128: ["bwd_pre_kernel<128>", "bwd_dq_kernel<128>", "bwd_dkdv_kern
                256: ["bwd_pre_kernel<256>", "bwd_dq_kernel<256>", "bwd_dkdv_pair_kernel<256>"]}
 
 
+def _code_text(src: str) -> str:
+    """The source with comments, trailing blanks and empty lines removed: an
+    edit to a comment leaves the compiled kernel, and so its counters, as they
+    were. (The sources hold no string literal containing a comment marker.)"""
+    import re
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lines = (ln.split("//", 1)[0].rstrip() for ln in src.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_digest(kernel: str) -> str:
+    """Digest of the code (not the comments) of the sources a kernel is
+    compiled from."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
