@@ -425,7 +425,7 @@ def mi_attn_bwd(q, k, v, out, dout, lse, cu_seqlens_q=None, cu_seqlens_k=None,
     """Backward of mi_attn_fwd (interface page, `_flash_attn_bwd` contract):
     returns (dq, dk, dv) shaped like q, k, v, given the forward's out and lse
     and the output gradient dout. Dense (B, S, H, D) or packed (T, H, D)
-    tensors with cu_seqlens_q/k as for mi_attn_fwd; head_dim 64, 128 or 256; no
+    tensors with cu_seqlens_q/k as for mi_attn_fwd; head_dim 64, 96, 128, 192 or 256; no
     paged K/V or learnable sink. workspace: a uint8 device tensor of at least
     mi_attn_bwd_workspace_bytes bytes, or None to allocate one.
     """

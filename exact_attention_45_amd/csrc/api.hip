@@ -507,8 +507,8 @@ int check_bwd(const mi_attn_bwd_params* p, mi_attn::BwdArgs* a) {
   if (p->num_heads_q % p->num_heads_kv != 0)
     return fail(MI_ATTN_EINVAL, "num_heads_q (%d) must be a multiple of num_heads_kv (%d)",
                 p->num_heads_q, p->num_heads_kv);
-  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
-    return fail(MI_ATTN_EUNSUPPORTED, "backward head_dim %d not supported (64, 128, 256)",
+  if (!dim_supported(p->head_dim))
+    return fail(MI_ATTN_EUNSUPPORTED, "backward head_dim %d not supported (64, 96, 128, 192, 256)",
                 p->head_dim);
   if (!isfinite(p->softmax_scale) || p->softmax_scale < 0.0f)
     return fail(MI_ATTN_EUNSUPPORTED, "softmax_scale must be finite and >= 0");
@@ -647,9 +647,9 @@ int mi_attn_bwd(const mi_attn_bwd_params* p, void* stream) {
                    ? reinterpret_cast<float*>(static_cast<char*>(p->workspace) + 2 * rows_b)
                    : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = p->head_dim == 64    ? mi_attn::launch_bwd<64>(a, s)
-                 : p->head_dim == 128 ? mi_attn::launch_bwd<128>(a, s)
-                                      : mi_attn::launch_bwd<256>(a, s);
+  hipError_t e = by_dim(p->head_dim, [&](auto dc) {
+    return mi_attn::launch_bwd<decltype(dc)::value>(a, s);
+  });
   if (e != hipSuccess) return fail(MI_ATTN_EHIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

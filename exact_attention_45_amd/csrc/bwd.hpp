@@ -46,14 +46,14 @@ struct BwdArgs {
 
 constexpr int kBwdBlockM = 128;   // dQ kernel: packed query rows per workgroup
 constexpr int kBwdBlockN = 128;   // dK/dV kernel: keys per workgroup (32 per wave)
-constexpr int kBwdBlockNPair = 64;  // paired dK/dV kernel (head_dim 256): keys per workgroup
+constexpr int kBwdBlockNPair = 64;  // paired dK/dV kernel (head_dim 192, 256): keys per workgroup
 constexpr int kBwdTileM = 64;     // dK/dV kernel: queries per step
 constexpr int kBwdTileN = 64;     // dQ kernel: keys per step
 
-// Keys per dK/dV workgroup at a head dimension: head_dim 256 runs the paired
-// kernel, whose two waves per 32 keys each hold one of the dK, dV
+// Keys per dK/dV workgroup at a head dimension: head_dim 192 and 256 run the
+// paired kernel, whose two waves per 32 keys each hold one of the dK, dV
 // accumulators.
-inline int bwd_block_n(int head_dim) { return head_dim == 256 ? kBwdBlockNPair : kBwdBlockN; }
+inline int bwd_block_n(int head_dim) { return head_dim > 128 ? kBwdBlockNPair : kBwdBlockN; }
 
 // Elements of the dpsum workspace (float32) for a; lse_log2 has as many.
 inline int64_t bwd_dpsum_elems(const BwdArgs& a) {

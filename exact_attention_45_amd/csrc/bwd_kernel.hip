@@ -1,4 +1,5 @@
-// Attention backward for head_dim 64/128/256: dQ, dK, dV of exact attention.
+// Attention backward for head_dim 64/96/128/192/256: dQ, dK, dV of exact
+// attention.
 //
 // Method (Blackwell backward page flash_bwd_sm100.py: P is recomputed from
 // the scores and the forward LSE in the exp2 domain, dV = P^T dO,
@@ -23,7 +24,7 @@
 //                    already summed over the group; with several, float32
 //                    partials go to the workspace and
 //   bwd_dkv_reduce_kernel  sums them in split order (deterministic)
-// At head_dim 256 bwd_dkdv_pair_kernel takes the dK/dV walk: 64 keys per
+// At head_dim 192 and 256 bwd_dkdv_pair_kernel takes the dK/dV walk: 64 keys per
 // workgroup, each 32-key column served by two waves, one computing P and
 // dV, the other dP, dS and dK (P of half the tile's queries and the raw
 // scores of the other half pass between them through LDS).
@@ -49,10 +50,19 @@ namespace mi_attn {
 
 // ---------------------------------------------------------------- dPsum ----
 
+// Head dims 96 and 192 run in the layouts of 128 and 256 (bwd_width): LDS
+// tile rows, lane groups and swizzles have the wider shape, every product
+// loops over the real head_dim only, and tile descriptors end at the real
+// row, so the padding columns are never read.
+template <int D>
+constexpr int bwd_width() {
+  return D == 96 ? 128 : (D == 192 ? 256 : D);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs a) {
-  constexpr int CPR = D / 8;         // lanes per (token, head) row, 8 elements each
-  constexpr int RPB = 256 / CPR;     // rows per workgroup
+  constexpr int CPR = bwd_width<D>() / 8;  // lanes per (token, head) row, 8 elements each
+  constexpr int RPB = 256 / CPR;           // rows per workgroup
   const int64_t ntok = a.cu_q != nullptr ? (int64_t)a.total_q : (int64_t)a.batch * a.seqlen_q;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
   const int c = threadIdx.x % CPR;
@@ -71,7 +81,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdArgs a) {
     out_idx = (b * a.hq + h) * a.seqlen_q + pos;
   }
   float acc = 0.0f;
-  if (ok) {
+  if (ok && c < D / 8) {  // lanes past the row (D = 96, 192) add nothing
     const bf16x8 o = as_bf16x8(ld16(static_cast<const __bf16*>(a.o) + o_off + 8 * c));
     const bf16x8 g = as_bf16x8(ld16(static_cast<const __bf16*>(a.dout) + do_off + 8 * c));
 #pragma unroll
@@ -168,9 +178,10 @@ __device__ __forceinline__ void acc_to_frags(const f32x16 x[2], bf16x8 f[4]) {
 // At head_dim 256 the row's Q^T, dO^T fragments and the dQ accumulators
 // alone take 256 registers: one wave per SIMD.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_width<D>() == 256 ? 1 : 2)))
 void bwd_dq_kernel(const BwdArgs a) {
-  using T = BwdTile<D>;
+  constexpr int DL = bwd_width<D>();  // layout head dim
+  using T = BwdTile<DL>;
   constexpr int ROW_B = T::ROW_B, CPR = T::CPR, TILE_B = T::TILE_B;
   constexpr int BM = kBwdBlockM, BN = kBwdTileN;
   static_assert(BN == T::ROWS, "one staged tile per key step");
@@ -261,14 +272,14 @@ void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int row = RPI * (NI * wave + i) + lane / CPR;
-    kdo[i] = (uint32_t)(row * a.k_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
-    vdo[i] = (uint32_t)(row * a.v_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
+    kdo[i] = (uint32_t)(row * a.k_rs * 2 + ((lane % CPR) ^ tswz<DL>(row)) * 16);
+    vdo[i] = (uint32_t)(row * a.v_rs * 2 + ((lane % CPR) ^ tswz<DL>(row)) * 16);
   }
   const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
   auto issue = [&](int n0, int buf) __attribute__((always_inline)) {
     const int nrows = min(sk - n0, BN);  // >= 1; rows past it read as zero
-    const auto kr = make_rsrc(kp + (int64_t)n0 * a.k_rs, (uint32_t)((nrows - 1) * a.k_rs * 2 + ROW_B));
-    const auto vr = make_rsrc(vp + (int64_t)n0 * a.v_rs, (uint32_t)((nrows - 1) * a.v_rs * 2 + ROW_B));
+    const auto kr = make_rsrc(kp + (int64_t)n0 * a.k_rs, (uint32_t)((nrows - 1) * a.k_rs * 2 + D * 2));
+    const auto vr = make_rsrc(vp + (int64_t)n0 * a.v_rs, (uint32_t)((nrows - 1) * a.v_rs * 2 + D * 2));
 #pragma unroll
     for (int i = 0; i < NI; ++i) dma16(kr, kdo[i], lds_w + (uint32_t)(buf * BUF_B + i * 1024));
 #pragma unroll
@@ -278,7 +289,7 @@ void bwd_dq_kernel(const BwdArgs a) {
 
   int rd[D / 16];
 #pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ tswz<D>(c32)) * 16);
+  for (int cc = 0; cc < D / 16; ++cc) rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ tswz<DL>(c32)) * 16);
   int tr[2];
   tr_offsets(lane, ROW_B, tr);
 
@@ -433,7 +444,8 @@ __device__ __forceinline__ int64_t dkdv_item(int64_t L, int64_t W, int64_t NB) {
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_dkdv_kernel(const BwdArgs a) {
-  constexpr int ROW_B = D * 2, CPR = D / 8;
+  constexpr int DL = bwd_width<D>();  // layout head dim
+  constexpr int ROW_B = DL * 2, CPR = DL / 8;
   constexpr int BNK = kBwdBlockN, BM = kBwdTileM;
   static_assert(BNK == 128 && BM == 64, "four 32-key waves, 64-query tiles");
   constexpr int TILE_B = BM * ROW_B;
@@ -535,8 +547,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int row = RPI * (NI * wave + i) + lane / CPR;
-    qdo[i] = (uint32_t)(row * a.q_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
-    gdo[i] = (uint32_t)(row * a.do_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
+    qdo[i] = (uint32_t)(row * a.q_rs * 2 + ((lane % CPR) ^ tswz<DL>(row)) * 16);
+    gdo[i] = (uint32_t)(row * a.do_rs * 2 + ((lane % CPR) ^ tswz<DL>(row)) * 16);
   }
   const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
   const uint32_t lds_s = (uint32_t)uniform((int)(lds_addr(smem) + 2 * TILE_B + (wave & 1) * 256));
@@ -549,8 +561,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
                        (int64_t)h * a.q_hs;
     const __bf16* g0 = static_cast<const __bf16*>(a.dout) + do_base + (int64_t)m0 * a.do_rs +
                        (int64_t)h * a.do_hs;
-    const auto qr = make_rsrc(q0, (uint32_t)((nrows - 1) * a.q_rs * 2 + ROW_B));
-    const auto gr = make_rsrc(g0, (uint32_t)((nrows - 1) * a.do_rs * 2 + ROW_B));
+    const auto qr = make_rsrc(q0, (uint32_t)((nrows - 1) * a.q_rs * 2 + D * 2));
+    const auto gr = make_rsrc(g0, (uint32_t)((nrows - 1) * a.do_rs * 2 + D * 2));
 #pragma unroll
     for (int i = 0; i < NI; ++i) dma16(qr, qdo[i], lds_w + (uint32_t)(buf * BUF_B + i * 1024));
 #pragma unroll
@@ -567,7 +579,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 
   int rd[D / 16];
 #pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ tswz<D>(c32)) * 16);
+  for (int cc = 0; cc < D / 16; ++cc) rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ tswz<DL>(c32)) * 16);
   int tr[2];
   tr_offsets(lane, ROW_B, tr);
 
@@ -738,7 +750,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 
 // ----------------------------------------------------- dK dV, paired waves ----
 
-// The dK/dV walk for head_dim 256. Holding the lane's K and V fragments and
+// The dK/dV walk for head_dim 256 (and 192, in its layout). Holding the
+// lane's K and V fragments and
 // both 32 x 256 accumulators (dK^T, dV^T) takes ~540 registers, past the
 // 512 a wave can have, so each 32-key column is served by a pair of waves
 // that split the four products without repeating any:
@@ -753,7 +766,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_dkdv_pair_kernel(const BwdArgs a) {
-  constexpr int ROW_B = D * 2, CPR = D / 8;
+  constexpr int DL = bwd_width<D>();  // layout head dim
+  constexpr int ROW_B = DL * 2, CPR = DL / 8;
   constexpr int BNK = kBwdBlockNPair, BM = kBwdTileM;
   static_assert(BNK == 64 && BM == 64, "two 32-key wave pairs, 64-query tiles");
   constexpr int TILE_B = BM * ROW_B;
@@ -851,8 +865,8 @@ void bwd_dkdv_pair_kernel(const BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int row = RPI * (NI * wave + i) + lane / CPR;
-    qdo[i] = (uint32_t)(row * a.q_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
-    gdo[i] = (uint32_t)(row * a.do_rs * 2 + ((lane % CPR) ^ tswz<D>(row)) * 16);
+    qdo[i] = (uint32_t)(row * a.q_rs * 2 + ((lane % CPR) ^ tswz<DL>(row)) * 16);
+    gdo[i] = (uint32_t)(row * a.do_rs * 2 + ((lane % CPR) ^ tswz<DL>(row)) * 16);
   }
   const uint32_t lds_w = (uint32_t)uniform((int)(lds_addr(smem) + NI * wave * 1024));
   const uint32_t lds_s = (uint32_t)uniform((int)(lds_addr(smem) + 2 * TILE_B + (wave & 1) * 256));
@@ -865,8 +879,8 @@ void bwd_dkdv_pair_kernel(const BwdArgs a) {
                        (int64_t)h * a.q_hs;
     const __bf16* g0 = static_cast<const __bf16*>(a.dout) + do_base + (int64_t)m0 * a.do_rs +
                        (int64_t)h * a.do_hs;
-    const auto qr = make_rsrc(q0, (uint32_t)((nrows - 1) * a.q_rs * 2 + ROW_B));
-    const auto gr = make_rsrc(g0, (uint32_t)((nrows - 1) * a.do_rs * 2 + ROW_B));
+    const auto qr = make_rsrc(q0, (uint32_t)((nrows - 1) * a.q_rs * 2 + D * 2));
+    const auto gr = make_rsrc(g0, (uint32_t)((nrows - 1) * a.do_rs * 2 + D * 2));
 #pragma unroll
     for (int i = 0; i < NI; ++i) dma16(qr, qdo[i], lds_w + (uint32_t)(buf * BUF_B + i * 1024));
 #pragma unroll
@@ -883,7 +897,7 @@ void bwd_dkdv_pair_kernel(const BwdArgs a) {
 
   int rd[D / 16];
 #pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ tswz<D>(c32)) * 16);
+  for (int cc = 0; cc < D / 16; ++cc) rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ tswz<DL>(c32)) * 16);
   int tr[2];
   tr_offsets(lane, ROW_B, tr);
   // this pair's P exchange: chunk i (4 floats) of lane l at 1024 i + 16 l
@@ -1138,8 +1152,9 @@ template <int D>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   const int64_t ntok = a.cu_q != nullptr ? (int64_t)a.total_q : (int64_t)a.batch * a.seqlen_q;
   const int64_t pre_rows = ntok * a.hq;
+  constexpr int DL = bwd_width<D>();
   if (pre_rows > 0) {
-    const int64_t rpb = 256 / (D / 8);
+    const int64_t rpb = 256 / (DL / 8);
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((pre_rows + rpb - 1) / rpb)),
                        dim3(256), 0, s, a);
   }
@@ -1147,10 +1162,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   if (mblocks > 0 && a.batch > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)mblocks, a.hkv, a.batch), dim3(256), 0,
                        s, a);
-  constexpr int BN = D == 256 ? kBwdBlockNPair : kBwdBlockN;
+  constexpr int BN = DL == 256 ? kBwdBlockNPair : kBwdBlockN;
   const int64_t nblocks = ((int64_t)a.seqlen_k + BN - 1) / BN;
   if (nblocks > 0 && a.batch > 0) {
-    if constexpr (D == 256)
+    if constexpr (DL == 256)
       hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D>),
                          dim3((unsigned)nblocks, a.hkv, a.batch * a.splits), dim3(256), 0, s, a);
     else
@@ -1166,7 +1181,9 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
 }
 
 template hipError_t launch_bwd<64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd<96>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd<128>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd<192>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd<256>(const BwdArgs&, hipStream_t);
 
 }  // namespace mi_attn

@@ -42,9 +42,8 @@
  *     contiguous; base pointers and strides must keep 16-byte alignment of
  *     each row (head_dim % 8 == 0, strides % 8 == 0, pointers 16-byte
  *     aligned).
- *   - Supported head_dim: 64, 96, 128, 192, 256 for mi_attn_fwd, the decode
- *     and the combine; 64, 128, 256 for the backward (the interface page
- *     allows <= 256 in multiples of 8; other sizes return
+ *   - Supported head_dim: 64, 96, 128, 192, 256 for every entry point (the
+ *     interface page allows <= 256 in multiples of 8; other sizes return
  *     MI_ATTN_EUNSUPPORTED).
  *   - Return value: MI_ATTN_OK, or a negative mi_attn_status; on error
  *     nothing is enqueued and mi_attn_last_error() describes the problem.
@@ -323,7 +322,7 @@ int mi_attn_combine(const float *o_partial, const float *lse_partial, void *out,
  * cu_seqlens_k are given together or not at all. Paged K/V and the
  * learnable sink are not part of the backward.
  *
- * head_dim 64, 128 or 256 (others return MI_ATTN_EUNSUPPORTED). The result
+ * head_dim 64, 96, 128, 192 or 256 (others return MI_ATTN_EUNSUPPORTED). The result
  * is deterministic: nothing is accumulated with atomics. The caller owns
  * every buffer, including the workspace (size from
  * mi_attn_bwd_workspace_bytes; a smaller one returns MI_ATTN_EWORKSPACE):

@@ -244,9 +244,9 @@ def _bwd(**kw):
 def _bwd_ws(batch, hq, hkv, d, rows_q, max_k):
     """One float32 row sum and one base-2 LSE per (query row, head), then float32 dK and dV
     partials of each split of the dK/dV walk (splits: about 512 workgroups of
-    128 keys, 64 at head_dim 256, at most 4), each part 256-byte rounded."""
+    128 keys, 64 at head_dim 192 and 256, at most 4), each part 256-byte rounded."""
     rnd = lambda x: -(-x // 256) * 256
-    bn = 64 if d == 256 else 128
+    bn = 64 if d > 128 else 128
     wg = -(-max_k // bn) * hkv * batch
     splits = max(1, min(4, -(-512 // wg)))
     parts = splits * batch * max_k * hkv * 2 * d if splits > 1 else 0
@@ -265,13 +265,15 @@ def test_bwd_workspace_size(lib):
         p = _bwd(head_dim=256, **kw)
         S = kw.get("seqlen_q", 1000)
         assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(p)) == _bwd_ws(2, 8, 2, 256, 2 * S, S)
-    assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(_bwd(head_dim=96))) == 0
+    assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(_bwd(head_dim=96))) == _bwd_ws(
+        2, 8, 2, 96, 2000, 1000)
+    assert lib.mi_attn_bwd_workspace_bytes(ctypes.byref(_bwd(head_dim=80))) == 0
     assert "head_dim" in mi.mi_attn_last_error()
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(head_dim=192), mi.MI_ATTN_EUNSUPPORTED),
-    (dict(head_dim=96), mi.MI_ATTN_EUNSUPPORTED),
+    (dict(head_dim=80), mi.MI_ATTN_EUNSUPPORTED),
+    (dict(head_dim=160), mi.MI_ATTN_EUNSUPPORTED),
     (dict(num_heads_q=7), mi.MI_ATTN_EINVAL),
     (dict(dout=0), mi.MI_ATTN_EINVAL),
     (dict(dk=FAKE + 4), mi.MI_ATTN_EINVAL),

@@ -83,6 +83,11 @@ DENSE = [
     # share each walk with interleaved key blocks
     ("interleaved_xcd_mqa4_d256_s1024", 1, 1024, 1024, 4, 1, 256, True, None, None),
     ("interleaved_xcd_mqa4_d128_s2048", 1, 2048, 2048, 4, 1, 128, True, None, None),
+    # head dims 96 and 192 (the layouts of 128 and 256, products over the real columns)
+    ("gqa4_d96_causal_s300", 1, 300, 300, 8, 2, 96, True, None, None),
+    ("window_30_5_d96_sq_lt_sk", 2, 150, 260, 4, 2, 96, False, 30, 5),
+    ("gqa2_d192_causal_s333", 1, 333, 333, 4, 2, 192, True, None, None),
+    ("mha_d192_s200_split", 2, 200, 200, 2, 2, 192, False, None, None),
 ]
 
 
@@ -100,7 +105,7 @@ def test_bwd_dense_elementwise(gpu_lib, case):
         print(name, nm, check_grad(host_f64(got), r, f"{name} {nm}"))
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [96, 128, 192, 256])
 def test_bwd_varlen_elementwise(gpu_lib, D):
     """Packed sequences with an empty query sequence, a one-token one and
     ragged tails; GQA 4:1, causal (bottom-right per sequence)."""
@@ -250,7 +255,8 @@ def test_bwd_zero_scale(gpu_lib):
     """softmax_scale = 0: P is uniform over each row's visible keys, dQ = dK =
     0, dV = P^T dO; masked keys (causal, rows with no key) must not give NaN."""
     print("[case] bwd zero scale", flush=True)
-    for B, Sq, Sk, D in ((1, 130, 130, 128), (1, 90, 40, 64), (1, 100, 100, 256)):
+    for B, Sq, Sk, D in ((1, 130, 130, 128), (1, 90, 40, 64), (1, 100, 100, 256), (1, 70, 70, 96),
+                         (1, 66, 66, 192)):
         w = W.dense_case(93 + Sq, B, Sq, Sk, 4, 2, D, causal=True, softmax_scale=0.0)
         g = W.grad_output(93 + Sq, (B, Sq, 4, D))
         dq, dk, dv = run_dense(gpu_lib, w, g)
@@ -260,11 +266,11 @@ def test_bwd_zero_scale(gpu_lib):
             print("scale0", nm, check_grad(host_f64(got), r, f"scale0 {nm}"))
 
 
-def test_bwd_rejects_head_dim_192(gpu_lib):
-    """The forward serves head_dim 192; the backward does not."""
-    w = W.dense_case(3, 1, 64, 64, 2, 1, 192)
+def test_bwd_rejects_head_dim_80(gpu_lib):
+    """A head dim outside 64/96/128/192/256 is refused before any launch."""
+    w = W.dense_case(3, 1, 64, 64, 2, 1, 80)
     q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
-    out, lse = gpu_lib.mi_attn_fwd(q, k, v)
+    lse = torch.zeros(1, 2, 64, dtype=torch.float32, device="cuda")
     with pytest.raises(gpu_lib.MiAttnError) as e:
-        gpu_lib.mi_attn_bwd(q, k, v, out, out, lse)
+        gpu_lib.mi_attn_bwd(q, k, v, q, q, lse)
     assert e.value.code == gpu_lib.MI_ATTN_EUNSUPPORTED

@@ -64,16 +64,6 @@ def test_dims_varlen_paged_softcap_sink(gpu_lib, d):
     print("paged", check(host_f64(out), o_ref, host_f64(lse), l_ref, what=f"paged d{d}"))
 
 
-def test_dims_unsupported_elsewhere(gpu_lib):
-    """The backward keeps head dims 64/128/256."""
-    w = W.dense_case(5, 1, 64, 64, 2, 1, 96)
-    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
-    out, lse = gpu_lib.mi_attn_fwd(q, k, v)
-    with pytest.raises(gpu_lib.MiAttnError) as e:
-        gpu_lib.mi_attn_bwd(q, k, v, out, out, lse)
-    assert e.value.code == gpu_lib.MI_ATTN_EUNSUPPORTED
-
-
 @pytest.mark.parametrize("d,hq,hkv,s", [(96, 32, 4, 4096), (192, 16, 2, 8192)])
 def test_dims_full_size_sampled(gpu_lib, d, hq, hkv, s):
     """The bench's D96 (GQA 32/4, S4096) and D192 (GQA 16/2, S8192) causal prefills:
