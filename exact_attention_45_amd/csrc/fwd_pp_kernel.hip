@@ -406,7 +406,12 @@ void fwd_pp_kernel(const FwdArgs a) {
     vmcnt_wait<0>();
   }
 
-  // ---- epilogue: combine the two lane halves' row sums, normalise, store
+  // ---- epilogue: combine the two lane halves' row sums, normalise, store.
+  // O leaves through LDS, free once every wave is past the loop: each wave
+  // writes its 32 normalised rows there, then stores them as whole rows of
+  // 16-byte chunks, so each output line is written in full by one
+  // instruction. (Stored in place, 8 bytes per lane, the lines were written
+  // in pieces and the write counter read up to 1.4x the output bytes.)
   const float l_tot = pair_sum(l_run);
   float inv = poison ? __builtin_nanf("") : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
   float lse_row = l_tot > 0.0f ? m_run * a.scale + __logf(l_tot) : kNegInf;
@@ -415,18 +420,40 @@ void fwd_pp_kernel(const FwdArgs a) {
     lse_row = merge_sink(lse_row, (float)a.sink[hq], &w);
     inv *= w;
   }
-  if (valid) {
-    __bf16* op = static_cast<__bf16*>(a.out) + o_base + (int64_t)pos * a.o_rs +
-                 (int64_t)hq * a.o_hs;
+  constexpr int OS = 2 * D + 16;  // LDS row stride of the staged O, bytes
+  static_assert(8 * 32 * OS <= C::NBUF * BUF_B, "staged O fits the tile buffers");
+  char* so = smem + wave * 32 * OS;
+  lds_barrier();  // every wave is done with the K/V tiles (and its loads landed)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = db * 32 + 8 * i + 4 * half;
-        *reinterpret_cast<bf16x4*>(op + d0) =
-            cvt4(o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
-                 o[db][4 * i + 3] * inv);
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = db * 32 + 8 * i + 4 * half;
+      *reinterpret_cast<bf16x4*>(so + c32 * OS + 2 * d0) =
+          cvt4(o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
+               o[db][4 * i + 3] * inv);
+    }
+  // the lanes read chunks other lanes of this wave wrote: a wave's LDS
+  // accesses complete in order, and the empty asm keeps the compiler's order
+  asm volatile("" ::: "memory");
+  {
+    constexpr int CH = D / 8;                 // 16-byte chunks per row
+    constexpr int NST = (32 * CH + 63) / 64;  // store instructions per wave
+#pragma unroll
+    for (int k = 0; k < NST; ++k) {
+      const int ci = k * 64 + lane;
+      const int rr = ci / CH, cc = ci - rr * CH;
+      const int prow_r = row0 + grp * 128 + wig * 32 + rr;
+      if (rr < 32 && prow_r < rows) {
+        const int pos_r = prow_r / r;
+        const int hq_r = hk * r + (prow_r - pos_r * r);
+        const uint4 val = *reinterpret_cast<const uint4*>(so + rr * OS + 16 * cc);
+        *reinterpret_cast<uint4*>(static_cast<__bf16*>(a.out) + o_base + (int64_t)pos_r * a.o_rs +
+                                  (int64_t)hq_r * a.o_hs + 8 * cc) = val;
       }
+    }
+  }
+  if (valid) {
     if (half == 0 && a.lse != nullptr) {
       const float lse = poison ? __builtin_nanf("") : lse_row;
       const int64_t li = a.cu_q != nullptr
