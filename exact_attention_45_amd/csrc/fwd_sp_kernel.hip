@@ -587,7 +587,14 @@ void fwd_sp_kernel(const FwdArgs a) {
     vmcnt_wait<0>();
   }
 
-  // ---- epilogue: combine the two lane halves' row sums, normalise, store
+  // ---- epilogue: combine the two lane halves' row sums, normalise, store.
+  // O leaves through LDS, free once every wave is past the loop: each wave
+  // writes its normalised rows there, then stores them as whole rows of
+  // 16-byte chunks, so each output line is written by one instruction.
+  constexpr int OS = 2 * D + 16;  // LDS row stride of the staged O, bytes
+  static_assert(4 * 32 * QB * OS <= 4 * TILE_B, "staged O fits the tile buffers");
+  char* so = smem + wave * 32 * QB * OS;
+  lds_barrier();  // every wave is done with the K/V tiles (and its loads landed)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = pair_sum(l_run[qb]);
@@ -598,24 +605,42 @@ void fwd_sp_kernel(const FwdArgs a) {
       lse_row = merge_sink(lse_row, (float)a.sink[hq[qb]], &w);
       inv *= w;
     }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * half;
+        *reinterpret_cast<bf16x4*>(so + (qb * 32 + c32) * OS + 2 * d0) =
+            cvt4(o[db][qb][4 * i] * inv, o[db][qb][4 * i + 1] * inv, o[db][qb][4 * i + 2] * inv,
+                 o[db][qb][4 * i + 3] * inv);
+      }
     if (valid[qb]) {
-      __bf16* op = static_cast<__bf16*>(a.out) + o_base + (int64_t)pos[qb] * a.o_rs +
-                   (int64_t)hq[qb] * a.o_hs;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d0 = db * 32 + 8 * i + 4 * half;
-          *reinterpret_cast<bf16x4*>(op + d0) =
-              cvt4(o[db][qb][4 * i] * inv, o[db][qb][4 * i + 1] * inv, o[db][qb][4 * i + 2] * inv,
-                   o[db][qb][4 * i + 3] * inv);
-        }
       if (half == 0 && a.lse != nullptr) {
         const float lse = poison ? __builtin_nanf("") : lse_row;
         const int64_t li = a.cu_q != nullptr
                                ? (int64_t)hq[qb] * a.total_q + q_tok0 + pos[qb]
                                : ((int64_t)b * a.hq + hq[qb]) * sq + pos[qb];
         a.lse[li] = lse;
+      }
+    }
+  }
+  // the lanes read chunks other lanes of this wave wrote: a wave's LDS
+  // accesses complete in order, and the empty asm keeps the compiler's order
+  asm volatile("" ::: "memory");
+  {
+    constexpr int CH = D / 8;                      // 16-byte chunks per row
+    constexpr int NST = (32 * QB * CH + 63) / 64;  // store instructions per wave
+#pragma unroll
+    for (int k = 0; k < NST; ++k) {
+      const int ci = k * 64 + lane;
+      const int rr = ci / CH, cc = ci - rr * CH;
+      const int prow_r = row0 + wave * 32 * QB + rr;
+      if (rr < 32 * QB && prow_r < rows) {
+        const int pos_r = prow_r / r;
+        const int hq_r = hk * r + (prow_r - pos_r * r);
+        const uint4 val = *reinterpret_cast<const uint4*>(so + rr * OS + 16 * cc);
+        *reinterpret_cast<uint4*>(static_cast<__bf16*>(a.out) + o_base + (int64_t)pos_r * a.o_rs +
+                                  (int64_t)hq_r * a.o_hs + 8 * cc) = val;
       }
     }
   }
