@@ -281,21 +281,21 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
 }
 
 // Four OCP fp8 bytes (little-endian in w; e4m3, or e5m2 when E5M2) -> four
-// bf16 values (exact): the hardware conversion gives fp32, and every e4m3 and
-// e5m2 value is a bf16 value.
+// bf16 values, exact: one hardware conversion per byte pair goes straight to
+// bf16 with a scale of 1.0, so each result is the format's value itself, and
+// every e4m3 and e5m2 value is a bf16 value.
 template <bool E5M2>
 __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
-  typedef __attribute__((ext_vector_type(2))) float f32x2;
-  f32x2 lo, hi;
+  typedef __attribute__((ext_vector_type(2))) __bf16 b16x2;
+  b16x2 lo, hi;
   if constexpr (E5M2) {
-    lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
-    hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true);
   } else {
-    lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-    hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
   }
-  const bf16x4 r = cvt4(lo[0], lo[1], hi[0], hi[1]);
-  return __builtin_bit_cast(uint2, r);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 }  // namespace mi_attn
