@@ -73,21 +73,22 @@ void fwd_pp_kernel(const FwdArgs a) {
 
   // ---- work item (heavy query blocks first; see fwd_work_item)
   int hk, b, mb;
-  if (!fwd_work_item<BM>(a, hk, b, mb)) return;
+  FwdSeq seq;
+  if (!fwd_work_item<BM>(a, hk, b, mb, seq)) return;
 
   int sq = a.seqlen_q, sk = a.seqlen_k;
   int64_t q_base, k_base, v_base, o_base;
   int q_tok0 = 0;
   if (a.cu_q != nullptr) {
-    q_tok0 = a.cu_q[b];
-    sq = a.cu_q[b + 1] - q_tok0;
+    q_tok0 = seq.q0;
+    sq = seq.q1 - seq.q0;
     q_base = (int64_t)q_tok0 * a.q_rs;
     o_base = (int64_t)q_tok0 * a.o_rs;
   } else {
     q_base = (int64_t)b * a.q_bs;
     o_base = (int64_t)b * a.o_bs;
   }
-  fwd_kv_extent<PAGED>(a, b, sk, k_base, v_base);
+  fwd_kv_extent<PAGED>(a, b, seq, sk, k_base, v_base);
   sq = uniform(sq);
   sk = uniform(sk);
   const int r = a.group;

@@ -53,18 +53,42 @@ inline int64_t fwd_blocks_per_head(const FwdArgs& a, int bm) {
   return packed < dense ? packed : dense;
 }
 
+// Sequence bounds a packed varlen launch reads for its work item: query
+// tokens [q0, q1) and, with cu_k, key tokens [k0, k1); `used` is seqused_k[b]
+// (paged caches). Fields whose array is NULL are left 0.
+struct FwdSeq {
+  int q0, q1, k0, k1, used;
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within each
+// 16-lane row, then the row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Work item (KV head hk, sequence b, query block mb) of prefill workgroup
 // blockIdx.x. Dense batches: heavy (late) query blocks first, (KV head,
 // sequence) fastest. Packed varlen batches: KV head fastest, then block g of
 // the concatenation of every sequence's blocks, each sequence's last
-// (heaviest) block first; the sequence lengths are read eight at a time
-// (independent scalar loads, one memory latency per eight sequences).
+// (heaviest) block first. The search takes 64 sequences per step, one per
+// lane: each lane loads its sequence's bounds (cu_q, and cu_k / seqused_k
+// when given; all loads of a step issued together, one memory latency), the
+// block counts are prefix-summed across the wave, and the first lane whose
+// running total passes g holds the sequence; its bounds come back in `seq`.
 // Returns false for a workgroup past the last block.
 template <int BM>
-__device__ __forceinline__ bool fwd_work_item(const FwdArgs& a, int& hk, int& b, int& mb) {
+__device__ __forceinline__ bool fwd_work_item(const FwdArgs& a, int& hk, int& b, int& mb,
+                                              FwdSeq& seq) {
   // every quantity here is the same in all lanes: keep it in scalar registers
   const auto scalar = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
   const int lin = (int)blockIdx.x;
+  seq = FwdSeq{0, 0, 0, 0, 0};
   if (a.cu_q == nullptr) {
     const int nhb = a.hkv * a.batch;
     const int hb = scalar(lin % nhb);
@@ -75,21 +99,30 @@ __device__ __forceinline__ bool fwd_work_item(const FwdArgs& a, int& hk, int& b,
   }
   hk = scalar(lin % a.hkv);
   int g = scalar(lin / a.hkv);
-  for (int j0 = 0; j0 < a.batch; j0 += 8) {
-    int cu[9];
-#pragma unroll
-    for (int i = 0; i < 9; ++i) cu[i] = a.cu_q[min(j0 + i, a.batch)];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int len = cu[i + 1] - cu[i];  // 0 past the last sequence
-      const int nb = len > 0 ? (int)(((int64_t)len * a.group + BM - 1) / BM) : 0;
-      if (g < nb) {
-        b = scalar(j0 + i);
-        mb = scalar(nb - 1 - g);
-        return true;
-      }
-      g -= nb;
+  const int lane = (int)(threadIdx.x & 63);
+  for (int j0 = 0; j0 < a.batch; j0 += 64) {
+    const int j = j0 + lane;
+    const int ja = min(j, a.batch), jb = min(j + 1, a.batch);
+    const int q0 = a.cu_q[ja], q1 = a.cu_q[jb];
+    const int k0 = a.cu_k != nullptr ? a.cu_k[ja] : 0;
+    const int k1 = a.cu_k != nullptr ? a.cu_k[jb] : 0;
+    const int used = a.seqused_k != nullptr ? a.seqused_k[min(j, a.batch - 1)] : 0;
+    const int len = q1 - q0;  // 0 past the last sequence
+    const int nb = len > 0 ? (int)(((int64_t)len * a.group + BM - 1) / BM) : 0;
+    const int incl = wave_incl_sum(nb);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > g);
+    if (hit != 0) {
+      const int l = scalar(__builtin_ctzll(hit));
+      b = scalar(j0 + l);
+      mb = scalar(__builtin_amdgcn_readlane(incl, l) - 1 - g);
+      seq.q0 = scalar(__builtin_amdgcn_readlane(q0, l));
+      seq.q1 = scalar(__builtin_amdgcn_readlane(q1, l));
+      seq.k0 = scalar(__builtin_amdgcn_readlane(k0, l));
+      seq.k1 = scalar(__builtin_amdgcn_readlane(k1, l));
+      seq.used = scalar(__builtin_amdgcn_readlane(used, l));
+      return true;
     }
+    g -= scalar(__builtin_amdgcn_readlane(incl, 63));
   }
   return false;
 }
@@ -101,18 +134,18 @@ __device__ __forceinline__ bool fwd_work_item(const FwdArgs& a, int& hk, int& b,
 // PAGED is a compile-time copy of (a.page_table != nullptr): the dense
 // kernels carry no paging code.
 template <bool PAGED>
-__device__ __forceinline__ void fwd_kv_extent(const FwdArgs& a, int b, int& sk, int64_t& k_base,
-                                              int64_t& v_base) {
+__device__ __forceinline__ void fwd_kv_extent(const FwdArgs& a, int b, const FwdSeq& seq, int& sk,
+                                              int64_t& k_base, int64_t& v_base) {
   if constexpr (PAGED) {
     const int cap = a.max_pages * a.page_size;
-    sk = a.seqused_k != nullptr ? min(max(a.seqused_k[b], 0), cap) : cap;
+    const int used = a.seqused_k == nullptr ? cap : a.cu_q != nullptr ? seq.used : a.seqused_k[b];
+    sk = min(max(used, 0), cap);
     k_base = 0;
     v_base = 0;
   } else if (a.cu_k != nullptr) {
-    const int k_tok0 = a.cu_k[b];
-    sk = a.cu_k[b + 1] - k_tok0;
-    k_base = (int64_t)k_tok0 * a.k_rs;
-    v_base = (int64_t)k_tok0 * a.v_rs;
+    sk = seq.k1 - seq.k0;
+    k_base = (int64_t)seq.k0 * a.k_rs;
+    v_base = (int64_t)seq.k0 * a.v_rs;
   } else {
     sk = a.seqlen_k;
     k_base = (int64_t)b * a.k_bs;

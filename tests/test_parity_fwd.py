@@ -80,13 +80,13 @@ VARLEN_CASES = [
     ("window", [513, 77, 1030, 5], None, True, 64, 0, 8, 4, 128),
     ("cross_lengths_noncausal", [10, 200, 0, 33], [50, 20, 7, 0], False, None, None, 4, 1, 64),
     ("d256_causal", [100, 260], None, True, None, None, 4, 2, 256),
-    # more than eight sequences: the block search walks the lengths eight at a
-    # time; empty sequences in both chunks
+    # more than eight sequences, empty ones among them
     ("many_sequences", [33, 0, 257, 5, 128, 1, 0, 96, 300, 64, 0, 17, 200, 2, 129, 40, 0, 90, 11],
      None, True, None, None, 8, 2, 128),
     ("many_sequences_d256", [65, 0, 3, 140, 1, 0, 77, 129, 12, 200, 0], None, True, None, None,
      4, 2, 256),
-    # many short sequences with empty ones and the longest last (a row with two
+    # more sequences than a wave has lanes (the block search takes 64 per
+    # step), many short with empty ones and the longest last (a row with two
     # visible keys here is where bf16 P rounding passes 1e-2: tests/gpu_util.py)
     ("over_64_sequences", [(i * 37) % 97 if i % 11 else 0 for i in range(149)] + [390],
      None, True, None, None, 8, 2, 128),

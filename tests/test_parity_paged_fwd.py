@@ -48,6 +48,10 @@ CASES = [
     ("d128_full_rows_no_seqused", 2, 8, 2, 128, 128, 2, None, 100, True, None, None),
     ("d128_packed_q", 4, 8, 2, 128, 64, 5, [300, 0, 190, 64], [100, 7, 0, 64], True, None, None),
     ("d256_packed_q_window", 3, 4, 2, 256, 128, 3, [380, 128, 250], [90, 128, 1], True, 60, None),
+    # more sequences than a wave has lanes: the work-item search reads
+    # cu_seqlens_q and seqused_k 64 sequences at a time
+    ("d128_packed_q_over_64_seqs", 70, 4, 2, 128, 64, 2, [(i * 29) % 128 for i in range(70)],
+     [min((i * 13) % 21 if i % 9 else 0, (i * 29) % 128) for i in range(70)], True, None, None),
 ]
 
 
