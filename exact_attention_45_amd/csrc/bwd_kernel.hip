@@ -309,13 +309,21 @@ void bwd_dq_kernel(const BwdArgs a) {
     }
     // element (kb, v) holds key n0 + 4*half + 32*kb + 8*(v>>2) + (v&3)
     const uint64_t vis = vis64(lo - n0 - 4 * half, hi - n0 - 4 * half);
+    // the mask runs only on tiles where some lane of the wave has a key
+    // outside its visible range (edge tiles; a wave-uniform branch)
+    const bool edge = __builtin_amdgcn_ballot_w64(vis != ~0ull) != 0;
+    auto mask = [&](int kb) __attribute__((always_inline)) {
+      if (edge) {
+        const uint32_t w = (uint32_t)(vis >> (32 * kb));
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb][v] = mask_by_bit(s[kb][v], w, 8 * (v >> 2) + (v & 3));
+      }
+    };
     // dS^T elements [e0, e1) of block kb, in place of S^T
     auto ds = [&](int kb, int e0, int e1) __attribute__((always_inline)) {
-      const uint32_t w = (uint32_t)(vis >> (32 * kb));
 #pragma unroll
       for (int v = e0; v < e1; ++v) {
-        const float x = mask_by_bit(s[kb][v], w, 8 * (v >> 2) + (v & 3));
-        const float p = fast_exp2(fmaf(x, c, -lse2));
+        const float p = fast_exp2(fmaf(s[kb][v], c, -lse2));
         s[kb][v] = p * (dp[kb][v] - dps);
       }
     };
@@ -340,10 +348,14 @@ void bwd_dq_kernel(const BwdArgs a) {
           dp[kb] = mfma32(f, gf[i >> 1], dp[kb]);
         else
           s[kb] = mfma32(f, qf[i >> 1], s[kb]);
-        if (kb == 1) ds(0, 16 * i / NS, 16 * (i + 1) / NS);
+        if (kb == 1) {
+          if (i == 0) mask(0);
+          ds(0, 16 * i / NS, 16 * (i + 1) / NS);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    mask(1);
     bf16x8 dsf[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -614,13 +626,21 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         l4[qb][i] = *reinterpret_cast<const f32x4*>(l2s + qo);
         d4[qb][i] = *reinterpret_cast<const f32x4*>(dss + qo);
       }
+    // the mask runs only on tiles where some lane of the wave has a query
+    // outside its visible range (edge tiles; a wave-uniform branch)
+    const bool edge = __builtin_amdgcn_ballot_w64(vis != ~0ull) != 0;
+    auto mask = [&](int qb) __attribute__((always_inline)) {
+      if (edge) {
+        const uint32_t w = (uint32_t)(vis >> (32 * qb));
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[qb][v] = mask_by_bit(s[qb][v], w, 8 * (v >> 2) + (v & 3));
+      }
+    };
     // softmax elements [e0, e1) of block qb: P, then dS in place of dP
     auto sm = [&](int qb, int e0, int e1) __attribute__((always_inline)) {
-      const uint32_t w = (uint32_t)(vis >> (32 * qb));
 #pragma unroll
       for (int v = e0; v < e1; ++v) {
-        const float x = mask_by_bit(s[qb][v], w, 8 * (v >> 2) + (v & 3));
-        const float p = fast_exp2(fmaf(x, c, -l4[qb][v >> 2][v & 3]));
+        const float p = fast_exp2(fmaf(s[qb][v], c, -l4[qb][v >> 2][v & 3]));
         s[qb][v] = p;
         dp[qb][v] = p * (dp[qb][v] - d4[qb][v >> 2][v & 3]);
       }
@@ -646,10 +666,14 @@ void bwd_dkdv_kernel(const BwdArgs a) {
           dp[qb] = mfma32(f, vf[i >> 1], dp[qb]);
         else
           s[qb] = mfma32(f, kf[i >> 1], s[qb]);
-        if (qb == 1) sm(0, 16 * i / NS, 16 * (i + 1) / NS);
+        if (qb == 1) {
+          if (i == 0) mask(0);
+          sm(0, 16 * i / NS, 16 * (i + 1) / NS);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    mask(1);
     bf16x8 pf[4], dsf[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
