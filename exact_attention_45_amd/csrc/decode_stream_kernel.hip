@@ -55,10 +55,11 @@ namespace mi_attn {
 template <int D, int KV>
 struct StreamCfg {
   static constexpr bool FP8 = KV != 0;
-  // K/V register sets per wave. Three for fp8 as well: with half the bytes
-  // per slice, 4 or 6 sets in flight measured slower (110 and 128 us against
-  // 96 us for the B16 Sk32768 fp8 workload).
-  static constexpr int NS = 3;
+  // K/V register sets per wave. fp8 slices carry half the bytes, yet more
+  // fp8 sets in flight measured slower on the B16 Sk32768 workload (split +
+  // combine: 2 sets 86.0-87.3 us, 3 sets 87.3-88.5, 4 sets 101, 5 sets 115);
+  // bf16 measured the same with 2 or 3.
+  static constexpr int NS = FP8 ? 2 : 3;
   static constexpr float RESCALE_LOG2 = 8.0f;   // lazy-rescale threshold
   static constexpr int SLICE = 32;              // keys per slice
   static constexpr int ROW_B = D * 2;           // bytes per bf16 K/V row (LDS)
