@@ -615,9 +615,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     }
     // element (qb, v) holds query m0 + 4*half + 32*qb + 8*(v>>2) + (v&3), key `key`
     const uint64_t vis = vis64(qlo - m0 - 4 * half, qhi - m0 - 4 * half);
+    // row statistics of query block qb, read from LDS a few matrix
+    // instructions before the block's softmax slices need them (so they are
+    // not live through the other block's work)
     f32x4 l4[2][4], d4[2][4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    auto load_stats = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int qo = 32 * qb + 8 * i + 4 * half;
@@ -626,6 +628,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         l4[qb][i] = *reinterpret_cast<const f32x4*>(l2s + qo);
         d4[qb][i] = *reinterpret_cast<const f32x4*>(dss + qo);
       }
+    };
     // the mask runs only on tiles where some lane of the wave has a query
     // outside its visible range (edge tiles; a wave-uniform branch)
     const bool edge = __builtin_amdgcn_ballot_w64(vis != ~0ull) != 0;
@@ -666,6 +669,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
           dp[qb] = mfma32(f, vf[i >> 1], dp[qb]);
         else
           s[qb] = mfma32(f, kf[i >> 1], s[qb]);
+        if (g == NS - 4) load_stats(0);
+        if (g == N - 4) load_stats(1);
         if (qb == 1) {
           if (i == 0) mask(0);
           sm(0, 16 * i / NS, 16 * (i + 1) / NS);
