@@ -92,6 +92,12 @@ VARLEN_CASES = [
      None, True, None, None, 8, 2, 128),
     ("over_64_sequences_window_d256", [(i * 53) % 131 if i % 7 else 0 for i in range(70)] + [300],
      None, True, 100, 0, 4, 2, 256),
+    # exactly one wave of sequences, and one more (the second search step
+    # holds a single sequence)
+    ("exactly_64_sequences", [(i * 41) % 90 + 1 for i in range(64)], None, True, None, None, 8, 2,
+     128),
+    ("65_sequences_last_alone", [(i * 29) % 70 for i in range(64)] + [257], None, True, None, None,
+     4, 4, 128),
 ]
 
 
