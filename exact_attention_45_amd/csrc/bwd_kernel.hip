@@ -190,7 +190,19 @@ void bwd_dq_kernel(const BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, half = lane >> 5;
-  const int mb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  // Work item: heavy (late) query blocks first, (KV head, sequence) fastest.
+  // Workgroups are dispatched in linear order and dealt round-robin to the
+  // XCDs, so consecutive ones take different KV heads: each XCD's L2 holds
+  // the K/V of few heads, and the longest causal blocks start first.
+  int mb, hk, b;
+  {
+    const int nhb = a.hkv * a.batch;
+    const int lin = uniform((int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)));
+    const int hb = uniform(lin % nhb);
+    mb = uniform((int)gridDim.x - 1 - lin / nhb);
+    hk = uniform(hb % a.hkv);
+    b = uniform(hb / a.hkv);
+  }
 
   int sq = a.seqlen_q, sk = a.seqlen_k, q_tok0 = 0;
   int64_t q_base, do_base, dq_base, k_base, v_base;
