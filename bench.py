@@ -439,8 +439,8 @@ def backward_workloads(mi, W, torch, args, runs, ws):
 
 def extra_workloads(mi, W, torch, args, extra):
     """--all-configs: head dims 96/192, paged prefill, softcap, the multi-token
-    decode step and fp8 decode (median of event-timed launches, stderr and
-    "other_workloads")."""
+    decode step, fp8 decode and the tile decode kernel at D192/D256 (median of
+    event-timed launches, stderr and "other_workloads")."""
     n = max(5, args.steps)
     paged = W.paged_prefill_case(1002, 1, 32, 4, 128, 256, 16, None, seqlen_q=4096,
                                  causal=True, name="paged256_causal_gqa32x4_s4096_d128")
@@ -490,6 +490,22 @@ def extra_workloads(mi, W, torch, args, extra):
                           "bytes_per_launch": decode_bytes(w8)}
         log(f"[bench] {w8.name}: {med * 1e3:.1f} us, {gb:.0f} GB/s")
         del d8, w8
+        torch.cuda.empty_cache()
+    # head dims the streaming decode kernel does not take (the tile kernel):
+    # B8 Hq32 Hkv4 Sk16384 with 256-token pages, the heuristic's split count
+    for wd in (W.paged_decode_case(1008, 8, 32, 4, 256, 256, 64,
+                                   name="paged_decode_b8_gqa32x4_sk16384_d256"),
+               W.paged_decode_case(1009, 8, 32, 4, 192, 256, 64,
+                                   name="paged_decode_b8_gqa32x4_sk16384_d192"),
+               W.paged_decode_fp8_case(1010, 8, 32, 4, 256, 256, 64,
+                                       name="paged_decode_fp8_b8_sk16384_d256", fmt="e4m3")):
+        dd = Decode(mi, wd, torch)
+        med = timed_extra(torch, dd, n)
+        gb = decode_bytes(wd) / (med * 1e-3) / 1e9
+        extra[wd.name] = {"median_us": med * 1e3, "gbs": gb, "frac": gb / PEAK_HBM_GBS,
+                          "bytes_per_launch": decode_bytes(wd)}
+        log(f"[bench] {wd.name}: {med * 1e3:.1f} us, {gb:.0f} GB/s")
+        del dd, wd
         torch.cuda.empty_cache()
 
 
