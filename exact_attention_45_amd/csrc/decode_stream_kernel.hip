@@ -1,6 +1,6 @@
 // Split-KV decode over a paged K/V cache: per-wave streaming variant, used
 // when every aligned 32-key slice lies inside one page (page_size a multiple
-// of 32) and head_dim is 64 or 128.
+// of 32) and head_dim is 64, 128 or 256.
 //
 // Same method as decode_kernel.hip (split-K decoding page, triton_splitk.py
 // `FwOp.apply`; interface page, the num_splits path of `_flash_attn_fwd`):
@@ -58,8 +58,9 @@ struct StreamCfg {
   // K/V register sets per wave. fp8 slices carry half the bytes, yet more
   // fp8 sets in flight measured slower on the B16 Sk32768 workload (split +
   // combine: 2 sets 86.0-87.3 us, 3 sets 87.3-88.5, 4 sets 101, 5 sets 115);
-  // bf16 measured the same with 2 or 3.
-  static constexpr int NS = FP8 ? 2 : 3;
+  // bf16 measured the same with 2 or 3. A bf16 set at D = 256 is 128
+  // registers (32 KB per slice), next to O's 128 and Q's 64: one set.
+  static constexpr int NS = D == 256 ? 1 : (FP8 ? 2 : 3);
   static constexpr float RESCALE_LOG2 = 8.0f;   // lazy-rescale threshold
   static constexpr int SLICE = 32;              // keys per slice
   static constexpr int ROW_B = D * 2;           // bytes per bf16 K/V row (LDS)
@@ -194,21 +195,25 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   const int ld_c = lane % CPR;
   const uint32_t ld_off = (uint32_t)(ld_r * ts2 + ld_c * 16);
   // K slot: chunk c of row r at position c ^ kswz(r), conflict-free for the
-  // fragment reads (16 lanes read one logical chunk of 16 consecutive keys);
-  // V slot: chunk c at vswz(r, c), for the transposing reads
+  // fragment reads (16 lanes read one logical chunk of 16 consecutive keys:
+  // 16 distinct positions within a 256-byte bank window at D >= 128, whose
+  // rows are whole multiples of it); V slot: chunk c at vswz(r, c), for the
+  // transposing reads
   auto kswz = [](int key) {
-    return D == 128 ? (((key & 3) << 1) | ((key >> 2) & 1) | (((key >> 3) & 1) << 3)) : ((key >> 1) & 7);
+    return D >= 128 ? (((key & 3) << 1) | ((key >> 2) & 1) | (((key >> 3) & 1) << 3)) : ((key >> 1) & 7);
   };
   char* kslot = smem + wave * 2 * SLICE_B;
   char* vslot = kslot + SLICE_B;
-  // over the load instructions u, kswz(row) repeats with period 4 and
-  // vswz(row, .) with period 2
-  int k_st[4], v_st[2];
+  // over the load instructions u (rows RPL*u + ld_r), kswz(row), a function
+  // of key bits 0..3, repeats with period KP and vswz(row, .) (bits 0..2)
+  // with period VP
+  constexpr int KP = RPL >= 16 ? 1 : 16 / RPL, VP = RPL >= 8 ? 1 : 8 / RPL;
+  int k_st[KP], v_st[VP];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
+  for (int p = 0; p < KP; ++p) {
     const int row = RPL * p + ld_r;
     k_st[p] = row * ROW_B + ((ld_c ^ kswz(row)) * 16);
-    if (p < 2) v_st[p] = row * ROW_B + vswz<D>(row, ld_c) * 16;
+    if (p < VP) v_st[p] = row * ROW_B + vswz<D>(row, ld_c) * 16;
   }
   const int fk = kswz(c32);
   int k_rd[D / 16];
@@ -254,8 +259,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
     if constexpr (!FP8) {
 #pragma unroll
       for (int u = 0; u < NLD; ++u) {
-        *reinterpret_cast<uint4*>(kslot + k_st[u & 3] + (u >> 2) * 4 * RPL * ROW_B) = kreg[slot][u];
-        *reinterpret_cast<uint4*>(vslot + v_st[u & 1] + (u >> 1) * 2 * RPL * ROW_B) = vreg[slot][u];
+        *reinterpret_cast<uint4*>(kslot + k_st[u % KP] + (u / KP) * KP * RPL * ROW_B) = kreg[slot][u];
+        *reinterpret_cast<uint4*>(vslot + v_st[u % VP] + (u / VP) * VP * RPL * ROW_B) = vreg[slot][u];
       }
     } else {
       // 16 fp8 values = dims 16*ld_c .. +15 of row RPL*u + ld_r: bf16
@@ -408,7 +413,9 @@ hipError_t launch_decode_stream_fp8(const DecodeArgs& a, hipStream_t s) {
 
 template hipError_t launch_decode_stream<64>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream<128>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode_stream<256>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream_fp8<64>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream_fp8<128>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode_stream_fp8<256>(const DecodeArgs&, hipStream_t);
 
 }  // namespace mi_attn
