@@ -513,7 +513,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombineArgs a) {
 
 template <int D>
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  if constexpr (D == 64 || D == 128 || D == 256) {
+  if constexpr (D != 96) {
     if (decode_streams(D, a.page_size))
       return a.kv_fp8 ? launch_decode_stream_fp8<D>(a, s) : launch_decode_stream<D>(a, s);
   }

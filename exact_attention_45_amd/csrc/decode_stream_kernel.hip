@@ -1,6 +1,6 @@
 // Split-KV decode over a paged K/V cache: per-wave streaming variant, used
 // when every aligned 32-key slice lies inside one page (page_size a multiple
-// of 32) and head_dim is 64, 128 or 256.
+// of 32) and head_dim is 64, 128, 192 or 256.
 //
 // Same method as decode_kernel.hip (split-K decoding page, triton_splitk.py
 // `FwOp.apply`; interface page, the num_splits path of `_flash_attn_fwd`):
@@ -55,19 +55,24 @@ namespace mi_attn {
 template <int D, int KV>
 struct StreamCfg {
   static constexpr bool FP8 = KV != 0;
+  // D = 192 runs in the layout of 256 (LDS rows, fragments, accumulators):
+  // the lanes of a row's last 64 columns load nothing new and stage zeros,
+  // and only the first D output columns are written
+  static constexpr int DL = D == 192 ? 256 : D;
   // K/V register sets per wave. fp8 slices carry half the bytes, yet more
   // fp8 sets in flight measured slower on the B16 Sk32768 workload (split +
   // combine: 2 sets 86.0-87.3 us, 3 sets 87.3-88.5, 4 sets 101, 5 sets 115);
   // bf16 measured the same with 2 or 3. A bf16 set at D = 256 is 128
   // registers (32 KB per slice), next to O's 128 and Q's 64: one set.
-  static constexpr int NS = D == 256 ? 1 : (FP8 ? 2 : 3);
+  static constexpr int NS = DL == 256 ? 1 : (FP8 ? 2 : 3);
   static constexpr float RESCALE_LOG2 = 8.0f;   // lazy-rescale threshold
   static constexpr int SLICE = 32;              // keys per slice
-  static constexpr int ROW_B = D * 2;           // bytes per bf16 K/V row (LDS)
+  static constexpr int ROW_B = DL * 2;          // bytes per bf16 K/V row (LDS)
   static constexpr int SLICE_B = SLICE * ROW_B; // bytes per K (or V) slice in LDS
   static constexpr int GROW_B = FP8 ? D : D * 2; // bytes per K/V row in the cache
   static constexpr int CPR = GROW_B / 16;       // 16-byte chunks per cache row
-  static constexpr int RPL = 64 / CPR;          // rows per load instruction
+  static constexpr int LPR = (FP8 ? DL : DL * 2) / 16;  // lanes per row of a load
+  static constexpr int RPL = 64 / LPR;          // rows per load instruction
   static constexpr int NLD = SLICE / RPL;       // load instructions per tensor per slice
   static constexpr int SLOT_B = 4 * 2 * SLICE_B; // K and V slots of the four waves
   static constexpr int LDS_B = SLOT_B;
@@ -104,7 +109,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   constexpr bool FP8 = KV != 0;
   using C = StreamCfg<D, KV>;
   constexpr int NS = C::NS, ROW_B = C::ROW_B, SLICE_B = C::SLICE_B, CPR = C::CPR;
-  constexpr int RPL = C::RPL, NLD = C::NLD, GROW_B = C::GROW_B;
+  constexpr int RPL = C::RPL, NLD = C::NLD, GROW_B = C::GROW_B, DL = C::DL, LPR = C::LPR;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_B];
 
   const int tid = threadIdx.x;
@@ -155,16 +160,17 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   // ---- this lane's query row (MFMA B operand)
   const bool valid = row.valid;
   const __bf16* qp = static_cast<const __bf16*>(a.q) + row.token * a.q_bs + (int64_t)row.hq * a.q_hs;
-  bf16x8 qf[D / 16];
+  bf16x8 qf[DL / 16];
 #pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) {
-    const bf16x8 x = as_bf16x8(ld16(qp + 16 * cc + 8 * half));
-    qf[cc] = valid ? x : zero_bf16x8();
+  for (int cc = 0; cc < DL / 16; ++cc) {
+    const int e0 = 16 * cc + 8 * half;  // columns past D (layout padding) are zero
+    const bf16x8 x = as_bf16x8(ld16(qp + (e0 < D ? e0 : 0)));
+    qf[cc] = valid && e0 < D ? x : zero_bf16x8();
   }
 
-  f32x16 o[D / 32];
+  f32x16 o[DL / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) o[i] = zero_f32x16();
+  for (int i = 0; i < DL / 32; ++i) o[i] = zero_f32x16();
   float m_run = kNegInf;
   float l_run = 0.0f;
   // fp8: the key descale joins the score scale, the value descale the output
@@ -190,10 +196,12 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)hk * GROW_B;
   const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
   // loads: instruction u covers slice rows RPL*u .. +RPL-1, lane j row
-  // RPL*u + j / CPR at chunk j % CPR
-  const int ld_r = lane / CPR;
-  const int ld_c = lane % CPR;
-  const uint32_t ld_off = (uint32_t)(ld_r * ts2 + ld_c * 16);
+  // RPL*u + j / LPR at chunk j % LPR; a lane whose chunk lies past the row
+  // (D = 192) gets an offset past every descriptor's end, so its loads touch
+  // no memory and return zeros, which it stages as the layout's padding
+  const int ld_r = lane / LPR;
+  const int ld_c = lane % LPR;
+  const uint32_t ld_off = ld_c < CPR ? (uint32_t)(ld_r * ts2 + ld_c * 16) : 0x80000000u;
   // K slot: chunk c of row r at position c ^ kswz(r), conflict-free for the
   // fragment reads (16 lanes read one logical chunk of 16 consecutive keys:
   // 16 distinct positions within a 256-byte bank window at D >= 128, whose
@@ -213,12 +221,16 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   for (int p = 0; p < KP; ++p) {
     const int row = RPL * p + ld_r;
     k_st[p] = row * ROW_B + ((ld_c ^ kswz(row)) * 16);
-    if (p < VP) v_st[p] = row * ROW_B + vswz<D>(row, ld_c) * 16;
+    if (p < VP) v_st[p] = row * ROW_B + vswz<DL>(row, ld_c) * 16;
   }
   const int fk = kswz(c32);
-  int k_rd[D / 16];
+  // fragment cc reads chunk 2*cc + half; kswz only moves chunks within a
+  // 256-byte window (16 chunks), so fragments cc and cc + 8 differ by 256
+  // bytes and eight address registers serve D = 256
+  constexpr int NKR = DL / 16 < 8 ? DL / 16 : 8;
+  int k_rd[NKR];
 #pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) k_rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ fk) * 16);
+  for (int cc = 0; cc < NKR; ++cc) k_rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ fk) * 16);
 
   uint4 kreg[NS][NLD];
   uint4 vreg[NS][NLD];
@@ -250,6 +262,15 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   const int tr_key = tr_j >> 2;
   const int tr_c = (tr_g & 1) * 2 + ((tr_j & 3) >> 1);
   const int tr_e = (tr_j & 1) * 8;
+  // a transposing read of keys k = 16 tt + v_key (+ 8) at chunk 4 db + tr_c:
+  // vswz depends on key bits 0..2 only, which the offsets 16 tt and 8 keep,
+  // and moves chunks within a 16-chunk window, so d-blocks db and db + 4
+  // differ by 256 bytes: NVR address registers serve every (db, tt)
+  const int v_key = 4 * half + tr_key;
+  constexpr int NVR = DL / 32 < 4 ? DL / 32 : 4;
+  int v_rd[NVR];
+#pragma unroll
+  for (int j = 0; j < NVR; ++j) v_rd[j] = v_key * ROW_B + vswz<DL>(v_key, 4 * j + tr_c) * 16 + tr_e;
 
   // K and V rows of register set `slot` into this wave's LDS slots (LDS
   // operations of one wave complete in order, so the previous slice's reads
@@ -277,8 +298,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
         char* vr = vslot + row * ROW_B;
         *reinterpret_cast<uint4*>(kr + (((2 * ld_c) ^ kswz(row)) * 16)) = make_uint4(k0.x, k0.y, k1.x, k1.y);
         *reinterpret_cast<uint4*>(kr + (((2 * ld_c + 1) ^ kswz(row)) * 16)) = make_uint4(k2.x, k2.y, k3.x, k3.y);
-        *reinterpret_cast<uint4*>(vr + vswz<D>(row, 2 * ld_c) * 16) = make_uint4(v0.x, v0.y, v1.x, v1.y);
-        *reinterpret_cast<uint4*>(vr + vswz<D>(row, 2 * ld_c + 1) * 16) = make_uint4(v2.x, v2.y, v3.x, v3.y);
+        *reinterpret_cast<uint4*>(vr + vswz<DL>(row, 2 * ld_c) * 16) = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        *reinterpret_cast<uint4*>(vr + vswz<DL>(row, 2 * ld_c + 1) * 16) = make_uint4(v2.x, v2.y, v3.x, v3.y);
       }
     }
   };
@@ -288,8 +309,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
     const char* vs = vslot;
     f32x16 s = zero_f32x16();
 #pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc)
-      s = mfma32(*reinterpret_cast<const bf16x8*>(kslot + k_rd[cc]), qf[cc], s);
+    for (int cc = 0; cc < DL / 16; ++cc)
+      s = mfma32(*reinterpret_cast<const bf16x8*>(kslot + k_rd[cc % NKR] + (cc / NKR) * 256), qf[cc], s);
     if constexpr (SC) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = softcap_raw(s[v], sc_k1x, sc_k2);
@@ -343,13 +364,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const int k0 = 16 * tt + 4 * half + tr_key;
-        const int k1 = k0 + 8;
-        const int cc = 4 * db + tr_c;
-        const bf16x4 v0 = ds_read_tr16(
-            reinterpret_cast<const __bf16*>(vs + k0 * ROW_B + vswz<D>(k0, cc) * 16 + tr_e));
-        const bf16x4 v1 = ds_read_tr16(
-            reinterpret_cast<const __bf16*>(vs + k1 * ROW_B + vswz<D>(k1, cc) * 16 + tr_e));
+        // keys 16 tt + v_key and that + 8, chunk 4 db + tr_c (see v_rd)
+        const char* p = vs + v_rd[db % NVR] + (db / NVR) * 256 + 16 * tt * ROW_B;
+        const bf16x4 v0 = ds_read_tr16(reinterpret_cast<const __bf16*>(p));
+        const bf16x4 v1 = ds_read_tr16(reinterpret_cast<const __bf16*>(p + 8 * ROW_B));
         o[db] = mfma32(cat(v0, v1), pf[tt], o[db]);
       }
     }
@@ -413,9 +431,11 @@ hipError_t launch_decode_stream_fp8(const DecodeArgs& a, hipStream_t s) {
 
 template hipError_t launch_decode_stream<64>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream<128>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode_stream<192>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream<256>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream_fp8<64>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream_fp8<128>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode_stream_fp8<192>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream_fp8<256>(const DecodeArgs&, hipStream_t);
 
 }  // namespace mi_attn

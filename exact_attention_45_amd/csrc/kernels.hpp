@@ -276,10 +276,11 @@ constexpr int kFwdPPBlockM = 256; // ping-pong kernel, D = 64/128 (8 waves x 32)
 constexpr int kFwdBlockN = 64;    // keys per K/V tile
 constexpr int kDecBlockN = 128;   // keys per decode tile (4 waves x 32)
 
-// The per-wave streaming decode kernel serves head_dim 64, 128 and 256 when
-// every aligned 32-key slice lies in one page; the tile kernel serves the rest.
+// The per-wave streaming decode kernel serves head_dim 64, 128, 192 and 256
+// when every aligned 32-key slice lies in one page; the tile kernel serves the
+// rest (head_dim 96, other page sizes).
 constexpr bool decode_streams(int head_dim, int page_size) {
-  return (head_dim == 64 || head_dim == 128 || head_dim == 256) && page_size % 32 == 0;
+  return head_dim != 96 && page_size % 32 == 0;
 }
 
 template <int D> hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t s);

@@ -42,11 +42,16 @@ CASES = [
     ("more_splits_than_tiles", 1, 8, 1, 128, 64, 2, 0, [100], 64, None),
     ("window_left", 2, 16, 4, 128, 128, 6, 2, [700, 90], 4, 200),
     ("gqa3_nonpow2", 2, 6, 2, 128, 256, 2, 0, [400, 512], 2, None),
-    # head dims 96 and 192 (the tile kernel at the LDS width of 128 / 256)
+    # head dim 96 (the tile kernel at the LDS width of 128); 192 (the
+    # streaming kernel at the width of 256 when the page size is a multiple
+    # of 32, else the tile kernel)
     ("d96_page16_gqa4", 2, 8, 2, 96, 16, 30, 2, [480, 37], 6, None),
     ("d96_page256_mha", 1, 4, 4, 96, 256, 3, 0, [700], 4, None),
     ("d192_page64_window", 2, 8, 1, 192, 64, 6, 1, [380, 64], 3, 150),
     ("d192_page32_ragged", 3, 16, 2, 192, 32, 10, 0, [1, 320, 129], 5, None),
+    # the tile kernel at head dims 192 and 256 (page sizes not multiples of 32)
+    ("d192_page16_tile", 2, 16, 2, 192, 16, 25, 0, [390, 17], 4, None),
+    ("d256_page48_tile", 2, 8, 2, 256, 48, 8, 1, [380, 47], 3, None),
 ]
 
 
@@ -183,7 +188,8 @@ VARLEN_CASES = [
     ("window_causal_mha", 2, 4, 4, 128, 64, 6, [384, 200], [8, 6], 3, True, 50),
     ("gqa32_rows_span_blocks", 2, 32, 1, 128, 64, 4, [256, 77], [8, 3], 2, True, None),
     ("more_tokens_than_keys", 1, 8, 2, 128, 64, 2, [3], [6], 2, True, None),
-    ("d256_tile_path", 2, 8, 2, 256, 32, 9, [288, 100], [3, 2], 5, True, None),
+    ("d256_stream_path", 2, 8, 2, 256, 32, 9, [288, 100], [3, 2], 5, True, None),
+    ("d256_page48_tile_path", 2, 8, 2, 256, 48, 8, [380, 47], [4, 2], 3, True, None),
     ("page48_tile_path", 2, 8, 2, 128, 48, 8, [380, 47], [5, 1], 3, True, 100),
     ("d96_spec_causal", 2, 8, 2, 96, 64, 5, [300, 17], [4, 2], 3, True, None),
     ("d192_spec_window", 2, 8, 2, 192, 32, 9, [288, 100], [3, 5], 4, True, 60),

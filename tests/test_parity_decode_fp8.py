@@ -58,13 +58,15 @@ CASES = [
     ("gqa32_heuristic_splits", 2, 32, 1, 128, 128, 8, 1, [1024, 333], 0, None, True),
     ("window_left", 2, 8, 2, 128, 256, 4, 0, [900, 300], 3, 150, True),
     ("empty_and_tiny", 4, 8, 2, 64, 64, 3, 0, [0, 1, 64, 65], 8, None, True),
-    # the tile kernel: head dims 96 / 192 / 256 and page sizes that are not
-    # multiples of 32
-    ("tile_d256_page32", 2, 8, 2, 256, 32, 9, 1, [288, 100], 5, None, True),
+    # the streaming kernel at head dims 192 (in the width of 256) and 256
+    ("stream_d256_page32", 2, 8, 2, 256, 32, 9, 1, [288, 100], 5, None, True),
+    ("stream_d192_page64_gqa8", 2, 16, 2, 192, 64, 6, 1, [350, 130], 4, None, True),
+    # the tile kernel: head dim 96 and page sizes that are not multiples of 32
     ("tile_page16_d128", 2, 16, 2, 128, 16, 30, 2, [470, 33], 6, None, True),
     ("tile_d96_page48_window", 2, 8, 2, 96, 48, 8, 0, [380, 47], 3, 100, True),
-    ("tile_d192_page64_gqa8", 2, 16, 2, 192, 64, 6, 1, [350, 130], 4, None, True),
     ("tile_page48_d64_empty", 3, 8, 4, 64, 48, 4, 0, [0, 150, 47], 2, None, False),
+    ("tile_d256_page48", 2, 8, 2, 256, 48, 8, 0, [380, 47], 3, None, True),
+    ("tile_d192_page16", 2, 16, 2, 192, 16, 25, 1, [390, 200], 4, None, True),
 ]
 
 
@@ -82,7 +84,7 @@ def test_fp8_decode_elementwise(gpu_lib, case):
 
 E5M2_CASES = [c for c in CASES if c[0] in ("gqa8_page256_ragged", "gqa4_page64_d64",
                                             "window_left", "empty_and_tiny",
-                                            "tile_d256_page32", "tile_d96_page48_window")]
+                                            "stream_d256_page32", "tile_d96_page48_window")]
 
 
 @pytest.mark.parametrize("case", E5M2_CASES, ids=[c[0] for c in E5M2_CASES])
