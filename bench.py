@@ -439,7 +439,7 @@ def backward_workloads(mi, W, torch, args, runs, ws):
 
 def extra_workloads(mi, W, torch, args, extra):
     """--all-configs: head dims 96/192, paged prefill, softcap, the multi-token
-    decode step, fp8 decode and the tile decode kernel at D192/D256 (median of
+    decode step, fp8 decode and the decode at D96/D192/D256 (median of
     event-timed launches, stderr and "other_workloads")."""
     n = max(5, args.steps)
     paged = W.paged_prefill_case(1002, 1, 32, 4, 128, 256, 16, None, seqlen_q=4096,
@@ -491,12 +491,14 @@ def extra_workloads(mi, W, torch, args, extra):
         log(f"[bench] {w8.name}: {med * 1e3:.1f} us, {gb:.0f} GB/s")
         del d8, w8
         torch.cuda.empty_cache()
-    # head dims the streaming decode kernel does not take (the tile kernel):
-    # B8 Hq32 Hkv4 Sk16384 with 256-token pages, the heuristic's split count
+    # the decode at head dims 96, 192, 256: B8 Hq32 Hkv4 Sk16384 with 256-token
+    # pages, the heuristic's split count
     for wd in (W.paged_decode_case(1008, 8, 32, 4, 256, 256, 64,
                                    name="paged_decode_b8_gqa32x4_sk16384_d256"),
                W.paged_decode_case(1009, 8, 32, 4, 192, 256, 64,
                                    name="paged_decode_b8_gqa32x4_sk16384_d192"),
+               W.paged_decode_case(1012, 8, 32, 4, 96, 256, 64,
+                                   name="paged_decode_b8_gqa32x4_sk16384_d96"),
                W.paged_decode_fp8_case(1010, 8, 32, 4, 256, 256, 64,
                                        name="paged_decode_fp8_b8_sk16384_d256", fmt="e4m3")):
         dd = Decode(mi, wd, torch)

@@ -513,10 +513,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombineArgs a) {
 
 template <int D>
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  if constexpr (D != 96) {
-    if (decode_streams(D, a.page_size))
-      return a.kv_fp8 ? launch_decode_stream_fp8<D>(a, s) : launch_decode_stream<D>(a, s);
-  }
+  if (decode_streams(D, a.page_size))
+    return a.kv_fp8 ? launch_decode_stream_fp8<D>(a, s) : launch_decode_stream<D>(a, s);
   const int64_t grid = (int64_t)a.batch * a.hkv * a.row_blocks * a.num_splits;
   if (grid <= 0) return hipSuccess;
   if (a.kv_fp8 == 2)

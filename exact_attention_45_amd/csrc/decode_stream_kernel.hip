@@ -1,6 +1,6 @@
 // Split-KV decode over a paged K/V cache: per-wave streaming variant, used
 // when every aligned 32-key slice lies inside one page (page_size a multiple
-// of 32) and head_dim is 64, 128, 192 or 256.
+// of 32), at every head dim (96 and 192 in the layouts of 128 and 256).
 //
 // Same method as decode_kernel.hip (split-K decoding page, triton_splitk.py
 // `FwOp.apply`; interface page, the num_splits path of `_flash_attn_fwd`):
@@ -55,10 +55,10 @@ namespace mi_attn {
 template <int D, int KV>
 struct StreamCfg {
   static constexpr bool FP8 = KV != 0;
-  // D = 192 runs in the layout of 256 (LDS rows, fragments, accumulators):
-  // the lanes of a row's last 64 columns load nothing new and stage zeros,
-  // and only the first D output columns are written
-  static constexpr int DL = D == 192 ? 256 : D;
+  // D = 96 and 192 run in the layouts of 128 and 256 (LDS rows, fragments,
+  // accumulators): the lanes of a row's padding columns load nothing and
+  // stage zeros, and only the first D output columns are written
+  static constexpr int DL = D == 192 ? 256 : (D == 96 ? 128 : D);
   // K/V register sets per wave. fp8 slices carry half the bytes, yet more
   // fp8 sets in flight measured slower on the B16 Sk32768 workload (split +
   // combine: 2 sets 86.0-87.3 us, 3 sets 87.3-88.5, 4 sets 101, 5 sets 115);
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   // rows are whole multiples of it); V slot: chunk c at vswz(r, c), for the
   // transposing reads
   auto kswz = [](int key) {
-    return D >= 128 ? (((key & 3) << 1) | ((key >> 2) & 1) | (((key >> 3) & 1) << 3)) : ((key >> 1) & 7);
+    return DL >= 128 ? (((key & 3) << 1) | ((key >> 2) & 1) | (((key >> 3) & 1) << 3)) : ((key >> 1) & 7);
   };
   char* kslot = smem + wave * 2 * SLICE_B;
   char* vslot = kslot + SLICE_B;
@@ -430,10 +430,12 @@ hipError_t launch_decode_stream_fp8(const DecodeArgs& a, hipStream_t s) {
 }
 
 template hipError_t launch_decode_stream<64>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode_stream<96>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream<128>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream<192>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream<256>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream_fp8<64>(const DecodeArgs&, hipStream_t);
+template hipError_t launch_decode_stream_fp8<96>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream_fp8<128>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream_fp8<192>(const DecodeArgs&, hipStream_t);
 template hipError_t launch_decode_stream_fp8<256>(const DecodeArgs&, hipStream_t);

@@ -276,11 +276,12 @@ constexpr int kFwdPPBlockM = 256; // ping-pong kernel, D = 64/128 (8 waves x 32)
 constexpr int kFwdBlockN = 64;    // keys per K/V tile
 constexpr int kDecBlockN = 128;   // keys per decode tile (4 waves x 32)
 
-// The per-wave streaming decode kernel serves head_dim 64, 128, 192 and 256
-// when every aligned 32-key slice lies in one page; the tile kernel serves the
-// rest (head_dim 96, other page sizes).
+// The per-wave streaming decode kernel serves every head dim when each
+// aligned 32-key slice lies in one page (page_size a multiple of 32); the
+// tile kernel serves the other page sizes.
 constexpr bool decode_streams(int head_dim, int page_size) {
-  return head_dim != 96 && page_size % 32 == 0;
+  (void)head_dim;
+  return page_size % 32 == 0;
 }
 
 template <int D> hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t s);
