@@ -42,9 +42,8 @@ CASES = [
     ("more_splits_than_tiles", 1, 8, 1, 128, 64, 2, 0, [100], 64, None),
     ("window_left", 2, 16, 4, 128, 128, 6, 2, [700, 90], 4, 200),
     ("gqa3_nonpow2", 2, 6, 2, 128, 256, 2, 0, [400, 512], 2, None),
-    # head dim 96 (the tile kernel at the LDS width of 128); 192 (the
-    # streaming kernel at the width of 256 when the page size is a multiple
-    # of 32, else the tile kernel)
+    # head dims 96 and 192 (in the layouts of 128 and 256: the streaming
+    # kernel when the page size is a multiple of 32, else the tile kernel)
     ("d96_page16_gqa4", 2, 8, 2, 96, 16, 30, 2, [480, 37], 6, None),
     ("d96_page256_mha", 1, 4, 4, 96, 256, 3, 0, [700], 4, None),
     ("d192_page64_window", 2, 8, 1, 192, 64, 6, 1, [380, 64], 3, 150),

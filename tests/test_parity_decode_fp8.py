@@ -61,7 +61,7 @@ CASES = [
     # the streaming kernel at head dims 192 (in the width of 256) and 256
     ("stream_d256_page32", 2, 8, 2, 256, 32, 9, 1, [288, 100], 5, None, True),
     ("stream_d192_page64_gqa8", 2, 16, 2, 192, 64, 6, 1, [350, 130], 4, None, True),
-    # the tile kernel: head dim 96 and page sizes that are not multiples of 32
+    # the tile kernel: page sizes that are not multiples of 32
     ("tile_page16_d128", 2, 16, 2, 128, 16, 30, 2, [470, 33], 6, None, True),
     ("tile_d96_page48_window", 2, 8, 2, 96, 48, 8, 0, [380, 47], 3, 100, True),
     ("tile_page48_d64_empty", 3, 8, 4, 64, 48, 4, 0, [0, 150, 47], 2, None, False),
@@ -99,7 +99,7 @@ def test_e5m2_decode_elementwise(gpu_lib, case):
     print(name, check(host_f64(out), o_ref, host_f64(lse), l_ref, what=name))
 
 
-@pytest.mark.parametrize("D,ps", [(128, 64), (256, 64), (96, 48)])  # stream, tile, tile
+@pytest.mark.parametrize("D,ps", [(128, 64), (256, 64), (96, 48), (256, 48)])  # stream, stream, tile, tile
 def test_e5m2_every_finite_code_decodes_exactly(gpu_lib, D, ps):
     """As the e4m3 case below for e5m2: each of its 248 finite codes placed in
     V comes back exactly (every e5m2 value is a bf16 value)."""
@@ -128,7 +128,7 @@ def test_fp8_mixed_formats_rejected(gpu_lib):
     assert e.value.code == gpu_lib.MI_ATTN_EINVAL
 
 
-@pytest.mark.parametrize("D,ps", [(128, 64), (256, 64), (192, 16)])  # stream, tile, tile
+@pytest.mark.parametrize("D,ps", [(128, 64), (256, 64), (192, 16)])  # stream, stream, tile
 def test_fp8_every_code_decodes_exactly(gpu_lib, D, ps):
     """One key per sequence: O is that key's V row times its descale, so every
     finite e4m3 code placed in V must come back exactly (vs = 1, the value is
@@ -190,7 +190,7 @@ def test_fp8_tile_path_key_descale_edges(gpu_lib, descale):
         check(o[1:], o_ref[1:], l[1:], l_ref[1:], what="other sequence")
 
 
-@pytest.mark.parametrize("D,ps", [(128, 64), (256, 32)])  # stream kernel, tile kernel
+@pytest.mark.parametrize("D,ps", [(128, 64), (256, 32), (256, 48)])  # stream, stream, tile
 def test_fp8_varlen_decode(gpu_lib, D, ps):
     """fp8 e4m3 cache with descales and three causal query tokens per
     sequence (packed by cu_seqlens_q): against the oracle's paged prefill over
