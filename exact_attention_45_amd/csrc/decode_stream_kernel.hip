@@ -1,6 +1,6 @@
 // Split-KV decode over a paged K/V cache: per-wave streaming variant, used
 // when every aligned 32-key slice lies inside one page (page_size a multiple
-// of 32), at every head dim (96 and 192 in the layouts of 128 and 256).
+// of 32), at every head dim (96 and 192 in the LDS layouts of 128 and 256).
 //
 // Same method as decode_kernel.hip (split-K decoding page, triton_splitk.py
 // `FwOp.apply`; interface page, the num_splits path of `_flash_attn_fwd`):
@@ -17,7 +17,8 @@
 //     it writes its normalised partial straight from registers. The waves
 //     never synchronise.
 //   * K and V of a slice are loaded into registers with 16-byte loads in row
-//     order (each instruction reads four whole 256-byte rows: measured on
+//     order, every lane a chunk of the cache (at D = 128 each instruction
+//     reads four whole 256-byte rows: measured on
 //     MI355X, reading a head's rows this way streams at ~6.5 TB/s, while the
 //     MFMA-fragment order, 32 rows x 32 bytes per instruction, manages ~3.9).
 //     Both go to a wave-private LDS slot just before use; K is read back as
@@ -55,15 +56,18 @@ namespace mi_attn {
 template <int D, int KV>
 struct StreamCfg {
   static constexpr bool FP8 = KV != 0;
-  // D = 96 and 192 run in the layouts of 128 and 256 (LDS rows, fragments,
-  // accumulators): the lanes of a row's padding columns load nothing and
-  // stage zeros, and only the first D output columns are written
+  // D = 96 and 192 keep LDS rows of 128 and 256 columns (the swizzles below
+  // permute chunks within 256-byte windows); their padding columns are never
+  // written or read: the loads cover only the cache's chunks, and the
+  // fragment reads only the first D columns
   static constexpr int DL = D == 192 ? 256 : (D == 96 ? 128 : D);
   // K/V register sets per wave. fp8 slices carry half the bytes, yet more
   // fp8 sets in flight measured slower on the B16 Sk32768 workload (split +
   // combine: 2 sets 86.0-87.3 us, 3 sets 87.3-88.5, 4 sets 101, 5 sets 115);
   // bf16 measured the same with 2 or 3. A bf16 set at D = 256 is 128
-  // registers (32 KB per slice), next to O's 128 and Q's 64: one set.
+  // registers (32 KB per slice), next to O's 128 and Q's 64: one set; at
+  // D = 192 a second set (96 registers) spilled and ran 43% slower. At D = 96
+  // a fourth set measured no faster than three.
   static constexpr int NS = DL == 256 ? 1 : (FP8 ? 2 : 3);
   static constexpr float RESCALE_LOG2 = 8.0f;   // lazy-rescale threshold
   static constexpr int SLICE = 32;              // keys per slice
@@ -71,9 +75,19 @@ struct StreamCfg {
   static constexpr int SLICE_B = SLICE * ROW_B; // bytes per K (or V) slice in LDS
   static constexpr int GROW_B = FP8 ? D : D * 2; // bytes per K/V row in the cache
   static constexpr int CPR = GROW_B / 16;       // 16-byte chunks per cache row
-  static constexpr int LPR = (FP8 ? DL : DL * 2) / 16;  // lanes per row of a load
-  static constexpr int RPL = 64 / LPR;          // rows per load instruction
-  static constexpr int NLD = SLICE / RPL;       // load instructions per tensor per slice
+  // loads: chunk f = 64 u + lane of the slice's SLICE x CPR chunks (row
+  // f / CPR, chunk f % CPR) for instruction u; CPR is even, so NLD
+  // instructions cover the slice exactly. The (row, chunk) pattern repeats
+  // every P instructions (the odd part of CPR) shifted by R rows.
+  static constexpr int NLD = SLICE * CPR / 64;  // load instructions per tensor per slice
+  static constexpr int P = CPR / (CPR & -CPR);
+  static constexpr int R = 64 / (CPR & -CPR);
+  // the K swizzle is a function of key bits 0..3, the V swizzle of bits
+  // 0..2: the staging addresses repeat every KP (VP) instructions, shifted by
+  // KROWS (VROWS) rows
+  static constexpr int KP = P * (R >= 16 ? 1 : 16 / R);
+  static constexpr int VP = P * (R >= 8 ? 1 : 8 / R);
+  static constexpr int KROWS = KP / P * R, VROWS = VP / P * R;
   static constexpr int SLOT_B = 4 * 2 * SLICE_B; // K and V slots of the four waves
   static constexpr int LDS_B = SLOT_B;
 };
@@ -109,7 +123,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   constexpr bool FP8 = KV != 0;
   using C = StreamCfg<D, KV>;
   constexpr int NS = C::NS, ROW_B = C::ROW_B, SLICE_B = C::SLICE_B, CPR = C::CPR;
-  constexpr int RPL = C::RPL, NLD = C::NLD, GROW_B = C::GROW_B, DL = C::DL, LPR = C::LPR;
+  constexpr int NLD = C::NLD, GROW_B = C::GROW_B, DL = C::DL, P = C::P, R = C::R;
+  constexpr int KP = C::KP, VP = C::VP;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_B];
 
   const int tid = threadIdx.x;
@@ -160,17 +175,16 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   // ---- this lane's query row (MFMA B operand)
   const bool valid = row.valid;
   const __bf16* qp = static_cast<const __bf16*>(a.q) + row.token * a.q_bs + (int64_t)row.hq * a.q_hs;
-  bf16x8 qf[DL / 16];
+  bf16x8 qf[D / 16];
 #pragma unroll
-  for (int cc = 0; cc < DL / 16; ++cc) {
-    const int e0 = 16 * cc + 8 * half;  // columns past D (layout padding) are zero
-    const bf16x8 x = as_bf16x8(ld16(qp + (e0 < D ? e0 : 0)));
-    qf[cc] = valid && e0 < D ? x : zero_bf16x8();
+  for (int cc = 0; cc < D / 16; ++cc) {
+    const bf16x8 x = as_bf16x8(ld16(qp + 16 * cc + 8 * half));
+    qf[cc] = valid ? x : zero_bf16x8();
   }
 
-  f32x16 o[DL / 32];
+  f32x16 o[D / 32];
 #pragma unroll
-  for (int i = 0; i < DL / 32; ++i) o[i] = zero_f32x16();
+  for (int i = 0; i < D / 32; ++i) o[i] = zero_f32x16();
   float m_run = kNegInf;
   float l_run = 0.0f;
   // fp8: the key descale joins the score scale, the value descale the output
@@ -195,13 +209,16 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)hk * GROW_B;
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)hk * GROW_B;
   const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
-  // loads: instruction u covers slice rows RPL*u .. +RPL-1, lane j row
-  // RPL*u + j / LPR at chunk j % LPR; a lane whose chunk lies past the row
-  // (D = 192) gets an offset past every descriptor's end, so its loads touch
-  // no memory and return zeros, which it stages as the layout's padding
-  const int ld_r = lane / LPR;
-  const int ld_c = lane % LPR;
-  const uint32_t ld_off = ld_c < CPR ? (uint32_t)(ld_r * ts2 + ld_c * 16) : 0x80000000u;
+  // loads: instruction u = P q + p reads chunk ld_c[p] of slice row
+  // ld_r[p] + R q (this lane's chunk f = 64 u + lane, see StreamCfg)
+  int ld_r[P], ld_c[P];
+  uint32_t ld_off[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    ld_r[p] = (64 * p + lane) / CPR;
+    ld_c[p] = (64 * p + lane) % CPR;
+    ld_off[p] = (uint32_t)(ld_r[p] * ts2 + ld_c[p] * 16);
+  }
   // K slot: chunk c of row r at position c ^ kswz(r), conflict-free for the
   // fragment reads (16 lanes read one logical chunk of 16 consecutive keys:
   // 16 distinct positions within a 256-byte bank window at D >= 128, whose
@@ -212,22 +229,21 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   };
   char* kslot = smem + wave * 2 * SLICE_B;
   char* vslot = kslot + SLICE_B;
-  // over the load instructions u (rows RPL*u + ld_r), kswz(row), a function
-  // of key bits 0..3, repeats with period KP and vswz(row, .) (bits 0..2)
-  // with period VP
-  constexpr int KP = RPL >= 16 ? 1 : 16 / RPL, VP = RPL >= 8 ? 1 : 8 / RPL;
+  // staging address of load u: k_st[u % KP] + (u / KP) KROWS rows, and
+  // v_st[u % VP] + (u / VP) VROWS rows
   int k_st[KP], v_st[VP];
 #pragma unroll
   for (int p = 0; p < KP; ++p) {
-    const int row = RPL * p + ld_r;
-    k_st[p] = row * ROW_B + ((ld_c ^ kswz(row)) * 16);
-    if (p < VP) v_st[p] = row * ROW_B + vswz<DL>(row, ld_c) * 16;
+    const int row = ld_r[p % P] + R * (p / P);
+    const int ch = ld_c[p % P];
+    k_st[p] = row * ROW_B + ((ch ^ kswz(row)) * 16);
+    if (p < VP) v_st[p] = row * ROW_B + vswz<DL>(row, ch) * 16;
   }
   const int fk = kswz(c32);
   // fragment cc reads chunk 2*cc + half; kswz only moves chunks within a
   // 256-byte window (16 chunks), so fragments cc and cc + 8 differ by 256
-  // bytes and eight address registers serve D = 256
-  constexpr int NKR = DL / 16 < 8 ? DL / 16 : 8;
+  // bytes and eight address registers serve D = 192 and 256
+  constexpr int NKR = D / 16 < 8 ? D / 16 : 8;
   int k_rd[NKR];
 #pragma unroll
   for (int cc = 0; cc < NKR; ++cc) k_rd[cc] = c32 * ROW_B + (((2 * cc + half) ^ fk) * 16);
@@ -251,8 +267,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
     const auto vr = make_rsrc(vbase + row0 * ts2, nrec);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      kreg[slot][u] = buf_ld16_nt(kr, ld_off + (uint32_t)(RPL * u * ts2));
-      vreg[slot][u] = buf_ld16_nt(vr, ld_off + (uint32_t)(RPL * u * ts2));
+      kreg[slot][u] = buf_ld16_nt(kr, ld_off[u % P] + (uint32_t)(R * (u / P) * ts2));
+      vreg[slot][u] = buf_ld16_nt(vr, ld_off[u % P] + (uint32_t)(R * (u / P) * ts2));
     }
   };
 
@@ -267,7 +283,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
   // and moves chunks within a 16-chunk window, so d-blocks db and db + 4
   // differ by 256 bytes: NVR address registers serve every (db, tt)
   const int v_key = 4 * half + tr_key;
-  constexpr int NVR = DL / 32 < 4 ? DL / 32 : 4;
+  constexpr int NVR = D / 32 < 4 ? D / 32 : 4;
   int v_rd[NVR];
 #pragma unroll
   for (int j = 0; j < NVR; ++j) v_rd[j] = v_key * ROW_B + vswz<DL>(v_key, 4 * j + tr_c) * 16 + tr_e;
@@ -280,15 +296,16 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
     if constexpr (!FP8) {
 #pragma unroll
       for (int u = 0; u < NLD; ++u) {
-        *reinterpret_cast<uint4*>(kslot + k_st[u % KP] + (u / KP) * KP * RPL * ROW_B) = kreg[slot][u];
-        *reinterpret_cast<uint4*>(vslot + v_st[u % VP] + (u / VP) * VP * RPL * ROW_B) = vreg[slot][u];
+        *reinterpret_cast<uint4*>(kslot + k_st[u % KP] + (u / KP) * C::KROWS * ROW_B) = kreg[slot][u];
+        *reinterpret_cast<uint4*>(vslot + v_st[u % VP] + (u / VP) * C::VROWS * ROW_B) = vreg[slot][u];
       }
     } else {
-      // 16 fp8 values = dims 16*ld_c .. +15 of row RPL*u + ld_r: bf16
-      // chunks 2*ld_c and 2*ld_c + 1 of that row, each at its swizzled place
+      // 16 fp8 values = dims 16 ch .. +15 of the load's row: bf16 chunks
+      // 2 ch and 2 ch + 1 of that row, each at its swizzled place
 #pragma unroll
       for (int u = 0; u < NLD; ++u) {
-        const int row = RPL * u + ld_r;
+        const int row = ld_r[u % P] + R * (u / P);
+        const int ch = ld_c[u % P];
         const uint4 kx = kreg[slot][u], vx = vreg[slot][u];
         const uint2 k0 = fp8x4_to_bf16x4<KV == 2>(kx.x), k1 = fp8x4_to_bf16x4<KV == 2>(kx.y);
         const uint2 k2 = fp8x4_to_bf16x4<KV == 2>(kx.z), k3 = fp8x4_to_bf16x4<KV == 2>(kx.w);
@@ -296,10 +313,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
         const uint2 v2 = fp8x4_to_bf16x4<KV == 2>(vx.z), v3 = fp8x4_to_bf16x4<KV == 2>(vx.w);
         char* kr = kslot + row * ROW_B;
         char* vr = vslot + row * ROW_B;
-        *reinterpret_cast<uint4*>(kr + (((2 * ld_c) ^ kswz(row)) * 16)) = make_uint4(k0.x, k0.y, k1.x, k1.y);
-        *reinterpret_cast<uint4*>(kr + (((2 * ld_c + 1) ^ kswz(row)) * 16)) = make_uint4(k2.x, k2.y, k3.x, k3.y);
-        *reinterpret_cast<uint4*>(vr + vswz<DL>(row, 2 * ld_c) * 16) = make_uint4(v0.x, v0.y, v1.x, v1.y);
-        *reinterpret_cast<uint4*>(vr + vswz<DL>(row, 2 * ld_c + 1) * 16) = make_uint4(v2.x, v2.y, v3.x, v3.y);
+        *reinterpret_cast<uint4*>(kr + (((2 * ch) ^ kswz(row)) * 16)) = make_uint4(k0.x, k0.y, k1.x, k1.y);
+        *reinterpret_cast<uint4*>(kr + (((2 * ch + 1) ^ kswz(row)) * 16)) = make_uint4(k2.x, k2.y, k3.x, k3.y);
+        *reinterpret_cast<uint4*>(vr + vswz<DL>(row, 2 * ch) * 16) = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        *reinterpret_cast<uint4*>(vr + vswz<DL>(row, 2 * ch + 1) * 16) = make_uint4(v2.x, v2.y, v3.x, v3.y);
       }
     }
   };
@@ -309,7 +326,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeArgs a) 
     const char* vs = vslot;
     f32x16 s = zero_f32x16();
 #pragma unroll
-    for (int cc = 0; cc < DL / 16; ++cc)
+    for (int cc = 0; cc < D / 16; ++cc)
       s = mfma32(*reinterpret_cast<const bf16x8*>(kslot + k_rd[cc % NKR] + (cc / NKR) * 256), qf[cc], s);
     if constexpr (SC) {
 #pragma unroll

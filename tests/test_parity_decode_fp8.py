@@ -58,7 +58,9 @@ CASES = [
     ("gqa32_heuristic_splits", 2, 32, 1, 128, 128, 8, 1, [1024, 333], 0, None, True),
     ("window_left", 2, 8, 2, 128, 256, 4, 0, [900, 300], 3, 150, True),
     ("empty_and_tiny", 4, 8, 2, 64, 64, 3, 0, [0, 1, 64, 65], 8, None, True),
-    # the streaming kernel at head dims 192 (in the width of 256) and 256
+    # the streaming kernel at head dims 96, 192 (LDS rows of 128 and 256
+    # columns, loads spread over the cache's chunks only) and 256
+    ("stream_d96_page32_ragged", 3, 8, 2, 96, 32, 12, 1, [1, 370, 129], 5, None, True),
     ("stream_d256_page32", 2, 8, 2, 256, 32, 9, 1, [288, 100], 5, None, True),
     ("stream_d192_page64_gqa8", 2, 16, 2, 192, 64, 6, 1, [350, 130], 4, None, True),
     # the tile kernel: page sizes that are not multiples of 32
@@ -99,7 +101,7 @@ def test_e5m2_decode_elementwise(gpu_lib, case):
     print(name, check(host_f64(out), o_ref, host_f64(lse), l_ref, what=name))
 
 
-@pytest.mark.parametrize("D,ps", [(128, 64), (256, 64), (96, 48), (256, 48)])  # stream, stream, tile, tile
+@pytest.mark.parametrize("D,ps", [(128, 64), (256, 64), (96, 64), (96, 48), (256, 48)])  # 3 stream, 2 tile
 def test_e5m2_every_finite_code_decodes_exactly(gpu_lib, D, ps):
     """As the e4m3 case below for e5m2: each of its 248 finite codes placed in
     V comes back exactly (every e5m2 value is a bf16 value)."""
@@ -128,7 +130,7 @@ def test_fp8_mixed_formats_rejected(gpu_lib):
     assert e.value.code == gpu_lib.MI_ATTN_EINVAL
 
 
-@pytest.mark.parametrize("D,ps", [(128, 64), (256, 64), (192, 16)])  # stream, stream, tile
+@pytest.mark.parametrize("D,ps", [(128, 64), (256, 64), (192, 64), (192, 16)])  # 3 stream, tile
 def test_fp8_every_code_decodes_exactly(gpu_lib, D, ps):
     """One key per sequence: O is that key's V row times its descale, so every
     finite e4m3 code placed in V must come back exactly (vs = 1, the value is
