@@ -69,13 +69,17 @@ def test_softcap_prefill_varlen_and_paged(gpu_lib):
 
 
 DECODE = [
-    # (name, D, page_size, kv) -- stream kernel (bf16, fp8) and the tile kernel (page 48,
-    # D256, fp8 at D256)
+    # (name, D, page_size, kv) -- the streaming kernel (page sizes that are multiples
+    # of 32) and the tile kernel (other page sizes)
     ("stream_bf16_d128", 128, 64, "bf16"),
     ("stream_fp8_d128", 128, 256, "fp8_e4m3"),
+    ("stream_d256", 256, 64, "bf16"),
+    ("stream_fp8_d256", 256, 64, "fp8_e4m3"),
+    ("stream_d96", 96, 32, "bf16"),
+    ("stream_fp8_d192", 192, 64, "fp8_e4m3"),
     ("tile_page48_d128", 128, 48, "bf16"),
-    ("tile_d256", 256, 64, "bf16"),
-    ("tile_fp8_d256", 256, 64, "fp8_e4m3"),
+    ("tile_page48_d256", 256, 48, "bf16"),
+    ("tile_fp8_page16_d192", 192, 16, "fp8_e4m3"),
 ]
 
 
@@ -85,7 +89,7 @@ def test_softcap_decode(gpu_lib, case):
     print(f"[case] softcap decode {name}", flush=True)
     seed = zlib.crc32(name.encode()) % 10000
     B, Hq, Hkv, pps = 3, 16, 2, 6
-    used = [1, 200, ps * pps]
+    used = [1, min(200, ps * pps - 5), ps * pps]  # ragged, within the pages' capacity
     if kv == "bf16":
         w = W.paged_decode_case(seed, B, Hq, Hkv, D, ps, pps, seqused_k=used, num_splits=3)
         kc, vc = dev_bf16(w.k), dev_bf16(w.v)
