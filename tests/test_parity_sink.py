@@ -66,9 +66,11 @@ def test_sink_varlen_and_paged(gpu_lib):
     check(host_f64(out), o_ref, host_f64(lse), l_ref, what="paged")
 
 
+@pytest.mark.parametrize("D,ps,pps", [(128, 256, 4), (96, 64, 16), (192, 32, 32), (256, 48, 21)],
+                         ids=["stream_d128", "stream_d96", "stream_d192", "tile_d256_page48"])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_sink_decode(gpu_lib, fp8):
-    B, Hq, Hkv, D, ps, pps = 3, 16, 2, 128, 256, 4
+def test_sink_decode(gpu_lib, fp8, D, ps, pps):
+    B, Hq, Hkv = 3, 16, 2
     sk = sink_bits(80, Hq)
     if fp8:
         w = W.paged_decode_fp8_case(81, B, Hq, Hkv, D, ps, pps, seqused_k=[1000, 1, 513],
