@@ -192,7 +192,7 @@ def test_fp8_tile_path_key_descale_edges(gpu_lib, descale):
         check(o[1:], o_ref[1:], l[1:], l_ref[1:], what="other sequence")
 
 
-@pytest.mark.parametrize("D,ps", [(128, 64), (256, 32), (256, 48)])  # stream, stream, tile
+@pytest.mark.parametrize("D,ps", [(128, 64), (256, 32), (96, 32), (192, 64), (256, 48)])  # 4 stream, tile
 def test_fp8_varlen_decode(gpu_lib, D, ps):
     """fp8 e4m3 cache with descales and three causal query tokens per
     sequence (packed by cu_seqlens_q): against the oracle's paged prefill over
